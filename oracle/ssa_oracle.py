@@ -1,0 +1,280 @@
+"""CPU oracle for the SSA per-layer attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this
+module.  The product path (the HIP library and its Python binding) never calls it and
+shares no code with it; the only thing both sides share is the seeded input generator
+in `workloads.py`, which holds none of the method's arithmetic.
+
+Everything here is plain numpy in float64, computed from the exact values of the same
+bf16 / fp32 inputs the GPU receives.  Each function follows a passage of Shen et al.,
+"SSA: Sparse Sparse Attention by Aligning Full and Sparse Attention Outputs in Feature
+Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
+
+  block_pool            sec. 3 (p. 4): contiguous blocks of s tokens, one mean-pooled
+                        key per block.
+  block_topk            sec. 3 (p. 4) and App. D (p. 21): each query scores the blocks
+                        that precede its own with the pooled keys and keeps the top-k
+                        blocks; its own block is always kept and counts toward k.
+  attend_full           sec. 3 (p. 3): causal softmax attention over every preceding
+                        token (and the token itself).
+  attend_sparse         sec. 3 (p. 4): softmax attention over the tokens of the kept
+                        blocks (the "reduced K and V"), causal inside the own block.
+  attend_sparse_gather  the same quantity formed per query by gathering the kept
+                        blocks' keys and values (a second route used as a pin).
+  dropped_mass          App. B (p. 19) and sec. 4.2 (p. 6): the full-attention
+                        probability mass on tokens the sparse stream does not attend.
+  align_stats           sec. 5 (pp. 6-7): per-token comparison of the two streams'
+                        outputs (Euclidean distance) and the dropped mass obtained from
+                        the two log-sum-exps.
+
+Readings where the pages are silent (listed in full in the design notes):
+  * candidates are the blocks strictly before the query's block; the own block is
+    always attended (causal inside) and counts toward k;
+  * fewer candidates than k-1: all of them are kept;
+  * the block score is the raw dot product q . mean(K_block) (no scale, no softmax);
+  * ties in score go to the lower block index;
+  * selected blocks are listed in ascending order, -1 pads unused slots;
+  * the softmax scale is an explicit argument (1/sqrt(D) in every workload);
+  * the alignment distance is the Euclidean (not squared) L2 norm over the head dim.
+
+Every function here is pinned by the CPU tests in tests/test_oracle_pins.py (brute
+force on tiny inputs, closed forms, identities, special cases); none is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "block_pool", "block_scores", "block_topk", "attend_full", "attend_sparse",
+    "attend_sparse_gather", "dropped_mass", "align_stats", "attended_blocks",
+    "attended_count",
+]
+
+
+def _rows(L: int, rows) -> np.ndarray:
+    return np.arange(L, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------
+# sec. 3: block partition and mean-pooled keys
+# ----------------------------------------------------------------------------------
+def block_pool(k: np.ndarray, s: int) -> np.ndarray:
+    """Mean of each contiguous block of s keys: [B,H,L,D] -> [B,H,L//s,D] (float64)."""
+    B, H, L, D = k.shape
+    if L % s:
+        raise ValueError("L must be a multiple of the block size")
+    return np.asarray(k, dtype=np.float64).reshape(B, H, L // s, s, D).mean(axis=3)
+
+
+def block_scores(q_rows: np.ndarray, k_mean_bh: np.ndarray) -> np.ndarray:
+    """Raw block scores q_t . kbar_j for the given query rows of one (b, h): [R, n]."""
+    return np.asarray(q_rows, dtype=np.float64) @ np.asarray(k_mean_bh, dtype=np.float64).T
+
+
+# ----------------------------------------------------------------------------------
+# sec. 3 / App. D: per-query top-k over the preceding blocks
+# ----------------------------------------------------------------------------------
+def block_topk(q: np.ndarray, k_mean: np.ndarray, s: int, topk: int, rows=None,
+               return_scores: bool = False):
+    """Selected blocks per query row.
+
+    For the query at position t (block b_t = t // s): score every block j < b_t by
+    q_t . kbar_j, order the candidates by (score descending, index ascending), keep the
+    first min(topk - 1, b_t), add b_t, and list them in ascending order padded with -1
+    to width topk.
+
+    Returns idx [B,H,R,topk] int32 and, if return_scores, a dict with
+      "sigma_m":  the score of the last kept candidate (m-th largest, m = topk-1),
+      "sigma_m1": the score of the best candidate left out ((m+1)-th largest),
+    both [B,H,R] float64 (NaN where that candidate does not exist), and
+      "scores":   [B,H,R,topk] float64 scores of the listed blocks (+inf for b_t,
+                  -inf for padding).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    n = L // s
+    R = _rows(L, rows)
+    if not 1 <= topk <= n:
+        raise ValueError("topk must be in [1, n]")
+    idx = np.full((B, H, len(R), topk), -1, dtype=np.int32)
+    sig_m = np.full((B, H, len(R)), np.nan)
+    sig_m1 = np.full((B, H, len(R)), np.nan)
+    sel_sc = np.full((B, H, len(R), topk), -np.inf)
+    blocks_of_rows = R // s
+    for b in range(B):
+        for h in range(H):
+            for qb in np.unique(blocks_of_rows):
+                pos = np.nonzero(blocks_of_rows == qb)[0]
+                m = min(topk - 1, int(qb))
+                if qb > 0:
+                    sc = block_scores(q[b, h, R[pos]], k_mean[b, h, :qb])     # [r, qb]
+                    # stable sort on -score keeps equal scores in ascending block order
+                    order = np.argsort(-sc, axis=1, kind="stable")
+                    kept = np.sort(order[:, :m], axis=1)
+                    if m > 0:
+                        sig_m[b, h, pos] = np.take_along_axis(sc, order[:, m - 1:m], 1)[:, 0]
+                    if m < qb:
+                        sig_m1[b, h, pos] = np.take_along_axis(sc, order[:, m:m + 1], 1)[:, 0]
+                    idx[b, h, pos, :m] = kept
+                    sel_sc[b, h, pos, :m] = np.take_along_axis(sc, kept, 1)
+                idx[b, h, pos, m] = qb
+                sel_sc[b, h, pos, m] = np.inf
+    if return_scores:
+        return idx, {"sigma_m": sig_m, "sigma_m1": sig_m1, "scores": sel_sc}
+    return idx
+
+
+# ----------------------------------------------------------------------------------
+# sec. 3: attended key set of the sparse stream
+# ----------------------------------------------------------------------------------
+def attended_blocks(idx_row: np.ndarray, t: int, s: int) -> list:
+    """Blocks the sparse stream attends for the query at t: its own block b_t plus the
+    listed blocks below it (-1 and out-of-range entries are not blocks)."""
+    bt = t // s
+    listed = {int(j) for j in np.asarray(idx_row).ravel() if 0 <= int(j) < bt}
+    return sorted(listed | {bt})
+
+
+def attended_count(t: int, s: int, topk: int) -> int:
+    """|A(t)| for a full selection: t+1 while b_t < topk, else (topk-1)*s + t%s + 1."""
+    bt = t // s
+    return t + 1 if bt < topk else (topk - 1) * s + (t % s) + 1
+
+
+def _sparse_key_mask(idx_rows: np.ndarray, R: np.ndarray, s: int, nkeys: int) -> np.ndarray:
+    """[r, nkeys] boolean: key i attended by row R[a] (i <= t and block(i) attended)."""
+    r = len(R)
+    n_blk = (nkeys + s - 1) // s
+    bt = R // s
+    blk = np.zeros((r, n_blk + 1), dtype=bool)
+    ids = np.asarray(idx_rows, dtype=np.int64)
+    valid = (ids >= 0) & (ids < bt[:, None])
+    rr = np.repeat(np.arange(r)[:, None], ids.shape[1], axis=1)
+    blk[rr[valid], ids[valid]] = True
+    blk[np.arange(r), bt] = True
+    keys = np.arange(nkeys)
+    mask = blk[:, keys // s] & (keys[None, :] <= R[:, None])
+    return mask
+
+
+def _masked_softmax_attend(logits: np.ndarray, mask: np.ndarray, v: np.ndarray):
+    lg = np.where(mask, logits, -np.inf)
+    m = lg.max(axis=1, keepdims=True)
+    e = np.exp(lg - m)
+    l = e.sum(axis=1, keepdims=True)
+    o = (e @ v) / l
+    lse = (m + np.log(l))[:, 0]
+    return o, lse, e / l
+
+
+# ----------------------------------------------------------------------------------
+# sec. 3: full causal attention
+# ----------------------------------------------------------------------------------
+def attend_full(q, k, v, scale: float, rows=None, want_o: bool = True):
+    """o_f(t) = sum_{i<=t} softmax_i(scale q_t.k_i) v_i and lse_f(t) = log sum_{i<=t}
+    exp(scale q_t.k_i), for the given rows.  Returns (o [B,H,R,D] or None, lse [B,H,R])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    R = _rows(L, rows)
+    nk = int(R.max()) + 1
+    o = np.zeros((B, H, len(R), D)) if want_o else None
+    lse = np.zeros((B, H, len(R)))
+    keys = np.arange(nk)
+    mask = keys[None, :] <= R[:, None]
+    for b in range(B):
+        for h in range(H):
+            kk = np.asarray(k[b, h, :nk], dtype=np.float64)
+            vv = np.asarray(v[b, h, :nk], dtype=np.float64)
+            logits = scale * (q[b, h, R] @ kk.T)
+            ob, lb, _ = _masked_softmax_attend(logits, mask, vv)
+            if want_o:
+                o[b, h] = ob
+            lse[b, h] = lb
+    return o, lse
+
+
+# ----------------------------------------------------------------------------------
+# sec. 3: sparse attention over the kept blocks (masked-dense route)
+# ----------------------------------------------------------------------------------
+def attend_sparse(q, k, v, idx, s: int, scale: float, rows=None):
+    """o_s(t) = sum_{i in A(t)} softmax_i(scale q_t.k_i) v_i, lse_s(t) = log sum_{i in A(t)}
+    exp(scale q_t.k_i), with A(t) = {i <= t : i // s attended}.  `idx` is [B,H,R,topk]
+    for the same rows.  Returns (o [B,H,R,D], lse [B,H,R])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    R = _rows(L, rows)
+    nk = int(R.max()) + 1
+    o = np.zeros((B, H, len(R), D))
+    lse = np.zeros((B, H, len(R)))
+    for b in range(B):
+        for h in range(H):
+            kk = np.asarray(k[b, h, :nk], dtype=np.float64)
+            vv = np.asarray(v[b, h, :nk], dtype=np.float64)
+            mask = _sparse_key_mask(idx[b, h], R, s, nk)
+            logits = scale * (q[b, h, R] @ kk.T)
+            o[b, h], lse[b, h], _ = _masked_softmax_attend(logits, mask, vv)
+    return o, lse
+
+
+def attend_sparse_gather(q, k, v, idx, s: int, scale: float, rows=None):
+    """Same quantity as attend_sparse, formed per query: gather the keys and values of
+    the attended blocks (keys <= t), softmax over the gathered logits."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    R = _rows(L, rows)
+    o = np.zeros((B, H, len(R), D))
+    lse = np.zeros((B, H, len(R)))
+    for b in range(B):
+        for h in range(H):
+            for a, t in enumerate(R):
+                blocks = attended_blocks(idx[b, h, a], int(t), s)
+                keys = np.concatenate([np.arange(j * s, min(j * s + s, t + 1)) for j in blocks])
+                kk = np.asarray(k[b, h, keys], dtype=np.float64)
+                vv = np.asarray(v[b, h, keys], dtype=np.float64)
+                lg = scale * (kk @ q[b, h, t])
+                m = lg.max()
+                e = np.exp(lg - m)
+                o[b, h, a] = (e @ vv) / e.sum()
+                lse[b, h, a] = m + np.log(e.sum())
+    return o, lse
+
+
+# ----------------------------------------------------------------------------------
+# App. B / sec. 4.2: dropped attention mass, summed from the full probabilities
+# ----------------------------------------------------------------------------------
+def dropped_mass(q, k, idx, s: int, scale: float, rows=None):
+    """delta(t) = sum over i <= t with i not in A(t) of the full causal attention
+    probability p_f(t, i).  Summed directly (not through log-sum-exps)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    R = _rows(L, rows)
+    nk = int(R.max()) + 1
+    out = np.zeros((B, H, len(R)))
+    keys = np.arange(nk)
+    causal = keys[None, :] <= R[:, None]
+    for b in range(B):
+        for h in range(H):
+            kk = np.asarray(k[b, h, :nk], dtype=np.float64)
+            logits = scale * (q[b, h, R] @ kk.T)
+            _, _, p = _masked_softmax_attend(logits, causal, np.zeros((nk, 1)))
+            keep = _sparse_key_mask(idx[b, h], R, s, nk)
+            out[b, h] = np.where(causal & ~keep, p, 0.0).sum(axis=1)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# sec. 5: per-token comparison of the two streams
+# ----------------------------------------------------------------------------------
+def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None):
+    """dist(t) = ||o_f(t) - o_s(t)||_2 over the head dim, and
+    dropped(t) = 1 - exp(lse_s(t) - lse_f(t)) = -expm1(lse_s - lse_f), clipped to [0, 1].
+    Either pair may be None (then that output is None)."""
+    dist = dropped = None
+    if o_full is not None and o_sparse is not None:
+        d = np.asarray(o_full, dtype=np.float64) - np.asarray(o_sparse, dtype=np.float64)
+        dist = np.sqrt((d * d).sum(axis=-1))
+    if lse_full is not None and lse_sparse is not None:
+        x = np.asarray(lse_sparse, dtype=np.float64) - np.asarray(lse_full, dtype=np.float64)
+        dropped = np.clip(-np.expm1(x), 0.0, 1.0)
+    return dist, dropped
