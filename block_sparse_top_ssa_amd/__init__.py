@@ -1,0 +1,140 @@
+"""SSA attention forward on MI355X: Python binding of libssa.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+libssa.so, called through its C ABI (include/ssa.h).  PyTorch provides device memory
+and the stream: each call enqueues on torch's current stream and does not synchronise.
+
+    k_mean = block_pool(k, block)
+    idx = block_topk(q, k_mean, block, topk)
+    o_s, lse_s = sparse_attn_fwd(q, k, v, idx, block)
+    o_f, lse_f = full_attn_fwd(q, k, v)
+    dist, dropped = align_stats(o_f, o_s, lse_f, lse_s)
+
+There is no fallback: if libssa.so is missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
+
+__all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
+           "set_kernel_variant", "SSAError", "lib", "abi_version"]
+
+
+def lib():
+    return load()
+
+
+def abi_version() -> int:
+    return int(load().ssa_abi_version())
+
+
+def set_kernel_variant(variant: int) -> int:
+    """0: MFMA kernels where they apply (default); 1: portable kernels only."""
+    return int(load().ssa_set_kernel_variant(int(variant)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSA_BF16
+    if t.dtype == torch.float32:
+        return SSA_F32
+    raise SSAError(3, f"unsupported tensor dtype {t.dtype}")
+
+
+def _dims(x: torch.Tensor, block: int) -> Dims:
+    if x.dim() != 4:
+        raise SSAError(2, "expected a [B, H, L, D] tensor")
+    B, H, L, D = x.shape
+    return Dims(B, H, L, D, int(block), _dtype_code(x))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise SSAError(4, "tensors must be contiguous device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _same(a: torch.Tensor, b: torch.Tensor, what: str):
+    if a.shape != b.shape or a.dtype != b.dtype:
+        raise SSAError(2, f"{what}: shape/dtype mismatch {tuple(a.shape)}/{a.dtype} vs {tuple(b.shape)}/{b.dtype}")
+
+
+def block_pool(k: torch.Tensor, block: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    d = _dims(k, block)
+    if out is None:
+        out = torch.empty((d.B, d.H, d.L // d.block, d.D), dtype=torch.float32, device=k.device)
+    check(load().ssa_block_pool(ctypes.byref(d), _ptr(k), _ptr(out), _stream(k)))
+    return out
+
+
+def block_topk(q: torch.Tensor, k_mean: torch.Tensor, block: int, topk: int, want_scores: bool = False,
+               out: torch.Tensor | None = None):
+    d = _dims(q, block)
+    if out is None:
+        out = torch.empty((d.B, d.H, d.L, topk), dtype=torch.int32, device=q.device)
+    sel = torch.empty((d.B, d.H, d.L, topk), dtype=torch.float32, device=q.device) if want_scores else None
+    check(load().ssa_block_topk(ctypes.byref(d), _ptr(q), _ptr(k_mean), int(topk), _ptr(out), _ptr(sel),
+                                _stream(q)))
+    return (out, sel) if want_scores else out
+
+
+def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    _same(q, k, "q/k")
+    _same(q, v, "q/v")
+    d = _dims(q, block)
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
+        raise SSAError(2, "idx must be int32 [B, H, L, topk]")
+    topk = idx.shape[3]
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
+    check(load().ssa_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(topk),
+                                     ctypes.c_float(scale), _ptr(out), _ptr(lse if want_lse else None),
+                                     _stream(q)))
+    return out, (lse if want_lse else None)
+
+
+def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
+                  block: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    _same(q, k, "q/k")
+    _same(q, v, "q/v")
+    d = _dims(q, block)
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    if want_o and out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
+    check(load().ssa_full_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale),
+                                   _ptr(out if want_o else None), _ptr(lse if want_lse else None),
+                                   _stream(q)))
+    return (out if want_o else None), (lse if want_lse else None)
+
+
+def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, block: int = 64,
+                dims_like: torch.Tensor | None = None):
+    """Per-token L2 distance (needs the o pair) and dropped mass (needs the lse pair)."""
+    ref = o_full if o_full is not None else dims_like
+    if ref is None:
+        raise SSAError(1, "align_stats needs o_full or dims_like to know [B, H, L, D]")
+    if o_full is not None:
+        _same(o_full, o_sparse, "o_full/o_sparse")
+    d = _dims(ref, block)
+    dist = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if o_full is not None else None
+    drop = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if lse_full is not None else None
+    check(load().ssa_align_stats(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
+                                 _ptr(lse_sparse), _ptr(dist), _ptr(drop), _stream(ref)))
+    return dist, drop

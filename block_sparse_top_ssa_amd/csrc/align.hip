@@ -1,0 +1,74 @@
+// Per-token comparison of the two streams.
+//   dist(t)    = ||o_full(t) - o_sparse(t)||_2 over the head dim (paper sec. 5, pp. 6-7:
+//                the counterpart outputs are compared at every layer);
+//   dropped(t) = clamp(-expm1(lse_sparse(t) - lse_full(t)), 0, 1): the full-attention mass
+//                on tokens the sparse stream leaves out (App. B p. 19, sec. 4.2 p. 6),
+//                since exp(lse_s - lse_f) is the full-attention mass the sparse set keeps.
+// HBM-bound streaming reduction: a row of D elements is D/E lanes wide (E elements per
+// 16-byte load); each wave handles 64/(D/E) tokens per step and loops over 4 steps.
+#include "launch.hpp"
+
+namespace ssa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void align_kernel(const T* __restrict__ of, const T* __restrict__ os,
+                                                    const float* __restrict__ lf, const float* __restrict__ ls,
+                                                    float* __restrict__ dist, float* __restrict__ drop,
+                                                    int64_t ntok) {
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  constexpr int TPW = kWave / LPR;  // tokens per wave step
+  constexpr int STEPS = 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * (TPW * STEPS);
+  const int c = lane % LPR;
+#pragma unroll
+  for (int u = 0; u < STEPS; ++u) {
+    const int64_t tok = first + u * TPW + lane / LPR;
+    const bool ok = tok < ntok;
+    if (dist) {
+      float acc = 0.f;
+      if (ok) {
+        float a[E], b[E];
+        Elem<T>::unpack(load16(of + tok * D + c * E), a);
+        Elem<T>::unpack(load16(os + tok * D + c * E), b);
+#pragma unroll
+        for (int e = 0; e < E; ++e) { const float df = a[e] - b[e]; acc = fmaf(df, df, acc); }
+      }
+#pragma unroll
+      for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o);
+      if (ok && c == 0) dist[tok] = sqrtf(acc);
+    }
+    if (drop && ok && c == 0) {
+      const float x = ls[tok] - lf[tok];
+      drop[tok] = fminf(fmaxf(-expm1f(x), 0.f), 1.f);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t run_align(const Dims& d, const void* of, const void* os, const float* lf, const float* ls,
+                            float* dist, float* drop, hipStream_t st) {
+  constexpr int LPR = D / Elem<T>::kPer16B;
+  const int64_t per_block = 4 * (kWave / LPR) * 4;
+  const int64_t ntok = d.tokens();
+  const int64_t grid = (ntok + per_block - 1) / per_block;
+  hipLaunchKernelGGL((align_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const T*>(of),
+                     static_cast<const T*>(os), lf, ls, dist, drop, ntok);
+  return hipGetLastError();
+}
+
+LaunchResult launch_align(const Dims& d, const void* of, const void* os, const float* lf, const float* ls,
+                          float* dist, float* drop, hipStream_t st) {
+  LaunchResult r;
+  if (d.dtype == 1)
+    r.err = d.D == 128 ? run_align<uint16_t, 128>(d, of, os, lf, ls, dist, drop, st)
+                       : run_align<uint16_t, 64>(d, of, os, lf, ls, dist, drop, st);
+  else
+    r.err = d.D == 128 ? run_align<float, 128>(d, of, os, lf, ls, dist, drop, st)
+                       : run_align<float, 64>(d, of, os, lf, ls, dist, drop, st);
+  return r;
+}
+
+}  // namespace ssa

@@ -1,0 +1,204 @@
+// C ABI of libssa: argument checks, device check, kernel choice, launch on the
+// caller's stream.  Declared and documented in include/ssa.h.
+#include <atomic>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/ssa.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+std::atomic<int32_t> g_variant{0};
+
+ssa_status fail(ssa_status code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ssa_status fail(ssa_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// Per-device "is gfx950" cache, filled once per device.
+constexpr int kMaxDevices = 64;
+std::atomic<int8_t> g_dev_ok[kMaxDevices];  // 0 unknown, 1 ok, -1 not gfx950
+std::mutex g_dev_mu;
+
+ssa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(SSA_ERR_DEVICE, "no HIP device: %s", hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(SSA_ERR_DEVICE, "device index %d out of range", dev);
+  int8_t st = g_dev_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    st = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(SSA_ERR_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+      st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+      g_dev_ok[dev].store(st, std::memory_order_release);
+    }
+  }
+  if (st != 1) return fail(SSA_ERR_DEVICE, "device %d is not gfx950 (MI355X)", dev);
+  return SSA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ssa_status check_dims(const ssa_dims* d, ssa::Dims* out) {
+  if (!d) return fail(SSA_ERR_NULL, "dims is NULL");
+  if (d->dtype != SSA_F32 && d->dtype != SSA_BF16) return fail(SSA_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->B < 1 || d->H < 1 || d->L < 1) return fail(SSA_ERR_SHAPE, "B, H, L must be >= 1 (got %d, %d, %d)", d->B, d->H, d->L);
+  if (d->D != 64 && d->D != 128) return fail(SSA_ERR_SHAPE, "head dim D must be 64 or 128 (got %d)", d->D);
+  if (d->block != 64 && d->block != 128) return fail(SSA_ERR_SHAPE, "block size must be 64 or 128 (got %d)", d->block);
+  if (d->L % d->block) return fail(SSA_ERR_SHAPE, "L=%d is not a multiple of the block size %d", d->L, d->block);
+  const int64_t tokens = (int64_t)d->B * d->H * d->L;
+  if (tokens > (int64_t(1) << 24)) return fail(SSA_ERR_SHAPE, "B*H*L=%lld exceeds 2^24", (long long)tokens);
+  *out = ssa::Dims{d->B, d->H, d->L, d->D, d->block, d->dtype};
+  return SSA_OK;
+}
+
+ssa_status check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(SSA_ERR_NULL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(SSA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", name, align);
+  return SSA_OK;
+}
+
+ssa_status check_opt_ptr(const void* p, const char* name, size_t align) {
+  if (p && !aligned(p, align)) return fail(SSA_ERR_UNSUPPORTED, "%s is not %zu-byte aligned", name, align);
+  return SSA_OK;
+}
+
+ssa_status check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f)) return fail(SSA_ERR_UNSUPPORTED, "scale must be finite and > 0");
+  return SSA_OK;
+}
+
+ssa_status finish(const ssa::LaunchResult& r, const char* what) {
+  if (r.unsupported) return fail(SSA_ERR_UNSUPPORTED, "%s: %s", what, r.unsupported);
+  if (r.err != hipSuccess) return fail(SSA_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(r.err));
+  g_last_error[0] = '\0';
+  return SSA_OK;
+}
+
+#define SSA_TRY(expr)              \
+  do {                             \
+    ssa_status _s = (expr);        \
+    if (_s != SSA_OK) return _s;   \
+  } while (0)
+
+bool use_mfma() { return g_variant.load(std::memory_order_relaxed) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_block_pool(const ssa_dims* dims, const void* k, float* k_mean, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(k_mean, "k_mean", 16));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_pool(d, k, k_mean, (hipStream_t)stream), "ssa_block_pool");
+}
+
+ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_mean, int32_t topk, int32_t* idx,
+                          float* sel_score, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k_mean, "k_mean", 16));
+  SSA_TRY(check_ptr(idx, "idx", 4));
+  SSA_TRY(check_opt_ptr(sel_score, "sel_score", 4));
+  if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::topk_mfma_supported(d, topk))
+    return finish(ssa::launch_topk_mfma(d, q, k_mean, topk, idx, sel_score, st), "ssa_block_topk");
+  return finish(ssa::launch_topk_generic(d, q, k_mean, topk, idx, sel_score, st), "ssa_block_topk");
+}
+
+ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,
+                               int32_t topk, float scale, void* o, float* lse, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(v, "v", 16));
+  SSA_TRY(check_ptr(idx, "idx", 4));
+  SSA_TRY(check_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::sparse_mfma_supported(d, topk))
+    return finish(ssa::launch_sparse_mfma(d, q, k, v, idx, topk, scale, o, lse, st), "ssa_sparse_attn_fwd");
+  return finish(ssa::launch_sparse_generic(d, q, k, v, idx, topk, scale, o, lse, st), "ssa_sparse_attn_fwd");
+}
+
+ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, float scale, void* o,
+                             float* lse, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(v, "v", 16));
+  if (!o && !lse) return fail(SSA_ERR_NULL, "ssa_full_attn_fwd needs o or lse");
+  SSA_TRY(check_opt_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::full_mfma_supported(d))
+    return finish(ssa::launch_full_mfma(d, q, k, v, scale, o, lse, st), "ssa_full_attn_fwd");
+  return finish(ssa::launch_full_generic(d, q, k, v, scale, o, lse, st), "ssa_full_attn_fwd");
+}
+
+ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void* o_sparse, const float* lse_full,
+                           const float* lse_sparse, float* l2_dist, float* dropped, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  if (!l2_dist && !dropped) return fail(SSA_ERR_NULL, "ssa_align_stats needs l2_dist or dropped");
+  if (l2_dist) {
+    SSA_TRY(check_ptr(o_full, "o_full", 16));
+    SSA_TRY(check_ptr(o_sparse, "o_sparse", 16));
+    SSA_TRY(check_ptr(l2_dist, "l2_dist", 4));
+  }
+  if (dropped) {
+    SSA_TRY(check_ptr(lse_full, "lse_full", 4));
+    SSA_TRY(check_ptr(lse_sparse, "lse_sparse", 4));
+    SSA_TRY(check_ptr(dropped, "dropped", 4));
+  }
+  SSA_TRY(check_device());
+  return finish(ssa::launch_align(d, o_full, o_sparse, lse_full, lse_sparse, l2_dist, dropped, (hipStream_t)stream),
+                "ssa_align_stats");
+}
+
+const char* ssa_status_str(ssa_status s) {
+  switch (s) {
+    case SSA_OK: return "SSA_OK";
+    case SSA_ERR_NULL: return "SSA_ERR_NULL";
+    case SSA_ERR_SHAPE: return "SSA_ERR_SHAPE";
+    case SSA_ERR_DTYPE: return "SSA_ERR_DTYPE";
+    case SSA_ERR_UNSUPPORTED: return "SSA_ERR_UNSUPPORTED";
+    case SSA_ERR_DEVICE: return "SSA_ERR_DEVICE";
+    case SSA_ERR_LAUNCH: return "SSA_ERR_LAUNCH";
+    default: return "SSA_ERR_UNKNOWN";
+  }
+}
+
+const char* ssa_last_error(void) { return g_last_error; }
+
+int32_t ssa_abi_version(void) { return SSA_ABI_VERSION; }
+
+int32_t ssa_set_kernel_variant(int32_t variant) { return g_variant.exchange(variant == 1 ? 1 : 0); }
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+// Dense causal attention forward (the full stream; paper sec. 3, p. 3: each query
+// attends to every preceding token), flash-style on MFMA bf16 with fp32 online softmax.
+//
+// Work split: a workgroup owns 256 consecutive query rows of one (b, h); each of its 4
+// waves owns 64 rows (4 column tiles of 16) and keeps their O^T accumulators, running
+// max and partial sums in registers for the whole sweep.  The workgroup sweeps 64-key
+// chunks from key 0 to its last row; chunk c+1 is loaded from HBM/L2 into registers
+// while chunk c is being used, then written to the other half of a double-buffered
+// LDS stage in MFMA-fragment order (K as is; V transposed in registers first), so
+// every wave reads its fragments with conflict-free 16-byte LDS reads.  A wave stops
+// at its own diagonal chunk, which is masked causally.
+// Grid order: the tiles with the most chunks first, heads innermost (B*H is usually a
+// multiple of 8, so each XCD keeps a fixed subset of heads and their K/V in its L2).
+// With o == NULL only the running max and sums are kept (log-sum-exp only).
+#include "launch.hpp"
+#include "mfma.hpp"
+
+namespace ssa {
+
+template <int D, bool WANT_O>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void full_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2) {
+  constexpr int NC = D / 32;   // contraction chunks of d for S^T
+  constexpr int NDT = D / 16;  // d tiles of O^T
+  constexpr int KF = 4 * NC;   // K fragments per 64-key chunk
+  constexpr int VF = 2 * NDT;  // V^T fragments per 64-key chunk
+  constexpr int KF_W = KF / 4, VF_W = VF / 4;  // fragments each wave loads
+  __shared__ u32x4 sk[2][KF][64];
+  __shared__ u32x4 sv[2][VF][64];
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int tile = ntile - 1 - (int)(blockIdx.x / BH);
+  const int64_t bh = blockIdx.x % BH;
+  const uint16_t* qh = q + bh * (int64_t)L * D;
+  const uint16_t* kh = k + bh * (int64_t)L * D;
+  const uint16_t* vh = v + bh * (int64_t)L * D;
+  const int r0 = tile * 256 + 64 * w;  // first row of this wave
+  const bool active = r0 < L;
+  const int cw = r0 / 64;               // this wave's diagonal chunk
+  const int cmax = min(tile * 4 + 3, L / 64 - 1);
+
+  u32x4 qf[4][NC];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+      qf[nt][cc] = active ? load_q_frag<D>(qh + (int64_t)(r0 + 16 * nt + n) * D, cc) : u32x4{0, 0, 0, 0};
+
+  f32x4 oacc[WANT_O ? NDT : 1][4];
+  float m[4], lsum[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    m[nt] = -__builtin_huge_valf();
+    lsum[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < (WANT_O ? NDT : 1); ++dt) oacc[dt][nt] = f32x4{0, 0, 0, 0};
+  }
+
+  u32x4 kreg[KF_W], vreg[VF_W];
+  auto issue_loads = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < KF_W; ++i) {
+      const int f = w * KF_W + i;
+      kreg[i] = load_k_frag<D>(kh, c * 64 + 16 * (f / NC), f % NC);
+    }
+    if (WANT_O) {
+#pragma unroll
+      for (int i = 0; i < VF_W; ++i) {
+        const int f = w * VF_W + i;
+        vreg[i] = load_v_raw<D>(vh, c * 64, f >> 1, f & 1);
+      }
+    }
+  };
+  auto stage_store = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < KF_W; ++i) sk[st][w * KF_W + i][lane] = kreg[i];
+    if (WANT_O) {
+#pragma unroll
+      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = transpose8x8_b16(vreg[i]);
+    }
+  };
+
+  issue_loads(0);
+  stage_store(0);
+  __syncthreads();
+
+  for (int c = 0; c <= cmax; ++c) {
+    const int st = c & 1;
+    const bool more = c + 1 <= cmax;
+    if (more) issue_loads(c + 1);
+    if (active && c <= cw) {
+      const bool diag = c == cw;
+      f32x4 sacc[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4 kf = sk[st][kt * NC + cc][lane];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
+        }
+      u32x4 pf[4][2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float sv2[16];
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[kt][nt][i] * sl2;
+            if (diag && (16 * kt + 4 * g + i > 16 * nt + n)) x = -__builtin_huge_valf();
+            sv2[kt * 4 + i] = x;
+            mx = fmaxf(mx, x);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[nt], mx);
+        const float alpha = exp2f(m[nt] - mnew);
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sv2[i] = exp2f(sv2[i] - mnew);
+          ps += sv2[i];
+        }
+        lsum[nt] = lsum[nt] * alpha + ps;
+        m[nt] = mnew;
+        if (WANT_O) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
+          pf[nt][0] = pack_p(&sv2[0], &sv2[4]);
+          pf[nt][1] = pack_p(&sv2[8], &sv2[12]);
+        }
+      }
+      if (WANT_O) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            const u32x4 vf = sv[st][dt * 2 + kc][lane];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
+          }
+      }
+    }
+    if (more) stage_store(st ^ 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    float l = lsum[nt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int row = r0 + 16 * nt + n;
+    if (WANT_O) {
+      const float inv = 1.f / l;
+      uint16_t* orow = o + (bh * (int64_t)L + row) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(oacc[dt][nt][0] * inv, oacc[dt][nt][1] * inv);
+        pk[1] = pack_bf16x2(oacc[dt][nt][2] * inv, oacc[dt][nt][3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * g) = pk;
+      }
+    }
+    if (lse && g == 0) lse[bh * (int64_t)L + row] = (m[nt] + log2f(l)) * kLn2;
+  }
+}
+
+bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 64 == 0; }
+
+template <int D, bool WANT_O>
+static hipError_t run_full(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
+                           float* lse, hipStream_t st) {
+  const int ntile = (d.L + 255) / 256;
+  const int64_t grid = (int64_t)ntile * d.bh();
+  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
+                              float* lse, hipStream_t st) {
+  LaunchResult r;
+  if (o)
+    r.err = d.D == 128 ? run_full<128, true>(d, q, k, v, scale, o, lse, st)
+                       : run_full<64, true>(d, q, k, v, scale, o, lse, st);
+  else
+    r.err = d.D == 128 ? run_full<128, false>(d, q, k, v, scale, o, lse, st)
+                       : run_full<64, false>(d, q, k, v, scale, o, lse, st);
+  return r;
+}
+
+}  // namespace ssa

@@ -1,0 +1,45 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+#include "common.hpp"
+
+namespace ssa {
+
+struct Dims {
+  int B, H, L, D, S, dtype;  // S = block size; dtype 0 = f32, 1 = bf16
+  int n() const { return L / S; }
+  int64_t bh() const { return (int64_t)B * H; }
+  int64_t tokens() const { return (int64_t)B * H * L; }
+};
+
+// Reports the reason a launcher refused a shape it cannot handle (no launch done).
+struct LaunchResult {
+  hipError_t err = hipSuccess;
+  const char* unsupported = nullptr;
+};
+
+LaunchResult launch_pool(const Dims& d, const void* k, float* k_mean, hipStream_t st);
+LaunchResult launch_align(const Dims& d, const void* o_full, const void* o_sparse, const float* lse_full,
+                          const float* lse_sparse, float* dist, float* dropped, hipStream_t st);
+
+// Portable vector-ALU kernels (any dtype, D in {64,128}).
+LaunchResult launch_topk_generic(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,
+                                 float* sel, hipStream_t st);
+LaunchResult launch_sparse_generic(const Dims& d, const void* q, const void* k, const void* v,
+                                   const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                   hipStream_t st);
+LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                                 void* o, float* lse, hipStream_t st);
+
+// MFMA kernels (bf16 only).  *_supported() tells whether the shape fits.
+bool topk_mfma_supported(const Dims& d, int topk);
+LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,
+                              float* sel, hipStream_t st);
+bool full_mfma_supported(const Dims& d);
+LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                              void* o, float* lse, hipStream_t st);
+bool sparse_mfma_supported(const Dims& d, int topk);
+LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v,
+                                const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                hipStream_t st);
+
+}  // namespace ssa

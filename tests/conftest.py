@@ -11,3 +11,21 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running oracle check")
+
+
+@pytest.fixture(scope="session")
+def libssa():
+    """The built C-ABI library (built in-tree first if it is missing)."""
+    from block_sparse_top_ssa_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_top_ssa_amd import build
+        build.build()
+    return _lib.load()
+
+
+def gpu_available():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False

@@ -1,0 +1,72 @@
+"""Comparison rules between the HIP path and the CPU oracle.
+
+  * selected blocks: bit-exact, except in rows where the oracle's m-th and (m+1)-th
+    largest scores (m = topk-1) differ by less than 1e-5 relative; there the two sets
+    may differ only in blocks whose oracle score lies in that tied band, and both must
+    hold the same number of blocks and the own block;
+  * float outputs: max abs error <= 2e-2 for bf16 and 1e-4 for fp32 I/O;
+  * L2 distance computed end to end: |error| <= 2 * tol * sqrt(D) (per-element tolerance
+    through the triangle inequality); from identical inputs: 1e-5 relative.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as W
+
+TIE_REL = 1e-5
+TOL = {W.BF16: 2e-2, W.F32: 1e-4}
+
+
+def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """The generator's arrays (bf16 bit patterns or float32) as device tensors."""
+    if dtype == W.BF16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def compare_idx(gpu_idx: np.ndarray, ora_idx: np.ndarray, extra: dict, q64: np.ndarray,
+                km64: np.ndarray, rows: np.ndarray, s: int, topk: int) -> dict:
+    """Check the selection rule row by row; returns counts (exact, tolerated)."""
+    assert gpu_idx.shape == ora_idx.shape
+    neq = np.nonzero((gpu_idx != ora_idx).any(axis=-1))
+    tolerated = 0
+    for b, h, a in zip(*neq):
+        t = int(rows[a])
+        bt = t // s
+        m = min(topk - 1, bt)
+        g = gpu_idx[b, h, a].tolist()
+        o = ora_idx[b, h, a].tolist()
+        assert g[m] == bt and all(x == -1 for x in g[m + 1:]), f"malformed GPU row {(b, h, t)}: {g}"
+        gk, ok = set(g[:m]), set(o[:m])
+        assert len(gk) == m and g[:m] == sorted(gk), f"GPU row {(b, h, t)} not ascending/distinct: {g}"
+        sm, sm1 = extra["sigma_m"][b, h, a], extra["sigma_m1"][b, h, a]
+        band = TIE_REL * max(abs(sm), abs(sm1))
+        assert abs(sm - sm1) < band, (
+            f"selection differs at (b={b}, h={h}, t={t}) outside a tie: sigma_m={sm!r} sigma_m+1={sm1!r}\n"
+            f" gpu={g}\n oracle={o}")
+        for j in gk ^ ok:
+            sj = float(q64[b, h, t] @ km64[b, h, j])
+            assert sm1 - band <= sj <= sm + band, f"block {j} of row {(b, h, t)} outside the tied band"
+        tolerated += 1
+    return {"rows": int(np.prod(gpu_idx.shape[:3])), "tolerated": tolerated}
+
+
+def max_abs(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.size == 0:
+        return 0.0
+    return float(np.max(np.abs(a - b)))
+
+
+def assert_close(gpu, ora, tol, what):
+    err = max_abs(gpu, ora)
+    assert np.all(np.isfinite(np.asarray(gpu, dtype=np.float64))), f"{what}: non-finite GPU values"
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.1e}"
+    return err

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every symbol include/ssa.h declares, and rejects bad
+arguments with the documented status codes before any GPU work (CPU-only: the pointers
+below are never dereferenced, because every call fails validation first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_top_ssa_amd import _lib
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(libssa):
+    names = _declared()
+    assert set(names) == set(_lib.PROTOTYPES), "binding prototypes and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_version_and_status_strings(libssa):
+    v = int(re.search(r"#define SSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert libssa.ssa_abi_version() == v
+    for code, name in _lib.STATUS.items():
+        assert libssa.ssa_status_str(code).decode() == name
+    assert libssa.ssa_status_str(99).decode() == "SSA_ERR_UNKNOWN"
+
+
+def test_variant_switch(libssa):
+    prev = libssa.ssa_set_kernel_variant(1)
+    assert libssa.ssa_set_kernel_variant(prev) == 1
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+
+
+def _dims(B=1, H=2, L=256, D=128, block=64, dtype=_lib.SSA_BF16):
+    return _lib.Dims(B, H, L, D, block, dtype)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), 3), (dict(D=96), 2), (dict(block=32), 2), (dict(L=200), 2), (dict(B=0), 2),
+    (dict(H=-1), 2), (dict(B=1 << 10, H=1 << 10, L=1 << 10), 2),
+])
+def test_bad_dims(libssa, kw, code):
+    d = _dims(**kw)
+    assert libssa.ssa_block_pool(ctypes.byref(d), FAKE, FAKE, None) == code
+    assert libssa.ssa_last_error().decode()
+
+
+def test_null_and_alignment(libssa):
+    d = _dims()
+    assert libssa.ssa_block_pool(None, FAKE, FAKE, None) == 1
+    assert libssa.ssa_block_pool(ctypes.byref(d), None, FAKE, None) == 1
+    assert libssa.ssa_block_pool(ctypes.byref(d), MISALIGNED, FAKE, None) == 4
+    assert libssa.ssa_block_topk(ctypes.byref(d), FAKE, FAKE, 2, None, None, None) == 1
+    assert libssa.ssa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 2, 0.1, None, None, None) == 1
+    assert libssa.ssa_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, 0.1, None, None, None) == 1
+    assert libssa.ssa_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, MISALIGNED, 0.1, FAKE, None, None) == 4
+    assert libssa.ssa_align_stats(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
+    assert libssa.ssa_align_stats(ctypes.byref(d), FAKE, None, None, None, FAKE, None, None) == 1
+    assert libssa.ssa_align_stats(ctypes.byref(d), None, None, FAKE, None, None, FAKE, None) == 1
+
+
+@pytest.mark.parametrize("topk", [0, -1, 5])
+def test_topk_range(libssa, topk):
+    d = _dims(L=256, block=64)   # n = 4
+    assert libssa.ssa_block_topk(ctypes.byref(d), FAKE, FAKE, topk, FAKE, None, None) == 2
+    assert libssa.ssa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, topk, 0.1, FAKE, None, None) == 2
+
+
+@pytest.mark.parametrize("scale", [0.0, -1.0, float("nan"), float("inf")])
+def test_bad_scale(libssa, scale):
+    d = _dims()
+    assert libssa.ssa_full_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, scale, FAKE, None, None) == 4
+    assert libssa.ssa_sparse_attn_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 2, scale, FAKE, None, None) == 4
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path; a GPU is present")
+def test_valid_call_without_device_reports_device_error(libssa):
+    d = _dims()
+    assert libssa.ssa_block_pool(ctypes.byref(d), FAKE, FAKE, None) == 5
+    assert "device" in libssa.ssa_last_error().decode().lower() or libssa.ssa_last_error()

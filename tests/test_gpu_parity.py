@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (called through the C ABI via the ctypes binding) against
+the CPU oracle on the same seeded inputs.  Needs an MI355X.
+
+Rules (tests/parity.py): selections bit-exact up to score ties within 1e-5 relative;
+outputs within 2e-2 (bf16) / 1e-4 (fp32) max abs error.  Every workload runs the MFMA
+path (variant 0); the small ones also run the portable vector-ALU path (variant 1).
+"""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import workloads as W
+from parity import TOL, assert_close, compare_idx, max_abs, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import block_sparse_top_ssa_amd as ssa  # noqa: E402
+import oracle.ssa_oracle as O  # noqa: E402
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(params=[0, 1], ids=["mfma", "portable"])
+def variant(request):
+    prev = ssa.set_kernel_variant(request.param)
+    yield request.param
+    ssa.set_kernel_variant(prev)
+
+
+def gpu_pipeline(inp: W.Inputs, topk: int, lse_only_full=False, tag=""):
+    w = inp.workload
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    say(f"[gpu] {tag} B={w.B} H={w.H} L={w.L} D={w.D} s={s} topk={topk} dtype={w.dtype}")
+    q, k, v = (to_device(a, w.dtype) for a in (inp.q, inp.k, inp.v))
+    km = ssa.block_pool(k, s)
+    idx, sel = ssa.block_topk(q, km, s, topk, want_scores=True)
+    o_s, lse_s = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+    o_f, lse_f = ssa.full_attn_fwd(q, k, v, scale, want_o=not lse_only_full, block=s)
+    if o_f is not None:
+        dist, drop = ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)
+    else:
+        dist, drop = ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)
+    torch.cuda.synchronize()
+    out = dict(km=km.cpu().numpy().astype(np.float64), idx=idx.cpu().numpy(), sel=sel.cpu().numpy(),
+               o_s=to_f64(o_s), lse_s=to_f64(lse_s), lse_f=to_f64(lse_f), drop=to_f64(drop),
+               o_f=None if o_f is None else to_f64(o_f), dist=None if dist is None else to_f64(dist))
+    say(f"[gpu] {tag} done")
+    return out
+
+
+@functools.lru_cache(maxsize=4)
+def _inputs(name):
+    return W.make_workload(name)
+
+
+def _oracle_checks(inp, g, topk, rows, lse_only_full=False, check_idx=True):
+    """Compare one pipeline run with the oracle on `rows` (None = all)."""
+    w = inp.workload
+    tol = TOL[w.dtype]
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    q64, k64, v64 = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    R = np.arange(w.L) if rows is None else rows
+    km = O.block_pool(k64, s)
+    assert_close(g["km"], km, 1e-5 * max(1.0, float(np.abs(km).max())), "k_mean")
+    report = {}
+    if check_idx:
+        oidx, extra = O.block_topk(q64, km, s, topk, rows=R, return_scores=True)
+        report.update(compare_idx(g["idx"][:, :, R], oidx, extra, q64, km, R, s, topk))
+    gidx = g["idx"][:, :, R]
+    # the sparse stream is checked on the GPU's own selection (identical up to ties)
+    o_s, lse_s = O.attend_sparse(q64, k64, v64, gidx, s, scale, rows=R)
+    report["o_s"] = assert_close(g["o_s"][:, :, R], o_s, tol, "o_sparse")
+    report["lse_s"] = assert_close(g["lse_s"][:, :, R], lse_s, tol, "lse_sparse")
+    o_f, lse_f = O.attend_full(q64, k64, v64, scale, rows=R, want_o=not lse_only_full)
+    if not lse_only_full:
+        report["o_f"] = assert_close(g["o_f"][:, :, R], o_f, tol, "o_full")
+    report["lse_f"] = assert_close(g["lse_f"][:, :, R], lse_f, tol, "lse_full")
+    dm = O.dropped_mass(q64, k64, gidx, s, scale, rows=R)
+    report["dropped"] = assert_close(g["drop"][:, :, R], dm, tol, "dropped mass")
+    if not lse_only_full:
+        dist, _ = O.align_stats(o_f, o_s)
+        report["dist"] = assert_close(g["dist"][:, :, R], dist, 2 * tol * math.sqrt(w.D), "l2 distance")
+        # the same statistics from identical inputs (the GPU's own outputs)
+        d2, dm2 = O.align_stats(g["o_f"], g["o_s"], g["lse_f"], g["lse_s"])
+        assert np.allclose(g["dist"], d2, rtol=1e-5, atol=1e-6)
+        assert np.allclose(g["drop"], dm2, rtol=1e-5, atol=1e-6)
+    # selected scores (GPU float32) against the oracle's float64 scores of the same blocks
+    sel = g["sel"][:, :, R]
+    valid = (gidx >= 0) & (gidx < (R // s)[None, None, :, None])
+    for b in range(w.B):
+        for h in range(w.H):
+            vv = valid[b, h]
+            if vv.any():
+                ra, ca = np.nonzero(vv)
+                sc = np.einsum("rd,rd->r", q64[b, h, R[ra]], km[b, h, gidx[b, h, ra, ca]])
+                assert np.allclose(sel[b, h, ra, ca], sc, rtol=1e-5, atol=1e-5 * np.abs(sc).max())
+    assert np.all(np.isposinf(sel[gidx == (R // s)[None, None, :, None]]))
+    assert np.all(np.isneginf(sel[gidx == -1]))
+    say(f"[oracle] {report}")
+    return report
+
+
+# ----------------------------------------------------------------------------------
+# block pool
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+@pytest.mark.parametrize("D,s", [(128, 64), (64, 128), (128, 128)])
+def test_pool_integer_keys_bit_exact(variant, dtype, D, s):
+    """Integer keys make every float32 block sum exact, so GPU == oracle bit for bit."""
+    kk = W.integer_tensor((2, 3, 4 * s, D), -8, 8, seed=11)
+    a = W.f32_to_bf16_bits(kk) if dtype == W.BF16 else kk
+    say(f"[gpu] pool integer D={D} s={s} {dtype}")
+    km = ssa.block_pool(to_device(a, dtype), s).cpu().numpy()
+    np.testing.assert_array_equal(km, O.block_pool(kk.astype(np.float64), s).astype(np.float32))
+
+
+# ----------------------------------------------------------------------------------
+# selection special cases with closed forms
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("s,topk", [(64, 1), (64, 3), (64, 16), (128, 5)])
+def test_topk_q_zero_closed_form(variant, s, topk):
+    """q = 0: every score is exactly 0; the tie rule keeps blocks 0..m-1 plus b_t."""
+    inp = W.make_qkv(1, 2, 16 * s, 128, s, W.BF16, "none", seed=12, q_zero=True)
+    q, k = to_device(inp.q, W.BF16), to_device(inp.k, W.BF16)
+    km = ssa.block_pool(k, s)
+    idx = ssa.block_topk(q, km, s, topk).cpu().numpy()
+    for t in range(16 * s):
+        bt = t // s
+        m = min(topk - 1, bt)
+        assert idx[0, 1, t].tolist() == list(range(m)) + [bt] + [-1] * (topk - m - 1)
+
+
+def test_topk_integer_ties_exact(variant):
+    """Small integer q and k: block means are multiples of 1/64 and every score is exact
+    in float32, with many exact ties; the selection must equal the oracle's exactly."""
+    B, H, L, D, s, topk = 1, 4, 4096, 128, 64, 9
+    q = W.integer_tensor((B, H, L, D), -1, 1, seed=13)
+    k = W.integer_tensor((B, H, L, D), -2, 2, seed=14)
+    qd, kd = to_device(W.f32_to_bf16_bits(q), W.BF16), to_device(W.f32_to_bf16_bits(k), W.BF16)
+    km = ssa.block_pool(kd, s)
+    idx = ssa.block_topk(qd, km, s, topk).cpu().numpy()
+    oidx = O.block_topk(q.astype(np.float64), O.block_pool(k.astype(np.float64), s), s, topk)
+    np.testing.assert_array_equal(idx, oidx)
+
+
+# ----------------------------------------------------------------------------------
+# whole pipeline on the small workloads (every row)
+# ----------------------------------------------------------------------------------
+def test_fp32_L1024_D64_all_rows(variant):
+    inp = _inputs("fp32_L1024_D64")
+    g = gpu_pipeline(inp, 4, tag="fp32_L1024_D64")
+    _oracle_checks(inp, g, 4, rows=None)
+
+
+def test_bf16_L4096_lowrank_all_rows(variant):
+    inp = _inputs("bf16_L4096_lowrank")
+    g = gpu_pipeline(inp, 16, tag="bf16_L4096_lowrank")
+    _oracle_checks(inp, g, 16, rows=None)
+
+
+@pytest.mark.parametrize("topk", [4, 8, 16, 32, 64, 128])
+def test_bf16_L8192_ksweep(topk):
+    inp = _inputs("bf16_L8192_ksweep")
+    w = inp.workload
+    g = gpu_pipeline(inp, topk, tag=f"bf16_L8192_ksweep k={topk}")
+    rows = W.sample_rows(w.L, w.s, topk, w.sample_rows, seed=w.seed + topk)
+    rep = _oracle_checks(inp, g, topk, rows=rows, check_idx=False)
+    # selection on every row
+    q64 = inp.as_f64("q")
+    km = O.block_pool(inp.as_f64("k"), w.s)
+    oidx, extra = O.block_topk(q64, km, w.s, topk, return_scores=True)
+    rep.update(compare_idx(g["idx"], oidx, extra, q64, km, np.arange(w.L), w.s, topk))
+    say(f"[oracle] k={topk} selection {rep}")
+    if topk == w.n:
+        # keeping every block is full attention
+        assert max_abs(g["o_s"], g["o_f"]) <= 2e-2
+        assert max_abs(g["lse_s"], g["lse_f"]) <= 1e-4
+        assert np.all(g["drop"] <= 1e-4)
+
+
+# ----------------------------------------------------------------------------------
+# closed forms on the GPU
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("s,topk,L", [(64, 4, 1024), (128, 3, 1024), (64, 1, 512)])
+def test_q_zero_closed_forms(variant, s, topk, L):
+    """q = 0: o_s(t) is the mean of v over A(t), lse_s = log|A(t)|, o_f the prefix mean,
+    and the dropped mass 1 - |A(t)|/(t+1)."""
+    inp = W.make_qkv(1, 2, L, 128, s, W.BF16, "none", seed=15, q_zero=True)
+    g = gpu_pipeline(inp, topk, tag="q=0")
+    v = inp.as_f64("v")
+    cnt = np.array([O.attended_count(t, s, topk) for t in range(L)])
+    pref = np.cumsum(v, axis=2) / np.arange(1, L + 1)[None, None, :, None]
+    assert_close(g["o_f"], pref, 2e-2, "o_full prefix mean")
+    assert_close(g["lse_f"][0, 0], np.log(np.arange(1, L + 1)), 1e-4, "lse_full")
+    assert_close(g["lse_s"][0, 0], np.log(cnt), 1e-4, "lse_sparse")
+    assert_close(g["drop"][0, 0], 1 - cnt / np.arange(1, L + 1), 1e-4, "dropped")
+    for t in range(0, L, 37):
+        bt = t // s
+        m = min(topk - 1, bt)
+        keys = [i for j in list(range(m)) + [bt] for i in range(j * s, min(j * s + s, t + 1))]
+        assert_close(g["o_s"][:, :, t], v[:, :, keys].mean(axis=2), 2e-2, f"o_sparse row {t}")
+
+
+# ----------------------------------------------------------------------------------
+# edge shapes: one block, ragged tiles, odd head counts, D = 64 in bf16
+# ----------------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,L,D,s,topk", [
+    (1, 1, 64, 128, 64, 1),      # a single block
+    (1, 3, 192, 128, 64, 2),     # L not a multiple of the 256-row tile
+    (2, 1, 640, 64, 64, 3),      # bf16 with D = 64
+    (1, 2, 384, 128, 128, 2),    # block 128, ragged tile
+    (3, 1, 1280, 128, 64, 20),   # topk = n
+])
+def test_edge_shapes(variant, B, H, L, D, s, topk):
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=16)
+    inp.workload = W.Workload("edge", B, H, L, D, s, (topk,), W.BF16, "none", 16)
+    g = gpu_pipeline(inp, topk, tag=f"edge {B}x{H}x{L}x{D} s={s}")
+    _oracle_checks(inp, g, topk, rows=None)
+
+
+def test_huge_logit_row_recomputed(variant):
+    """A key far more aligned with the query than anything in the query's own block
+    (logit gap ~75) must still give the exact sparse softmax."""
+    B, H, L, D, s = 1, 1, 1024, 128, 64
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=17)
+    qf, kf = W.bf16_bits_to_f32(inp.q), W.bf16_bits_to_f32(inp.k)
+    qf[0, 0, 900] = 0.0
+    qf[0, 0, 900, 0] = 30.0
+    kf[0, 0, 130] = 0.0
+    kf[0, 0, 130, 0] = 30.0
+    inp.q, inp.k = W.f32_to_bf16_bits(qf), W.f32_to_bf16_bits(kf)
+    inp.workload = W.Workload("huge", B, H, L, D, s, (4,), W.BF16, "none", 17)
+    g = gpu_pipeline(inp, 4, tag="huge logit")
+    assert 2 in g["idx"][0, 0, 900].tolist()
+    _oracle_checks(inp, g, 4, rows=np.array([0, 130, 899, 900, 901, 1023]))
+
+
+# ----------------------------------------------------------------------------------
+# long-context workloads: sampled rows for outputs, selection on every row
+# ----------------------------------------------------------------------------------
+def _big(name, head_groups):
+    inp = _inputs(name)
+    w = inp.workload
+    topk = w.ks[0]
+    g = gpu_pipeline(inp, topk, lse_only_full=w.sparse_only, tag=name)
+    rows = W.sample_rows(w.L, w.s, topk, w.sample_rows, seed=w.seed)
+    _oracle_checks(inp, g, topk, rows=rows, lse_only_full=w.sparse_only, check_idx=False)
+    q64 = inp.as_f64("q")
+    km = O.block_pool(inp.as_f64("k"), w.s)
+    tot = {"rows": 0, "tolerated": 0}
+    for hs in head_groups:
+        sl = slice(hs[0], hs[1])
+        oidx, extra = O.block_topk(q64[:, sl], km[:, sl], w.s, topk, return_scores=True)
+        r = compare_idx(g["idx"][:, sl], oidx, extra, q64[:, sl], km[:, sl], np.arange(w.L), w.s, topk)
+        tot = {k: tot[k] + r[k] for k in tot}
+        say(f"[oracle] {name} heads {hs}: {r}")
+    return tot
+
+
+@pytest.mark.slow
+def test_bf16_L32768_sink():
+    _big("bf16_L32768_sink", [(0, 8), (8, 16), (16, 24), (24, 32)])
+
+
+@pytest.mark.slow
+def test_bf16_L131072_drift():
+    _big("bf16_L131072_drift", [(0, 2), (2, 4), (4, 6), (6, 8)])
