@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Throughput of the SSA per-layer attention forward (both streams) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input already
+resident in HBM: block pool -> causal top-k selection -> sparse attention -> full
+attention -> alignment statistics (L2 distance and dropped mass).  Default workload:
+bf16, B=1, H=32, L=32768, D=128, s=64, k=32 (token 0 an 8x-norm sink key).
+
+Prints ONE JSON line.  `value` is tokens/s of the whole step (B*L / step time).  The
+per-kernel times come from HIP events recorded on the stream the kernels run on
+(torch's current stream) around each call inside the timed steps.  `roofline` is
+given for the sparse-attention kernel, the one the metric names, on its useful
+FLOPs 4*D*sum_t |A(t)|.  `cpu_baseline` times the CPU oracle's sparse stream on a
+bounded sample of the same workload (rank 0, this process).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+                    [--no-cpu-baseline] [--copy-calib]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+METRIC = "sparse-attn fwd tokens/s and TFLOP/s (% MFMA bf16 peak) at L=32K"
+
+
+def attended_total(L: int, s: int, k: int) -> int:
+    """sum_t |A(t)| with |A(t)| = t+1 while t//s < k, else (k-1)*s + t%s + 1."""
+    t = np.arange(L, dtype=np.int64)
+    a = np.where(t // s < k, t + 1, (k - 1) * s + t % s + 1)
+    return int(a.sum())
+
+
+def work_model(w: W.Workload, k: int) -> dict:
+    e = 2 if w.dtype == W.BF16 else 4
+    BH, L, D, s, n = w.B * w.H, w.L, w.D, w.s, w.n
+    t = np.arange(L, dtype=np.int64)
+    cand = int((t // s).sum())                  # candidate blocks scored per (b, h)
+    return {
+        "pool": {"bytes": BH * (L * D * e + n * D * 4)},
+        "topk": {"flops": 2 * D * BH * cand, "bytes": BH * (L * D * e + n * D * 4 + L * k * 4)},
+        "sparse": {"flops": 4 * D * BH * attended_total(L, s, k)},
+        "full": {"flops": 4 * D * BH * (L * (L + 1) // 2)},
+        "align": {"bytes": BH * L * (2 * D * e + 4 * 4)},
+    }
+
+
+def cpu_baseline(inp: W.Inputs, k: int, budget_s: float = 15.0) -> dict:
+    """The CPU oracle's sparse stream (pool, select, sparse attention) on the last
+    2048 query rows of as many heads as fit in about `budget_s` seconds."""
+    import oracle.ssa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = inp.workload
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    rows = np.arange(max(0, w.L - 2048), w.L)
+    done_rows, heads, t_total = 0, 0, 0.0
+    for h in range(w.H):
+        def head64(a):
+            x = a[:1, h:h + 1]
+            return (W.bf16_bits_to_f32(x) if w.dtype == W.BF16 else x).astype(np.float64)
+
+        q, kk, vv = head64(inp.q), head64(inp.k), head64(inp.v)
+        t0 = time.perf_counter()
+        km = O.block_pool(kk, s)
+        idx = O.block_topk(q, km, s, k, rows=rows)
+        O.attend_sparse(q, kk, vv, idx, s, scale, rows=rows)
+        t_total += time.perf_counter() - t0
+        done_rows += len(rows)
+        heads += 1
+        if t_total >= budget_s:
+            break
+    try:
+        cpu = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        cpu = ""
+    tps = done_rows / t_total
+    whole = w.B * w.H * w.L / tps
+    return {"value": tps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle sparse stream (block pool + top-k select + masked sparse attention) "
+                      f"on the last {len(rows)} query rows of {heads} of {w.B * w.H} heads (b=0), "
+                      f"{t_total:.1f} s; tokens/s = timed rows / wall time; whole workload extrapolated: "
+                      f"{whole:.0f} s",
+            "cpu_model": cpu}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--topk", type=int, default=0, help="blocks per query (default: the workload's first k)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels shard by head with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_top_ssa_amd as ssa
+
+    w = W.WORKLOADS[args.workload]
+    k = args.topk or w.ks[0]
+    inp = W.make_workload(args.workload)
+
+    def dev(a):
+        if w.dtype == W.BF16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    q, kk, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    B, H, L, D = w.B, w.H, w.L, w.D
+    km = torch.empty((B, H, w.n, D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, H, L, k), dtype=torch.int32, device="cuda")
+    o_s = torch.empty_like(q)
+    o_f = None if w.sparse_only else torch.empty_like(q)
+    lse_s = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    lse_f = torch.empty_like(lse_s)
+
+    names = ["pool", "topk", "sparse", "full", "align"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ssa.block_pool(kk, s, out=km)
+        mark(1)
+        ssa.block_topk(q, km, s, k, out=idx)
+        mark(2)
+        ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s)
+        mark(3)
+        ssa.full_attn_fwd(q, kk, v, scale, want_o=o_f is not None, block=s, out=o_f, lse=lse_f)
+        mark(4)
+        if o_f is not None:
+            ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)
+        else:
+            ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}
+
+    if args.copy_calib:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    model = work_model(w, k)
+    kernels = {}
+    for nm in names:
+        ms = per[nm]
+        ent = {"ms": round(ms, 4)}
+        if "flops" in model[nm]:
+            tf = model[nm]["flops"] / (ms * 1e-3) / 1e12
+            ent["tflops"] = round(tf, 2)
+            peak = PEAK_FP32_TFLOPS if nm == "topk" else PEAK_BF16_TFLOPS
+            ent["frac_peak"] = round(tf / peak, 4)
+        if "bytes" in model[nm]:
+            gb = model[nm]["bytes"] / (ms * 1e-3) / 1e9
+            ent["gbps"] = round(gb, 1)
+            if "flops" not in model[nm]:
+                ent["frac_peak"] = round(gb / PEAK_HBM_GBPS, 4)
+        kernels[nm] = ent
+    if o_f is None:
+        kernels["full"]["note"] = "log-sum-exp only (value products skipped)"
+        kernels["full"]["tflops"] = round(model["full"]["flops"] / 2 / (per["full"] * 1e-3) / 1e12, 2)
+
+    sp_tflops = model["sparse"]["flops"] / (per["sparse"] * 1e-3) / 1e12
+    tokens = B * L
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) q, k, v with the workload's key structure; no dataset, no weights)",
+        "config": {"workload": w.name, "B": B, "H": H, "L": L, "D": D, "block": s, "topk": k,
+                   "step": "pool+topk+sparse_attn+full_attn" + ("(lse only)" if o_f is None else "") + "+align"},
+        "sparse_attn": {"tokens_per_s": round(tokens / (per["sparse"] * 1e-3), 1),
+                        "tflops": round(sp_tflops, 2), "pct_mfma_bf16_peak": round(100 * sp_tflops / PEAK_BF16_TFLOPS, 2),
+                        "ms": round(per["sparse"], 4), "useful_flops": model["sparse"]["flops"]},
+        "roofline": {"kernel": "ssa_sparse_attn_fwd", "bound": "mfma", "achieved": round(sp_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sp_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, k)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,9 +24,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   __bf16 h = (__bf16)f;
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16 (one v_cvt_pk_bf16_f32, nearest-even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
+// 2^x with the hardware v_exp_f32 (results below 2^-126 may flush to zero).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Element access for the two I/O types: float, or bf16 held as uint16_t bits.
 template <typename T> struct Elem;

@@ -64,6 +64,43 @@ __device__ __forceinline__ u32x4 transpose8x8_b16(u32x4 x) {
   return x;
 }
 
+// Same transpose with DPP lane moves only (no LDS crossbar traffic).
+__device__ __forceinline__ u32x4 transpose8x8_b16_dpp(u32x4 x) {
+  const int p = threadIdx.x & 7;
+  {  // lanes p and p^4: rows shifted by 4 inside each 16-lane row; banks 0,2 hold p < 4
+    const int x0 = (int)x[0], x1 = (int)x[1], x2 = (int)x[2], x3 = (int)x[3];
+    x[2] = (uint32_t)__builtin_amdgcn_update_dpp(x2, x0, 0x104, 0xF, 0x5, false);  // row_shl:4
+    x[3] = (uint32_t)__builtin_amdgcn_update_dpp(x3, x1, 0x104, 0xF, 0x5, false);
+    x[0] = (uint32_t)__builtin_amdgcn_update_dpp(x0, x2, 0x114, 0xF, 0xA, false);  // row_shr:4
+    x[1] = (uint32_t)__builtin_amdgcn_update_dpp(x1, x3, 0x114, 0xF, 0xA, false);
+  }
+  {  // lanes p and p^2: quad_perm [2,3,0,1]
+    const bool up = (p & 2) == 0;
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? x[1] : x[0]), 0x4E, 0xF, 0xF, false);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? x[3] : x[2]), 0x4E, 0xF, 0xF, false);
+    if (up) { x[1] = r0; x[3] = r1; } else { x[0] = r0; x[2] = r1; }
+  }
+  {  // lanes p and p^1: quad_perm [1,0,3,2], 16-bit halves
+    const bool up = (p & 1) == 0;
+    const uint32_t h01 = (x[0] >> 16) | (x[1] & 0xFFFF0000u), h23 = (x[2] >> 16) | (x[3] & 0xFFFF0000u);
+    const uint32_t l01 = (x[0] & 0xFFFFu) | (x[1] << 16), l23 = (x[2] & 0xFFFFu) | (x[3] << 16);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? h01 : l01), 0xB1, 0xF, 0xF, false);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(up ? h23 : l23), 0xB1, 0xF, 0xF, false);
+    if (up) {
+      x[0] = (x[0] & 0xFFFFu) | (r0 << 16);
+      x[1] = (x[1] & 0xFFFFu) | (r0 & 0xFFFF0000u);
+      x[2] = (x[2] & 0xFFFFu) | (r1 << 16);
+      x[3] = (x[3] & 0xFFFFu) | (r1 & 0xFFFF0000u);
+    } else {
+      x[0] = (r0 & 0xFFFFu) | (x[0] & 0xFFFF0000u);
+      x[1] = (r0 >> 16) | (x[1] & 0xFFFF0000u);
+      x[2] = (r1 & 0xFFFFu) | (x[2] & 0xFFFF0000u);
+      x[3] = (r1 >> 16) | (x[3] & 0xFFFF0000u);
+    }
+  }
+  return x;
+}
+
 // A fragment of K for S^T: keys key0 + l%16, contraction chunk cc (32 values of d),
 // slot group g = l/16 holds d = 32 cc + 8 g .. +7 (one 16-byte load).
 template <int D>

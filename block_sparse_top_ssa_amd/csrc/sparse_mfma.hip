@@ -55,12 +55,12 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
   return s;
 }
 
-template <int D, int S, int T>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void sparse_fwd_kernel(
+template <int D, int S, int T, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH,
     int ntile, float sl2, float scale) {
-  constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
+  constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64, NTH = NW * 64;
   constexpr int RS = D + 1;  // O state row stride (floats)
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -86,26 +86,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* vh = v + bh * (int64_t)L * D;
   const int32_t* ih = idx + bh * (int64_t)L * topk;
 
-  // ---------------------------------------------------------------- 1. inverted index
-  for (int j = tid; j < nb; j += 256) cnt[j] = 0;
-  if (tid < T) flag[tid] = 0;
-  if (tid == 0) *nextp = 0;
-  __syncthreads();
-  if (tid < rows) {
-    const int t = t0 + tid, bt = t / S;
+  // Walk the valid entries of one row's idx list: distinct blocks below b_t, each
+  // greater than the entry used before it.  Entries are loaded 8 at a time.
+  auto for_each_entry = [&](int t, auto&& fn) {
+    const int bt = t / S;
     const int32_t* ir = ih + (int64_t)t * topk;
     int prev = -1;
-    for (int e = 0; e < topk; ++e) {
-      const int j = ir[e];
-      if (j > prev && j < bt) {
-        prev = j;
-        atomicAdd(&cnt[j], 1);
+    for (int e0 = 0; e0 < topk; e0 += 8) {
+      int jj[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) jj[u] = e0 + u < topk ? ir[e0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = jj[u];
+        if (j > prev && j < bt) {
+          prev = j;
+          fn(j);
+        }
       }
     }
-  }
+  };
+
+  // ---------------------------------------------------------------- 1. inverted index
+  for (int j = tid; j < nb; j += NTH) cnt[j] = 0;
+  for (int r = tid; r < T; r += NTH) flag[r] = 0;
+  if (tid == 0) *nextp = 0;
+  __syncthreads();
+  if (tid < rows) for_each_entry(t0 + tid, [&](int j) { atomicAdd(&cnt[j], 1); });
   __syncthreads();
   {  // exclusive prefix sum of cnt[0..nb) into off[0..nb]; thread-contiguous segments
-    const int seg = (nb + 255) / 256;
+    const int seg = (nb + NTH - 1) / NTH;
     const int b0 = min(nb, tid * seg), b1 = min(nb, b0 + seg);
     int local = 0;
     for (int j = b0; j < b1; ++j) local += cnt[j];
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int y = __shfl_up(incl, o2);
       if (lane >= o2) incl += y;
     }
-    __shared__ int wsum[4];
+    __shared__ int wsum[NW];
     if (lane == 63) wsum[w] = incl;
     __syncthreads();
     int base = 0;
@@ -125,50 +135,89 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       off[j] = run;
       run += cnt[j];
     }
-    if (tid == 255) off[nb] = base + incl;
+    if (tid == NTH - 1) off[nb] = base + incl;
   }
   __syncthreads();
-  for (int j = tid; j < nb; j += 256) cnt[j] = off[j];  // cnt becomes the fill cursor
+  for (int j = tid; j < nb; j += NTH) cnt[j] = off[j];  // cnt becomes the fill cursor
   __syncthreads();
-  if (tid < rows) {
-    const int t = t0 + tid, bt = t / S;
-    const int32_t* ir = ih + (int64_t)t * topk;
-    int prev = -1;
-    for (int e = 0; e < topk; ++e) {
-      const int j = ir[e];
-      if (j > prev && j < bt) {
-        prev = j;
-        list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid;
-      }
-    }
-  }
+  if (tid < rows) for_each_entry(t0 + tid, [&](int j) { list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid; });
 
   // ---------------------------------------------------------------- 2. own-block phase
-  for (int qc = w; qc < T / 64; qc += 4) {
-    const int r0 = 64 * qc;        // tile-relative first row of this 64-row chunk
+  // Unit = 32 rows (two 16-row column tiles) of one 64-row query chunk against the
+  // 64-key chunk holding them (causal).  These rows belong to this wave alone here.
+  for (int u = w; u < T / 32; u += NW) {
+    const int r0 = 32 * u;  // tile-relative first row of the unit
     if (r0 >= rows) break;
-    const int c_diag = (t0 + r0) / 64;
-    u32x4 qf[4][NC];
+    const int qc = r0 / 64, rq = r0 % 64;  // query chunk and row offset inside it
+    const int c_diag = (t0 + 64 * qc) / 64;
+    u32x4 kf[4][NC], vf[NDT][2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(t0 + r0 + 16 * nt + n) * D, cc);
-    f32x4 oacc[NDT][4];
-    float mref[4], lsum[4];
-    int guard_hit[4];
+      for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c_diag * 64 + 16 * kt, cc);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      lsum[nt] = 0.f;
-      guard_hit[nt] = 0;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] = f32x4{0, 0, 0, 0};
+      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c_diag * 64, dt, kc);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      vf[dt][0] = transpose8x8_b16_dpp(vf[dt][0]);
+      vf[dt][1] = transpose8x8_b16_dpp(vf[dt][1]);
     }
-    // for a 128-token block, rows in its second half also see the first half unmasked
-    const int nchunks = (CPB == 2 && (c_diag & 1)) ? 2 : 1;
-    for (int pass = 0; pass < nchunks; ++pass) {
-      const int c = pass == 0 ? c_diag : c_diag - 1;
-      const bool masked = pass == 0;
-      u32x4 kf[4][NC], vf[NDT][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int rl = rq + 16 * nt;  // row offset inside the 64-row chunk (relative to key 0 of the chunk)
+      const int r = r0 + 16 * nt + n;
+      u32x4 qf[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qh + (int64_t)(t0 + r) * D, cc);
+      f32x4 sacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        sacc[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
+      }
+      float p[16];
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[kt][i] * sl2;
+          if (16 * kt + 4 * g + i > rl + n) x = -__builtin_huge_valf();
+          p[kt * 4 + i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(p[i] - mx);
+        ps += p[i];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
+      float* orow = ost + r * RS;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        f32x4 acc = f32x4{0, 0, 0, 0};
+        acc = mfma_bf16(vf[dt][0], pf0, acc);
+        acc = mfma_bf16(vf[dt][1], pf1, acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = acc[i];
+      }
+      if (g == 0) {
+        lst[r] = ps;
+        mrf[r] = mx;
+      }
+    }
+    if (CPB == 2 && (c_diag & 1)) {
+      // a 128-token block: rows in its second half also see its first half, unmasked
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // m_ref written by other lanes
+      const int c = c_diag - 1;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -176,77 +225,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c * 64, dt, kc);
+        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, dt, kc));
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = r0 + 16 * nt + n;
+        u32x4 qf[NC];
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qh + (int64_t)(t0 + r) * D, cc);
         f32x4 sacc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           sacc[kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[nt][cc], sacc[kt]);
+          for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
         }
-        float p[16];
-        float mx = -__builtin_huge_valf();
+        const float mr = mrf[r];
+        float p[16], ps = 0.f, mx = -__builtin_huge_valf();
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = sacc[kt][i] * sl2;
-            if (masked && (16 * kt + 4 * g + i > 16 * nt + n)) x = -__builtin_huge_valf();
-            p[kt * 4 + i] = x;
+            const float x = sacc[kt][i] * sl2 - mr;
             mx = fmaxf(mx, x);
+            p[kt * 4 + i] = fast_exp2(x);
+            ps += p[kt * 4 + i];
           }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        if (pass == 0) mref[nt] = mx;
-        else guard_hit[nt] |= (mx - mref[nt] > kGuard);
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = exp2f(p[i] - mref[nt]);
-          ps += p[i];
-        }
-        lsum[nt] += ps;
+        if (mx > kGuard) flag[r] = 1;
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
         const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-        if (nt == 0) {  // V^T fragments are needed from the first column tile on
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            vf[dt][0] = transpose8x8_b16(vf[dt][0]);
-            vf[dt][1] = transpose8x8_b16(vf[dt][1]);
-          }
-        }
+        float* orow = ost + r * RS;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          oacc[dt][nt] = mfma_bf16(vf[dt][0], pf0, oacc[dt][nt]);
-          oacc[dt][nt] = mfma_bf16(vf[dt][1], pf1, oacc[dt][nt]);
+          f32x4 acc = f32x4{0, 0, 0, 0};
+          acc = mfma_bf16(vf[dt][0], pf0, acc);
+          acc = mfma_bf16(vf[dt][1], pf1, acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] += acc[i];
         }
+        if (g == 0) lst[r] += ps;
       }
-    }
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      float l = lsum[nt];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
-      const int r = r0 + 16 * nt + n;
-      float* orow = ost + r * RS;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = oacc[dt][nt][i];
-      if (g == 0) {
-        lst[r] = l;
-        mrf[r] = mref[nt];
-      }
-      int gh = guard_hit[nt];
-      gh |= __shfl_xor(gh, 16);
-      gh |= __shfl_xor(gh, 32);
-      if (g == 0 && gh) flag[r] = 1;
     }
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- 3. kept-block phase
+  // Each wave takes the next block with rows (ascending), holds one 64-key chunk's K
+  // and V^T fragments in registers and sweeps its rows 16 at a time; the next tile's
+  // query fragments are loaded while the current one is in flight.
   auto grab = [&]() -> int {
     int j = 0;
     if (lane == 0) {
@@ -256,52 +282,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     return __shfl(j, 0);
   };
-  int j = grab(), ch = 0;
-  u32x4 kf[4][NC], vf[NDT][2];
-  auto load_k = [&](int jj, int cc_) {
-    const int c = jj * CPB + cc_;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
-  };
-  auto load_v = [&](int jj, int cc_) {
-    const int c = jj * CPB + cc_;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c * 64, dt, kc);
-  };
-  if (j < nb) {
-    load_k(j, 0);
-    load_v(j, 0);
-  }
-  while (j < nb) {
+  for (int j = grab(); j < nb; j = grab()) {
     const int beg = off[j], count = off[j + 1] - beg;
-    int jn = j, chn = ch + 1;
-    if (chn == CPB) {
-      jn = grab();
-      chn = 0;
-    }
     const int ntiles = (count + 15) / 16;
-    bool v_ready = false;
-    for (int t0n = 0; t0n < ntiles; t0n += 4) {
-      const int nts = min(4, ntiles - t0n);
-      u32x4 pf[4][2];
-      int rr[4];
-      float mr[4];
+    for (int ch = 0; ch < CPB; ++ch) {
+      const int c = j * CPB + ch;
+      // issue order matters for the in-order load counter: K, then the first tile's
+      // rows and Q, then V (only needed after the first score tile)
+      u32x4 kf[4][NC], vf[NDT][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u >= nts) break;
-        const int e = (t0n + u) * 16 + n;
-        const bool valid = e < count;
-        const int r = valid ? list[beg + e] : 0;
-        rr[u] = valid ? r : -1;
-        mr[u] = mrf[r];
-        u32x4 qf[NC];
-        const uint16_t* qrow = qh + (int64_t)(t0 + r) * D;
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qrow, cc);
+        for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
+      int r = n < count ? list[beg + n] : -1;
+      u32x4 qf[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qh + (int64_t)(t0 + (r < 0 ? 0 : r)) * D, cc);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c * 64, dt, kc);
+      for (int it = 0; it < ntiles; ++it) {
+        // prefetch the next tile's rows and Q
+        const int e2 = (it + 1) * 16 + n;
+        const int r2 = (it + 1 < ntiles && e2 < count) ? list[beg + e2] : -1;
+        u32x4 qn[NC];
+        if (it + 1 < ntiles) {
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) qn[cc] = load_q_frag<D>(qh + (int64_t)(t0 + (r2 < 0 ? 0 : r2)) * D, cc);
+        }
+        const float mr = mrf[r < 0 ? 0 : r];
         f32x4 sacc[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
@@ -314,37 +324,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = sacc[kt][i] * sl2 - mr[u];
+            const float x = sacc[kt][i] * sl2 - mr;
             mx = fmaxf(mx, x);
-            p[kt * 4 + i] = valid ? exp2f(x) : 0.f;
+            p[kt * 4 + i] = r >= 0 ? fast_exp2(x) : 0.f;
             ps += p[kt * 4 + i];
           }
-        if (valid && mx > kGuard) flag[r] = 1;
+        if (r >= 0 && mx > kGuard) flag[r] = 1;
         ps += __shfl_xor(ps, 16);
         ps += __shfl_xor(ps, 32);
-        if (valid && g == 0) atomicAdd(&lst[r], ps);
-        pf[u][0] = pack_p(&p[0], &p[4]);
-        pf[u][1] = pack_p(&p[8], &p[12]);
-      }
-      if (t0n + 4 >= ntiles && jn < nb) load_k(jn, chn);  // K of this chunk no longer needed
-      if (!v_ready) {
+        if (r >= 0 && g == 0) atomicAdd(&lst[r], ps);
+        const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
+        if (it == 0) {
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          vf[dt][0] = transpose8x8_b16(vf[dt][0]);
-          vf[dt][1] = transpose8x8_b16(vf[dt][1]);
+          for (int dt = 0; dt < NDT; ++dt) {
+            vf[dt][0] = transpose8x8_b16_dpp(vf[dt][0]);
+            vf[dt][1] = transpose8x8_b16_dpp(vf[dt][1]);
+          }
         }
-        v_ready = true;
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (u >= nts) break;
-        const int r = rr[u];
         float* orow = ost + (r < 0 ? 0 : r) * RS;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           f32x4 acc = f32x4{0, 0, 0, 0};
-          acc = mfma_bf16(vf[dt][0], pf[u][0], acc);
-          acc = mfma_bf16(vf[dt][1], pf[u][1], acc);
+          acc = mfma_bf16(vf[dt][0], pf0, acc);
+          acc = mfma_bf16(vf[dt][1], pf1, acc);
           if (r >= 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -352,16 +354,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                      __HIP_MEMORY_SCOPE_WORKGROUP);
           }
         }
+        r = r2;
+        if (it + 1 < ntiles) {
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) qf[cc] = qn[cc];
+        }
       }
     }
-    if (jn < nb) load_v(jn, chn);
-    j = jn;
-    ch = chn;
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- 4. finalize
-  for (int it = tid; it < rows * (D / 8); it += 256) {
+  for (int it = tid; it < rows * (D / 8); it += NTH) {
     const int r = it / (D / 8), c8 = it % (D / 8);
     if (flag[r]) continue;
     const float inv = 1.f / lst[r];
@@ -372,15 +376,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     store16(o + (bh * (int64_t)L + t0 + r) * D + 8 * c8, Elem<uint16_t>::pack(x));
   }
   if (lse)
-    for (int r = tid; r < rows; r += 256)
+    for (int r = tid; r < rows; r += NTH)
       if (!flag[r]) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lst[r])) * kLn2;
 
   // ---------------------------------------------------------------- 5. exact recompute of flagged rows
   int any = 0;
-  for (int r = tid; r < rows; r += 256) any |= flag[r];
+  for (int r = tid; r < rows; r += NTH) any |= flag[r];
   if (!__syncthreads_or(any)) return;
   float* qs = reinterpret_cast<float*>(smem + lay.ost) + w * D;  // O state no longer needed
-  for (int r = w; r < rows; r += 4) {
+  for (int r = w; r < rows; r += NW) {
     if (!flag[r]) continue;
     const int t = t0 + r;
     for (int d = lane; d < D; d += 64) qs[d] = bf16_bits_to_f32(qh[(int64_t)t * D + d]);
@@ -415,16 +419,18 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
   return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)) > 0;
 }
 
+constexpr int kSparseWaves = 8;
+
 template <int D, int S, int T>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
   const int lds = sparse_lds_layout<D>(T, d.n(), topk).total;
-  auto kern = sparse_fwd_kernel<D, S, T>;
+  auto kern = sparse_fwd_kernel<D, S, T, kSparseWaves>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSparseWaves * 64), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), idx, topk,
                      static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale);
   return hipGetLastError();

@@ -1,0 +1,272 @@
+// Per-query causal top-k block selection (paper sec. 3, p. 4: each query scores the
+// blocks before its own with their mean-pooled keys and keeps the best k, its own
+// block always included; App. D, p. 21: the block-scoring stage).
+//
+// All rows of one query block share the same candidates (the blocks before it), so a
+// workgroup owns one query block of one (b, h) and streams the candidates in chunks
+// of 64:
+//  * scores on MFMA: sigma = q . kbar with kbar (float32) split exactly into three
+//    bf16 terms hi + mid + lo (each the bf16 rounding of what is left), so three bf16
+//    products per element give the float32 dot product (bf16 x bf16 products are
+//    exact in the float32 accumulator).  Each wave scores 16 candidates against all
+//    rows of the block and leaves the scores in LDS;
+//  * selection: per row, one wave turns the chunk's 64 scores into 64-bit keys
+//    (score, then lower block index first), sorts them with a bitonic network across
+//    the lanes and merges them into the row's running list of the best KP keys
+//    (KP = 64 * E, a power of two >= topk - 1), kept in LDS;
+//  * output: the best min(topk-1, b_t) keys, re-sorted by block index, plus b_t.
+#include "launch.hpp"
+#include "mfma.hpp"
+
+namespace ssa {
+
+// bitonic compare-exchange across lanes at distance j; `desc` = this pair sorts descending
+__device__ __forceinline__ uint64_t cx_lanes(uint64_t x, int j, bool desc) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t y = shfl_xor_u64(x, j);
+  const bool lower = (lane & j) == 0;
+  const bool keep_max = lower == desc;
+  return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+}
+
+// full bitonic sort of 64 lane values; ascending if `asc`
+__device__ __forceinline__ uint64_t sort64(uint64_t x, bool asc) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k2 = 2; k2 <= 64; k2 <<= 1)
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      const bool blk_asc = ((lane & k2) == 0) == asc;
+      x = cx_lanes(x, j, !blk_asc);
+    }
+  return x;
+}
+
+// bitonic merge (half-cleaners) of KP = 64*E values laid out as p = e*64 + lane,
+// into descending order
+template <int E>
+__device__ __forceinline__ void merge_desc(uint64_t (&x)[E]) {
+#pragma unroll
+  for (int je = E / 2; je > 0; je >>= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((e & je) == 0) {
+        const uint64_t a = x[e], b = x[e + je];
+        x[e] = a > b ? a : b;
+        x[e + je] = a > b ? b : a;
+      }
+#pragma unroll
+  for (int j = 32; j > 0; j >>= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = cx_lanes(x[e], j, true);
+}
+
+// full bitonic sort ascending of KP = 64*E values (p = e*64 + lane)
+template <int E>
+__device__ __forceinline__ void sort_asc(uint64_t (&x)[E]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k2 = 2; k2 <= 64 * E; k2 <<= 1)
+#pragma unroll
+    for (int j = k2 >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int je = j / 64;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if ((e & je) == 0) {
+            const int p = e * 64 + lane;
+            const bool asc = (p & k2) == 0;
+            const uint64_t a = x[e], b = x[e + je];
+            const bool sw = asc ? (a > b) : (a < b);
+            x[e] = sw ? b : a;
+            x[e + je] = sw ? a : b;
+          }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int p = e * 64 + lane;
+          x[e] = cx_lanes(x[e], j, (p & k2) != 0);
+        }
+      }
+    }
+}
+
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  const float r1 = x - bf16_bits_to_f32(hi);
+  mid = f32_to_bf16_bits(r1);
+  const float r2 = r1 - bf16_bits_to_f32(mid);
+  lo = f32_to_bf16_bits(r2);
+}
+
+template <int D, int S, int E>
+__global__ __launch_bounds__(256) void topk_mfma_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
+                                                        int32_t* __restrict__ idx, float* __restrict__ sel, int L,
+                                                        int n, int BH, int topk) {
+  constexpr int NC = D / 32, NT = S / 16, KP = 64 * E, SCS = 65;
+  __shared__ float sc[S][SCS];
+  __shared__ uint64_t lists[S][KP];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int nn = lane & 15, g = lane >> 4;
+  const int qb = n - 1 - (int)(blockIdx.x / BH);
+  const int64_t bh = blockIdx.x % BH;
+  const int m = min(topk - 1, qb);
+  const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
+  const float* kmh = km + bh * (int64_t)n * D;
+  int32_t* ih = idx + (bh * L + (int64_t)qb * S) * topk;
+  float* sh = sel ? sel + (bh * L + (int64_t)qb * S) * topk : nullptr;
+  const float inf = __builtin_huge_valf();
+
+  if (m == qb || m == 0) {
+    // every candidate kept (or none to keep): no selection needed
+    for (int it = tid; it < S * topk; it += 256) {
+      const int r = it / topk, p = it % topk;
+      ih[it] = p < qb && m == qb ? p : (p == m ? qb : -1);
+      if (sh) {
+        float v = p == m ? inf : -inf;
+        if (p < m) {
+          float acc = 0.f;
+          const uint16_t* qr = qh + (int64_t)r * D;
+          const float* kr = kmh + (int64_t)p * D;
+          for (int d = 0; d < D; ++d) acc = fmaf(bf16_bits_to_f32(qr[d]), kr[d], acc);
+          v = acc;
+        }
+        sh[it] = v;
+      }
+    }
+    return;
+  }
+
+  for (int it = tid; it < S * KP; it += 256) (&lists[0][0])[it] = 0;
+  u32x4 qf[NT][NC];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(16 * nt + nn) * D, cc);
+
+  const int nchunks = (qb + 63) / 64;
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    const int cb = chunk * 64;
+    // ---- scores: wave w takes candidates cb + 16w .. +15 against every row
+    {
+      const int j = cb + 16 * w + nn;
+      const bool valid = j < qb;
+      u32x4 ah[NC], am[NC], al[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        float x[8];
+        if (valid) {
+          const float* src = kmh + (int64_t)j * D + 32 * cc + 8 * g;
+          const u32x4 w0 = load16(src), w1 = load16(src + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = __uint_as_float(w0[e]);
+            x[4 + e] = __uint_as_float(w1[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.f;
+        }
+        uint32_t h[8], md[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split3(x[e], h[e], md[e], lo[e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ah[cc][e] = h[2 * e] | (h[2 * e + 1] << 16);
+          am[cc][e] = md[2 * e] | (md[2 * e + 1] << 16);
+          al[cc][e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          acc = mfma_bf16(al[cc], qf[nt][cc], acc);
+          acc = mfma_bf16(am[cc], qf[nt][cc], acc);
+          acc = mfma_bf16(ah[cc], qf[nt][cc], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[16 * nt + nn][16 * w + 4 * g + i] = acc[i];
+      }
+    }
+    __syncthreads();
+    // ---- selection: wave w merges the chunk into rows w, w+4, ...
+    for (int r = w; r < S; r += 4) {
+      const int j = cb + lane;
+      uint64_t key = j < qb ? make_key(sc[r][lane], j) : 0ull;
+      key = sort64(key, true);
+      uint64_t x[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = lists[r][e * 64 + lane];
+      x[E - 1] = x[E - 1] > key ? x[E - 1] : key;
+      merge_desc<E>(x);
+#pragma unroll
+      for (int e = 0; e < E; ++e) lists[r][e * 64 + lane] = x[e];
+    }
+    __syncthreads();
+  }
+
+  // ---- output: the best m blocks in ascending block order, then qb, then -1
+  for (int r = w; r < S; r += 4) {
+    uint64_t x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = e * 64 + lane;
+      const uint64_t kk = lists[r][p];
+      x[e] = p < m ? (((uint64_t)key_index(kk) << 32) | (kk >> 32)) : ~0ull;
+    }
+    sort_asc<E>(x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = e * 64 + lane;
+      if (p < topk) {
+        ih[(int64_t)r * topk + p] = p < m ? (int)(x[e] >> 32) : (p == m ? qb : -1);
+        if (sh) sh[(int64_t)r * topk + p] = p < m ? unorderable_f32((uint32_t)x[e]) : (p == m ? inf : -inf);
+      }
+    }
+  }
+}
+
+static int e_for(int topk) {
+  const int need = topk - 1;
+  int e = 1;
+  while (64 * e < need) e <<= 1;
+  return e;
+}
+
+bool topk_mfma_supported(const Dims& d, int topk) {
+  if (d.dtype != 1 || (d.D != 64 && d.D != 128)) return false;
+  const int e = e_for(topk);
+  return d.S * 64 * e <= 8192;  // running lists: S rows x KP keys x 8 bytes <= 64 KB
+}
+
+template <int D, int S, int E>
+static hipError_t run_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
+                           hipStream_t st) {
+  const int64_t grid = (int64_t)d.n() * d.bh();
+  hipLaunchKernelGGL((topk_mfma_kernel<D, S, E>), dim3((unsigned)grid), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t dispatch_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
+                                hipStream_t st) {
+  const int e = e_for(topk);
+  if (d.S == 64) {
+    if (e == 1) return run_topk<D, 64, 1>(d, q, km, topk, idx, sel, st);
+    return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);
+  }
+  return run_topk<D, 128, 1>(d, q, km, topk, idx, sel, st);
+}
+
+LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
+                              hipStream_t st) {
+  LaunchResult r;
+  r.err = d.D == 128 ? dispatch_topk<128>(d, q, km, topk, idx, sel, st)
+                     : dispatch_topk<64>(d, q, km, topk, idx, sel, st);
+  return r;
+}
+
+}  // namespace ssa
