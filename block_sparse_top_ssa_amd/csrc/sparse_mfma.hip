@@ -13,13 +13,19 @@
 //  2. own-block phase: each 64-row query chunk against its own 64-key chunk (causal)
 //     on MFMA; the row max of these logits becomes the row's fixed reference m_ref,
 //     and O, l start from this chunk;
-//  3. kept-block phase: waves take blocks in ascending order; for each 64-key chunk
-//     of the block they hold its K and V^T fragments in registers and sweep the rows
-//     that kept it in 16-row tiles: S^T = K Q^T, p = exp2(s - m_ref), O^T = V^T P^T,
-//     then add O and l into LDS with float atomics.  Because every row uses the fixed
-//     reference m_ref, the partial sums from different waves and blocks simply add,
-//     in any order, with no rescaling.  K of the next chunk is loaded while the
-//     current one's V products run, and V of the next chunk while its K products run.
+//  3. kept-block phase, in lockstep rounds of two roles per SIMD:
+//     * four score waves each take the blocks j = s (mod 4) in ascending order and,
+//       per round, one 16-row tile of the rows that kept the current 64-key chunk:
+//       S^T = K Q^T, p = exp2(s - m_ref) rounded to bf16, row sums of the rounded p;
+//       P^T, the row ids and the sums go to a double-buffered LDS slot;
+//     * four value waves each own a 32-column slice of the O state of every row; per
+//       round they read the four slots of the previous round, load the V^T fragments
+//       of their slice (prefetched one round ahead), form O^T = V^T P^T for their
+//       columns and add it into the O state with plain 16-byte read-add-write.
+//     Each O element has a single writer, so no atomics are needed (LDS float atomics
+//     run at a fraction of a lane per clock on this chip); one barrier per round.
+//     Because every row uses the fixed reference m_ref, partial sums from different
+//     blocks simply add, in any order, with no rescaling.
 //  4. finalize: o = O / l (bf16), lse = m_ref + log l.
 //
 // m_ref is an attained logit of the row, so l >= 1 and nothing underflows.  If any
@@ -33,35 +39,62 @@
 namespace ssa {
 
 constexpr float kGuard = 90.f;  // log2 units
+constexpr int kSlotBytes = 2256;  // P^T fragments (2 KB), 16 row ids, 2 x 16 row sums, chunk ids
 
 struct SparseLds {
   // byte offsets inside the dynamic LDS block
-  int ost, lst, mref, flag, cnt, off, list, next, total;
+  int ost, lst, lse2, mref, cnt, off, misc, slots, flag, list, total;
 };
 
 template <int D>
 __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) {
   SparseLds s;
   int o = 0;
-  s.ost = o;  o += T * (D + 1) * 4;   // O state, row stride D+1 floats
-  s.lst = o;  o += T * 4;
-  s.mref = o; o += T * 4;
-  s.flag = o; o += T * 4;
-  s.cnt = o;  o += nb * 4;
-  s.off = o;  o += (nb + 1) * 4;
-  s.next = o; o += 16;
-  s.list = o; o += T * topk;  // malformed rows may list up to topk blocks below b_t
+  s.ost = o;   o += T * D * 4;   // O state, rows of D floats, 16-byte granules XOR-swizzled by row
+  s.lst = o;   o += T * 4;   // row sums of the bf16-rounded p (normalise o)
+  s.lse2 = o;  o += T * 4;   // row sums of the float32 p (log-sum-exp)
+  s.mref = o;  o += T * 4;
+  s.cnt = o;   o += nb * 4;
+  s.off = o;   o += (nb + 1) * 4;
+  s.misc = o;  o += 32;
+  o = (o + 15) & ~15;
+  s.slots = o; o += 4 * kSlotBytes;
+  s.flag = o;  o += T;
+  s.list = o;  o += T * topk;  // malformed rows may list up to topk blocks below b_t
   s.total = (o + 15) & ~15;
   return s;
 }
 
-template <int D, int S, int T, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void sparse_fwd_kernel(
+// float offset of the 16-byte granule holding O[r][d .. d+3] (d % 4 == 0)
+template <int D>
+__device__ __forceinline__ int ost_granule(int r, int d) {
+  return r * D + ((((d >> 2) ^ (r & 7))) << 2);
+}
+
+struct Slot {
+  u32x4 p[2][64];
+  int rows[16];
+  float ps_round[16], ps_exact[16];
+  int chunk, next_chunk, pad0, pad1;
+};
+static_assert(sizeof(Slot) == kSlotBytes, "slot layout");
+
+// sum of the 8 bf16 values packed in a P^T fragment
+__device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s += lo_bf16(w[i]) + hi_bf16(w[i]);
+  return s;
+}
+
+template <int D, int S, int T>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH,
     int ntile, float sl2, float scale) {
-  constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64, NTH = NW * 64;
-  constexpr int RS = D + 1;  // O state row stride (floats)
+  constexpr int NW = 8, NTH = 512;
+  constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
+  constexpr int DTW = NDT / 4;  // d tiles per value wave
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
@@ -74,11 +107,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   const SparseLds lay = sparse_lds_layout<D>(T, nb, topk);
   float* ost = reinterpret_cast<float*>(smem + lay.ost);
   float* lst = reinterpret_cast<float*>(smem + lay.lst);
+  float* lsx = reinterpret_cast<float*>(smem + lay.lse2);
   float* mrf = reinterpret_cast<float*>(smem + lay.mref);
-  int* flag = reinterpret_cast<int*>(smem + lay.flag);
   int* cnt = reinterpret_cast<int*>(smem + lay.cnt);
   int* off = reinterpret_cast<int*>(smem + lay.off);
-  int* nextp = reinterpret_cast<int*>(smem + lay.next);
+  int* misc = reinterpret_cast<int*>(smem + lay.misc);
+  Slot* slots = reinterpret_cast<Slot*>(smem + lay.slots);  // one per score wave
+  uint8_t* flag = smem + lay.flag;
   uint8_t* list = smem + lay.list;
 
   const uint16_t* qh = q + bh * (int64_t)L * D;
@@ -110,7 +145,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   // ---------------------------------------------------------------- 1. inverted index
   for (int j = tid; j < nb; j += NTH) cnt[j] = 0;
   for (int r = tid; r < T; r += NTH) flag[r] = 0;
-  if (tid == 0) *nextp = 0;
   __syncthreads();
   if (tid < rows) for_each_entry(t0 + tid, [&](int j) { atomicAdd(&cnt[j], 1); });
   __syncthreads();
@@ -158,15 +192,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c_diag * 64, dt, kc);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      vf[dt][0] = transpose8x8_b16_dpp(vf[dt][0]);
-      vf[dt][1] = transpose8x8_b16_dpp(vf[dt][1]);
-    }
+      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c_diag * 64, dt, kc));
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int rl = rq + 16 * nt;  // row offset inside the 64-row chunk (relative to key 0 of the chunk)
+      const int rl = rq + 16 * nt;  // row offset inside the 64-row chunk
       const int r = r0 + 16 * nt + n;
       u32x4 qf[NC];
 #pragma unroll
@@ -191,26 +220,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      float ps = 0.f;
+      float px = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = fast_exp2(p[i] - mx);
-        ps += p[i];
+        px += p[i];
       }
+      const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
+      float ps = sum_bf16x8(pf0) + sum_bf16x8(pf1);  // sum of the rounded p the products use
       ps += __shfl_xor(ps, 16);
       ps += __shfl_xor(ps, 32);
-      const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-      float* orow = ost + r * RS;
+      px += __shfl_xor(px, 16);
+      px += __shfl_xor(px, 32);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         f32x4 acc = f32x4{0, 0, 0, 0};
         acc = mfma_bf16(vf[dt][0], pf0, acc);
         acc = mfma_bf16(vf[dt][1], pf1, acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] = acc[i];
+        *reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * dt + 4 * g)) = acc;
       }
       if (g == 0) {
         lst[r] = ps;
+        lsx[r] = px;
         mrf[r] = mx;
       }
     }
@@ -240,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
           for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
         }
         const float mr = mrf[r];
-        float p[16], ps = 0.f, mx = -__builtin_huge_valf();
+        float p[16], mx = -__builtin_huge_valf(), px = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -248,136 +279,218 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
             const float x = sacc[kt][i] * sl2 - mr;
             mx = fmaxf(mx, x);
             p[kt * 4 + i] = fast_exp2(x);
-            ps += p[kt * 4 + i];
+            px += p[kt * 4 + i];
           }
         if (mx > kGuard) flag[r] = 1;
+        const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
+        float ps = sum_bf16x8(pf0) + sum_bf16x8(pf1);
         ps += __shfl_xor(ps, 16);
         ps += __shfl_xor(ps, 32);
-        const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-        float* orow = ost + r * RS;
+        px += __shfl_xor(px, 16);
+        px += __shfl_xor(px, 32);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           f32x4 acc = f32x4{0, 0, 0, 0};
           acc = mfma_bf16(vf[dt][0], pf0, acc);
           acc = mfma_bf16(vf[dt][1], pf1, acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) orow[16 * dt + 4 * g + i] += acc[i];
+          f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * dt + 4 * g));
+          *gp = *gp + acc;
         }
-        if (g == 0) lst[r] += ps;
+        if (g == 0) {
+          lst[r] += ps;
+          lsx[r] += px;
+        }
       }
     }
   }
-  __syncthreads();
 
   // ---------------------------------------------------------------- 3. kept-block phase
-  // Each wave takes the next block with rows (ascending), holds one 64-key chunk's K
-  // and V^T fragments in registers and sweeps its rows 16 at a time; the next tile's
-  // query fragments are loaded while the current one is in flight.
-  auto grab = [&]() -> int {
-    int j = 0;
-    if (lane == 0) {
-      do {
-        j = atomicAdd(nextp, 1);
-      } while (j < nb && off[j + 1] == off[j]);
-    }
-    return __shfl(j, 0);
+  // score wave s (w < 4) owns blocks j = s (mod 4); its items are (block, chunk, tile)
+  auto next_block = [&](int from) -> int {  // next non-empty block >= from, same residue
+    int j = from;
+    while (j < nb && off[j + 1] == off[j]) j += 4;
+    return j < nb ? j : nb;
   };
-  for (int j = grab(); j < nb; j = grab()) {
+  __syncthreads();  // off[] and the own-block state are complete
+  if (w < 4 && lane == 0) {
+    int items = 0;
+    for (int j = next_block(w); j < nb; j = next_block(j + 4)) items += CPB * ((off[j + 1] - off[j] + 15) / 16);
+    misc[w] = items;
+  }
+  __syncthreads();
+  const int my_items = w < 4 ? misc[w] : 0;
+  const int rounds = max(max(misc[0], misc[1]), max(misc[2], misc[3]));
+
+  // score-wave state (waves 0-3): the loaded operands of the next tile to score, and
+  // the scored tile waiting to be published
+  int j = w < 4 ? next_block(w) : nb, ch = 0, it = 0, r_cur = -1;
+  u32x4 kf[4][NC], qf[NC];
+  u32x4 pub0 = u32x4{0, 0, 0, 0}, pub1 = u32x4{0, 0, 0, 0};
+  int pub_r = -1, pub_c = -1, pub_nc = -1;
+  float pub_ps = 0.f, pub_px = 0.f;
+  int scored = 0;
+  auto load_item = [&](bool new_chunk) {
     const int beg = off[j], count = off[j + 1] - beg;
-    const int ntiles = (count + 15) / 16;
-    for (int ch = 0; ch < CPB; ++ch) {
+    const int e = it * 16 + n;
+    r_cur = e < count ? (int)list[beg + e] : -1;
+    if (new_chunk) {
       const int c = j * CPB + ch;
-      // issue order matters for the in-order load counter: K, then the first tile's
-      // rows and Q, then V (only needed after the first score tile)
-      u32x4 kf[4][NC], vf[NDT][2];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
-      int r = n < count ? list[beg + n] : -1;
-      u32x4 qf[NC];
+    }
+    const uint16_t* qrow = qh + (int64_t)(t0 + (r_cur < 0 ? 0 : r_cur)) * D;
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qh + (int64_t)(t0 + (r < 0 ? 0 : r)) * D, cc);
+    for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qrow, cc);
+  };
+  auto score_item = [&]() {
+    const int r = r_cur;
+    const float mr = mrf[r < 0 ? 0 : r];
+    f32x4 sacc[4];
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = load_v_raw<D>(vh, c * 64, dt, kc);
-      for (int it = 0; it < ntiles; ++it) {
-        // prefetch the next tile's rows and Q
-        const int e2 = (it + 1) * 16 + n;
-        const int r2 = (it + 1 < ntiles && e2 < count) ? list[beg + e2] : -1;
-        u32x4 qn[NC];
-        if (it + 1 < ntiles) {
+      for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
+    }
+    float p[16], mx = -__builtin_huge_valf(), px = 0.f;
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) qn[cc] = load_q_frag<D>(qh + (int64_t)(t0 + (r2 < 0 ? 0 : r2)) * D, cc);
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = sacc[kt][i] * sl2 - mr;
+        mx = fmaxf(mx, x);
+        p[kt * 4 + i] = r >= 0 ? fast_exp2(x) : 0.f;
+        px += p[kt * 4 + i];
+      }
+    if (r >= 0 && mx > kGuard) flag[r] = 1;
+    pub0 = pack_p(&p[0], &p[4]);
+    pub1 = pack_p(&p[8], &p[12]);
+    float ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // sum of the rounded p the products use
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    px += __shfl_xor(px, 16);
+    px += __shfl_xor(px, 32);
+    pub_ps = ps;
+    pub_px = px;
+    pub_r = r;
+    pub_c = j * CPB + ch;
+    // advance to the next tile and issue its loads (scored next round)
+    const int ntl = (off[j + 1] - off[j] + 15) / 16;
+    bool new_chunk = false;
+    if (++it == ntl) {
+      it = 0;
+      new_chunk = true;
+      if (++ch == CPB) {
+        ch = 0;
+        j = next_block(j + 4);
+      }
+    }
+    ++scored;
+    const bool more = scored < my_items;
+    pub_nc = more ? j * CPB + ch : -1;
+    if (more) load_item(new_chunk);
+  };
+  if (w < 4 && my_items > 0) {
+    load_item(true);
+    score_item();
+  }
+  // value-wave state (waves 4-7): V^T fragments of its column slice, per score-wave stream
+  const int pw = w - 4;
+  u32x4 vfr[4][DTW][2];
+  int vchunk[4] = {-1, -1, -1, -1};
+  bool vready[4] = {false, false, false, false};
+  auto load_v = [&](int s, int c) {
+#pragma unroll
+    for (int dl = 0; dl < DTW; ++dl)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) vfr[s][dl][kc] = load_v_raw<D>(vh, c * 64, pw * DTW + dl, kc);
+  };
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    if (w < 4) {  // publish the tile scored for this round
+      Slot& sl = slots[w];
+      const bool have = rd < my_items;
+      if (have) {
+        sl.p[0][lane] = pub0;
+        sl.p[1][lane] = pub1;
+        if (g == 0) {
+          sl.rows[n] = pub_r;
+          sl.ps_round[n] = pub_ps;
+          sl.ps_exact[n] = pub_px;
         }
-        const float mr = mrf[r < 0 ? 0 : r];
-        f32x4 sacc[4];
+      }
+      if (lane == 0) {
+        sl.chunk = have ? pub_c : -1;
+        sl.next_chunk = have ? pub_nc : -1;
+      }
+    }
+    __syncthreads();
+    if (w < 4) {
+      // ------------------------------------------------------------ score wave: next tile
+      if (rd + 1 < my_items) score_item();
+    } else {
+      // ------------------------------------------------------------ value wave
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          sacc[kt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
-        }
-        float p[16], ps = 0.f, mx = -__builtin_huge_valf();
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = sacc[kt][i] * sl2 - mr;
-            mx = fmaxf(mx, x);
-            p[kt * 4 + i] = r >= 0 ? fast_exp2(x) : 0.f;
-            ps += p[kt * 4 + i];
+      for (int s = 0; s < 4; ++s) {
+        const Slot& sl = slots[s];
+        const int c = sl.chunk;
+        if (c >= 0) {
+          if (c != vchunk[s]) {
+            load_v(s, c);
+            vchunk[s] = c;
+            vready[s] = false;
           }
-        if (r >= 0 && mx > kGuard) flag[r] = 1;
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        if (r >= 0 && g == 0) atomicAdd(&lst[r], ps);
-        const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-        if (it == 0) {
+          if (!vready[s]) {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            vf[dt][0] = transpose8x8_b16_dpp(vf[dt][0]);
-            vf[dt][1] = transpose8x8_b16_dpp(vf[dt][1]);
+            for (int dl = 0; dl < DTW; ++dl) {
+              vfr[s][dl][0] = transpose8x8_b16_dpp(vfr[s][dl][0]);
+              vfr[s][dl][1] = transpose8x8_b16_dpp(vfr[s][dl][1]);
+            }
+            vready[s] = true;
           }
-        }
-        float* orow = ost + (r < 0 ? 0 : r) * RS;
+          const u32x4 pf0 = sl.p[0][lane], pf1 = sl.p[1][lane];
+          const int r = sl.rows[n];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          f32x4 acc = f32x4{0, 0, 0, 0};
-          acc = mfma_bf16(vf[dt][0], pf0, acc);
-          acc = mfma_bf16(vf[dt][1], pf1, acc);
-          if (r >= 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              __hip_atomic_fetch_add(orow + 16 * dt + 4 * g + i, acc[i], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WORKGROUP);
+          for (int dl = 0; dl < DTW; ++dl) {
+            f32x4 acc = f32x4{0, 0, 0, 0};
+            acc = mfma_bf16(vfr[s][dl][0], pf0, acc);
+            acc = mfma_bf16(vfr[s][dl][1], pf1, acc);
+            if (r >= 0) {
+              f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
+              *gp = *gp + acc;
+            }
           }
-        }
-        r = r2;
-        if (it + 1 < ntiles) {
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) qf[cc] = qn[cc];
+          if (pw == 0 && g == 0 && r >= 0) {
+            lst[r] += sl.ps_round[n];
+            lsx[r] += sl.ps_exact[n];
+          }
+          const int nc = sl.next_chunk;
+          if (nc >= 0 && nc != c) {
+            load_v(s, nc);  // used next round
+            vchunk[s] = nc;
+            vready[s] = false;
+          }
         }
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---------------------------------------------------------------- 4. finalize
   for (int it = tid; it < rows * (D / 8); it += NTH) {
     const int r = it / (D / 8), c8 = it % (D / 8);
     if (flag[r]) continue;
     const float inv = 1.f / lst[r];
-    const float* src = ost + r * RS + 8 * c8;
-    float x[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = src[e] * inv;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(ost + ost_granule<D>(r, 8 * c8));
+    const f32x4 b = *reinterpret_cast<const f32x4*>(ost + ost_granule<D>(r, 8 * c8 + 4));
+    float x[8] = {a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv, b[0] * inv, b[1] * inv, b[2] * inv, b[3] * inv};
     store16(o + (bh * (int64_t)L + t0 + r) * D + 8 * c8, Elem<uint16_t>::pack(x));
   }
   if (lse)
     for (int r = tid; r < rows; r += NTH)
-      if (!flag[r]) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lst[r])) * kLn2;
+      if (!flag[r]) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lsx[r])) * kLn2;
 
   // ---------------------------------------------------------------- 5. exact recompute of flagged rows
   int any = 0;
@@ -403,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4,
   }
 }
 
-static constexpr int kMaxLds = 160 * 1024;
+static constexpr int kMaxLds = 160 * 1024 - 256;  // leave room for the static LDS (scan partials)
 
 template <int D>
 static int pick_tile(const Dims& d, int topk) {
@@ -419,18 +532,16 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
   return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)) > 0;
 }
 
-constexpr int kSparseWaves = 8;
-
 template <int D, int S, int T>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
                              int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
   const int lds = sparse_lds_layout<D>(T, d.n(), topk).total;
-  auto kern = sparse_fwd_kernel<D, S, T, kSparseWaves>;
+  auto kern = sparse_fwd_kernel<D, S, T>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSparseWaves * 64), lds, st, static_cast<const uint16_t*>(q),
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), idx, topk,
                      static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale);
   return hipGetLastError();
