@@ -59,6 +59,36 @@ def work_model(w: W.Workload, k: int) -> dict:
     }
 
 
+KERNEL_SOURCES = {"pool": "pool.hip", "topk": "topk_mfma.hip", "sparse": "sparse_mfma.hip",
+                  "full": "full_mfma.hip", "align": "align.hip"}
+SHARED_HEADERS = ("common.hpp", "mfma.hpp", "rowattn.hpp")
+
+
+def measured_traffic(workload: str) -> dict:
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/hbm_traffic.json), per kernel, only where the kernel's source and the
+    shared headers are unchanged since the counters were taken; otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    out = {k: None for k in KERNEL_SOURCES}
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return out
+    if rec.get("workload") != workload:
+        return out
+    csrc = os.path.join(ROOT, "block_sparse_top_ssa_amd", "csrc")
+    hdr = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in SHARED_HEADERS)).hexdigest()
+    for k, fn in KERNEL_SOURCES.items():
+        t = rec.get("kernels", {}).get(k)
+        if not t:
+            continue
+        src = hashlib.sha256(open(os.path.join(csrc, fn), "rb").read()).hexdigest()
+        if t.get("source_sha256") == src and t.get("headers_sha256") == hdr:
+            out[k] = int(round(t["fetch_bytes"] + t["write_bytes"]))
+    return out
+
+
 def cpu_baseline(inp: W.Inputs, k: int, budget_s: float = 15.0) -> dict:
     """The CPU oracle's sparse stream (pool, select, sparse attention) on the last
     2048 query rows of as many heads as fit in about `budget_s` seconds."""
@@ -182,6 +212,7 @@ def main():
         torch.cuda.synchronize()
 
     model = work_model(w, k)
+    traffic = measured_traffic(w.name)
     kernels = {}
     for nm in names:
         ms = per[nm]
@@ -196,6 +227,7 @@ def main():
             ent["gbps"] = round(gb, 1)
             if "flops" not in model[nm]:
                 ent["frac_peak"] = round(gb / PEAK_HBM_GBPS, 4)
+        ent["hbm_bytes_measured"] = traffic[nm]
         kernels[nm] = ent
     if o_f is None:
         kernels["full"]["note"] = "log-sum-exp only (value products skipped)"
@@ -223,7 +255,8 @@ def main():
                         "ms": round(per["sparse"], 4), "useful_flops": model["sparse"]["flops"]},
         "roofline": {"kernel": "ssa_sparse_attn_fwd", "bound": "mfma", "achieved": round(sp_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sp_tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": traffic["sparse"], "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
+                     "WRITE_SIZE, scaled by a 1 GiB copy; null when the kernel changed since)"},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

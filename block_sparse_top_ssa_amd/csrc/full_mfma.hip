@@ -9,8 +9,8 @@
 // LDS stage in MFMA-fragment order (K as is; V transposed in registers first), so
 // every wave reads its fragments with conflict-free 16-byte LDS reads.  A wave stops
 // at its own diagonal chunk, which is masked causally.
-// Grid order: the tiles with the most chunks first, heads innermost (B*H is usually a
-// multiple of 8, so each XCD keeps a fixed subset of heads and their K/V in its L2).
+// Grid order: head-major (the resident workgroups cover one or two heads, whose K/V
+// then stay in L2 / the last-level cache), tiles with the most chunks first.
 // With o == NULL only the running max and sums are kept (log-sum-exp only).
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -31,8 +31,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int tile = ntile - 1 - (int)(blockIdx.x / BH);
-  const int64_t bh = blockIdx.x % BH;
+  // head-major order: the resident workgroups cover few heads, so their K/V stay in
+  // the L2 / last-level cache; within a head the tiles with the most work go first
+  const int64_t bh = blockIdx.x / ntile;
+  const int tile = ntile - 1 - (int)(blockIdx.x % ntile);
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
   const uint16_t* vh = v + bh * (int64_t)L * D;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < KF_W; ++i) sk[st][w * KF_W + i][lane] = kreg[i];
     if (WANT_O) {
 #pragma unroll
-      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = transpose8x8_b16(vreg[i]);
+      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = transpose8x8_b16_dpp(vreg[i]);
     }
   };
 
@@ -122,11 +124,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mnew = fmaxf(m[nt], mx);
-        const float alpha = exp2f(m[nt] - mnew);
+        const float alpha = fast_exp2(m[nt] - mnew);
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sv2[i] = exp2f(sv2[i] - mnew);
+          sv2[i] = fast_exp2(sv2[i] - mnew);
           ps += sv2[i];
         }
         lsum[nt] = lsum[nt] * alpha + ps;
