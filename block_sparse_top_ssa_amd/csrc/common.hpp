@@ -68,6 +68,14 @@ template <> struct Elem<uint16_t> {
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Logical workgroup id such that consecutive logical ids run on the same XCD (the
+// dispatcher hands workgroup i to XCD i % 8): XCD x gets logical ids
+// [x*G/8, (x+1)*G/8) in order.  Identity when G is not a multiple of 8.
+__device__ __forceinline__ int64_t xcd_logical(int64_t i, int64_t G) {
+  if (G % 8) return i;
+  return (i % 8) * (G / 8) + i / 8;
+}
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

@@ -9,13 +9,17 @@
 // LDS stage in MFMA-fragment order (K as is; V transposed in registers first), so
 // every wave reads its fragments with conflict-free 16-byte LDS reads.  A wave stops
 // at its own diagonal chunk, which is masked causally.
-// Grid order: head-major (the resident workgroups cover one or two heads, whose K/V
-// then stay in L2 / the last-level cache), tiles with the most chunks first.
+// Grid order: head-major, tiles with the most chunks first, remapped so that each XCD
+// works through a contiguous range (one head at a time), keeping that head's K/V in its
+// L2.  The softmax exponent reference trails the running row max by up to 2^8, so the
+// O accumulators are rescaled only when the max jumps (rare after the first chunks).
 // With o == NULL only the running max and sums are kept (log-sum-exp only).
 #include "launch.hpp"
 #include "mfma.hpp"
 
 namespace ssa {
+
+constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the row max
 
 template <int D, bool WANT_O>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void full_fwd_kernel(
@@ -33,8 +37,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int n = lane & 15, g = lane >> 4;
   // head-major order: the resident workgroups cover few heads, so their K/V stay in
   // the L2 / last-level cache; within a head the tiles with the most work go first
-  const int64_t bh = blockIdx.x / ntile;
-  const int tile = ntile - 1 - (int)(blockIdx.x % ntile);
+  const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);
+  const int64_t bh = wg / ntile;
+  const int tile = ntile - 1 - (int)(wg % ntile);
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
   const uint16_t* vh = v + bh * (int64_t)L * D;
@@ -110,34 +115,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       u32x4 pf[4][2];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        float sv2[16];
+        float sr[16];
         float mx = -__builtin_huge_valf();
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float x = sacc[kt][nt][i] * sl2;
+            float x = sacc[kt][nt][i];
             if (diag && (16 * kt + 4 * g + i > 16 * nt + n)) x = -__builtin_huge_valf();
-            sv2[kt * 4 + i] = x;
+            sr[kt * 4 + i] = x;
             mx = fmaxf(mx, x);
           }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[nt], mx);
-        const float alpha = fast_exp2(m[nt] - mnew);
+        // The exponent reference m[nt] only moves when this chunk's max passes it by
+        // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely.
+        const float mxs = mx * sl2;
+        const bool need = mxs > m[nt] + kLag;
+        if (__builtin_amdgcn_ballot_w64(need)) {
+          const float mnew = need ? mxs : m[nt];
+          const float alpha = fast_exp2(m[nt] - mnew);
+          lsum[nt] *= alpha;
+          if (WANT_O) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
+          }
+          m[nt] = mnew;
+        }
+        const float mneg = -m[nt];
         float ps = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sv2[i] = fast_exp2(sv2[i] - mnew);
-          ps += sv2[i];
+          sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
+          ps += sr[i];
         }
-        lsum[nt] = lsum[nt] * alpha + ps;
-        m[nt] = mnew;
+        lsum[nt] += ps;
         if (WANT_O) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
-          pf[nt][0] = pack_p(&sv2[0], &sv2[4]);
-          pf[nt][1] = pack_p(&sv2[8], &sv2[12]);
+          pf[nt][0] = pack_p(&sr[0], &sr[4]);
+          pf[nt][1] = pack_p(&sr[8], &sr[12]);
         }
       }
       if (WANT_O) {

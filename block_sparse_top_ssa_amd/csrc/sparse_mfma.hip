@@ -101,8 +101,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int n = lane & 15, g = lane >> 4;
   // head-major order: the resident workgroups cover few heads, so their K/V stay in
   // the L2 / last-level cache; within a head the tiles with the most work go first
-  const int64_t bh = blockIdx.x / ntile;
-  const int tile = ntile - 1 - (int)(blockIdx.x % ntile);
+  const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);  // one head per XCD at a time
+  const int64_t bh = wg / ntile;
+  const int tile = ntile - 1 - (int)(wg % ntile);
   const int t0 = tile * T;
   const int rows = min(T, L - t0);
   const int nb = (t0 + rows - 1) / S;  // candidate blocks: those below the last row's block

@@ -108,8 +108,9 @@ __global__ __launch_bounds__(256) void topk_mfma_kernel(const uint16_t* __restri
   __shared__ uint64_t lists[S][KP];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   const int nn = lane & 15, g = lane >> 4;
-  const int64_t bh = blockIdx.x / n;  // head-major: few heads' block means live at a time
-  const int qb = n - 1 - (int)(blockIdx.x % n);
+  const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);  // one head per XCD at a time
+  const int64_t bh = wg / n;
+  const int qb = n - 1 - (int)(wg % n);
   const int m = min(topk - 1, qb);
   const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
   const float* kmh = km + bh * (int64_t)n * D;
