@@ -39,7 +39,7 @@
 namespace ssa {
 
 constexpr float kGuard = 90.f;  // log2 units
-constexpr int kSlotBytes = 2256;  // P^T fragments (2 KB), 16 row ids, 2 x 16 row sums, chunk ids
+constexpr int kSlotBytes = 2640;  // P^T fragments (2 KB), 16 row ids, 2 x 64 partial row sums, chunk ids
 
 struct SparseLds {
   // byte offsets inside the dynamic LDS block
@@ -74,7 +74,7 @@ __device__ __forceinline__ int ost_granule(int r, int d) {
 struct Slot {
   u32x4 p[2][64];
   int rows[16];
-  float ps_round[16], ps_exact[16];
+  float ps_round[16][4], ps_exact[16][4];  // per row, the partial sums of its 4 lanes
   int chunk, next_chunk, pad0, pad1;
 };
 static_assert(sizeof(Slot) == kSlotBytes, "slot layout");
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto score_item = [&]() {
     const int r = r_cur;
-    const float mr = mrf[r < 0 ? 0 : r];
+    const float mr = r >= 0 ? mrf[r] : __builtin_huge_valf();  // no row: every p is 0
     f32x4 sacc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -362,20 +362,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = sacc[kt][i] * sl2 - mr;
+        const float x = fmaf(sacc[kt][i], sl2, -mr);
         mx = fmaxf(mx, x);
-        p[kt * 4 + i] = r >= 0 ? fast_exp2(x) : 0.f;
+        p[kt * 4 + i] = fast_exp2(x);
         px += p[kt * 4 + i];
       }
-    if (r >= 0 && mx > kGuard) flag[r] = 1;
+    if (mx > kGuard) flag[r] = 1;  // mx is -inf for r < 0
     pub0 = pack_p(&p[0], &p[4]);
     pub1 = pack_p(&p[8], &p[12]);
-    float ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // sum of the rounded p the products use
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    px += __shfl_xor(px, 16);
-    px += __shfl_xor(px, 32);
-    pub_ps = ps;
+    pub_ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // this lane's part of the rounded-p sum
     pub_px = px;
     pub_r = r;
     pub_c = j * CPB + ch;
@@ -418,11 +413,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (have) {
         sl.p[0][lane] = pub0;
         sl.p[1][lane] = pub1;
-        if (g == 0) {
-          sl.rows[n] = pub_r;
-          sl.ps_round[n] = pub_ps;
-          sl.ps_exact[n] = pub_px;
-        }
+        if (g == 0) sl.rows[n] = pub_r;
+        sl.ps_round[n][g] = pub_ps;
+        sl.ps_exact[n][g] = pub_px;
       }
       if (lane == 0) {
         sl.chunk = have ? pub_c : -1;
@@ -435,45 +428,68 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (rd + 1 < my_items) score_item();
     } else {
       // ------------------------------------------------------------ value wave
+      // (1) slot headers and P^T; (2) V^T of freshly loaded chunks; (3) all products;
+      // (4) next round's V loads (registers are free once the products are issued);
+      // (5) read-add-write into the owned columns, slot by slot (slots may share rows).
+      int sc[4], sn[4], sr[4];
+      u32x4 sp[4][2];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const Slot& sl = slots[s];
-        const int c = sl.chunk;
-        if (c >= 0) {
-          if (c != vchunk[s]) {
-            load_v(s, c);
-            vchunk[s] = c;
-            vready[s] = false;
-          }
-          if (!vready[s]) {
+        sc[s] = __builtin_amdgcn_readfirstlane(slots[s].chunk);  // uniform: scalar branches
+        sn[s] = __builtin_amdgcn_readfirstlane(slots[s].next_chunk);
+        sr[s] = slots[s].rows[n];
+        sp[s][0] = slots[s].p[0][lane];
+        sp[s][1] = slots[s].p[1][lane];
+      }
 #pragma unroll
-            for (int dl = 0; dl < DTW; ++dl) {
-              vfr[s][dl][0] = transpose8x8_b16_dpp(vfr[s][dl][0]);
-              vfr[s][dl][1] = transpose8x8_b16_dpp(vfr[s][dl][1]);
-            }
-            vready[s] = true;
-          }
-          const u32x4 pf0 = sl.p[0][lane], pf1 = sl.p[1][lane];
-          const int r = sl.rows[n];
+      for (int s = 0; s < 4; ++s) {
+        if (sc[s] >= 0 && sc[s] != vchunk[s]) {  // first tile of a stream: not prefetched
+          load_v(s, sc[s]);
+          vchunk[s] = sc[s];
+          vready[s] = false;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (sc[s] >= 0 && !vready[s]) {
 #pragma unroll
           for (int dl = 0; dl < DTW; ++dl) {
-            f32x4 acc = f32x4{0, 0, 0, 0};
-            acc = mfma_bf16(vfr[s][dl][0], pf0, acc);
-            acc = mfma_bf16(vfr[s][dl][1], pf1, acc);
-            if (r >= 0) {
-              f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
-              *gp = *gp + acc;
-            }
+            vfr[s][dl][0] = transpose8x8_b16_dpp(vfr[s][dl][0]);
+            vfr[s][dl][1] = transpose8x8_b16_dpp(vfr[s][dl][1]);
           }
-          if (pw == 0 && g == 0 && r >= 0) {
-            lst[r] += sl.ps_round[n];
-            lsx[r] += sl.ps_exact[n];
+          vready[s] = true;
+        }
+      }
+      f32x4 acc[4][DTW];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int dl = 0; dl < DTW; ++dl) {
+          acc[s][dl] = mfma_bf16(vfr[s][dl][0], sp[s][0], f32x4{0, 0, 0, 0});
+          acc[s][dl] = mfma_bf16(vfr[s][dl][1], sp[s][1], acc[s][dl]);
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (sc[s] >= 0 && sn[s] >= 0 && sn[s] != sc[s]) {
+          load_v(s, sn[s]);  // used next round
+          vchunk[s] = sn[s];
+          vready[s] = false;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int r = sr[s];
+        if (sc[s] >= 0 && r >= 0) {
+#pragma unroll
+          for (int dl = 0; dl < DTW; ++dl) {
+            f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
+            *gp = *gp + acc[s][dl];
           }
-          const int nc = sl.next_chunk;
-          if (nc >= 0 && nc != c) {
-            load_v(s, nc);  // used next round
-            vchunk[s] = nc;
-            vready[s] = false;
+          if (pw == 0 && g == 0) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&slots[s].ps_round[n][0]);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&slots[s].ps_exact[n][0]);
+            lst[r] += (a[0] + a[1]) + (a[2] + a[3]);
+            lsx[r] += (b[0] + b[1]) + (b[2] + b[3]);
           }
         }
       }
