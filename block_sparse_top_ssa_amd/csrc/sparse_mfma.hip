@@ -43,7 +43,7 @@ constexpr int kSlotBytes = 2640;  // P^T fragments (2 KB), 16 row ids, 2 x 64 pa
 
 struct SparseLds {
   // byte offsets inside the dynamic LDS block
-  int ost, lst, lse2, mref, cnt, off, misc, slots, flag, list, total;
+  int ost, lst, lse2, mref, cnt, off, misc, slots, flag, list, dump, total;
 };
 
 template <int D>
@@ -61,6 +61,8 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
   s.slots = o; o += 4 * kSlotBytes;
   s.flag = o;  o += T;
   s.list = o;  o += T * topk;  // malformed rows may list up to topk blocks below b_t
+  o = (o + 15) & ~15;
+  s.dump = o;  o += 4 * 64 * 16;  // per value-wave lane: target of the updates it skips
   s.total = (o + 15) & ~15;
   return s;
 }
@@ -327,7 +329,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // score-wave state (waves 0-3): the loaded operands of the next tile to score, and
   // the scored tile waiting to be published
   int j = w < 4 ? next_block(w) : nb, ch = 0, it = 0, r_cur = -1;
-  u32x4 kf[4][NC], qf[NC];
+  // Operand registers live across rounds: a score wave keeps the K fragments of its
+  // current chunk in `ra`, a value wave its V^T fragments; one array serves both roles
+  // so the two never hold registers at the same time.
+  constexpr int RA = 4 * NC > 8 * DTW ? 4 * NC : 8 * DTW;
+  u32x4 ra[RA], qf[NC];
   u32x4 pub0 = u32x4{0, 0, 0, 0}, pub1 = u32x4{0, 0, 0, 0};
   int pub_r = -1, pub_c = -1, pub_nc = -1;
   float pub_ps = 0.f, pub_px = 0.f;
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
+        for (int cc = 0; cc < NC; ++cc) ra[kt * NC + cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
     }
     const uint16_t* qrow = qh + (int64_t)(t0 + (r_cur < 0 ? 0 : r_cur)) * D;
 #pragma unroll
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kt = 0; kt < 4; ++kt) {
       sacc[kt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
+      for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(ra[kt * NC + cc], qf[cc], sacc[kt]);
     }
     float p[16], mx = -__builtin_huge_valf(), px = 0.f;
 #pragma unroll
@@ -396,14 +402,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   // value-wave state (waves 4-7): V^T fragments of its column slice, per score-wave stream
   const int pw = w - 4;
-  u32x4 vfr[4][DTW][2];
   int vchunk[4] = {-1, -1, -1, -1};
   bool vready[4] = {false, false, false, false};
   auto load_v = [&](int s, int c) {
 #pragma unroll
     for (int dl = 0; dl < DTW; ++dl)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) vfr[s][dl][kc] = load_v_raw<D>(vh, c * 64, pw * DTW + dl, kc);
+      for (int kc = 0; kc < 2; ++kc) ra[(s * DTW + dl) * 2 + kc] = load_v_raw<D>(vh, c * 64, pw * DTW + dl, kc);
   };
 
   for (int rd = 0; rd < rounds; ++rd) {
@@ -454,8 +459,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (sc[s] >= 0 && !vready[s]) {
 #pragma unroll
           for (int dl = 0; dl < DTW; ++dl) {
-            vfr[s][dl][0] = transpose8x8_b16_dpp(vfr[s][dl][0]);
-            vfr[s][dl][1] = transpose8x8_b16_dpp(vfr[s][dl][1]);
+            ra[(s * DTW + dl) * 2] = transpose8x8_b16_dpp(ra[(s * DTW + dl) * 2]);
+            ra[(s * DTW + dl) * 2 + 1] = transpose8x8_b16_dpp(ra[(s * DTW + dl) * 2 + 1]);
           }
           vready[s] = true;
         }
@@ -465,8 +470,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int dl = 0; dl < DTW; ++dl) {
-          acc[s][dl] = mfma_bf16(vfr[s][dl][0], sp[s][0], f32x4{0, 0, 0, 0});
-          acc[s][dl] = mfma_bf16(vfr[s][dl][1], sp[s][1], acc[s][dl]);
+          acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2], sp[s][0], f32x4{0, 0, 0, 0});
+          acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2 + 1], sp[s][1], acc[s][dl]);
         }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -476,22 +481,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           vready[s] = false;
         }
       }
+      // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
+      // any lane), and the in-order LDS queue of the wave makes each slot's writes land
+      // before the next slot's reads.  Value wave 0 also adds the rounded-p row sums,
+      // wave 1 the exact ones.  Every lane reads and writes for each slot; lanes with no
+      // row use their own dump granule, so the code has no branches and exact waits.
+      float* dump = reinterpret_cast<float*>(smem + lay.dump) + (pw * 64 + lane) * 4;
+      const int sum_off = pw == 0 ? offsetof(Slot, ps_round) : offsetof(Slot, ps_exact);
+      float* const lsum = pw == 0 ? lst : lsx;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int r = sr[s];
-        if (sc[s] >= 0 && r >= 0) {
+        const bool live = sc[s] >= 0 && sr[s] >= 0;
+        float* gp[DTW];
 #pragma unroll
-          for (int dl = 0; dl < DTW; ++dl) {
-            f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
-            *gp = *gp + acc[s][dl];
-          }
-          if (pw == 0 && g == 0) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(&slots[s].ps_round[n][0]);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&slots[s].ps_exact[n][0]);
-            lst[r] += (a[0] + a[1]) + (a[2] + a[3]);
-            lsx[r] += (b[0] + b[1]) + (b[2] + b[3]);
-          }
-        }
+        for (int dl = 0; dl < DTW; ++dl)
+          gp[dl] = live ? ost + ost_granule<D>(sr[s], 16 * (pw * DTW + dl) + 4 * g) : dump;
+        float* pl = live && pw < 2 && g == 0 ? lsum + sr[s] : dump;
+        const f32x4 part =
+            *reinterpret_cast<const f32x4*>(reinterpret_cast<const unsigned char*>(&slots[s]) + sum_off + n * 16);
+        f32x4 cur[DTW];
+#pragma unroll
+        for (int dl = 0; dl < DTW; ++dl) cur[dl] = *reinterpret_cast<const f32x4*>(gp[dl]);
+        const float l0 = *pl;
+#pragma unroll
+        for (int dl = 0; dl < DTW; ++dl) *reinterpret_cast<f32x4*>(gp[dl]) = cur[dl] + acc[s][dl];
+        *pl = l0 + ((part[0] + part[1]) + (part[2] + part[3]));
       }
     }
     __syncthreads();
