@@ -8,6 +8,8 @@
 // each key block that any of its rows kept exactly once, multiplying only the rows
 // that kept it (gathered into 16-row MFMA column tiles):
 //
+//  0. (separate pass) V is rewritten once into MFMA fragment order, so the PV operand
+//     V^T is loaded with one coalesced 16-byte load per lane and no lane transposes;
 //  1. inverted index: from idx, count per block the rows that kept it, prefix-sum,
 //     and list the row ids per block (LDS, one byte per entry);
 //  2. own-block phase: each 64-row query chunk against its own 64-key chunk (causal)
@@ -17,13 +19,14 @@
 //     * four score waves each take the blocks j = s (mod 4) in ascending order and,
 //       per round, one 16-row tile of the rows that kept the current 64-key chunk:
 //       S^T = K Q^T, p = exp2(s - m_ref) rounded to bf16, row sums of the rounded p;
-//       P^T, the row ids and the sums go to a double-buffered LDS slot;
+//       P^T, the row ids and the sums go to the wave's LDS slot;
 //     * four value waves each own a 32-column slice of the O state of every row; per
 //       round they read the four slots of the previous round, load the V^T fragments
 //       of their slice (prefetched one round ahead), form O^T = V^T P^T for their
 //       columns and add it into the O state with plain 16-byte read-add-write.
 //     Each O element has a single writer, so no atomics are needed (LDS float atomics
-//     run at a fraction of a lane per clock on this chip); one barrier per round.
+//     run at a fraction of a lane per clock on this chip).  Two barriers per round:
+//     after the slots are published and after they are consumed.
 //     Because every row uses the fixed reference m_ref, partial sums from different
 //     blocks simply add, in any order, with no rescaling.
 //  4. finalize: o = O / l (bf16), lse = m_ref + log l.
@@ -32,6 +35,8 @@
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass
 // 2^kGuard), the row is flagged and recomputed exactly by one wave with a running-max
 // softmax at the end; with unit-scale inputs this does not happen.
+#include <mutex>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 #include "rowattn.hpp"
@@ -89,11 +94,28 @@ __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
   return s;
 }
 
+// ---------------------------------------------------------------- V in fragment order
+// Fragment (chunk c, d tile dt, key half kc) of a head: 64 lanes x 16 bytes; lane
+// l = 16 g + i holds V[64 c + kappa(kc, g, 0..7)][16 dt + i], the A operand of
+// O^T = V^T P^T.  One workgroup per 64-key chunk.
+template <int D>
+__global__ __launch_bounds__(256) void vfrag_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt, int L) {
+  constexpr int F = 2 * (D / 16);  // fragments per chunk
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t chunk = blockIdx.x;  // over B*H*(L/64), head-major
+  const int nck = L / 64;
+  const int64_t bh = chunk / nck;
+  const int c = (int)(chunk % nck);
+  const uint16_t* vh = v + bh * (int64_t)L * D;
+  for (int f = w; f < F; f += 4)
+    vt[(chunk * F + f) * 64 + lane] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, f >> 1, f & 1));
+}
+
 template <int D, int S, int T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH,
-    int ntile, float sl2, float scale) {
+    const u32x4* __restrict__ vt, const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale) {
   constexpr int NW = 8, NTH = 512;
   constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
   constexpr int DTW = NDT / 4;  // d tiles per value wave
@@ -124,7 +146,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
   const uint16_t* vh = v + bh * (int64_t)L * D;
+  const u32x4* vth = vt + bh * (int64_t)(L / 64) * NDT * 2 * 64;
   const int32_t* ih = idx + bh * (int64_t)L * topk;
+  auto vt_frag = [&](int c, int dt, int kc) -> u32x4 { return vth[((int64_t)(c * NDT + dt) * 2 + kc) * 64 + lane]; };
 
   // Walk the valid entries of one row's idx list: distinct blocks below b_t, each
   // greater than the entry used before it.  Entries are loaded 8 at a time.
@@ -197,7 +221,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c_diag * 64, dt, kc));
+      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = vt_frag(c_diag, dt, kc);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int rl = rq + 16 * nt;  // row offset inside the 64-row chunk
@@ -261,7 +285,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, dt, kc));
+        for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = vt_frag(c, dt, kc);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int r = r0 + 16 * nt + n;
@@ -403,12 +427,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // value-wave state (waves 4-7): V^T fragments of its column slice, per score-wave stream
   const int pw = w - 4;
   int vchunk[4] = {-1, -1, -1, -1};
-  bool vready[4] = {false, false, false, false};
   auto load_v = [&](int s, int c) {
 #pragma unroll
     for (int dl = 0; dl < DTW; ++dl)
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) ra[(s * DTW + dl) * 2 + kc] = load_v_raw<D>(vh, c * 64, pw * DTW + dl, kc);
+      for (int kc = 0; kc < 2; ++kc) ra[(s * DTW + dl) * 2 + kc] = vt_frag(c, pw * DTW + dl, kc);
   };
 
   for (int rd = 0; rd < rounds; ++rd) {
@@ -433,9 +456,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (rd + 1 < my_items) score_item();
     } else {
       // ------------------------------------------------------------ value wave
-      // (1) slot headers and P^T; (2) V^T of freshly loaded chunks; (3) all products;
-      // (4) next round's V loads (registers are free once the products are issued);
-      // (5) read-add-write into the owned columns, slot by slot (slots may share rows).
+      // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
+      // loaded a round ahead); (3) all products; (4) next round's V^T loads (registers
+      // are free once the products are issued); (5) read-add-write into the owned
+      // columns, slot by slot (slots may share rows).
       int sc[4], sn[4], sr[4];
       u32x4 sp[4][2];
 #pragma unroll
@@ -451,18 +475,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (sc[s] >= 0 && sc[s] != vchunk[s]) {  // first tile of a stream: not prefetched
           load_v(s, sc[s]);
           vchunk[s] = sc[s];
-          vready[s] = false;
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (sc[s] >= 0 && !vready[s]) {
-#pragma unroll
-          for (int dl = 0; dl < DTW; ++dl) {
-            ra[(s * DTW + dl) * 2] = transpose8x8_b16_dpp(ra[(s * DTW + dl) * 2]);
-            ra[(s * DTW + dl) * 2 + 1] = transpose8x8_b16_dpp(ra[(s * DTW + dl) * 2 + 1]);
-          }
-          vready[s] = true;
         }
       }
       f32x4 acc[4][DTW];
@@ -478,7 +490,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (sc[s] >= 0 && sn[s] >= 0 && sn[s] != sc[s]) {
           load_v(s, sn[s]);  // used next round
           vchunk[s] = sn[s];
-          vready[s] = false;
         }
       }
       // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
@@ -565,9 +576,38 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
   return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)) > 0;
 }
 
+// ---------------------------------------------------------------- workspace
+// The V^T copy lives in stream-ordered memory from a pool the library keeps per
+// device: freed blocks stay in the pool, so after the first call of a size the
+// allocation is a pool hit that neither blocks the host nor synchronises the device.
+static hipError_t workspace_pool(hipMemPool_t* out) {
+  static std::mutex mu;
+  static hipMemPool_t pools[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    e = hipMemPoolCreate(&p, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = ~0ull;
+    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    pools[dev] = p;
+  }
+  *out = pools[dev];
+  return hipSuccess;
+}
+
 template <int D, int S, int T>
-static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             int topk, float scale, void* o, float* lse, hipStream_t st) {
+static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
+                             const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
   const int lds = sparse_lds_layout<D>(T, d.n(), topk).total;
@@ -575,28 +615,48 @@ static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const 
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), idx, topk,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, idx, topk,
                      static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale);
   return hipGetLastError();
 }
 
 template <int D, int S>
-static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
-                             int topk, float scale, void* o, float* lse, hipStream_t st) {
+static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
+                             const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int T = pick_tile<D>(d, topk);
-  if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, idx, topk, scale, o, lse, st);
-  return run_sparse<D, S, 128>(d, q, k, v, idx, topk, scale, o, lse, st);
+  if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  return run_sparse<D, S, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+}
+
+template <int D>
+static hipError_t run_vfrag(const Dims& d, const void* v, u32x4* vt, hipStream_t st) {
+  const int64_t grid = d.bh() * (d.L / 64);
+  hipLaunchKernelGGL((vfrag_kernel<D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(v), vt,
+                     d.L);
+  return hipGetLastError();
 }
 
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
                                 int topk, float scale, void* o, float* lse, hipStream_t st) {
   LaunchResult r;
-  if (d.D == 128)
-    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, idx, topk, scale, o, lse, st)
-                      : dispatch_t<128, 128>(d, q, k, v, idx, topk, scale, o, lse, st);
-  else
-    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, idx, topk, scale, o, lse, st)
-                      : dispatch_t<64, 128>(d, q, k, v, idx, topk, scale, o, lse, st);
+  hipMemPool_t pool = nullptr;
+  r.err = workspace_pool(&pool);
+  if (r.err != hipSuccess) return r;
+  void* ws = nullptr;
+  r.err = hipMallocFromPoolAsync(&ws, (size_t)d.tokens() * d.D * 2, pool, st);
+  if (r.err != hipSuccess) return r;
+  u32x4* vt = static_cast<u32x4*>(ws);
+  r.err = d.D == 128 ? run_vfrag<128>(d, v, vt, st) : run_vfrag<64>(d, v, vt, st);
+  if (r.err == hipSuccess) {
+    if (d.D == 128)
+      r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
+                        : dispatch_t<128, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+    else
+      r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
+                        : dispatch_t<64, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  }
+  const hipError_t ef = hipFreeAsync(ws, st);
+  if (r.err == hipSuccess) r.err = ef;
   return r;
 }
 

@@ -14,9 +14,10 @@
  *               query at position t lies in block b_t = t / s.
  *  Pointers     every data pointer is a DEVICE pointer (hipMalloc'd, or torch CUDA
  *               memory); q, k, v, o and k_mean 16-byte aligned, idx, lse, sel_score,
- *               l2_dist and dropped 4-byte aligned.  The caller owns every buffer; the library
- *               allocates nothing, keeps no pointer after a call returns, and does not
- *               write outside the outputs named by a call.
+ *               l2_dist and dropped 4-byte aligned.  The caller owns every buffer it
+ *               passes.  The library keeps no pointer to them after a call returns and
+ *               writes nothing outside the outputs named by a call.  One call allocates:
+ *               ssa_sparse_attn_fwd on bf16 takes a transient workspace (see there).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -27,8 +28,9 @@
  *               B*H*L <= 2^24; the current device is gfx950.  A failed launch returns
  *               SSA_ERR_LAUNCH.  ssa_last_error() gives a thread-local message for the
  *               last failing call.  The library never prints, aborts or throws.
- *  Threads      stateless apart from a per-device properties cache filled once;
- *               calls from several threads are safe.
+ *  Threads      stateless apart from a per-device properties cache and a per-device
+ *               workspace pool, each created once under a lock; calls from several
+ *               threads are safe.
  *  Determinism  ssa_block_pool, ssa_block_topk, ssa_full_attn_fwd and ssa_align_stats
  *               are deterministic.  ssa_sparse_attn_fwd accumulates partial sums in an
  *               order that can differ between runs (last-bit fp32 differences, which
@@ -106,6 +108,12 @@ ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_me
  *   o        [B,H,L,D] (dtype)               out: o(t) = sum_{i in A(t)} softmax_i(scale q_t.k_i) v_i,
  *            A(t) = {i <= t : i/s attended}
  *   lse      [B,H,L] float32 or NULL         out (optional): log sum_{i in A(t)} exp(scale q_t.k_i)
+ *   Workspace (bf16 only): B*H*L*D*2 bytes holding v in the layout the matrix-core
+ *   products read, taken from a stream-ordered memory pool that the library keeps per
+ *   device and returned to it on `stream` before the call returns.  The pool keeps the
+ *   memory for reuse, so after the first call of a given size the allocation neither
+ *   blocks the host nor synchronises the device.  If it cannot be had, the call
+ *   returns SSA_ERR_LAUNCH with the HIP message and enqueues nothing else.
  */
 ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v,
                                const int32_t* idx, int32_t topk, float scale, void* o, float* lse,
