@@ -19,14 +19,14 @@
 //     * four score waves each take the blocks j = s (mod 4) in ascending order and,
 //       per round, one 16-row tile of the rows that kept the current 64-key chunk:
 //       S^T = K Q^T, p = exp2(s - m_ref) rounded to bf16, row sums of the rounded p;
-//       P^T, the row ids and the sums go to the wave's LDS slot;
+//       P^T, the row ids and the sums go to the wave's slot in a double-buffered set;
 //     * four value waves each own a 32-column slice of the O state of every row; per
 //       round they read the four slots of the previous round, load the V^T fragments
 //       of their slice (prefetched one round ahead), form O^T = V^T P^T for their
 //       columns and add it into the O state with plain 16-byte read-add-write.
 //     Each O element has a single writer, so no atomics are needed (LDS float atomics
-//     run at a fraction of a lane per clock on this chip).  Two barriers per round:
-//     after the slots are published and after they are consumed.
+//     run at a fraction of a lane per clock on this chip).  While the value waves fold
+//     one slot set, the score waves fill the other: one barrier per round.
 //     Because every row uses the fixed reference m_ref, partial sums from different
 //     blocks simply add, in any order, with no rescaling.
 //  4. finalize: o = O / l (bf16), lse = m_ref + log l.
@@ -44,11 +44,11 @@
 namespace ssa {
 
 constexpr float kGuard = 90.f;  // log2 units
-constexpr int kSlotBytes = 2640;  // P^T fragments (2 KB), 16 row ids, 2 x 64 partial row sums, chunk ids
+constexpr int kSlotBytes = 2256;  // P^T fragments (2 KB), 16 row ids, 2 x 16 row sums, chunk ids
 
 struct SparseLds {
   // byte offsets inside the dynamic LDS block
-  int ost, lst, lse2, mref, cnt, off, misc, slots, flag, list, dump, total;
+  int ost, lst, lse2, mref, off, misc, slots, flag, list, total;
 };
 
 template <int D>
@@ -59,15 +59,13 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
   s.lst = o;   o += T * 4;   // row sums of the bf16-rounded p (normalise o)
   s.lse2 = o;  o += T * 4;   // row sums of the float32 p (log-sum-exp)
   s.mref = o;  o += T * 4;
-  s.cnt = o;   o += nb * 4;
   s.off = o;   o += (nb + 1) * 4;
   s.misc = o;  o += 32;
   o = (o + 15) & ~15;
-  s.slots = o; o += 4 * kSlotBytes;
+  s.slots = o;  // 2 sets x 4 slots; the per-block counters of the index build live here first
+  o += 8 * kSlotBytes > nb * 4 ? 8 * kSlotBytes : nb * 4;
   s.flag = o;  o += T;
   s.list = o;  o += T * topk;  // malformed rows may list up to topk blocks below b_t
-  o = (o + 15) & ~15;
-  s.dump = o;  o += 4 * 64 * 16;  // per value-wave lane: target of the updates it skips
   s.total = (o + 15) & ~15;
   return s;
 }
@@ -81,7 +79,7 @@ __device__ __forceinline__ int ost_granule(int r, int d) {
 struct Slot {
   u32x4 p[2][64];
   int rows[16];
-  float ps_round[16][4], ps_exact[16][4];  // per row, the partial sums of its 4 lanes
+  float ps_round[16], ps_exact[16];  // row sums of the bf16-rounded and of the float32 p
   int chunk, next_chunk, pad0, pad1;
 };
 static_assert(sizeof(Slot) == kSlotBytes, "slot layout");
@@ -136,10 +134,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float* lst = reinterpret_cast<float*>(smem + lay.lst);
   float* lsx = reinterpret_cast<float*>(smem + lay.lse2);
   float* mrf = reinterpret_cast<float*>(smem + lay.mref);
-  int* cnt = reinterpret_cast<int*>(smem + lay.cnt);
+  int* cnt = reinterpret_cast<int*>(smem + lay.slots);  // index build only
   int* off = reinterpret_cast<int*>(smem + lay.off);
   int* misc = reinterpret_cast<int*>(smem + lay.misc);
-  Slot* slots = reinterpret_cast<Slot*>(smem + lay.slots);  // one per score wave
+  Slot* slots = reinterpret_cast<Slot*>(smem + lay.slots);  // [2][4]: set, score wave
   uint8_t* flag = smem + lay.flag;
   uint8_t* list = smem + lay.list;
 
@@ -400,8 +398,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (mx > kGuard) flag[r] = 1;  // mx is -inf for r < 0
     pub0 = pack_p(&p[0], &p[4]);
     pub1 = pack_p(&p[8], &p[12]);
-    pub_ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // this lane's part of the rounded-p sum
-    pub_px = px;
+    pub_ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // sum of the rounded p the products use
+    pub_ps += __shfl_xor(pub_ps, 16);
+    pub_ps += __shfl_xor(pub_ps, 32);
+    pub_px = px + __shfl_xor(px, 16);
+    pub_px += __shfl_xor(pub_px, 32);
     pub_r = r;
     pub_c = j * CPB + ch;
     // advance to the next tile and issue its loads (scored next round)
@@ -434,26 +435,34 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int kc = 0; kc < 2; ++kc) ra[(s * DTW + dl) * 2 + kc] = vt_frag(c, pw * DTW + dl, kc);
   };
 
-  for (int rd = 0; rd < rounds; ++rd) {
-    if (w < 4) {  // publish the tile scored for this round
-      Slot& sl = slots[w];
-      const bool have = rd < my_items;
-      if (have) {
-        sl.p[0][lane] = pub0;
-        sl.p[1][lane] = pub1;
-        if (g == 0) sl.rows[n] = pub_r;
-        sl.ps_round[n][g] = pub_ps;
-        sl.ps_exact[n][g] = pub_px;
-      }
-      if (lane == 0) {
-        sl.chunk = have ? pub_c : -1;
-        sl.next_chunk = have ? pub_nc : -1;
+  // The tile scored last goes to the wave's slot in set `set` (chunk -1: nothing).
+  auto publish = [&](int set, bool have) {
+    Slot& sl = slots[set * 4 + w];
+    if (have) {
+      sl.p[0][lane] = pub0;
+      sl.p[1][lane] = pub1;
+      if (g == 0) {
+        sl.rows[n] = pub_r;
+        sl.ps_round[n] = pub_ps;
+        sl.ps_exact[n] = pub_px;
       }
     }
-    __syncthreads();
+    if (lane == 0) {
+      sl.chunk = have ? pub_c : -1;
+      sl.next_chunk = have ? pub_nc : -1;
+    }
+  };
+  if (w < 4) publish(0, my_items > 0);
+  __syncthreads();
+  // Round rd: the value waves fold slot set rd % 2 while the score waves score their
+  // next tile and publish it in the other set; one barrier per round.
+  for (int rd = 0; rd < rounds; ++rd) {
+    const Slot* const cs = slots + (rd & 1) * 4;
     if (w < 4) {
       // ------------------------------------------------------------ score wave: next tile
-      if (rd + 1 < my_items) score_item();
+      const bool more = rd + 1 < my_items;
+      if (more) score_item();
+      publish((rd + 1) & 1, more);
     } else {
       // ------------------------------------------------------------ value wave
       // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
@@ -464,11 +473,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       u32x4 sp[4][2];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sc[s] = __builtin_amdgcn_readfirstlane(slots[s].chunk);  // uniform: scalar branches
-        sn[s] = __builtin_amdgcn_readfirstlane(slots[s].next_chunk);
-        sr[s] = slots[s].rows[n];
-        sp[s][0] = slots[s].p[0][lane];
-        sp[s][1] = slots[s].p[1][lane];
+        sc[s] = __builtin_amdgcn_readfirstlane(cs[s].chunk);  // uniform: scalar branches
+        sn[s] = __builtin_amdgcn_readfirstlane(cs[s].next_chunk);
+        sr[s] = cs[s].rows[n];
+        sp[s][0] = cs[s].p[0][lane];
+        sp[s][1] = cs[s].p[1][lane];
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -495,28 +504,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
       // any lane), and the in-order LDS queue of the wave makes each slot's writes land
       // before the next slot's reads.  Value wave 0 also adds the rounded-p row sums,
-      // wave 1 the exact ones.  Every lane reads and writes for each slot; lanes with no
-      // row use their own dump granule, so the code has no branches and exact waits.
-      float* dump = reinterpret_cast<float*>(smem + lay.dump) + (pw * 64 + lane) * 4;
-      const int sum_off = pw == 0 ? offsetof(Slot, ps_round) : offsetof(Slot, ps_exact);
-      float* const lsum = pw == 0 ? lst : lsx;
+      // wave 1 the exact ones.
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bool live = sc[s] >= 0 && sr[s] >= 0;
-        float* gp[DTW];
+        const int r = sr[s];
+        if (sc[s] >= 0 && r >= 0) {
+          f32x4 cv[DTW];
+          f32x4* gp[DTW];
 #pragma unroll
-        for (int dl = 0; dl < DTW; ++dl)
-          gp[dl] = live ? ost + ost_granule<D>(sr[s], 16 * (pw * DTW + dl) + 4 * g) : dump;
-        float* pl = live && pw < 2 && g == 0 ? lsum + sr[s] : dump;
-        const f32x4 part =
-            *reinterpret_cast<const f32x4*>(reinterpret_cast<const unsigned char*>(&slots[s]) + sum_off + n * 16);
-        f32x4 cur[DTW];
+          for (int dl = 0; dl < DTW; ++dl) {
+            gp[dl] = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
+            cv[dl] = *gp[dl];
+          }
+          if (pw < 2 && g == 0) {
+            float* ls = pw == 0 ? lst : lsx;
+            ls[r] += pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
+          }
 #pragma unroll
-        for (int dl = 0; dl < DTW; ++dl) cur[dl] = *reinterpret_cast<const f32x4*>(gp[dl]);
-        const float l0 = *pl;
-#pragma unroll
-        for (int dl = 0; dl < DTW; ++dl) *reinterpret_cast<f32x4*>(gp[dl]) = cur[dl] + acc[s][dl];
-        *pl = l0 + ((part[0] + part[1]) + (part[2] + part[3]));
+          for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
+        }
       }
     }
     __syncthreads();
