@@ -4,17 +4,27 @@
 //
 // All rows of one query block share the same candidates (the blocks before it), so a
 // workgroup owns one query block of one (b, h) and streams the candidates in chunks
-// of 64:
-//  * scores on MFMA: sigma = q . kbar with kbar (float32) split exactly into three
-//    bf16 terms hi + mid + lo (each the bf16 rounding of what is left), so three bf16
-//    products per element give the float32 dot product (bf16 x bf16 products are
-//    exact in the float32 accumulator).  Each wave scores 16 candidates against all
-//    rows of the block and leaves the scores in LDS;
-//  * selection: per row, one wave turns the chunk's 64 scores into 64-bit keys
-//    (score, then lower block index first), sorts them with a bitonic network across
-//    the lanes and merges them into the row's running list of the best KP keys
-//    (KP = 64 * E, a power of two >= topk - 1), kept in LDS;
-//  * output: the best min(topk-1, b_t) keys, re-sorted by block index, plus b_t.
+// of 64.  Scores are on MFMA: sigma = q . kbar with kbar (float32) split exactly into
+// three bf16 terms hi + mid + lo (each the bf16 rounding of what is left), so three
+// bf16 products per element give the float32 dot product (bf16 x bf16 products are
+// exact in the float32 accumulator).  Each wave scores 16 candidates against all rows
+// of the block and leaves the scores in LDS.  Candidates are ordered by 64-bit keys
+// (score, then lower block index first), so all keys of a row are distinct.
+//
+// Selection of the m = topk - 1 best keys per row (one wave per row at a time):
+//  * m <= 64 (two passes over the scores, computed twice):
+//    1. every lane keeps the largest key among the candidates it sees (j = lane mod
+//       64); the m-th largest of these 64 lane maxima is a lower bound on the row's
+//       m-th largest key, because they are m of its keys;
+//    2. the keys at or above that bound are collected in index order (about 31-45 for
+//       m = 31 on unstructured scores); their m-th largest is then exactly the row's m-th
+//       largest key, and the keys at or above it are emitted in index order.  If more
+//       than 64 keys reach the bound, the m-th largest of the first 64 collected is a
+//       strictly higher bound and pass 2 runs again (only for such rows);
+//  * m > 64: each chunk's 64 keys are sorted across the wave with a bitonic network and
+//    merged into the row's running list of the best 64*E keys in LDS; the result is
+//    re-sorted by block index.
+// Output per row: the selected blocks in ascending order, then b_t, then -1.
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -100,7 +110,7 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
 }
 
 template <int D, int S, int E>
-__global__ __launch_bounds__(256) void topk_mfma_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
+__global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
                                                         int32_t* __restrict__ idx, float* __restrict__ sel, int L,
                                                         int n, int BH, int topk) {
   constexpr int NC = D / 32, NT = S / 16, KP = 64 * E, SCS = 65;
@@ -229,6 +239,195 @@ __global__ __launch_bounds__(256) void topk_mfma_kernel(const uint16_t* __restri
   }
 }
 
+
+// Scores of one 64-candidate chunk against all S rows of the block into sc (wave w
+// takes candidates cb + 16 w .. +15).
+template <int D, int S>
+__device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], const float* __restrict__ kmh, int cb,
+                                            int qb, float (*sc)[65]) {
+  constexpr int NC = D / 32, NT = S / 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nn = lane & 15, g = lane >> 4;
+  const int j = cb + 16 * w + nn;
+  const bool valid = j < qb;
+  u32x4 ah[NC], am[NC], al[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    float x[8];
+    if (valid) {
+      const float* src = kmh + (int64_t)j * D + 32 * cc + 8 * g;
+      const u32x4 w0 = load16(src), w1 = load16(src + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = __uint_as_float(w0[e]);
+        x[4 + e] = __uint_as_float(w1[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    uint32_t h[8], md[8], lo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) split3(x[e], h[e], md[e], lo[e]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ah[cc][e] = h[2 * e] | (h[2 * e + 1] << 16);
+      am[cc][e] = md[2 * e] | (md[2 * e + 1] << 16);
+      al[cc][e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      acc = mfma_bf16(al[cc], qf[nt][cc], acc);
+      acc = mfma_bf16(am[cc], qf[nt][cc], acc);
+      acc = mfma_bf16(ah[cc], qf[nt][cc], acc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[16 * nt + nn][16 * w + 4 * g + i] = acc[i];
+  }
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Two-pass selection for m = topk - 1 <= 64 (see the top of the file).
+template <int D, int S>
+__global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
+                                                          int32_t* __restrict__ idx, float* __restrict__ sel, int L,
+                                                          int n, int BH, int topk) {
+  constexpr int NC = D / 32, NT = S / 16, RPW = S / 4;  // rows per wave
+  __shared__ float sc[S][65];
+  __shared__ uint64_t buf[S][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
+  const int nn = lane & 15;
+  const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);  // one head per XCD at a time
+  const int64_t bh = wg / n;
+  const int qb = n - 1 - (int)(wg % n);
+  const int m = min(topk - 1, qb);
+  const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
+  const float* kmh = km + bh * (int64_t)n * D;
+  int32_t* ih = idx + (bh * L + (int64_t)qb * S) * topk;
+  float* sh = sel ? sel + (bh * L + (int64_t)qb * S) * topk : nullptr;
+  const float inf = __builtin_huge_valf();
+
+  if (m == qb || m == 0) {
+    // every candidate kept (or none to keep): no selection needed
+    for (int it = tid; it < S * topk; it += 256) {
+      const int r = it / topk, p = it % topk;
+      ih[it] = p < qb && m == qb ? p : (p == m ? qb : -1);
+      if (sh) {
+        float v = p == m ? inf : -inf;
+        if (p < m) {
+          float acc = 0.f;
+          const uint16_t* qr = qh + (int64_t)r * D;
+          const float* kr = kmh + (int64_t)p * D;
+          for (int d = 0; d < D; ++d) acc = fmaf(bf16_bits_to_f32(qr[d]), kr[d], acc);
+          v = acc;
+        }
+        sh[it] = v;
+      }
+    }
+    return;
+  }
+
+  u32x4 qf[NT][NC];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(16 * nt + nn) * D, cc);
+  const int nchunks = (qb + 63) / 64;
+
+  // ---- pass 1: lane maxima, and from them a lower bound on each row's m-th key
+  uint64_t lmax[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) lmax[i] = 0;
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    const int cb = chunk * 64;
+    score_chunk<D, S>(qf, kmh, cb, qb, sc);
+    __syncthreads();
+    const int j = cb + lane;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = w + 4 * i;
+      lmax[i] = max_u64(lmax[i], j < qb ? make_key(sc[r][lane], j) : 0ull);
+    }
+    __syncthreads();
+  }
+  uint64_t thr[RPW];
+  bool act[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    thr[i] = shfl_u64(sort64(lmax[i], false), m - 1);  // descending: lane m-1 holds the m-th key
+    act[i] = true;
+  }
+
+  // ---- pass 2: collect the keys at or above the bound, in index order
+  int cnt[RPW];
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+      if (act[i]) cnt[i] = 0;
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+      const int cb = chunk * 64;
+      score_chunk<D, S>(qf, kmh, cb, qb, sc);
+      __syncthreads();
+      const int j = cb + lane;
+#pragma unroll
+      for (int i = 0; i < RPW; ++i) {
+        if (!act[i]) continue;
+        const int r = w + 4 * i;
+        const uint64_t key = j < qb ? make_key(sc[r][lane], j) : 0ull;
+        const bool pass = key >= thr[i];
+        const uint64_t mask = __builtin_amdgcn_ballot_w64(pass);
+        const int pos = cnt[i] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+        if (pass && pos < 64) buf[r][pos] = key;
+        cnt[i] += __builtin_popcountll(mask);
+      }
+      __syncthreads();
+    }
+    // rows that collected more than 64 keys: raise the bound to the m-th largest of
+    // the first 64 collected (a strictly higher bound) and collect again
+    bool again = false;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      if (!act[i]) continue;
+      if (cnt[i] > 64) {
+        const int r = w + 4 * i;
+        thr[i] = shfl_u64(sort64(buf[r][lane], false), m - 1);
+        again = true;
+      } else {
+        act[i] = false;
+      }
+    }
+    if (!__syncthreads_or(again)) break;
+  }
+
+  // ---- output: the m keys at or above the row's exact m-th key, in index order
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = w + 4 * i;
+    const int c = cnt[i];
+    const uint64_t y = lane < c ? buf[r][lane] : 0ull;
+    const uint64_t t = shfl_u64(sort64(y, false), m - 1);
+    const bool take = lane < c && y >= t;
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
+    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+    int32_t* orow = ih + (int64_t)r * topk;
+    float* srow = sh ? sh + (int64_t)r * topk : nullptr;
+    if (take) {
+      orow[pos] = key_index(y);
+      if (srow) srow[pos] = key_score(y);
+    }
+    for (int p = m + lane; p < topk; p += 64) {
+      orow[p] = p == m ? qb : -1;
+      if (srow) srow[p] = p == m ? inf : -inf;
+    }
+  }
+}
+
 static int e_for(int topk) {
   const int need = topk - 1;
   int e = 1;
@@ -242,11 +441,20 @@ bool topk_mfma_supported(const Dims& d, int topk) {
   return d.S * 64 * e <= 8192;  // running lists: S rows x KP keys x 8 bytes <= 64 KB
 }
 
+template <int D, int S>
+static hipError_t run_select(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
+                             hipStream_t st) {
+  const int64_t grid = (int64_t)d.n() * d.bh();
+  hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk);
+  return hipGetLastError();
+}
+
 template <int D, int S, int E>
 static hipError_t run_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                            hipStream_t st) {
   const int64_t grid = (int64_t)d.n() * d.bh();
-  hipLaunchKernelGGL((topk_mfma_kernel<D, S, E>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((topk_merge_kernel<D, S, E>), dim3((unsigned)grid), dim3(256), 0, st,
                      static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk);
   return hipGetLastError();
 }
@@ -255,10 +463,9 @@ template <int D>
 static hipError_t dispatch_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                                 hipStream_t st) {
   const int e = e_for(topk);
-  if (d.S == 64) {
-    if (e == 1) return run_topk<D, 64, 1>(d, q, km, topk, idx, sel, st);
-    return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);
-  }
+  if (e == 1) return d.S == 64 ? run_select<D, 64>(d, q, km, topk, idx, sel, st)
+                                : run_select<D, 128>(d, q, km, topk, idx, sel, st);
+  if (d.S == 64) return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);
   return run_topk<D, 128, 1>(d, q, km, topk, idx, sel, st);
 }
 

@@ -153,6 +153,33 @@ def test_topk_integer_ties_exact(variant):
     np.testing.assert_array_equal(idx, oidx)
 
 
+def test_topk_lane_clustered_scores_exact():
+    """Scores built so that the best blocks sit at few positions modulo 64 (the
+    candidate's lane in a 64-wide chunk): blocks j with j % 64 < 12 score
+    128 + 12 (j // 64) + j % 64, the others -(j % 64); q = e_0 and every key of block j
+    equals (score_j, 0, ..., 0), so kbar and every score are exact small integers.  In
+    the last query block more than 64 candidates reach the first lower bound of the
+    two-pass selection, which must then tighten it and still return exactly the
+    oracle's selection (ties among the negative scores go to the lower index)."""
+    B, H, n, D, s, topk = 1, 1, 256, 128, 64, 32
+    L = n * s
+    j = np.arange(n)
+    score = np.where(j % 64 < 12, 128 + 12 * (j // 64) + j % 64, -(j % 64)).astype(np.float32)
+    k = np.zeros((B, H, L, D), np.float32)
+    k[0, 0, :, 0] = np.repeat(score, s)
+    q = np.zeros((B, H, L, D), np.float32)
+    q[..., 0] = 1.0
+    qd, kd = to_device(W.f32_to_bf16_bits(q), W.BF16), to_device(W.f32_to_bf16_bits(k), W.BF16)
+    km = ssa.block_pool(kd, s)
+    idx = ssa.block_topk(qd, km, s, topk).cpu().numpy()
+    oidx = O.block_topk(q.astype(np.float64), O.block_pool(k.astype(np.float64), s), s, topk)
+    np.testing.assert_array_equal(idx, oidx)
+    # the last block keeps the 31 highest-scoring clustered blocks, then itself
+    last = idx[0, 0, -1]
+    expect = sorted(int(b) for b in j[:n - 1][np.argsort(-score[:n - 1], kind="stable")][:topk - 1])
+    assert list(last[:topk - 1]) == expect and last[topk - 1] == n - 1
+
+
 # ----------------------------------------------------------------------------------
 # whole pipeline on the small workloads (every row)
 # ----------------------------------------------------------------------------------
