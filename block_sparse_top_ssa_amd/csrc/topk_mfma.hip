@@ -30,27 +30,54 @@
 
 namespace ssa {
 
-// bitonic compare-exchange across lanes at distance j; `desc` = this pair sorts descending
-__device__ __forceinline__ uint64_t cx_lanes(uint64_t x, int j, bool desc) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t y = shfl_xor_u64(x, j);
-  const bool lower = (lane & j) == 0;
-  const bool keep_max = lower == desc;
-  return keep_max ? (x > y ? x : y) : (x < y ? x : y);
+// The value held by lane l ^ J, moved with DPP inside 16-lane rows (J <= 8), a
+// swizzle inside 32-lane halves (J = 16) or a permute (J = 32).
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t v) {
+  const int x = (int)v;
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  if constexpr (J == 4) {
+    const int t = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0x5, false);  // row_shl:4 into lanes 0-3, 8-11
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, x, 0x114, 0xF, 0xA, false);  // row_shr:4 into 4-7, 12-15
+  }
+  if constexpr (J == 8) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  if constexpr (J == 16) return (uint32_t)__builtin_amdgcn_ds_swizzle(x, 0x401F);  // and 31, xor 16
+  return (uint32_t)__shfl_xor(x, 32);
 }
 
-// full bitonic sort of 64 lane values; ascending if `asc`
-__device__ __forceinline__ uint64_t sort64(uint64_t x, bool asc) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k2 = 2; k2 <= 64; k2 <<= 1)
-#pragma unroll
-    for (int j = k2 >> 1; j > 0; j >>= 1) {
-      const bool blk_asc = ((lane & k2) == 0) == asc;
-      x = cx_lanes(x, j, !blk_asc);
-    }
-  return x;
+// Bitonic compare-exchange with lane l ^ J: the lane keeps the larger key of the pair
+// if keep_max, else the smaller.
+template <int J>
+__device__ __forceinline__ uint64_t cx_lanes(uint64_t x, bool keep_max) {
+  const uint64_t y = ((uint64_t)xor_lane<J>((uint32_t)(x >> 32)) << 32) | xor_lane<J>((uint32_t)x);
+  return (x > y) == keep_max ? x : y;
 }
+template <int J>
+__device__ __forceinline__ uint64_t cx_lanes_dir(uint64_t x, bool desc) {
+  const int lane = threadIdx.x & 63;
+  return cx_lanes<J>(x, ((lane & J) == 0) == desc);
+}
+
+// one bitonic stage (block size K2, distance J) of a full sort in direction `asc`
+template <int K2, int J>
+__device__ __forceinline__ uint64_t sort_stage(uint64_t x, bool asc) {
+  const int lane = threadIdx.x & 63;
+  const bool blk_asc = ((lane & K2) == 0) == asc;
+  return cx_lanes_dir<J>(x, !blk_asc);
+}
+template <int K2, int J>
+struct SortStages {
+  __device__ static __forceinline__ uint64_t run(uint64_t x, bool asc) {
+    x = sort_stage<K2, J>(x, asc);
+    if constexpr (J > 1) return SortStages<K2, J / 2>::run(x, asc);
+    else if constexpr (K2 < 64) return SortStages<K2 * 2, K2>::run(x, asc);
+    else return x;
+  }
+};
+
+// full bitonic sort of 64 lane values; ascending if `asc`
+__device__ __forceinline__ uint64_t sort64(uint64_t x, bool asc) { return SortStages<2, 1>::run(x, asc); }
 
 // bitonic merge (half-cleaners) of KP = 64*E values laid out as p = e*64 + lane,
 // into descending order
@@ -66,9 +93,17 @@ __device__ __forceinline__ void merge_desc(uint64_t (&x)[E]) {
         x[e + je] = a > b ? b : a;
       }
 #pragma unroll
-  for (int j = 32; j > 0; j >>= 1)
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<32>(x[e], true);
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = cx_lanes(x[e], j, true);
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<16>(x[e], true);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<8>(x[e], true);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<4>(x[e], true);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<2>(x[e], true);
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = cx_lanes_dir<1>(x[e], true);
 }
 
 // full bitonic sort ascending of KP = 64*E values (p = e*64 + lane)
@@ -95,7 +130,15 @@ __device__ __forceinline__ void sort_asc(uint64_t (&x)[E]) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const int p = e * 64 + lane;
-          x[e] = cx_lanes(x[e], j, (p & k2) != 0);
+          const bool desc = (p & k2) != 0;
+          switch (j) {
+            case 32: x[e] = cx_lanes_dir<32>(x[e], desc); break;
+            case 16: x[e] = cx_lanes_dir<16>(x[e], desc); break;
+            case 8: x[e] = cx_lanes_dir<8>(x[e], desc); break;
+            case 4: x[e] = cx_lanes_dir<4>(x[e], desc); break;
+            case 2: x[e] = cx_lanes_dir<2>(x[e], desc); break;
+            default: x[e] = cx_lanes_dir<1>(x[e], desc); break;
+          }
         }
       }
     }
