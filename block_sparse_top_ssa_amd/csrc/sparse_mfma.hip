@@ -73,7 +73,7 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
 // float offset of the 16-byte granule holding O[r][d .. d+3] (d % 4 == 0)
 template <int D>
 __device__ __forceinline__ int ost_granule(int r, int d) {
-  return r * D + ((((d >> 2) ^ (r & 7))) << 2);
+  return r * D + ((((d >> 2) ^ (r & 15))) << 2);
 }
 
 struct Slot {
