@@ -7,8 +7,10 @@
 // chunks from key 0 to its last row; chunk c+1 is loaded from HBM/L2 into registers
 // while chunk c is being used, then written to the other half of a double-buffered
 // LDS stage in MFMA-fragment order (K as is; V transposed in registers first), so
-// every wave reads its fragments with conflict-free 16-byte LDS reads.  A wave stops
-// at its own diagonal chunk, which is masked causally.
+// every wave reads its fragments with conflict-free 16-byte LDS reads.  V comes from a
+// copy already in fragment order (written by a short pass before this kernel), so
+// staging V^T is a plain copy.  A wave stops at its own diagonal chunk, which is masked
+// causally.
 // Grid order: head-major, tiles with the most chunks first, remapped so that each XCD
 // works through a contiguous range (one head at a time), keeping that head's K/V in its
 // L2.  The softmax exponent reference trails the running row max by up to 2^8, so the
@@ -23,7 +25,7 @@ constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the 
 
 template <int D, bool WANT_O>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void full_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
     uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2) {
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
   constexpr int NDT = D / 16;  // d tiles of O^T
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tile = ntile - 1 - (int)(wg % ntile);
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
-  const uint16_t* vh = v + bh * (int64_t)L * D;
+  const u32x4* vth = vt + bh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
   const int r0 = tile * 256 + 64 * w;  // first row of this wave
   const bool active = r0 < L;
   const int cw = r0 / 64;               // this wave's diagonal chunk
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < VF_W; ++i) {
         const int f = w * VF_W + i;
-        vreg[i] = load_v_raw<D>(vh, c * 64, f >> 1, f & 1);
+        vreg[i] = vth[((int64_t)c * VF + f) * 64 + lane];
       }
     }
   };
@@ -85,7 +87,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int i = 0; i < KF_W; ++i) sk[st][w * KF_W + i][lane] = kreg[i];
     if (WANT_O) {
 #pragma unroll
-      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = transpose8x8_b16_dpp(vreg[i]);
+      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = vreg[i];
     }
   };
 
@@ -195,13 +197,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 64 == 0; }
 
 template <int D, bool WANT_O>
-static hipError_t run_full(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
+static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
                            float* lse, hipStream_t st) {
   const int ntile = (d.L + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
   hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(256), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
+                     vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
                      scale * kLog2e);
   return hipGetLastError();
 }
@@ -209,12 +211,19 @@ static hipError_t run_full(const Dims& d, const void* q, const void* k, const vo
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
                               float* lse, hipStream_t st) {
   LaunchResult r;
-  if (o)
-    r.err = d.D == 128 ? run_full<128, true>(d, q, k, v, scale, o, lse, st)
-                       : run_full<64, true>(d, q, k, v, scale, o, lse, st);
-  else
-    r.err = d.D == 128 ? run_full<128, false>(d, q, k, v, scale, o, lse, st)
-                       : run_full<64, false>(d, q, k, v, scale, o, lse, st);
+  if (o) {
+    void* ws = nullptr;
+    r.err = vfrag_acquire(d, v, &ws, st);
+    if (r.err != hipSuccess) return r;
+    const u32x4* vt = static_cast<const u32x4*>(ws);
+    r.err = d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st)
+                       : run_full<64, true>(d, q, k, vt, scale, o, lse, st);
+    const hipError_t ef = vfrag_release(ws, st);
+    if (r.err == hipSuccess) r.err = ef;
+  } else {  // log-sum-exp only: V is not read
+    r.err = d.D == 128 ? run_full<128, false>(d, q, k, nullptr, scale, o, lse, st)
+                       : run_full<64, false>(d, q, k, nullptr, scale, o, lse, st);
+  }
   return r;
 }
 

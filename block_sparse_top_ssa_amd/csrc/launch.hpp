@@ -30,6 +30,13 @@ LaunchResult launch_sparse_generic(const Dims& d, const void* q, const void* k, 
 LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, const void* v, float scale,
                                  void* o, float* lse, hipStream_t st);
 
+// V of a bf16 [B,H,L,D] tensor rewritten into MFMA fragment order: per (b,h), 64-key
+// chunk c, 16-column tile dt and key half kc, 64 lanes x 16 bytes, lane 16 g + i holding
+// V[64 c + kappa(kc, g, 0..7)][16 dt + i].  The buffer (B*H*L*D*2 bytes) comes from a
+// stream-ordered pool kept per device; give it back with vfrag_release on the same stream.
+hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st);
+hipError_t vfrag_release(void* ws, hipStream_t st);
+
 // MFMA kernels (bf16 only).  *_supported() tells whether the shape fits.
 bool topk_mfma_supported(const Dims& d, int topk);
 LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,

@@ -35,8 +35,6 @@
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass
 // 2^kGuard), the row is flagged and recomputed exactly by one wave with a running-max
 // softmax at the end; with unit-scale inputs this does not happen.
-#include <mutex>
-
 #include "launch.hpp"
 #include "mfma.hpp"
 #include "rowattn.hpp"
@@ -90,23 +88,6 @@ __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) s += lo_bf16(w[i]) + hi_bf16(w[i]);
   return s;
-}
-
-// ---------------------------------------------------------------- V in fragment order
-// Fragment (chunk c, d tile dt, key half kc) of a head: 64 lanes x 16 bytes; lane
-// l = 16 g + i holds V[64 c + kappa(kc, g, 0..7)][16 dt + i], the A operand of
-// O^T = V^T P^T.  One workgroup per 64-key chunk.
-template <int D>
-__global__ __launch_bounds__(256) void vfrag_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt, int L) {
-  constexpr int F = 2 * (D / 16);  // fragments per chunk
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t chunk = blockIdx.x;  // over B*H*(L/64), head-major
-  const int nck = L / 64;
-  const int64_t bh = chunk / nck;
-  const int c = (int)(chunk % nck);
-  const uint16_t* vh = v + bh * (int64_t)L * D;
-  for (int f = w; f < F; f += 4)
-    vt[(chunk * F + f) * 64 + lane] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, f >> 1, f & 1));
 }
 
 template <int D, int S, int T>
@@ -582,35 +563,6 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
   return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)) > 0;
 }
 
-// ---------------------------------------------------------------- workspace
-// The V^T copy lives in stream-ordered memory from a pool the library keeps per
-// device: freed blocks stay in the pool, so after the first call of a size the
-// allocation is a pool hit that neither blocks the host nor synchronises the device.
-static hipError_t workspace_pool(hipMemPool_t* out) {
-  static std::mutex mu;
-  static hipMemPool_t pools[64] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(mu);
-  if (!pools[dev]) {
-    hipMemPoolProps props = {};
-    props.allocType = hipMemAllocationTypePinned;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t p = nullptr;
-    e = hipMemPoolCreate(&p, &props);
-    if (e != hipSuccess) return e;
-    uint64_t keep = ~0ull;
-    e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-    if (e != hipSuccess) return e;
-    pools[dev] = p;
-  }
-  *out = pools[dev];
-  return hipSuccess;
-}
-
 template <int D, int S, int T>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
                              const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
@@ -634,34 +586,20 @@ static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const 
   return run_sparse<D, S, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
 }
 
-template <int D>
-static hipError_t run_vfrag(const Dims& d, const void* v, u32x4* vt, hipStream_t st) {
-  const int64_t grid = d.bh() * (d.L / 64);
-  hipLaunchKernelGGL((vfrag_kernel<D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(v), vt,
-                     d.L);
-  return hipGetLastError();
-}
-
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
                                 int topk, float scale, void* o, float* lse, hipStream_t st) {
   LaunchResult r;
-  hipMemPool_t pool = nullptr;
-  r.err = workspace_pool(&pool);
-  if (r.err != hipSuccess) return r;
   void* ws = nullptr;
-  r.err = hipMallocFromPoolAsync(&ws, (size_t)d.tokens() * d.D * 2, pool, st);
+  r.err = vfrag_acquire(d, v, &ws, st);
   if (r.err != hipSuccess) return r;
-  u32x4* vt = static_cast<u32x4*>(ws);
-  r.err = d.D == 128 ? run_vfrag<128>(d, v, vt, st) : run_vfrag<64>(d, v, vt, st);
-  if (r.err == hipSuccess) {
-    if (d.D == 128)
-      r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
-                        : dispatch_t<128, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
-    else
-      r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
-                        : dispatch_t<64, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
-  }
-  const hipError_t ef = hipFreeAsync(ws, st);
+  const u32x4* vt = static_cast<const u32x4*>(ws);
+  if (d.D == 128)
+    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<128, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  else
+    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<64, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  const hipError_t ef = vfrag_release(ws, st);
   if (r.err == hipSuccess) r.err = ef;
   return r;
 }
