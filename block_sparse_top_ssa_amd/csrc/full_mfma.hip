@@ -106,14 +106,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+      // K fragments read one ahead of their products (the next LDS read is in flight
+      // while the current fragment's four products run)
+      u32x4 kf = sk[st][0][lane];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc)
+      for (int f = 0; f < KF; ++f) {
+        const int cc = f / 4, kt = f % 4;  // fragment kt * NC + cc, in cc-major order
+        const u32x4 kn = f + 1 < KF ? sk[st][((f + 1) % 4) * NC + (f + 1) / 4][lane] : kf;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const u32x4 kf = sk[st][kt * NC + cc][lane];
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
-        }
+        for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
+        kf = kn;
+      }
       u32x4 pf[4][2];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
@@ -158,14 +161,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
       if (WANT_O) {
+        u32x4 vf = sv[st][0][lane];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+        for (int f = 0; f < VF; ++f) {  // fragment dt * 2 + kc, read one ahead
+          const int dt = f / 2, kc = f % 2;
+          const u32x4 vn = f + 1 < VF ? sv[st][f + 1][lane] : vf;
 #pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const u32x4 vf = sv[st][dt * 2 + kc][lane];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
-          }
+          for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
+          vf = vn;
+        }
       }
     }
     if (more) stage_store(st ^ 1);
