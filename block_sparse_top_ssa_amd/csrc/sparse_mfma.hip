@@ -130,17 +130,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto vt_frag = [&](int c, int dt, int kc) -> u32x4 { return vth[((int64_t)(c * NDT + dt) * 2 + kc) * 64 + lane]; };
 
   // Walk the valid entries of one row's idx list: distinct blocks below b_t, each
-  // greater than the entry used before it.  Entries are loaded 8 at a time.
+  // greater than the entry used before it.  Entries are loaded 32 at a time.
   auto for_each_entry = [&](int t, auto&& fn) {
     const int bt = t / S;
     const int32_t* ir = ih + (int64_t)t * topk;
     int prev = -1;
-    for (int e0 = 0; e0 < topk; e0 += 8) {
-      int jj[8];
+    for (int e0 = 0; e0 < topk; e0 += 32) {
+      int jj[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) jj[u] = e0 + u < topk ? ir[e0 + u] : -1;
+      for (int u = 0; u < 32; ++u) jj[u] = e0 + u < topk ? ir[e0 + u] : -1;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 32; ++u) {
         const int j = jj[u];
         if (j > prev && j < bt) {
           prev = j;
@@ -320,10 +320,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return j < nb ? j : nb;
   };
   __syncthreads();  // off[] and the own-block state are complete
-  if (w < 4 && lane == 0) {
+  if (w < 4) {  // items of score wave w: tiles of the blocks j = w (mod 4), all lanes counting
     int items = 0;
-    for (int j = next_block(w); j < nb; j = next_block(j + 4)) items += CPB * ((off[j + 1] - off[j] + 15) / 16);
-    misc[w] = items;
+    for (int j = w + 4 * lane; j < nb; j += 256) items += CPB * ((off[j + 1] - off[j] + 15) / 16);
+#pragma unroll
+    for (int o2 = 32; o2 > 0; o2 >>= 1) items += __shfl_xor(items, o2);
+    if (lane == 0) misc[w] = items;
   }
   __syncthreads();
   const int my_items = w < 4 ? misc[w] : 0;
