@@ -1,9 +1,9 @@
 // Dense causal attention forward (the full stream; paper sec. 3, p. 3: each query
 // attends to every preceding token), flash-style on MFMA bf16 with fp32 online softmax.
 //
-// Work split: a workgroup owns 256 consecutive query rows of one (b, h); each of its 4
-// waves owns 64 rows (4 column tiles of 16) and keeps their O^T accumulators, running
-// max and partial sums in registers for the whole sweep.  The workgroup sweeps 64-key
+// Work split: a workgroup owns 256 consecutive query rows of one (b, h); each of its 8
+// waves owns 32 rows (2 column tiles of 16; two waves per SIMD) and keeps their O^T
+// accumulators, running max and partial sums in registers for the whole sweep.  The workgroup sweeps 64-key
 // chunks from key 0 to its last row; chunk c+1 is loaded from HBM/L2 into registers
 // while chunk c is being used, then written to the other half of a double-buffered
 // LDS stage in MFMA-fragment order (K as is; V transposed in registers first), so
@@ -23,15 +23,19 @@ namespace ssa {
 
 constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the row max
 
-template <int D, bool WANT_O>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void full_fwd_kernel(
+// NT = 16-row tiles per wave: 4 (4 waves x 64 rows, one wave per SIMD) or 2 (8 waves x
+// 32 rows, two waves per SIMD, so one wave's softmax can run beside the other's
+// products, at the cost of twice the LDS fragment reads).
+template <int D, bool WANT_O, int NT>
+__global__ __launch_bounds__(1024 / NT) __attribute__((amdgpu_waves_per_eu(4 / NT, 4 / NT))) void full_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
     uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2) {
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
   constexpr int NDT = D / 16;  // d tiles of O^T
   constexpr int KF = 4 * NC;   // K fragments per 64-key chunk
   constexpr int VF = 2 * NDT;  // V^T fragments per 64-key chunk
-  constexpr int KF_W = KF / 4, VF_W = VF / 4;  // fragments each wave loads
+  constexpr int NW = 16 / NT;  // waves per workgroup (256 rows)
+  constexpr int KF_W = KF / NW, VF_W = VF / NW;  // fragments each wave loads
   __shared__ u32x4 sk[2][KF][64];
   __shared__ u32x4 sv[2][VF][64];
 
@@ -45,22 +49,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
   const u32x4* vth = vt + bh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
-  const int r0 = tile * 256 + 64 * w;  // first row of this wave
+  const int r0 = tile * 256 + 16 * NT * w;  // first row of this wave
+  const int rq = r0 % 64;                    // its offset inside its diagonal chunk
   const bool active = r0 < L;
   const int cw = r0 / 64;               // this wave's diagonal chunk
   const int cmax = min(tile * 4 + 3, L / 64 - 1);
 
-  u32x4 qf[4][NC];
+  u32x4 qf[NT][NC];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc)
       qf[nt][cc] = active ? load_q_frag<D>(qh + (int64_t)(r0 + 16 * nt + n) * D, cc) : u32x4{0, 0, 0, 0};
 
-  f32x4 oacc[WANT_O ? NDT : 1][4];
-  float m[4], lsum[4];
+  f32x4 oacc[WANT_O ? NDT : 1][NT];
+  float m[NT], lsum[NT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -__builtin_huge_valf();
     lsum[nt] = 0.f;
 #pragma unroll
@@ -101,11 +106,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if (more) issue_loads(c + 1);
     if (active && c <= cw) {
       const bool diag = c == cw;
-      f32x4 sacc[4][4];
+      f32x4 sacc[4][NT];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
       // K fragments read one ahead of their products (the next LDS read is in flight
       // while the current fragment's four products run)
       u32x4 kf = sk[st][0][lane];
@@ -114,12 +119,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int cc = f / 4, kt = f % 4;  // fragment kt * NC + cc, in cc-major order
         const u32x4 kn = f + 1 < KF ? sk[st][((f + 1) % 4) * NC + (f + 1) / 4][lane] : kf;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
+        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
         kf = kn;
       }
-      u32x4 pf[4][2];
+      u32x4 pf[NT][2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < NT; ++nt) {
         float sr[16];
         float mx = -__builtin_huge_valf();
 #pragma unroll
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float x = sacc[kt][nt][i];
-            if (diag && (16 * kt + 4 * g + i > 16 * nt + n)) x = -__builtin_huge_valf();
+            if (diag && (16 * kt + 4 * g + i > rq + 16 * nt + n)) x = -__builtin_huge_valf();
             sr[kt * 4 + i] = x;
             mx = fmaxf(mx, x);
           }
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int dt = f / 2, kc = f % 2;
           const u32x4 vn = f + 1 < VF ? sv[st][f + 1][lane] : vf;
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
+          for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
           vf = vn;
         }
       }
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   if (!active) return;
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < NT; ++nt) {
     float l = lsum[nt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -200,12 +205,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 64 == 0; }
 
-template <int D, bool WANT_O>
+template <int D, bool WANT_O, int NT = 2>
 static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
                            float* lse, hipStream_t st) {
   const int ntile = (d.L + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
-  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O, NT>), dim3((unsigned)grid), dim3(1024 / NT), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
                      scale * kLog2e);
