@@ -87,6 +87,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
+// Max over the four lanes l, l^16, l^32, l^48 (one per 16-lane row) with the gfx950
+// row-swap permutes: VALU only, no LDS round trip.  Each swap exchanges alternate
+// rows (16 or 32 lanes) between two copies of x, so the two results hold both
+// partners of every pair.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
   lo = __shfl_xor(lo, m);

@@ -23,24 +23,30 @@ namespace ssa {
 
 constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the row max
 
-// NT = 16-row tiles per wave: 4 (4 waves x 64 rows, one wave per SIMD) or 2 (8 waves x
-// 32 rows, two waves per SIMD, so one wave's softmax can run beside the other's
-// products, at the cost of twice the LDS fragment reads).
-template <int D, bool WANT_O, int NT>
-__global__ __launch_bounds__(1024 / NT) __attribute__((amdgpu_waves_per_eu(4 / NT, 4 / NT))) void full_fwd_kernel(
+// Each wave owns NT = 2 column tiles of 16 rows; waves w and w + 4 share a SIMD and own
+// the two 32-row halves of the same 64-row block.  Per 64-key chunk a wave does three
+// steps: S (scores, MFMA), X (softmax, VALU) and A (accumulate P V, MFMA).  Between two
+// barriers the first wave of a SIMD runs A(c-1), S(c), X(c) and the second runs
+// X(c-1), A(c-1), S(c): one wave's matrix products run while its partner's softmax
+// does, instead of both waves queueing on the same unit at the same time.  The stage
+// of chunk c-1 (its V) is still read while chunk c+1 is written, hence three stages.
+template <int D, bool WANT_O>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void full_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
     uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2) {
+  constexpr int NT = 2;        // 16-row column tiles per wave
+  constexpr int NW = 8;        // waves per workgroup (256 rows)
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
   constexpr int NDT = D / 16;  // d tiles of O^T
   constexpr int KF = 4 * NC;   // K fragments per 64-key chunk
   constexpr int VF = 2 * NDT;  // V^T fragments per 64-key chunk
-  constexpr int NW = 16 / NT;  // waves per workgroup (256 rows)
   constexpr int KF_W = KF / NW, VF_W = VF / NW;  // fragments each wave loads
-  __shared__ u32x4 sk[2][KF][64];
-  __shared__ u32x4 sv[2][VF][64];
+  __shared__ u32x4 sk[3][KF][64];
+  __shared__ u32x4 sv[WANT_O ? 3 : 1][WANT_O ? VF : 1][64];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const bool late = w >= 4;  // second wave on its SIMD
   // head-major order: the resident workgroups cover few heads, so their K/V stay in
   // the L2 / last-level cache; within a head the tiles with the most work go first
   const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);
@@ -49,10 +55,10 @@ __global__ __launch_bounds__(1024 / NT) __attribute__((amdgpu_waves_per_eu(4 / N
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* kh = k + bh * (int64_t)L * D;
   const u32x4* vth = vt + bh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
-  const int r0 = tile * 256 + 16 * NT * w;  // first row of this wave
-  const int rq = r0 % 64;                    // its offset inside its diagonal chunk
+  const int rq = late ? 32 : 0;              // row offset inside the diagonal chunk
+  const int r0 = tile * 256 + 64 * (w & 3) + rq;  // first row of this wave
   const bool active = r0 < L;
-  const int cw = r0 / 64;               // this wave's diagonal chunk
+  const int cw = r0 / 64;                    // this wave's diagonal chunk
   const int cmax = min(tile * 4 + 3, L / 64 - 1);
 
   u32x4 qf[NT][NC];
@@ -96,89 +102,111 @@ __global__ __launch_bounds__(1024 / NT) __attribute__((amdgpu_waves_per_eu(4 / N
     }
   };
 
+  f32x4 sacc[4][NT];
+  u32x4 pf[NT][2];
+  // S: S^T tiles of the chunk in stage st.  All K fragment reads are issued before the
+  // first product (the scheduling barrier keeps the compiler from moving products in
+  // between), so their latency is paid once per chunk, not once per pair of products.
+  auto scores = [&](int st) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+    u32x4 kf[KF];
+#pragma unroll
+    for (int f = 0; f < KF; ++f) kf[f] = sk[st][(f % 4) * NC + f / 4][lane];  // cc-major order
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < KF; ++f) {
+      const int cc = f / 4, kt = f % 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+    }
+  };
+  // X: online softmax of sacc into pf (bf16 P^T fragments), m, lsum and O rescaling
+  auto softmax = [&](bool diag) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float sr[16];
+      float mx = -__builtin_huge_valf();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = sacc[kt][nt][i];
+          if (diag && (16 * kt + 4 * g + i > rq + 16 * nt + n)) x = -__builtin_huge_valf();
+          sr[kt * 4 + i] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = max_over_rows(mx);
+      // The exponent reference m[nt] only moves when this chunk's max passes it by
+      // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely.
+      const float mxs = mx * sl2;
+      const bool need = mxs > m[nt] + kLag;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float mnew = need ? mxs : m[nt];
+        const float alpha = fast_exp2(m[nt] - mnew);
+        lsum[nt] *= alpha;
+        if (WANT_O) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
+        }
+        m[nt] = mnew;
+      }
+      const float mneg = -m[nt];
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
+        ps += sr[i];
+      }
+      lsum[nt] += ps;
+      if (WANT_O) {
+        pf[nt][0] = pack_p(&sr[0], &sr[4]);
+        pf[nt][1] = pack_p(&sr[8], &sr[12]);
+      }
+    }
+  };
+  // A: O^T += V^T P^T for the chunk in stage st (all V^T fragment reads issued first)
+  auto accumulate = [&](int st) {
+    u32x4 vf[VF];
+#pragma unroll
+    for (int f = 0; f < VF; ++f) vf[f] = sv[st][f][lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < VF; ++f) {  // fragment dt * 2 + kc
+      const int dt = f / 2, kc = f % 2;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+    }
+  };
+
   issue_loads(0);
   stage_store(0);
   __syncthreads();
 
-  for (int c = 0; c <= cmax; ++c) {
-    const int st = c & 1;
+  int s0 = 0;  // stage holding chunk c; chunk c - 1 is in sp, chunk c + 1 goes to s1
+  for (int c = 0; c <= cmax + 1; ++c) {
+    const int s1 = s0 == 2 ? 0 : s0 + 1;
+    const int sp = s0 == 0 ? 2 : s0 - 1;
     const bool more = c + 1 <= cmax;
     if (more) issue_loads(c + 1);
-    if (active && c <= cw) {
-      const bool diag = c == cw;
-      f32x4 sacc[4][NT];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
-      // K fragments read one ahead of their products (the next LDS read is in flight
-      // while the current fragment's four products run)
-      u32x4 kf = sk[st][0][lane];
-#pragma unroll
-      for (int f = 0; f < KF; ++f) {
-        const int cc = f / 4, kt = f % 4;  // fragment kt * NC + cc, in cc-major order
-        const u32x4 kn = f + 1 < KF ? sk[st][((f + 1) % 4) * NC + (f + 1) / 4][lane] : kf;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf, qf[nt][cc], sacc[kt][nt]);
-        kf = kn;
-      }
-      u32x4 pf[NT][2];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float sr[16];
-        float mx = -__builtin_huge_valf();
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x = sacc[kt][nt][i];
-            if (diag && (16 * kt + 4 * g + i > rq + 16 * nt + n)) x = -__builtin_huge_valf();
-            sr[kt * 4 + i] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // The exponent reference m[nt] only moves when this chunk's max passes it by
-        // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely.
-        const float mxs = mx * sl2;
-        const bool need = mxs > m[nt] + kLag;
-        if (__builtin_amdgcn_ballot_w64(need)) {
-          const float mnew = need ? mxs : m[nt];
-          const float alpha = fast_exp2(m[nt] - mnew);
-          lsum[nt] *= alpha;
-          if (WANT_O) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
-          }
-          m[nt] = mnew;
-        }
-        const float mneg = -m[nt];
-        float ps = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
-          ps += sr[i];
-        }
-        lsum[nt] += ps;
-        if (WANT_O) {
-          pf[nt][0] = pack_p(&sr[0], &sr[4]);
-          pf[nt][1] = pack_p(&sr[8], &sr[12]);
-        }
-      }
-      if (WANT_O) {
-        u32x4 vf = sv[st][0][lane];
-#pragma unroll
-        for (int f = 0; f < VF; ++f) {  // fragment dt * 2 + kc, read one ahead
-          const int dt = f / 2, kc = f % 2;
-          const u32x4 vn = f + 1 < VF ? sv[st][f + 1][lane] : vf;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf, pf[nt][kc], oacc[dt][nt]);
-          vf = vn;
-        }
-      }
+    const bool prev = active && c >= 1 && c - 1 <= cw;  // chunk c - 1 still to finish
+    const bool cur = active && c <= cw;                 // chunk c to start
+    // (the causal mask is compiled only into the diagonal chunk's softmax)
+    if (late && prev) {
+      if (c - 1 == cw) softmax(true);
+      else softmax(false);
     }
-    if (more) stage_store(st ^ 1);
+    if (WANT_O && prev) accumulate(sp);
+    if (cur) scores(s0);
+    if (!late && cur) {
+      if (c == cw) softmax(true);
+      else softmax(false);
+    }
+    if (more) stage_store(s1);
     __syncthreads();
+    s0 = s1;
   }
 
   if (!active) return;
@@ -205,12 +233,12 @@ __global__ __launch_bounds__(1024 / NT) __attribute__((amdgpu_waves_per_eu(4 / N
 
 bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 64 == 0; }
 
-template <int D, bool WANT_O, int NT = 2>
+template <int D, bool WANT_O>
 static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
                            float* lse, hipStream_t st) {
   const int ntile = (d.L + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
-  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O, NT>), dim3((unsigned)grid), dim3(1024 / NT), 0, st,
+  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
                      scale * kLog2e);
