@@ -78,49 +78,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int dt = 0; dt < (WANT_O ? NDT : 1); ++dt) oacc[dt][nt] = f32x4{0, 0, 0, 0};
   }
 
-  u32x4 kreg[KF_W], vreg[VF_W];
-  auto issue_loads = [&](int c) {
+  // Each wave copies its share of every chunk's K and V^T fragments from global memory
+  // into the LDS stages, through one of two register sets: the loads for chunk c + 2
+  // are issued at the start of interval c, and the set loaded one interval earlier
+  // (chunk c + 1) is written out at its end.  The loads are unconditional (the chunk
+  // index is clamped) so the compiler can count them exactly and wait only for the
+  // older set.
+  u32x4 kA[KF_W], vA[VF_W], kB[KF_W], vB[VF_W];
+  auto issue_loads = [&](u32x4* kr, u32x4* vr, int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < KF_W; ++i) {
       const int f = w * KF_W + i;
-      kreg[i] = load_k_frag<D>(kh, c * 64 + 16 * (f / NC), f % NC);
+      kr[i] = load_k_frag<D>(kh, c * 64 + 16 * (f / NC), f % NC);
     }
     if (WANT_O) {
 #pragma unroll
-      for (int i = 0; i < VF_W; ++i) {
-        const int f = w * VF_W + i;
-        vreg[i] = vth[((int64_t)c * VF + f) * 64 + lane];
-      }
+      for (int i = 0; i < VF_W; ++i) vr[i] = vth[((int64_t)c * VF + w * VF_W + i) * 64 + lane];
     }
   };
-  auto stage_store = [&](int st) {
+  auto stage_store = [&](const u32x4* kr, const u32x4* vr, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < KF_W; ++i) sk[st][w * KF_W + i][lane] = kreg[i];
+    for (int i = 0; i < KF_W; ++i) sk[st][w * KF_W + i][lane] = kr[i];
     if (WANT_O) {
 #pragma unroll
-      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = vreg[i];
+      for (int i = 0; i < VF_W; ++i) sv[st][w * VF_W + i][lane] = vr[i];
     }
   };
 
   f32x4 sacc[4][NT];
   u32x4 pf[NT][2];
-  // S: S^T tiles of the chunk in stage st.  All K fragment reads are issued before the
-  // first product (the scheduling barrier keeps the compiler from moving products in
-  // between), so their latency is paid once per chunk, not once per pair of products.
+  // S: S^T tiles of the chunk in stage st.  The K fragments are read in two batches,
+  // each issued in full before its products (the scheduling barrier keeps the compiler
+  // from moving products in between), so LDS latency is paid twice per chunk rather
+  // than once per pair of products.
   auto scores = [&](int st) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
-    u32x4 kf[KF];
 #pragma unroll
-    for (int f = 0; f < KF; ++f) kf[f] = sk[st][(f % 4) * NC + f / 4][lane];  // cc-major order
-    __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h) {
+      u32x4 kf[KF / 2];
 #pragma unroll
-    for (int f = 0; f < KF; ++f) {
-      const int cc = f / 4, kt = f % 4;
+      for (int f = 0; f < KF / 2; ++f) {  // cc-major order
+        const int fg = h * KF / 2 + f;
+        kf[f] = sk[st][(fg % 4) * NC + fg / 4][lane];
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+      for (int f = 0; f < KF / 2; ++f) {
+        const int fg = h * KF / 2 + f, cc = fg / 4, kt = fg % 4;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+      }
     }
   };
   // X: online softmax of sacc into pf (bf16 P^T fragments), m, lsum and O rescaling
@@ -167,30 +177,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // A: O^T += V^T P^T for the chunk in stage st (all V^T fragment reads issued first)
+  // A: O^T += V^T P^T for the chunk in stage st (V^T fragments read in two batches)
   auto accumulate = [&](int st) {
-    u32x4 vf[VF];
 #pragma unroll
-    for (int f = 0; f < VF; ++f) vf[f] = sv[st][f][lane];
-    __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h) {
+      u32x4 vf[VF / 2];
 #pragma unroll
-    for (int f = 0; f < VF; ++f) {  // fragment dt * 2 + kc
-      const int dt = f / 2, kc = f % 2;
+      for (int f = 0; f < VF / 2; ++f) vf[f] = sv[st][h * VF / 2 + f][lane];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+      for (int f = 0; f < VF / 2; ++f) {  // fragment dt * 2 + kc
+        const int fg = h * VF / 2 + f, dt = fg / 2, kc = fg % 2;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+      }
     }
   };
 
-  issue_loads(0);
-  stage_store(0);
+  issue_loads(kA, vA, 0);
+  issue_loads(kB, vB, min(1, cmax));
+  stage_store(kA, vA, 0);
   __syncthreads();
 
   int s0 = 0;  // stage holding chunk c; chunk c - 1 is in sp, chunk c + 1 goes to s1
-  for (int c = 0; c <= cmax + 1; ++c) {
+  // one interval: loads into set (kL, vL), chunk c + 1 written out from set (kS, vS)
+  auto interval = [&](int c, u32x4* kL, u32x4* vL, const u32x4* kS, const u32x4* vS)
+                      __attribute__((always_inline)) {
     const int s1 = s0 == 2 ? 0 : s0 + 1;
     const int sp = s0 == 0 ? 2 : s0 - 1;
     const bool more = c + 1 <= cmax;
-    if (more) issue_loads(c + 1);
+    issue_loads(kL, vL, min(c + 2, cmax));
     const bool prev = active && c >= 1 && c - 1 <= cw;  // chunk c - 1 still to finish
     const bool cur = active && c <= cw;                 // chunk c to start
     // (the causal mask is compiled only into the diagonal chunk's softmax)
@@ -204,9 +220,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (c == cw) softmax(true);
       else softmax(false);
     }
-    if (more) stage_store(s1);
+    if (more) stage_store(kS, vS, s1);
     __syncthreads();
     s0 = s1;
+  };
+  for (int c = 0; c <= cmax + 1; c += 2) {
+    interval(c, kA, vA, kB, vB);
+    if (c + 1 <= cmax + 1) interval(c + 1, kB, vB, kA, vA);
   }
 
   if (!active) return;
