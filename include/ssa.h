@@ -16,8 +16,9 @@
  *               memory); q, k, v, o and k_mean 16-byte aligned, idx, lse, sel_score,
  *               l2_dist and dropped 4-byte aligned.  The caller owns every buffer it
  *               passes.  The library keeps no pointer to them after a call returns and
- *               writes nothing outside the outputs named by a call.  One call allocates:
- *               ssa_sparse_attn_fwd on bf16 takes a transient workspace (see there).
+ *               writes nothing outside the outputs named by a call.  Two calls allocate:
+ *               ssa_sparse_attn_fwd on bf16, and ssa_full_attn_fwd on bf16 with o given,
+ *               take a transient workspace (see ssa_sparse_attn_fwd).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -127,6 +128,8 @@ ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* 
  *   lse      [B,H,L] float32 or NULL         out: log sum_{i<=t} exp(scale q_t.k_i)
  *   At least one of o, lse must be given; with o == NULL only the log-sum-exp is
  *   computed (the value products are skipped).
+ *   Workspace (bf16 with o given): the same transient B*H*L*D*2-byte copy of v as
+ *   ssa_sparse_attn_fwd, from the same pool, with the same error behaviour.
  */
 ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v,
                              float scale, void* o, float* lse, void* stream);
