@@ -13,14 +13,18 @@
 //
 // Selection of the m = topk - 1 best keys per row (one wave per row at a time):
 //  * m <= 64 (two passes over the scores, computed twice):
-//    1. every lane keeps the largest key among the candidates it sees (j = lane mod
-//       64); the m-th largest of these 64 lane maxima is a lower bound on the row's
-//       m-th largest key, because they are m of its keys;
+//    1. every lane keeps the largest score (as order-preserving bits) among the
+//       candidates it sees (j = lane mod 64); the m-th largest t of these 64 lane
+//       maxima gives a lower bound (t, 0) on the row's m-th largest key, because m of
+//       its keys have score bits >= t;
 //    2. the keys at or above that bound are collected in index order (about 31-45 for
-//       m = 31 on unstructured scores); their m-th largest is then exactly the row's m-th
+//       m = 31 on unstructured scores); their m-th largest is exactly the row's m-th
 //       largest key, and the keys at or above it are emitted in index order.  If more
 //       than 64 keys reach the bound, the m-th largest of the first 64 collected is a
-//       strictly higher bound and pass 2 runs again (only for such rows);
+//       strictly higher bound and pass 2 runs again (only for such rows).
+//    Both m-th largest values come from a 32-bit sort of the score bits across the
+//    wave; equal scores at the cut are then settled by index with a ballot, which is
+//    exact because the collected keys sit in index order;
 //  * m > 64: each chunk's 64 keys are sorted across the wave with a bitonic network and
 //    merged into the row's running list of the best 64*E keys in LDS; the result is
 //    re-sorted by block index.
@@ -78,6 +82,54 @@ struct SortStages {
 
 // full bitonic sort of 64 lane values; ascending if `asc`
 __device__ __forceinline__ uint64_t sort64(uint64_t x, bool asc) { return SortStages<2, 1>::run(x, asc); }
+
+// The same network on 32-bit values (one lane move and a min/max per stage).
+template <int K2, int J>
+struct SortStages32 {
+  __device__ static __forceinline__ uint32_t run(uint32_t x, bool asc) {
+    const int lane = threadIdx.x & 63;
+    const bool blk_asc = ((lane & K2) == 0) == asc;
+    const bool keep_max = ((lane & J) == 0) == !blk_asc;
+    uint32_t a, y;
+    if constexpr (J >= 16) {
+      // the row swaps leave the lane's value and its partner's in the two results
+      const auto pr = J == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      a = pr[0];
+      y = pr[1];
+    } else {
+      a = x;
+      y = xor_lane<J>(x);
+    }
+    x = keep_max ? (a > y ? a : y) : (a < y ? a : y);
+    if constexpr (J > 1) return SortStages32<K2, J / 2>::run(x, asc);
+    else if constexpr (K2 < 64) return SortStages32<K2 * 2, K2>::run(x, asc);
+    else return x;
+  }
+};
+__device__ __forceinline__ uint32_t sort64_u32(uint32_t x, bool asc) { return SortStages32<2, 1>::run(x, asc); }
+
+// The m-th largest (1 <= m <= 64) of the 64-bit keys held by the lanes, where absent
+// lanes hold 0, at least m keys are present, and the present keys with equal score
+// bits sit in ascending block order along the lanes (true of keys collected in index
+// order).  Only the 32 score bits are sorted: with t the m-th largest of them, the
+// m-th key is the (m - #{score > t})-th key with score t in lane order.  Returns the
+// key; *t_out and *need_out describe the cut for the caller.
+__device__ __forceinline__ uint64_t kth_key_index_ordered(uint64_t y, int m, uint32_t* t_out, int* need_out,
+                                                          uint64_t* eq_out) {
+  const uint32_t hi = (uint32_t)(y >> 32);
+  const uint32_t t = (uint32_t)__shfl((int)sort64_u32(hi, false), m - 1);  // descending
+  const int n_gt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));
+  const int need = m - n_gt;  // >= 1
+  const uint64_t eq = __builtin_amdgcn_ballot_w64(hi == t);
+  const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
+  const uint64_t pick = __builtin_amdgcn_ballot_w64(hi == t && rank == need - 1);
+  const int src = (int)__builtin_ctzll(pick);
+  *t_out = t;
+  *need_out = need;
+  *eq_out = eq;
+  return shfl_u64(y, src);
+}
 
 // bitonic merge (half-cleaners) of KP = 64*E values laid out as p = e*64 + lane,
 // into descending order
@@ -382,8 +434,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
     for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(16 * nt + nn) * D, cc);
   const int nchunks = (qb + 63) / 64;
 
-  // ---- pass 1: lane maxima, and from them a lower bound on each row's m-th key
-  uint64_t lmax[RPW];
+  // ---- pass 1: lane maxima of the score bits, and from them a lower bound on each
+  // row's m-th key (the m lanes whose maximum reaches the m-th largest lane maximum t
+  // hold m distinct keys with score bits >= t, so (t, 0) is at most the m-th key)
+  uint32_t lmax[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) lmax[i] = 0;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
@@ -394,7 +448,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = w + 4 * i;
-      lmax[i] = max_u64(lmax[i], j < qb ? make_key(sc[r][lane], j) : 0ull);
+      const uint32_t h = j < qb ? orderable_f32(sc[r][lane]) : 0u;
+      lmax[i] = lmax[i] > h ? lmax[i] : h;
     }
     __syncthreads();
   }
@@ -402,7 +457,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
   bool act[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
-    thr[i] = shfl_u64(sort64(lmax[i], false), m - 1);  // descending: lane m-1 holds the m-th key
+    thr[i] = (uint64_t)(uint32_t)__shfl((int)sort64_u32(lmax[i], false), m - 1) << 32;  // descending: lane m-1
     act[i] = true;
   }
 
@@ -439,7 +494,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
       if (!act[i]) continue;
       if (cnt[i] > 64) {
         const int r = w + 4 * i;
-        thr[i] = shfl_u64(sort64(buf[r][lane], false), m - 1);
+        uint32_t t;
+        int need;
+        uint64_t eq;
+        thr[i] = kth_key_index_ordered(buf[r][lane], m, &t, &need, &eq);  // the first 64, index order
         again = true;
       } else {
         act[i] = false;
@@ -454,8 +512,14 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
     const int r = w + 4 * i;
     const int c = cnt[i];
     const uint64_t y = lane < c ? buf[r][lane] : 0ull;
-    const uint64_t t = shfl_u64(sort64(y, false), m - 1);
-    const bool take = lane < c && y >= t;
+    uint32_t t;
+    int need;
+    uint64_t eq;
+    (void)kth_key_index_ordered(y, m, &t, &need, &eq);
+    // all keys with score bits above t, and the first `need` (lowest blocks) at t
+    const uint32_t hi = (uint32_t)(y >> 32);
+    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
+    const bool take = lane < c && (hi > t || (hi == t && rank < need));
     const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
     const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
     int32_t* orow = ih + (int64_t)r * topk;
