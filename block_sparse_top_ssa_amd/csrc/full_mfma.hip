@@ -148,12 +148,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           sr[kt * 4 + i] = x;
           mx = fmaxf(mx, x);
         }
-      mx = max_over_rows(mx);
       // The exponent reference m[nt] only moves when this chunk's max passes it by
-      // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely.
-      const float mxs = mx * sl2;
-      const bool need = mxs > m[nt] + kLag;
-      if (__builtin_amdgcn_ballot_w64(need)) {
+      // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely; the row
+      // maximum across the four lanes of a row is formed only when some lane's own
+      // maximum passes (the decision per row is the same).
+      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m[nt] + kLag)) {
+        const float mxs = max_over_rows(mx) * sl2;
+        const bool need = mxs > m[nt] + kLag;
         const float mnew = need ? mxs : m[nt];
         const float alpha = fast_exp2(m[nt] - mnew);
         lsum[nt] *= alpha;
