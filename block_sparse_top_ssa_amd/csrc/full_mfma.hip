@@ -206,7 +206,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                       __attribute__((always_inline)) {
     const int s1 = s0 == 2 ? 0 : s0 + 1;
     const int sp = s0 == 0 ? 2 : s0 - 1;
-    const bool more = c + 1 <= cmax;
     issue_loads(kL, vL, min(c + 2, cmax));
     const bool prev = active && c >= 1 && c - 1 <= cw;  // chunk c - 1 still to finish
     const bool cur = active && c <= cw;                 // chunk c to start
@@ -221,7 +220,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (c == cw) softmax(true);
       else softmax(false);
     }
-    if (more) stage_store(kS, vS, s1);
+    // Unconditional, like the loads, so the compiler's load counting stays exact: past
+    // the last chunk the stage written holds a chunk that no wave reads again.
+    stage_store(kS, vS, s1);
     __syncthreads();
     s0 = s1;
   };
