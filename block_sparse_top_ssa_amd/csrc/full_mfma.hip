@@ -80,7 +80,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Each wave copies its share of every chunk's K and V^T fragments from global memory
   // into the LDS stages, through one of two register sets: the loads for chunk c + 2
-  // are issued at the start of interval c, and the set loaded one interval earlier
+  // are issued during interval c, and the set loaded one interval earlier
   // (chunk c + 1) is written out at its end.  The loads are unconditional (the chunk
   // index is clamped) so the compiler can count them exactly and wait only for the
   // older set.
@@ -206,7 +206,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                       __attribute__((always_inline)) {
     const int s1 = s0 == 2 ? 0 : s0 + 1;
     const int sp = s0 == 0 ? 2 : s0 - 1;
-    issue_loads(kL, vL, min(c + 2, cmax));
     const bool prev = active && c >= 1 && c - 1 <= cw;  // chunk c - 1 still to finish
     const bool cur = active && c <= cw;                 // chunk c to start
     // (the causal mask is compiled only into the diagonal chunk's softmax)
@@ -215,6 +214,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       else softmax(false);
     }
     if (WANT_O && prev) accumulate(sp);
+    // The loads for chunk c + 2 go out here rather than at the start: the compiler
+    // waits for the older set before reusing the registers, and by now it has landed.
+    issue_loads(kL, vL, min(c + 2, cmax));
     if (cur) scores(s0);
     if (!late && cur) {
       if (c == cw) softmax(true);
