@@ -203,6 +203,15 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
   const float r2 = r1 - bf16_bits_to_f32(mid);
   lo = f32_to_bf16_bits(r2);
 }
+// The same split for two values at once, packed as a bf16 pair per term (x0 in the low
+// half): one paired conversion per term, the same nearest-even rounding as split3.
+__device__ __forceinline__ void split3x2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = pack_bf16x2(x0, x1);
+  const float r0 = x0 - lo_bf16(hi), r1 = x1 - hi_bf16(hi);
+  mid = pack_bf16x2(r0, r1);
+  const float s0 = r0 - lo_bf16(mid), s1 = r1 - hi_bf16(mid);
+  lo = pack_bf16x2(s0, s1);
+}
 
 template <int D, int S, int E>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
@@ -361,14 +370,13 @@ __device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], c
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = 0.f;
     }
-    uint32_t h[8], md[8], lo[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) split3(x[e], h[e], md[e], lo[e]);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      ah[cc][e] = h[2 * e] | (h[2 * e + 1] << 16);
-      am[cc][e] = md[2 * e] | (md[2 * e + 1] << 16);
-      al[cc][e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+      uint32_t h, md, lo;
+      split3x2(x[2 * e], x[2 * e + 1], h, md, lo);
+      ah[cc][e] = h;
+      am[cc][e] = md;
+      al[cc][e] = lo;
     }
   }
 #pragma unroll
