@@ -107,30 +107,35 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   f32x4 sacc[4][NT];
   u32x4 pf[NT][2];
-  // S: S^T tiles of the chunk in stage st.  The K fragments are read in two batches,
-  // each issued in full before its products (the scheduling barrier keeps the compiler
-  // from moving products in between), so LDS latency is paid twice per chunk rather
-  // than once per pair of products.
+  // S: S^T tiles of the chunk in stage st.  The first half of the K fragments is read
+  // before any product; the second half is read one fragment per pair of products of
+  // the first half (scheduling-group barriers keep that order), so the LDS latency is
+  // paid once per chunk and the reads run eight fragments ahead of their use.
   auto scores = [&](int st) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+    u32x4 kf[KF];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 kf[KF / 2];
+    for (int f = 0; f < KF / 2; ++f) kf[f] = sk[st][(f % 4) * NC + f / 4][lane];  // cc-major order
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 0; f < KF / 2; ++f) {  // cc-major order
-        const int fg = h * KF / 2 + f;
-        kf[f] = sk[st][(fg % 4) * NC + fg / 4][lane];
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int f = 0; f < KF / 2; ++f) {  // first half's products, second half's reads between them
+      const int cc = f / 4, kt = f % 4;
 #pragma unroll
-      for (int f = 0; f < KF / 2; ++f) {
-        const int fg = h * KF / 2 + f, cc = fg / 4, kt = fg % 4;
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+      const int fg = KF / 2 + f;
+      kf[fg] = sk[st][(fg % 4) * NC + fg / 4][lane];
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
-      }
+    for (int f = KF / 2; f < KF; ++f) {
+      const int cc = f / 4, kt = f % 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
     }
   };
   // X: online softmax of sacc into pf (bf16 P^T fragments), m, lsum and O rescaling
@@ -178,20 +183,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
   };
-  // A: O^T += V^T P^T for the chunk in stage st (V^T fragments read in two batches)
+  // A: O^T += V^T P^T for the chunk in stage st (V^T fragments read as for S)
   auto accumulate = [&](int st) {
+    u32x4 vf[VF];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 vf[VF / 2];
+    for (int f = 0; f < VF / 2; ++f) vf[f] = sv[st][f][lane];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int f = 0; f < VF / 2; ++f) vf[f] = sv[st][h * VF / 2 + f][lane];
-      __builtin_amdgcn_sched_barrier(0);
+    for (int f = 0; f < VF / 2; ++f) {  // fragment dt * 2 + kc
+      const int dt = f / 2, kc = f % 2;
 #pragma unroll
-      for (int f = 0; f < VF / 2; ++f) {  // fragment dt * 2 + kc
-        const int fg = h * VF / 2 + f, dt = fg / 2, kc = fg % 2;
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+      vf[VF / 2 + f] = sv[st][VF / 2 + f][lane];
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
-      }
+    for (int f = VF / 2; f < VF; ++f) {
+      const int dt = f / 2, kc = f % 2;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
     }
   };
 
