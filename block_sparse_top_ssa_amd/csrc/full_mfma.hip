@@ -207,6 +207,62 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // A then S in one stream: the V^T fragments of stage sv_st and then the K fragments
+  // of stage sk_st, every read eight fragments ahead of its products except the first
+  // eight; mid() runs between the two halves of the value products.
+  auto acc_scores = [&](int sv_st, int sk_st, auto&& mid) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = f32x4{0, 0, 0, 0};
+    u32x4 vf[VF], kf[KF];
+#pragma unroll
+    for (int f = 0; f < VF / 2; ++f) vf[f] = sv[sv_st][f][lane];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < VF / 2; ++f) {
+      const int dt = f / 2, kc = f % 2;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+      vf[VF / 2 + f] = sv[sv_st][VF / 2 + f][lane];
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = VF / 2; f < VF; ++f) {
+      const int dt = f / 2, kc = f % 2;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[dt][nt] = mfma_bf16(vf[f], pf[nt][kc], oacc[dt][nt]);
+      const int fk = f - VF / 2;
+      if (fk < KF / 2) {
+        kf[fk] = sk[sk_st][(fk % 4) * NC + fk / 4][lane];
+        __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < KF / 2; ++f) {
+      const int cc = f / 4, kt = f % 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+      const int fg = KF / 2 + f;
+      kf[fg] = sk[sk_st][(fg % 4) * NC + fg / 4][lane];
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = KF / 2; f < KF; ++f) {
+      const int cc = f / 4, kt = f % 4;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
+    }
+  };
+
   issue_loads(kA, vA, 0);
   issue_loads(kB, vB, min(1, cmax));
   stage_store(kA, vA, 0);
@@ -225,11 +281,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (c - 1 == cw) softmax(true);
       else softmax(false);
     }
-    if (WANT_O && prev) accumulate(sp);
-    // The loads for chunk c + 2 go out here rather than at the start: the compiler
-    // waits for the older set before reusing the registers, and by now it has landed.
-    issue_loads(kL, vL, min(c + 2, cmax));
-    if (cur) scores(s0);
+    // Steady state: the value products of chunk c - 1 and the score products of chunk c
+    // as one pipelined stream (acc_scores); the loads for chunk c + 2 go out between
+    // them rather than at the start: the compiler waits for the older set before
+    // reusing the registers, and by then it has landed.
+    if (WANT_O && prev && cur) {
+      acc_scores(sp, s0, [&]() __attribute__((always_inline)) { issue_loads(kL, vL, min(c + 2, cmax)); });
+    } else {
+      if (WANT_O && prev) accumulate(sp);
+      issue_loads(kL, vL, min(c + 2, cmax));
+      if (cur) scores(s0);
+    }
     if (!late && cur) {
       if (c == cw) softmax(true);
       else softmax(false);
