@@ -344,36 +344,43 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restr
 }
 
 
-// Scores of one 64-candidate chunk against all S rows of the block into sc (wave w
-// takes candidates cb + 16 w .. +15).
+// The float32 kbar values a lane needs for one 64-candidate chunk (wave w takes the
+// candidates cb + 16 w .. +15; lane (nn, g) the columns 32 cc + 8 g .. +7).  The row
+// index is clamped into the pooled keys, so rows past the candidates load valid memory;
+// their scores are never used.
+template <int D>
+__device__ __forceinline__ void load_kchunk(const float* __restrict__ kmh, int cb, int n, float (&xk)[D / 32][8]) {
+  constexpr int NC = D / 32;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nn = lane & 15, g = lane >> 4;
+  const int j = min(cb + 16 * w + nn, n - 1);
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const float* src = kmh + (int64_t)j * D + 32 * cc + 8 * g;
+    const u32x4 w0 = load16(src), w1 = load16(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xk[cc][e] = __uint_as_float(w0[e]);
+      xk[cc][4 + e] = __uint_as_float(w1[e]);
+    }
+  }
+}
+
+// Scores of one 64-candidate chunk (its kbar values in xk) against all S rows of the
+// block into sc.
 template <int D, int S>
-__device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], const float* __restrict__ kmh, int cb,
-                                            int qb, float (*sc)[65]) {
+__device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], const float (&xk)[D / 32][8],
+                                            float (*sc)[65]) {
   constexpr int NC = D / 32, NT = S / 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nn = lane & 15, g = lane >> 4;
-  const int j = cb + 16 * w + nn;
-  const bool valid = j < qb;
   u32x4 ah[NC], am[NC], al[NC];
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
-    float x[8];
-    if (valid) {
-      const float* src = kmh + (int64_t)j * D + 32 * cc + 8 * g;
-      const u32x4 w0 = load16(src), w1 = load16(src + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = __uint_as_float(w0[e]);
-        x[4 + e] = __uint_as_float(w1[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t h, md, lo;
-      split3x2(x[2 * e], x[2 * e + 1], h, md, lo);
+      split3x2(xk[cc][2 * e], xk[cc][2 * e + 1], h, md, lo);
       ah[cc][e] = h;
       am[cc][e] = md;
       al[cc][e] = lo;
@@ -441,6 +448,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(16 * nt + nn) * D, cc);
   const int nchunks = (qb + 63) / 64;
+  // kbar of the next chunk to score, loaded one chunk ahead (after the last chunk of a
+  // pass, chunk 0 again for the next pass)
+  float xk[NC][8];
+  load_kchunk<D>(kmh, 0, n, xk);
 
   // ---- pass 1: lane maxima of the score bits, and from them a lower bound on each
   // row's m-th key (the m lanes whose maximum reaches the m-th largest lane maximum t
@@ -450,7 +461,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
   for (int i = 0; i < RPW; ++i) lmax[i] = 0;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     const int cb = chunk * 64;
-    score_chunk<D, S>(qf, kmh, cb, qb, sc);
+    score_chunk<D, S>(qf, xk, sc);
+    load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
     __syncthreads();
     const int j = cb + lane;
 #pragma unroll
@@ -477,7 +489,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
       if (act[i]) cnt[i] = 0;
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       const int cb = chunk * 64;
-      score_chunk<D, S>(qf, kmh, cb, qb, sc);
+      score_chunk<D, S>(qf, xk, sc);
+      load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
       __syncthreads();
       const int j = cb + lane;
 #pragma unroll
