@@ -408,7 +408,9 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
                                                           int32_t* __restrict__ idx, float* __restrict__ sel, int L,
                                                           int n, int BH, int topk) {
   constexpr int NC = D / 32, NT = S / 16, RPW = S / 4;  // rows per wave
-  __shared__ float sc[S][65];
+  // Scores of a chunk go to one of two buffers (chunk parity), so scoring the next chunk
+  // never overwrites scores other waves may still read: one barrier per chunk.
+  __shared__ float scb[2][S][65];
   __shared__ uint64_t buf[S][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   const int nn = lane & 15;
@@ -461,6 +463,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
   for (int i = 0; i < RPW; ++i) lmax[i] = 0;
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     const int cb = chunk * 64;
+    float (*sc)[65] = scb[chunk & 1];
     score_chunk<D, S>(qf, xk, sc);
     load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
     __syncthreads();
@@ -471,8 +474,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
       const uint32_t h = j < qb ? orderable_f32(sc[r][lane]) : 0u;
       lmax[i] = lmax[i] > h ? lmax[i] : h;
     }
-    __syncthreads();
   }
+  __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
   uint64_t thr[RPW];
   bool act[RPW];
 #pragma unroll
@@ -489,6 +492,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
       if (act[i]) cnt[i] = 0;
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       const int cb = chunk * 64;
+      float (*sc)[65] = scb[chunk & 1];
       score_chunk<D, S>(qf, xk, sc);
       load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
       __syncthreads();
@@ -505,8 +509,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
         if (pass && pos < 64) buf[r][pos] = key;
         cnt[i] += __builtin_popcountll(mask);
       }
-      __syncthreads();
     }
+    __syncthreads();  // buf complete; a repeated pass scores chunk 0 into buffer 0 again
     // rows that collected more than 64 keys: raise the bound to the m-th largest of
     // the first 64 collected (a strictly higher bound) and collect again
     bool again = false;
