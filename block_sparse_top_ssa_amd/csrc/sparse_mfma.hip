@@ -150,6 +150,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
+  // Operands of this wave's first own-block unit (phase 2), loaded before the index
+  // build so their latency passes while the index is built: K and V^T of the unit's
+  // diagonal chunk and Q of its 32 rows.
+  constexpr int NQ = 2 * NC;
+  u32x4 okf[4][NC], ovf[NDT][2], oqf[NQ];
+  auto own_load = [&](int u) __attribute__((always_inline)) {
+    const int r0 = 32 * u, qc = r0 / 64;
+    const int c_diag = (t0 + 64 * qc) / 64;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) okf[kt][cc] = load_k_frag<D>(kh, c_diag * 64 + 16 * kt, cc);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) ovf[dt][kc] = vt_frag(c_diag, dt, kc);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        oqf[nt * NC + cc] = load_q_frag<D>(qh + (int64_t)(t0 + r0 + 16 * nt + n) * D, cc);
+  };
+  if (32 * w < rows && w < T / 32) own_load(w);
+
   // ---------------------------------------------------------------- 1. inverted index
   for (int j = tid; j < nb; j += NTH) cnt[j] = 0;
   for (int r = tid; r < T; r += NTH) flag[r] = 0;
@@ -192,22 +216,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (r0 >= rows) break;
     const int qc = r0 / 64, rq = r0 % 64;  // query chunk and row offset inside it
     const int c_diag = (t0 + 64 * qc) / 64;
-    u32x4 kf[4][NC], vf[NDT][2];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c_diag * 64 + 16 * kt, cc);
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc) vf[dt][kc] = vt_frag(c_diag, dt, kc);
+    if (u != w) own_load(u);  // the first unit's operands were loaded before phase 1
+    auto& kf = okf;
+    auto& vf = ovf;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int rl = rq + 16 * nt;  // row offset inside the 64-row chunk
       const int r = r0 + 16 * nt + n;
       u32x4 qf[NC];
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) qf[cc] = load_q_frag<D>(qh + (int64_t)(t0 + r) * D, cc);
+      for (int cc = 0; cc < NC; ++cc) qf[cc] = oqf[nt * NC + cc];
       f32x4 sacc[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
