@@ -131,8 +131,48 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Walk the valid entries of one row's idx list: distinct blocks below b_t, each
   // greater than the entry used before it.  Entries are loaded 32 at a time.
+  // Rows of at most 32 entries (the usual case) are read once into registers, two
+  // entries per register as 16-bit values (block indices stay below 2^15 then; other
+  // values, which are never valid here, become -1), and walked from there by both
+  // passes of the index build; 16-byte loads when the rows are 16-byte aligned.
+  // Longer rows are re-read in batches of 32.
+  const bool idx_regs = topk <= 32 && L / S < 32768;
+  const bool idx_vec = idx_regs && topk % 4 == 0 && ((reinterpret_cast<uintptr_t>(ih) & 15) == 0);
+  auto pack16 = [](int32_t a, int32_t b) -> uint32_t {
+    const uint32_t ua = (a >= 0 && a < 32768) ? (uint32_t)a : 0xFFFFu;
+    const uint32_t ub = (b >= 0 && b < 32768) ? (uint32_t)b : 0xFFFFu;
+    return ua | (ub << 16);
+  };
+  uint32_t ent[16];
+  if (idx_regs && tid < rows) {
+    const int32_t* ir = ih + (int64_t)(t0 + tid) * topk;
+    if (idx_vec) {
+#pragma unroll
+      for (int u4 = 0; u4 < 8; ++u4) {
+        u32x4 x = u32x4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+        if (4 * u4 < topk) x = *reinterpret_cast<const u32x4*>(ir + 4 * u4);
+        ent[2 * u4] = pack16((int32_t)x[0], (int32_t)x[1]);
+        ent[2 * u4 + 1] = pack16((int32_t)x[2], (int32_t)x[3]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) ent[u] = pack16(2 * u < topk ? ir[2 * u] : -1, 2 * u + 1 < topk ? ir[2 * u + 1] : -1);
+    }
+  }
   auto for_each_entry = [&](int t, auto&& fn) {
     const int bt = t / S;
+    if (idx_regs) {  // this thread's row (t = t0 + tid), from registers
+      int prev = -1;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int j = (int)(int16_t)(ent[u >> 1] >> (16 * (u & 1)));
+        if (j > prev && j < bt) {
+          prev = j;
+          fn(j);
+        }
+      }
+      return;
+    }
     const int32_t* ir = ih + (int64_t)t * topk;
     int prev = -1;
     for (int e0 = 0; e0 < topk; e0 += 32) {
