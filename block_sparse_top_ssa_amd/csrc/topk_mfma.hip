@@ -12,7 +12,7 @@
 // (score, then lower block index first), so all keys of a row are distinct.
 //
 // Selection of the m = topk - 1 best keys per row (one wave per row at a time):
-//  * m <= 64 (two passes over the scores, computed twice):
+//  * m <= 40 (two passes over the scores, computed twice):
 //    1. every lane keeps the largest score (as order-preserving bits) among the
 //       candidates it sees (j = lane mod 64); the m-th largest t of these 64 lane
 //       maxima gives a lower bound (t, 0) on the row's m-th largest key, because m of
@@ -25,9 +25,10 @@
 //    Both m-th largest values come from a 32-bit sort of the score bits across the
 //    wave; equal scores at the cut are then settled by index with a ballot, which is
 //    exact because the collected keys sit in index order;
-//  * m > 64: each chunk's 64 keys are sorted across the wave with a bitonic network and
+//  * m > 40: each chunk's 64 keys are sorted across the wave with a bitonic network and
 //    merged into the row's running list of the best 64*E keys in LDS; the result is
-//    re-sorted by block index.
+//    re-sorted by block index.  (For m close to 64 the first pass's bound is weak: rows
+//    would collect far more than 64 keys and refine many times.)
 // Output per row: the selected blocks in ascending order, then b_t, then -1.
 #include "launch.hpp"
 #include "mfma.hpp"
@@ -402,7 +403,8 @@ __device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], c
 
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// Two-pass selection for m = topk - 1 <= 64 (see the top of the file).
+// Two-pass selection, exact for m = topk - 1 <= 64; dispatched for m <= kSelectMaxM
+// (see the top of the file).
 template <int D, int S>
 __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel, int L,
@@ -560,6 +562,8 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
   }
 }
 
+constexpr int kSelectMaxM = 40;  // largest m = topk - 1 given to the two-pass selection
+
 static int e_for(int topk) {
   const int need = topk - 1;
   int e = 1;
@@ -594,11 +598,16 @@ static hipError_t run_topk(const Dims& d, const void* q, const float* km, int to
 template <int D>
 static hipError_t dispatch_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                                 hipStream_t st) {
+  // Two-pass selection while its first bound is tight (m well below 64); above that the
+  // bound from 64 lane maxima is weak, rows collect far more than 64 keys and refine
+  // many times, so the sort-and-merge kernel is faster (measured: m = 39 select 1.68 ms
+  // vs merge 1.93 ms; m = 47 select 2.25 ms vs merge 1.91 ms at L = 32768, 32 heads).
+  if (topk - 1 <= kSelectMaxM) return d.S == 64 ? run_select<D, 64>(d, q, km, topk, idx, sel, st)
+                                                 : run_select<D, 128>(d, q, km, topk, idx, sel, st);
   const int e = e_for(topk);
-  if (e == 1) return d.S == 64 ? run_select<D, 64>(d, q, km, topk, idx, sel, st)
-                                : run_select<D, 128>(d, q, km, topk, idx, sel, st);
-  if (d.S == 64) return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);
-  return run_topk<D, 128, 1>(d, q, km, topk, idx, sel, st);
+  if (e == 1) return d.S == 64 ? run_topk<D, 64, 1>(d, q, km, topk, idx, sel, st)
+                                : run_topk<D, 128, 1>(d, q, km, topk, idx, sel, st);
+  return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);  // S = 128 with E = 2 is not supported
 }
 
 LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,

@@ -247,6 +247,8 @@ def test_q_zero_closed_forms(variant, s, topk, L):
     (2, 1, 640, 64, 64, 3),      # bf16 with D = 64
     (1, 2, 384, 128, 128, 2),    # block 128, ragged tile
     (3, 1, 1280, 128, 64, 20),   # topk = n
+    (1, 2, 8192, 128, 128, 48),  # m = 47: the merge selection with one 64-key list, block 128
+    (1, 2, 4096, 128, 64, 56),   # m = 55: the same with block 64
 ])
 def test_edge_shapes(variant, B, H, L, D, s, topk):
     inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=16)
