@@ -48,11 +48,12 @@ def attended_total(L: int, s: int, k: int) -> int:
 def work_model(w: W.Workload, k: int) -> dict:
     e = 2 if w.dtype == W.BF16 else 4
     BH, L, D, s, n = w.B * w.H, w.L, w.D, w.s, w.n
+    BHkv = w.B * w.hkv                          # key/value heads (grouped-query attention)
     t = np.arange(L, dtype=np.int64)
     cand = int((t // s).sum())                  # candidate blocks scored per (b, h)
     return {
-        "pool": {"bytes": BH * (L * D * e + n * D * 4)},
-        "topk": {"flops": 2 * D * BH * cand, "bytes": BH * (L * D * e + n * D * 4 + L * k * 4)},
+        "pool": {"bytes": BHkv * (L * D * e + n * D * 4)},
+        "topk": {"flops": 2 * D * BH * cand, "bytes": BH * (L * D * e + L * k * 4) + BHkv * n * D * 4},
         "sparse": {"flops": 4 * D * BH * attended_total(L, s, k)},
         "full": {"flops": 4 * D * BH * (L * (L + 1) // 2)},
         "align": {"bytes": BH * L * (2 * D * e + 4 * 4)},
@@ -107,7 +108,11 @@ def cpu_baseline(inp: W.Inputs, k: int, budget_s: float = 15.0) -> dict:
             x = a[:1, h:h + 1]
             return (W.bf16_bits_to_f32(x) if w.dtype == W.BF16 else x).astype(np.float64)
 
-        q, kk, vv = head64(inp.q), head64(inp.k), head64(inp.v)
+        def kvhead64(a):  # the key/value head query head h reads
+            x = a[:1, h // w.group:h // w.group + 1]
+            return (W.bf16_bits_to_f32(x) if w.dtype == W.BF16 else x).astype(np.float64)
+
+        q, kk, vv = head64(inp.q), kvhead64(inp.k), kvhead64(inp.v)
         t0 = time.perf_counter()
         km = O.block_pool(kk, s)
         idx = O.block_topk(q, km, s, k, rows=rows)
@@ -248,7 +253,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == W.BF16 else "f32",
         "data": "synthetic (seeded N(0,1) q, k, v with the workload's key structure; no dataset, no weights)",
-        "config": {"workload": w.name, "B": B, "H": H, "L": L, "D": D, "block": s, "topk": k,
+        "config": {"workload": w.name, "B": B, "H": H, "Hkv": w.hkv, "L": L, "D": D, "block": s, "topk": k,
                    "step": "pool+topk+sparse_attn+full_attn" + ("(lse only)" if o_f is None else "") + "+align"},
         "sparse_attn": {"tokens_per_s": round(tokens / (per["sparse"] * 1e-3), 1),
                         "tflops": round(sp_tflops, 2), "pct_mfma_bf16_peak": round(100 * sp_tflops / PEAK_BF16_TFLOPS, 2),

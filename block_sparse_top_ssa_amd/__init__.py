@@ -10,6 +10,10 @@ and the stream: each call enqueues on torch's current stream and does not synchr
     o_f, lse_f = full_attn_fwd(q, k, v)
     dist, dropped = align_stats(o_f, o_s, lse_f, lse_s)
 
+q is [B, H, L, D]; k and v may have fewer heads, [B, Hkv, L, D] with Hkv dividing H
+(grouped-query attention: query head h uses key/value head h // (H // Hkv)), and
+k_mean then has Hkv heads too.
+
 There is no fallback: if libssa.so is missing or the device is not gfx950, calls raise.
 """
 from __future__ import annotations
@@ -46,11 +50,11 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise SSAError(3, f"unsupported tensor dtype {t.dtype}")
 
 
-def _dims(x: torch.Tensor, block: int) -> Dims:
+def _dims(x: torch.Tensor, block: int, hkv: int = 0) -> Dims:
     if x.dim() != 4:
         raise SSAError(2, "expected a [B, H, L, D] tensor")
     B, H, L, D = x.shape
-    return Dims(B, H, L, D, int(block), _dtype_code(x))
+    return Dims(B, H, L, D, int(block), _dtype_code(x), int(hkv))
 
 
 def _ptr(t):
@@ -70,6 +74,15 @@ def _same(a: torch.Tensor, b: torch.Tensor, what: str):
         raise SSAError(2, f"{what}: shape/dtype mismatch {tuple(a.shape)}/{a.dtype} vs {tuple(b.shape)}/{b.dtype}")
 
 
+def _kv_heads(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor) -> int:
+    """Key/value heads of k and v ([B, Hkv, L, D], Hkv dividing q's H)."""
+    _same(k, v, "k/v")
+    if (k.dim() != 4 or k.dtype != q.dtype or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]
+            or q.shape[1] % k.shape[1]):
+        raise SSAError(2, f"k/v {tuple(k.shape)}/{k.dtype} do not fit q {tuple(q.shape)}/{q.dtype}")
+    return int(k.shape[1])
+
+
 def block_pool(k: torch.Tensor, block: int, out: torch.Tensor | None = None) -> torch.Tensor:
     d = _dims(k, block)
     if out is None:
@@ -80,7 +93,7 @@ def block_pool(k: torch.Tensor, block: int, out: torch.Tensor | None = None) -> 
 
 def block_topk(q: torch.Tensor, k_mean: torch.Tensor, block: int, topk: int, want_scores: bool = False,
                out: torch.Tensor | None = None):
-    d = _dims(q, block)
+    d = _dims(q, block, k_mean.shape[1] if k_mean.dim() == 4 else 0)
     if out is None:
         out = torch.empty((d.B, d.H, d.L, topk), dtype=torch.int32, device=q.device)
     sel = torch.empty((d.B, d.H, d.L, topk), dtype=torch.float32, device=q.device) if want_scores else None
@@ -91,9 +104,7 @@ def block_topk(q: torch.Tensor, k_mean: torch.Tensor, block: int, topk: int, wan
 
 def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
                     out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    _same(q, k, "q/k")
-    _same(q, v, "q/v")
-    d = _dims(q, block)
+    d = _dims(q, block, _kv_heads(q, k, v))
     if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
         raise SSAError(2, "idx must be int32 [B, H, L, topk]")
     topk = idx.shape[3]
@@ -110,9 +121,7 @@ def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_l
 
 def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
                   block: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    _same(q, k, "q/k")
-    _same(q, v, "q/v")
-    d = _dims(q, block)
+    d = _dims(q, block, _kv_heads(q, k, v))
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if want_o and out is None:
         out = torch.empty_like(q)

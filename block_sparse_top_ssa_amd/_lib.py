@@ -22,7 +22,8 @@ _F = ctypes.c_float
 
 
 class Dims(ctypes.Structure):
-    _fields_ = [("B", _I32), ("H", _I32), ("L", _I32), ("D", _I32), ("block", _I32), ("dtype", _I32)]
+    _fields_ = [("B", _I32), ("H", _I32), ("L", _I32), ("D", _I32), ("block", _I32), ("dtype", _I32),
+                ("Hkv", _I32)]
 
 
 _DP = ctypes.POINTER(Dims)

@@ -59,9 +59,11 @@ ssa_status check_dims(const ssa_dims* d, ssa::Dims* out) {
   if (d->D != 64 && d->D != 128) return fail(SSA_ERR_SHAPE, "head dim D must be 64 or 128 (got %d)", d->D);
   if (d->block != 64 && d->block != 128) return fail(SSA_ERR_SHAPE, "block size must be 64 or 128 (got %d)", d->block);
   if (d->L % d->block) return fail(SSA_ERR_SHAPE, "L=%d is not a multiple of the block size %d", d->L, d->block);
+  const int hkv = d->Hkv == 0 ? d->H : d->Hkv;
+  if (hkv < 1 || d->H % hkv) return fail(SSA_ERR_SHAPE, "Hkv=%d must be >= 1 and divide H=%d (0 means H)", d->Hkv, d->H);
   const int64_t tokens = (int64_t)d->B * d->H * d->L;
   if (tokens > (int64_t(1) << 24)) return fail(SSA_ERR_SHAPE, "B*H*L=%lld exceeds 2^24", (long long)tokens);
-  *out = ssa::Dims{d->B, d->H, d->L, d->D, d->block, d->dtype};
+  *out = ssa::Dims{d->B, d->H, d->L, d->D, d->block, d->dtype, hkv};
   return SSA_OK;
 }
 
@@ -106,7 +108,7 @@ ssa_status ssa_block_pool(const ssa_dims* dims, const void* k, float* k_mean, vo
   SSA_TRY(check_ptr(k, "k", 16));
   SSA_TRY(check_ptr(k_mean, "k_mean", 16));
   SSA_TRY(check_device());
-  return finish(ssa::launch_pool(d, k, k_mean, (hipStream_t)stream), "ssa_block_pool");
+  return finish(ssa::launch_pool(d.kv(), k, k_mean, (hipStream_t)stream), "ssa_block_pool");  // over K/V heads
 }
 
 ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_mean, int32_t topk, int32_t* idx,

@@ -33,7 +33,7 @@ constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the 
 template <int D, bool WANT_O>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void full_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2, int G) {
   constexpr int NT = 2;        // 16-row column tiles per wave
   constexpr int NW = 8;        // waves per workgroup (256 rows)
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
@@ -53,8 +53,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t bh = wg / ntile;
   const int tile = ntile - 1 - (int)(wg % ntile);
   const uint16_t* qh = q + bh * (int64_t)L * D;
-  const uint16_t* kh = k + bh * (int64_t)L * D;
-  const u32x4* vth = vt + bh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
+  const int64_t kvh = bh / G;  // K/V head of this query head
+  const uint16_t* kh = k + kvh * (int64_t)L * D;
+  const u32x4* vth = vt + kvh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
   const int rq = late ? 32 : 0;              // row offset inside the diagonal chunk
   const int r0 = tile * 256 + 64 * (w & 3) + rq;  // first row of this wave
   const bool active = r0 < L;
@@ -339,7 +340,7 @@ static hipError_t run_full(const Dims& d, const void* q, const void* k, const u3
   hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
-                     scale * kLog2e);
+                     scale * kLog2e, d.G());
   return hipGetLastError();
 }
 
@@ -348,7 +349,7 @@ LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const
   LaunchResult r;
   if (o) {
     void* ws = nullptr;
-    r.err = vfrag_acquire(d, v, &ws, st);
+    r.err = vfrag_acquire(d.kv(), v, &ws, st);
     if (r.err != hipSuccess) return r;
     const u32x4* vt = static_cast<const u32x4*>(ws);
     r.err = d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st)

@@ -19,7 +19,7 @@ constexpr int kTopkGenericMaxN = 4096;  // LDS holds 12 bytes per candidate
 template <typename T, int D>
 __global__ __launch_bounds__(256) void topk_generic_kernel(const T* __restrict__ q, const float* __restrict__ km,
                                                            int32_t* __restrict__ idx, float* __restrict__ sel,
-                                                           int L, int S, int topk, int P) {
+                                                           int L, int S, int topk, int P, int G) {
   extern __shared__ __align__(16) unsigned char smem[];
   float* qs = reinterpret_cast<float*>(smem);                   // [D]
   uint64_t* keys = reinterpret_cast<uint64_t*>(qs + D);         // [P]
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void topk_generic_kernel(const T* __restrict__
   const int tid = threadIdx.x;
   for (int d = tid; d < D; d += 256) qs[d] = Elem<T>::load1(q + row * D + d);
   __syncthreads();
-  const float* kmh = km + bh * (int64_t)n * D;
+  const float* kmh = km + (bh / G) * (int64_t)n * D;  // pooled keys of this head's K/V head
   for (int j = tid; j < P; j += 256) {
     if (j < bt) {
       float acc = 0.f;
@@ -95,7 +95,7 @@ template <typename T, int D, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                            const T* __restrict__ v, const int32_t* __restrict__ idx,
                                                            int topk, int L, int S, float scale, int64_t nrows,
-                                                           T* __restrict__ o, float* __restrict__ lse) {
+                                                           T* __restrict__ o, float* __restrict__ lse, int G) {
   __shared__ float qsh[4][D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
@@ -106,8 +106,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(const T* __restrict__
   for (int d = lane; d < D; d += 64) qs[d] = Elem<T>::load1(q + row * D + d);
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const T* kh = k + bh * (int64_t)L * D;
-  const T* vh = v + bh * (int64_t)L * D;
+  const T* kh = k + (bh / G) * (int64_t)L * D;  // K/V head of this query head
+  const T* vh = v + (bh / G) * (int64_t)L * D;
   float m = -__builtin_huge_valf(), l = 0.f, acc[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
@@ -139,7 +139,7 @@ static hipError_t run_topk_generic(const Dims& d, const void* q, const float* km
   const int P = next_pow2(max(1, d.n()));
   const size_t shm = D * sizeof(float) + (size_t)P * (8 + 4 + 1);
   hipLaunchKernelGGL((topk_generic_kernel<T, D>), dim3((unsigned)d.tokens()), dim3(256), shm, st,
-                     static_cast<const T*>(q), km, idx, sel, d.L, d.S, topk, P);
+                     static_cast<const T*>(q), km, idx, sel, d.L, d.S, topk, P, d.G());
   return hipGetLastError();
 }
 
@@ -165,7 +165,7 @@ static hipError_t run_attn_generic(const Dims& d, const void* q, const void* k, 
   const int64_t nrows = d.tokens();
   hipLaunchKernelGGL((attn_generic_kernel<T, D, SPARSE>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), idx, topk, d.L,
-                     d.S, scale, nrows, static_cast<T*>(o), lse);
+                     d.S, scale, nrows, static_cast<T*>(o), lse, d.G());
   return hipGetLastError();
 }
 

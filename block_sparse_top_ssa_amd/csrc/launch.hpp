@@ -6,9 +6,18 @@ namespace ssa {
 
 struct Dims {
   int B, H, L, D, S, dtype;  // S = block size; dtype 0 = f32, 1 = bf16
+  int Hkv;                   // key/value heads (divides H); query head h reads K/V head h / G
   int n() const { return L / S; }
   int64_t bh() const { return (int64_t)B * H; }
   int64_t tokens() const { return (int64_t)B * H * L; }
+  // query heads per K/V head; flat query head bh = b*H + h reads flat K/V head bh / G()
+  int G() const { return H / Hkv; }
+  // the same shape seen from the K/V heads (for k, v and the pooled keys)
+  Dims kv() const {
+    Dims k = *this;
+    k.H = Hkv;
+    return k;
+  }
 };
 
 // Reports the reason a launcher refused a shape it cannot handle (no launch done).
@@ -32,8 +41,9 @@ LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, co
 
 // V of a bf16 [B,H,L,D] tensor rewritten into MFMA fragment order: per (b,h), 64-key
 // chunk c, 16-column tile dt and key half kc, 64 lanes x 16 bytes, lane 16 g + i holding
-// V[64 c + kappa(kc, g, 0..7)][16 dt + i].  The buffer (B*H*L*D*2 bytes) comes from a
-// stream-ordered pool kept per device; give it back with vfrag_release on the same stream.
+// V[64 c + kappa(kc, g, 0..7)][16 dt + i].  d holds the key/value head count in H (callers
+// pass Dims::kv()), so the buffer is B*Hkv*L*D*2 bytes; it comes from a stream-ordered
+// pool kept per device; give it back with vfrag_release on the same stream.
 hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st);
 hipError_t vfrag_release(void* ws, hipStream_t st);
 

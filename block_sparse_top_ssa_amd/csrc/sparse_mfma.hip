@@ -94,7 +94,7 @@ template <int D, int S, int T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const u32x4* __restrict__ vt, const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale) {
+    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G) {
   constexpr int NW = 8, NTH = 512;
   constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
   constexpr int DTW = NDT / 4;  // d tiles per value wave
@@ -123,9 +123,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   uint8_t* list = smem + lay.list;
 
   const uint16_t* qh = q + bh * (int64_t)L * D;
-  const uint16_t* kh = k + bh * (int64_t)L * D;
-  const uint16_t* vh = v + bh * (int64_t)L * D;
-  const u32x4* vth = vt + bh * (int64_t)(L / 64) * NDT * 2 * 64;
+  const int64_t kvh = bh / G;  // K/V head of this query head
+  const uint16_t* kh = k + kvh * (int64_t)L * D;
+  const uint16_t* vh = v + kvh * (int64_t)L * D;
+  const u32x4* vth = vt + kvh * (int64_t)(L / 64) * NDT * 2 * 64;
   const int32_t* ih = idx + bh * (int64_t)L * topk;
   auto vt_frag = [&](int c, int dt, int kc) -> u32x4 { return vth[((int64_t)(c * NDT + dt) * 2 + kc) * 64 + lane]; };
 
@@ -634,7 +635,7 @@ static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const 
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, idx, topk,
-                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale);
+                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G());
   return hipGetLastError();
 }
 
@@ -650,7 +651,7 @@ LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, con
                                 int topk, float scale, void* o, float* lse, hipStream_t st) {
   LaunchResult r;
   void* ws = nullptr;
-  r.err = vfrag_acquire(d, v, &ws, st);
+  r.err = vfrag_acquire(d.kv(), v, &ws, st);
   if (r.err != hipSuccess) return r;
   const u32x4* vt = static_cast<const u32x4*>(ws);
   if (d.D == 128)

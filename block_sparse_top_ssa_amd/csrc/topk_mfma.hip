@@ -217,7 +217,7 @@ __device__ __forceinline__ void split3x2(float x0, float x1, uint32_t& hi, uint3
 template <int D, int S, int E>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
                                                         int32_t* __restrict__ idx, float* __restrict__ sel, int L,
-                                                        int n, int BH, int topk) {
+                                                        int n, int BH, int topk, int G) {
   constexpr int NC = D / 32, NT = S / 16, KP = 64 * E, SCS = 65;
   __shared__ float sc[S][SCS];
   __shared__ uint64_t lists[S][KP];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restr
   const int qb = n - 1 - (int)(wg % n);
   const int m = min(topk - 1, qb);
   const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
-  const float* kmh = km + bh * (int64_t)n * D;
+  const float* kmh = km + (bh / G) * (int64_t)n * D;  // pooled keys of this head's K/V head
   int32_t* ih = idx + (bh * L + (int64_t)qb * S) * topk;
   float* sh = sel ? sel + (bh * L + (int64_t)qb * S) * topk : nullptr;
   const float inf = __builtin_huge_valf();
@@ -408,7 +408,7 @@ __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a >
 template <int D, int S>
 __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
                                                           int32_t* __restrict__ idx, float* __restrict__ sel, int L,
-                                                          int n, int BH, int topk) {
+                                                          int n, int BH, int topk, int G) {
   constexpr int NC = D / 32, NT = S / 16, RPW = S / 4;  // rows per wave
   // Scores of a chunk go to one of two buffers (chunk parity), so scoring the next chunk
   // never overwrites scores other waves may still read: one barrier per chunk.
@@ -421,7 +421,7 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
   const int qb = n - 1 - (int)(wg % n);
   const int m = min(topk - 1, qb);
   const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
-  const float* kmh = km + bh * (int64_t)n * D;
+  const float* kmh = km + (bh / G) * (int64_t)n * D;  // pooled keys of this head's K/V head
   int32_t* ih = idx + (bh * L + (int64_t)qb * S) * topk;
   float* sh = sel ? sel + (bh * L + (int64_t)qb * S) * topk : nullptr;
   const float inf = __builtin_huge_valf();
@@ -582,7 +582,7 @@ static hipError_t run_select(const Dims& d, const void* q, const float* km, int 
                              hipStream_t st) {
   const int64_t grid = (int64_t)d.n() * d.bh();
   hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk);
+                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk, d.G());
   return hipGetLastError();
 }
 
@@ -591,7 +591,7 @@ static hipError_t run_topk(const Dims& d, const void* q, const float* km, int to
                            hipStream_t st) {
   const int64_t grid = (int64_t)d.n() * d.bh();
   hipLaunchKernelGGL((topk_merge_kernel<D, S, E>), dim3((unsigned)grid), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk);
+                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk, d.G());
   return hipGetLastError();
 }
 

@@ -7,9 +7,13 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  Tensors      q, k, v, o are [B, H, L, D] row-major contiguous (D innermost), element
- *               type given by ssa_dims.dtype (SSA_BF16 or SSA_F32).  Every head has its
- *               own keys and values (as many KV heads as query heads).
+ *  Tensors      q and o are [B, H, L, D], k and v are [B, Hkv, L, D], row-major
+ *               contiguous (D innermost), element type given by ssa_dims.dtype (SSA_BF16
+ *               or SSA_F32).  Hkv = ssa_dims.Hkv key/value heads (0 means H) divide the
+ *               H query heads into groups of G = H / Hkv consecutive heads that share
+ *               one key/value head: query head h reads key/value head h / G (grouped-
+ *               query attention, as in the paper's training setup with two key-value
+ *               heads, App. C, p. 20).  Every query head selects its own blocks.
  *               Blocks: block size s = ssa_dims.block, n = L / s blocks per sequence; the
  *               query at position t lies in block b_t = t / s.
  *  Pointers     every data pointer is a DEVICE pointer (hipMalloc'd, or torch CUDA
@@ -24,7 +28,8 @@
  *               synchronisation.  Outputs are valid once the stream reaches that point.
  *  Errors       arguments are checked before anything is enqueued, so a call that
  *               returns an error has done no work.  Checks: required pointers non-NULL
- *               and aligned as above; B, H, L >= 1; D in {64, 128}; block in {64, 128};
+ *               and aligned as above; B, H, L >= 1; Hkv = 0 or Hkv >= 1 dividing H;
+ *               D in {64, 128}; block in {64, 128};
  *               L % block == 0; 1 <= topk <= n; dtype known; scale finite and > 0;
  *               B*H*L <= 2^24; the current device is gfx950.  A failed launch returns
  *               SSA_ERR_LAUNCH.  ssa_last_error() gives a thread-local message for the
@@ -46,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 1
+#define SSA_ABI_VERSION 2 /* 2: ssa_dims.Hkv (grouped-query attention) */
 
 typedef int32_t ssa_status;
 enum {
@@ -62,17 +67,18 @@ enum {
 enum { SSA_F32 = 0, SSA_BF16 = 1 };
 
 typedef struct {
-  int32_t B, H, L, D; /* batch, heads, sequence length, head dim */
+  int32_t B, H, L, D; /* batch, query heads, sequence length, head dim */
   int32_t block;      /* block size s (tokens per block) */
   int32_t dtype;      /* SSA_F32 or SSA_BF16: element type of q, k, v and o */
+  int32_t Hkv;        /* key/value heads: 0 (= H) or a divisor of H */
 } ssa_dims;
 
 /*
  * ssa_block_pool -- mean-pooled block keys.
  *   Paper sec. 3 (p. 4): tokens are split into contiguous blocks of s, and each block
  *   is represented by the mean of its keys.
- *   k       [B,H,L,D] (dtype)               in
- *   k_mean  [B,H,n,D] float32               out: k_mean[b,h,j,:] = (1/s) sum_{i=js}^{js+s-1}
+ *   k       [B,Hkv,L,D] (dtype)             in
+ *   k_mean  [B,Hkv,n,D] float32             out: k_mean[b,h,j,:] = (1/s) sum_{i=js}^{js+s-1}
  *                                           k[b,h,i,:], summed in float32.
  */
 ssa_status ssa_block_pool(const ssa_dims* dims, const void* k, float* k_mean, void* stream);
@@ -83,7 +89,8 @@ ssa_status ssa_block_pool(const ssa_dims* dims, const void* k, float* k_mean, vo
  *   the blocks before its own with their pooled keys and keeps the best k; its own
  *   block is always kept and counts toward k.
  *   q          [B,H,L,D] (dtype)            in
- *   k_mean     [B,H,n,D] float32            in (as written by ssa_block_pool)
+ *   k_mean     [B,Hkv,n,D] float32          in (as written by ssa_block_pool); query head h
+ *                                           scores the pooled keys of key/value head h / G
  *   topk       1 <= topk <= n               blocks kept per query (k)
  *   idx        [B,H,L,topk] int32           out: for the query at t, the blocks j < b_t with
  *              the m = min(topk-1, b_t) largest scores sigma_tj = q_t . k_mean_j (raw dot
@@ -99,7 +106,8 @@ ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_me
  * ssa_sparse_attn_fwd -- softmax attention over the tokens of the kept blocks.
  *   Paper sec. 3 (p. 4): the kept blocks' tokens form reduced key and value matrices
  *   for the query; App. D (p. 21, the attend-over-selected-tokens stage).
- *   q, k, v  [B,H,L,D] (dtype)               in
+ *   q        [B,H,L,D] (dtype)               in
+ *   k, v     [B,Hkv,L,D] (dtype)             in (query head h attends key/value head h / G)
  *   idx      [B,H,L,topk] int32              in: rows as written by ssa_block_topk (distinct
  *            blocks in ascending order, -1 in unused slots).  The query's own block b_t
  *            is always attended, causally (keys i <= t), whether or not it is listed.
@@ -109,7 +117,7 @@ ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_me
  *   o        [B,H,L,D] (dtype)               out: o(t) = sum_{i in A(t)} softmax_i(scale q_t.k_i) v_i,
  *            A(t) = {i <= t : i/s attended}
  *   lse      [B,H,L] float32 or NULL         out (optional): log sum_{i in A(t)} exp(scale q_t.k_i)
- *   Workspace (bf16 only): B*H*L*D*2 bytes holding v in the layout the matrix-core
+ *   Workspace (bf16 only): B*Hkv*L*D*2 bytes holding v in the layout the matrix-core
  *   products read, taken from a stream-ordered memory pool that the library keeps per
  *   device and returned to it on `stream` before the call returns.  The pool keeps the
  *   memory for reuse, so after the first call of a given size the allocation neither
@@ -123,12 +131,13 @@ ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* 
 /*
  * ssa_full_attn_fwd -- dense causal attention.
  *   Paper sec. 3 (p. 3): every query attends to all preceding tokens (and itself).
- *   q, k, v  [B,H,L,D] (dtype)               in
+ *   q        [B,H,L,D] (dtype)               in
+ *   k, v     [B,Hkv,L,D] (dtype)             in (query head h attends key/value head h / G)
  *   o        [B,H,L,D] (dtype) or NULL       out: o(t) = sum_{i<=t} softmax_i(scale q_t.k_i) v_i
  *   lse      [B,H,L] float32 or NULL         out: log sum_{i<=t} exp(scale q_t.k_i)
  *   At least one of o, lse must be given; with o == NULL only the log-sum-exp is
  *   computed (the value products are skipped).
- *   Workspace (bf16 with o given): the same transient B*H*L*D*2-byte copy of v as
+ *   Workspace (bf16 with o given): the same transient B*Hkv*L*D*2-byte copy of v as
  *   ssa_sparse_attn_fwd, from the same pool, with the same error behaviour.
  */
 ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v,

@@ -46,13 +46,26 @@ FAKE = ctypes.c_void_p(1 << 20)       # 16-byte aligned, never dereferenced
 MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
 
 
-def _dims(B=1, H=2, L=256, D=128, block=64, dtype=_lib.SSA_BF16):
-    return _lib.Dims(B, H, L, D, block, dtype)
+def _dims(B=1, H=2, L=256, D=128, block=64, dtype=_lib.SSA_BF16, Hkv=0):
+    return _lib.Dims(B, H, L, D, block, dtype, Hkv)
+
+
+def test_dims_struct_matches_header():
+    """The ctypes struct lists the header's ssa_dims fields in order (int32 each)."""
+    body = re.search(r"typedef struct \{(.*?)\} ssa_dims;", open(HEADER).read(), re.S).group(1)
+    names = []
+    for line in body.splitlines():
+        decl = line.split("/*")[0].strip().rstrip(";")
+        if decl.startswith("int32_t"):
+            names += [x.strip() for x in decl[len("int32_t"):].split(",")]
+    assert names == [f[0] for f in _lib.Dims._fields_]
+    assert ctypes.sizeof(_lib.Dims) == 4 * len(names)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=7), 3), (dict(D=96), 2), (dict(block=32), 2), (dict(L=200), 2), (dict(B=0), 2),
     (dict(H=-1), 2), (dict(B=1 << 10, H=1 << 10, L=1 << 10), 2),
+    (dict(H=6, Hkv=4), 2), (dict(H=4, Hkv=-2), 2), (dict(H=4, Hkv=8), 2),
 ])
 def test_bad_dims(libssa, kw, code):
     d = _dims(**kw)

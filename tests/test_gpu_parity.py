@@ -68,10 +68,12 @@ def _oracle_checks(inp, g, topk, rows, lse_only_full=False, check_idx=True):
     w = inp.workload
     tol = TOL[w.dtype]
     s, scale = w.s, 1.0 / math.sqrt(w.D)
-    q64, k64, v64 = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    q64 = inp.as_f64("q")
     R = np.arange(w.L) if rows is None else rows
-    km = O.block_pool(k64, s)
-    assert_close(g["km"], km, 1e-5 * max(1.0, float(np.abs(km).max())), "k_mean")
+    km_kv = O.block_pool(inp.as_f64("k"), s)   # pooled keys of the key/value heads
+    assert_close(g["km"], km_kv, 1e-5 * max(1.0, float(np.abs(km_kv).max())), "k_mean")
+    # grouped key/value heads: each query head works with its group's k, v and kbar
+    k64, v64, km = (inp.kv_per_query_head(a) for a in (inp.as_f64("k"), inp.as_f64("v"), km_kv))
     report = {}
     if check_idx:
         oidx, extra = O.block_topk(q64, km, s, topk, rows=R, return_scores=True)
@@ -257,6 +259,22 @@ def test_edge_shapes(variant, B, H, L, D, s, topk):
     _oracle_checks(inp, g, topk, rows=None)
 
 
+@pytest.mark.parametrize("B,H,Hkv,L,D,s,topk", [
+    (2, 8, 2, 2048, 128, 64, 8),    # four query heads per key/value head
+    (1, 6, 3, 1024, 64, 128, 3),    # D = 64, block 128, groups of two
+    (1, 4, 1, 1280, 128, 64, 6),    # one key/value head for all, ragged 256-row tile
+])
+def test_grouped_kv_heads(variant, B, H, Hkv, L, D, s, topk):
+    """Grouped-query attention: query head h attends key/value head h // (H // Hkv) and
+    selects its own blocks from that head's pooled keys; the oracle runs on k and v
+    repeated per group."""
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "lowrank", seed=18, hkv=Hkv)
+    inp.workload = W.Workload("gqa", B, H, L, D, s, (topk,), W.BF16, "lowrank", 18, Hkv=Hkv)
+    g = gpu_pipeline(inp, topk, tag=f"gqa {B}x{H}/{Hkv}x{L}x{D} s={s}")
+    assert g["km"].shape == (B, Hkv, L // s, D)
+    _oracle_checks(inp, g, topk, rows=None)
+
+
 def test_huge_logit_row_recomputed(variant):
     """A key far more aligned with the query than anything in the query's own block
     (logit gap ~75) must still give the exact sparse softmax."""
@@ -285,7 +303,7 @@ def _big(name, head_groups):
     rows = W.sample_rows(w.L, w.s, topk, w.sample_rows, seed=w.seed)
     _oracle_checks(inp, g, topk, rows=rows, lse_only_full=w.sparse_only, check_idx=False)
     q64 = inp.as_f64("q")
-    km = O.block_pool(inp.as_f64("k"), w.s)
+    km = inp.kv_per_query_head(O.block_pool(inp.as_f64("k"), w.s))
     tot = {"rows": 0, "tolerated": 0}
     for hs in head_groups:
         sl = slice(hs[0], hs[1])
@@ -304,3 +322,8 @@ def test_bf16_L32768_sink():
 @pytest.mark.slow
 def test_bf16_L131072_drift():
     _big("bf16_L131072_drift", [(0, 2), (2, 4), (4, 6), (6, 8)])
+
+
+@pytest.mark.slow
+def test_bf16_L32768_gqa2():
+    _big("bf16_L32768_gqa2", [(0, 8), (8, 16), (16, 24), (24, 32)])

@@ -38,10 +38,20 @@ class Workload:
     seed: int
     sample_rows: int = 0        # rows per (b, h) the oracle checks for O / lse / stats; 0 = all
     sparse_only: bool = False   # full stream computed as LSE only (dropped mass)
+    Hkv: int = 0                # key/value heads (0: as many as query heads)
 
     @property
     def n(self) -> int:
         return self.L // self.s
+
+    @property
+    def hkv(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def group(self) -> int:
+        """Query heads per key/value head (query head h reads key/value head h // group)."""
+        return self.H // self.hkv
 
     @property
     def scale(self) -> float:
@@ -64,6 +74,10 @@ WORKLOADS = {
         # plus dropped-mass statistics (full stream as LSE only).
         Workload("bf16_L131072_drift", 1, 8, 131072, 128, 128, (64,), BF16, "sink_drift",
                  1005, sample_rows=256, sparse_only=True),
+        # bf16_L32768_sink's shape with two key/value heads shared by 16 query heads each
+        # (grouped-query attention, the paper's training setup).
+        Workload("bf16_L32768_gqa2", 1, 32, 32768, 128, 64, (32,), BF16, "sink", 1006,
+                 sample_rows=512, Hkv=2),
     ]
 }
 
@@ -112,15 +126,22 @@ class Inputs:
     def as_f64(self, name: str) -> np.ndarray:
         return self.as_f32(name).astype(np.float64)
 
+    def kv_per_query_head(self, a: np.ndarray) -> np.ndarray:
+        """A [B, Hkv, ...] key/value-side array repeated to one slice per query head
+        (query head h reads key/value head h // group)."""
+        g = self.workload.group
+        return a if g == 1 else np.repeat(a, g, axis=1)
+
 
 def _draw(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.standard_normal(shape, dtype=np.float32)
 
 
 def make_qkv(B, H, L, D, s, dtype=BF16, structure="none", seed=0, q_zero=False,
-             heads=None) -> Inputs:
-    """Draw q, k, v of shape [B, H, L, D] (q, k, v in that order from one generator
-    seeded with `seed`), add the key structure, and round to the element type.
+             heads=None, hkv=0) -> Inputs:
+    """Draw q of shape [B, H, L, D] and k, v of shape [B, Hkv, L, D] (Hkv = hkv or H;
+    q, k, v in that order from one generator seeded with `seed`), add the key
+    structure, and round to the element type.
 
     structure:
       "none"       q, k, v ~ N(0, 1)
@@ -132,30 +153,33 @@ def make_qkv(B, H, L, D, s, dtype=BF16, structure="none", seed=0, q_zero=False,
                    from 1024 to 131072 over d, phi ~ U[0, 2 pi) (drawn after v);
                    then k[:, :, 0, :] *= 8
     heads: optional subset of head indices to keep (the draw is still of the whole
-    tensor, so a subset has the same values as in the full draw).
+    tensor, so a subset has the same values as in the full draw); only with Hkv = H.
+    The key structure's per-head terms are per key/value head.
     """
     rng = np.random.default_rng(seed)
-    shape = (B, H, L, D)
-    q = _draw(rng, shape)
-    k = _draw(rng, shape)
-    v = _draw(rng, shape)
+    Hk = hkv or H
+    if H % Hk or (heads is not None and Hk != H):
+        raise ValueError("hkv must divide H, and a head subset needs hkv = H")
+    q = _draw(rng, (B, H, L, D))
+    k = _draw(rng, (B, Hk, L, D))
+    v = _draw(rng, (B, Hk, L, D))
     if structure == "scaled":
         f = np.float32(1.0 / 8.0)
         q *= f
         k *= f
         v *= f
     elif structure == "lowrank":
-        A = rng.standard_normal((H, D, 4), dtype=np.float32) * np.float32(0.5)
-        z = rng.standard_normal((B, H, L // s, 4), dtype=np.float32)
+        A = rng.standard_normal((Hk, D, 4), dtype=np.float32) * np.float32(0.5)
+        z = rng.standard_normal((B, Hk, L // s, 4), dtype=np.float32)
         bias = np.einsum("hdr,bhjr->bhjd", A, z).astype(np.float32)   # [B,H,n,D]
         k += np.repeat(bias, s, axis=2)
     elif structure == "sink":
         k[:, :, 0, :] *= np.float32(8.0)
     elif structure == "sink_drift":
         periods = np.geomspace(1024.0, 131072.0, D)
-        phi = rng.uniform(0.0, 2.0 * np.pi, size=(H, D))
+        phi = rng.uniform(0.0, 2.0 * np.pi, size=(Hk, D))
         t = np.arange(L, dtype=np.float64)[:, None]
-        for h in range(H):
+        for h in range(Hk):
             drift = (0.5 * np.sin(2.0 * np.pi * t / periods[None, :] + phi[h][None, :]))
             k[:, h] += drift.astype(np.float32)[None]
         k[:, :, 0, :] *= np.float32(8.0)
@@ -168,13 +192,13 @@ def make_qkv(B, H, L, D, s, dtype=BF16, structure="none", seed=0, q_zero=False,
     if dtype == BF16:
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
     wl = Workload("adhoc", B, H if heads is None else len(heads), L, D, s, (), dtype,
-                  structure, seed)
+                  structure, seed, Hkv=0 if Hk == H else Hk)
     return Inputs(wl, q, k, v)
 
 
 def make_workload(name: str, heads=None) -> Inputs:
     w = WORKLOADS[name]
-    inp = make_qkv(w.B, w.H, w.L, w.D, w.s, w.dtype, w.structure, w.seed, heads=heads)
+    inp = make_qkv(w.B, w.H, w.L, w.D, w.s, w.dtype, w.structure, w.seed, heads=heads, hkv=w.Hkv)
     inp.workload = w
     return inp
 
