@@ -26,6 +26,13 @@ Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
   align_stats           sec. 5 (pp. 6-7): per-token comparison of the two streams'
                         outputs (Euclidean distance) and the dropped mass obtained from
                         the two log-sum-exps.
+  open_block_mean       App. E (p. 22) names the missing key/value cache; with one new
+                        token per step, the pooled key of the query's own, still open
+                        block is the mean of the tokens it holds so far (sec. 3's block
+                        mean over a partial block).
+  decode_step           one decoding step with a key/value cache: the query at position
+                        t against the cached keys and values 0..t, both streams, formed
+                        from the cache alone (sec. 3, p. 3-4; App. E, p. 22).
 
 Readings where the pages are silent (listed in full in the design notes):
   * candidates are the blocks strictly before the query's block; the own block is
@@ -48,7 +55,7 @@ import numpy as np
 __all__ = [
     "block_pool", "block_scores", "block_topk", "attend_full", "attend_sparse",
     "attend_sparse_gather", "dropped_mass", "align_stats", "attended_blocks",
-    "attended_count",
+    "attended_count", "open_block_mean", "decode_step",
 ]
 
 
@@ -278,3 +285,59 @@ def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None):
         x = np.asarray(lse_sparse, dtype=np.float64) - np.asarray(lse_full, dtype=np.float64)
         dropped = np.clip(-np.expm1(x), 0.0, 1.0)
     return dist, dropped
+
+
+# ----------------------------------------------------------------------------------
+# App. E: decoding with a key/value cache (one new query per step)
+# ----------------------------------------------------------------------------------
+def open_block_mean(k_bh: np.ndarray, t: int, s: int) -> np.ndarray:
+    """Mean of the cached keys of the block holding position t, over the tokens present
+    once t is appended: (1/c) sum_{i = b_t s}^{t} k_i with c = t - b_t s + 1 (float64).
+    k_bh is the [L, D] cache of one (b, h); tokens after t are not read."""
+    start = (t // s) * s
+    rows = np.asarray(k_bh[start:t + 1], dtype=np.float64)
+    return rows.sum(axis=0) / rows.shape[0]
+
+
+def decode_step(q_t: np.ndarray, k_bh: np.ndarray, v_bh: np.ndarray, t: int, s: int, topk: int,
+                scale: float) -> dict:
+    """The query at position t of one (b, h) against its cache (keys and values 0..t;
+    rows after t are ignored).
+
+    Sparse stream: the complete blocks j < b_t are pooled from the cache (mean of their
+    s keys), scored by q_t . kbar_j, ordered by (score descending, j ascending); the
+    first min(topk - 1, b_t) are kept, b_t is added, and attention runs over the tokens
+    of the kept blocks with i <= t.  Full stream: attention over every i <= t.
+    Returns idx (topk int32, ascending, -1 padded), o_s, lse_s, o_f, lse_f (float64), and
+    sigma_m / sigma_m1, the scores of the last kept and the best left-out candidate (NaN
+    where that candidate does not exist)."""
+    q = np.asarray(q_t, dtype=np.float64)
+    K = np.asarray(k_bh[:t + 1], dtype=np.float64)
+    V = np.asarray(v_bh[:t + 1], dtype=np.float64)
+    bt = t // s
+    m = min(topk - 1, bt)
+    kept = []
+    sigma_m = sigma_m1 = np.nan
+    if m > 0:
+        kbar = K[:bt * s].reshape(bt, s, -1).mean(axis=1)
+        sc = kbar @ q
+        ranked = sorted(range(bt), key=lambda j: (-sc[j], j))
+        kept = sorted(ranked[:m])
+        sigma_m = sc[ranked[m - 1]]
+        if m < bt:
+            sigma_m1 = sc[ranked[m]]
+    blocks = kept + [bt]
+    idx = np.full(topk, -1, dtype=np.int32)
+    idx[:len(blocks)] = blocks
+
+    def attend(keys):
+        lg = scale * (K[keys] @ q)
+        mx = lg.max()
+        e = np.exp(lg - mx)
+        return (e @ V[keys]) / e.sum(), mx + np.log(e.sum())
+
+    sparse_keys = np.concatenate([np.arange(j * s, min(j * s + s, t + 1)) for j in blocks])
+    o_s, lse_s = attend(sparse_keys)
+    o_f, lse_f = attend(np.arange(t + 1))
+    return {"idx": idx, "o_s": o_s, "lse_s": lse_s, "o_f": o_f, "lse_f": lse_f,
+            "sigma_m": sigma_m, "sigma_m1": sigma_m1}

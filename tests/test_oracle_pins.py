@@ -439,3 +439,124 @@ def test_planted_mistakes_are_caught(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, f"planted slip in {name} ({fake.__name__}) went unnoticed"
+
+
+# ----------------------------------------------------------------------------------
+# decoding with a key/value cache: open_block_mean, decode_step
+# ----------------------------------------------------------------------------------
+def test_open_block_mean_closed_forms():
+    """The open block's mean over the c = t - b_t s + 1 tokens present: the token itself
+    when it opens a block, block_pool's mean when it closes one, and (integer keys) an
+    exact integer sum over c in between (summed here with a plain loop)."""
+    s, L, D = 8, 64, 5
+    ki = np.random.default_rng(7).integers(-50, 50, (L, D)).astype(np.float64)
+    km = O.block_pool(ki[None, None], s)[0, 0]
+    for t in range(L):
+        mean = O.open_block_mean(ki, t, s)
+        c = t % s + 1
+        brute = np.zeros(D)
+        for i in range((t // s) * s, t + 1):
+            brute += ki[i]
+        np.testing.assert_array_equal(np.round(mean * c), brute)
+        np.testing.assert_allclose(mean * c, brute, rtol=0, atol=1e-12)
+        if c == 1:
+            np.testing.assert_array_equal(mean, ki[t])
+        if c == s:
+            np.testing.assert_array_equal(mean, km[t // s])
+    # tokens after t are not read
+    poisoned = ki.copy()
+    poisoned[20:] = np.nan
+    np.testing.assert_array_equal(O.open_block_mean(poisoned, 19, s), O.open_block_mean(ki, 19, s))
+
+
+@pytest.mark.parametrize("topk", [1, 3, 10])
+def test_decode_step_matches_prefill_rows(topk):
+    """A decoding step at position t, formed from the cache alone (and blind to rows
+    after t), equals row t of the whole-sequence forward: selection, both streams."""
+    q, k, v, s, scale = _tiny_case(60, L=160, s=16)
+    km = O.block_pool(k, s)
+    idx = O.block_topk(q, km, s, topk)
+    o_s, l_s = O.attend_sparse(q, k, v, idx, s, scale)
+    o_f, l_f = O.attend_full(q, k, v, scale)
+    for h in range(q.shape[1]):
+        for t in range(q.shape[2]):
+            kc, vc = k[0, h].copy(), v[0, h].copy()
+            kc[t + 1:] = np.nan
+            vc[t + 1:] = np.nan
+            r = O.decode_step(q[0, h, t], kc, vc, t, s, topk, scale)
+            assert r["idx"].tolist() == idx[0, h, t].tolist(), (h, t)
+            np.testing.assert_allclose(r["o_s"], o_s[0, h, t], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(r["lse_s"], l_s[0, h, t], rtol=1e-13, atol=1e-14)
+            np.testing.assert_allclose(r["o_f"], o_f[0, h, t], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(r["lse_f"], l_f[0, h, t], rtol=1e-13, atol=1e-14)
+
+
+def test_decode_step_q_zero_closed_form():
+    """q = 0: all scores tie, so blocks 0..m-1 are kept; every logit is 0, so
+    lse_s = log |A(t)|, lse_f = log(t + 1) and o_f is the mean of v over 0..t."""
+    _, k, v, s, scale = _tiny_case(70, H=1, L=96, s=8)
+    q0 = np.zeros(k.shape[-1])
+    for topk in (1, 4, 12):
+        for t in range(k.shape[2]):
+            r = O.decode_step(q0, k[0, 0], v[0, 0], t, s, topk, scale)
+            bt = t // s
+            m = min(topk - 1, bt)
+            assert r["idx"].tolist() == list(range(m)) + [bt] + [-1] * (topk - m - 1)
+            assert math.isclose(r["lse_s"], math.log(O.attended_count(t, s, topk)), rel_tol=1e-13)
+            assert math.isclose(r["lse_f"], math.log(t + 1), rel_tol=1e-13, abs_tol=1e-15)
+            np.testing.assert_allclose(r["o_f"], v[0, 0, :t + 1].mean(axis=0), rtol=1e-12, atol=1e-13)
+
+
+def test_decode_planted_mistakes_are_caught(monkeypatch):
+    """Slips planted in a copy of decode_step (the open block scored as a candidate, a
+    strictly causal mask, ties to the higher block) fail one of the decode pins."""
+    def own_block_candidate(q_t, k_bh, v_bh, t, s, topk, scale):
+        q = np.asarray(q_t, dtype=np.float64)
+        K, V = np.asarray(k_bh[:t + 1], float), np.asarray(v_bh[:t + 1], float)
+        bt = t // s
+        cand = list(range(bt + 1))
+        sc = [q @ K[j * s:min(j * s + s, t + 1)].mean(axis=0) for j in cand]
+        kept = sorted(sorted(cand, key=lambda j: (-sc[j], j))[:topk])
+        if bt not in kept:
+            kept = sorted(kept[:topk - 1] + [bt])
+        return _finish(q, K, V, t, s, topk, scale, kept)
+
+    def strict_causal(q_t, k_bh, v_bh, t, s, topk, scale):
+        r = orig(q_t, k_bh, v_bh, t, s, topk, scale)
+        if t > 0:
+            r2 = orig(q_t, k_bh, v_bh, t - 1, s, topk, scale)
+            r["o_f"], r["lse_f"] = r2["o_f"], r2["lse_f"]
+        return r
+
+    def ties_high(q_t, k_bh, v_bh, t, s, topk, scale):
+        q = np.asarray(q_t, dtype=np.float64)
+        K, V = np.asarray(k_bh[:t + 1], float), np.asarray(v_bh[:t + 1], float)
+        bt = t // s
+        m = min(topk - 1, bt)
+        sc = [q @ K[j * s:j * s + s].mean(axis=0) for j in range(bt)]
+        kept = sorted(sorted(range(bt), key=lambda j: (-sc[j], -j))[:m]) + [bt]
+        return _finish(q, K, V, t, s, topk, scale, kept)
+
+    def _finish(q, K, V, t, s, topk, scale, blocks):
+        idx = np.full(topk, -1, np.int32)
+        idx[:len(blocks)] = blocks
+        keys = np.concatenate([np.arange(j * s, min(j * s + s, t + 1)) for j in blocks])
+        lg = scale * (K[keys] @ q)
+        e = np.exp(lg - lg.max())
+        lf = scale * (K @ q)
+        ef = np.exp(lf - lf.max())
+        return {"idx": idx, "o_s": e @ V[keys] / e.sum(), "lse_s": lg.max() + np.log(e.sum()),
+                "o_f": ef @ V / ef.sum(), "lse_f": lf.max() + np.log(ef.sum())}
+
+    orig = O.decode_step
+    checks = [lambda: test_decode_step_matches_prefill_rows(3), test_decode_step_q_zero_closed_form]
+    for fake in (own_block_candidate, strict_causal, ties_high):
+        with monkeypatch.context() as mp:
+            mp.setattr(O, "decode_step", fake)
+            failed = 0
+            for chk in checks:
+                try:
+                    chk()
+                except AssertionError:
+                    failed += 1
+            assert failed > 0, f"planted slip {fake.__name__} went unnoticed"
