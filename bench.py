@@ -15,6 +15,12 @@ bounded sample of the same workload (rank 0, this process).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                     [--no-cpu-baseline] [--copy-calib]
+
+`--path decode` measures decoding with a key/value cache instead: one step = one new
+token for each of B sequences (at different positions of a 32768-token cache): append
+(cache rows + open block's pooled key) -> selection + sparse attention -> full attention
+-> alignment statistics; `value` is tokens/s (B / step time) and `roofline` is given
+for the dominant kernel, the full-stream attention, against HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -65,22 +71,30 @@ KERNEL_SOURCES = {"pool": "pool.hip", "topk": "topk_mfma.hip", "sparse": "sparse
 SHARED_HEADERS = ("common.hpp", "mfma.hpp", "rowattn.hpp")
 
 
-def measured_traffic(workload: str) -> dict:
+DECODE_SOURCES = {"append": "decode.hip", "sparse": "decode.hip", "full": "decode.hip", "align": "align.hip"}
+
+
+def measured_traffic(workload: str, sources: dict = KERNEL_SOURCES) -> dict:
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-    (profiles/hbm_traffic.json), per kernel, only where the kernel's source and the
-    shared headers are unchanged since the counters were taken; otherwise None."""
+    (profiles/hbm_traffic.json, or profiles/hbm_traffic_<workload>.json), per kernel,
+    only where the kernel's source and the shared headers are unchanged since the
+    counters were taken; otherwise None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    out = {k: None for k in KERNEL_SOURCES}
-    try:
-        rec = json.load(open(path))
-    except (OSError, ValueError):
-        return out
-    if rec.get("workload") != workload:
+    out = {k: None for k in sources}
+    rec = None
+    for fn in ("hbm_traffic.json", f"hbm_traffic_{workload}.json"):
+        try:
+            r = json.load(open(os.path.join(ROOT, "profiles", fn)))
+        except (OSError, ValueError):
+            continue
+        if r.get("workload") == workload:
+            rec = r
+            break
+    if rec is None:
         return out
     csrc = os.path.join(ROOT, "block_sparse_top_ssa_amd", "csrc")
     hdr = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in SHARED_HEADERS)).hexdigest()
-    for k, fn in KERNEL_SOURCES.items():
+    for k, fn in sources.items():
         t = rec.get("kernels", {}).get(k)
         if not t:
             continue
@@ -146,11 +160,16 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
+    ap.add_argument("--path", default="prefill", choices=["prefill", "decode"],
+                    help="prefill: the whole-sequence forward (default); decode: one cached decoding step")
+    ap.add_argument("--decode-workload", default="bf16_L32768_decode", choices=sorted(W.DECODE_WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the kernels shard by head with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
+    if args.path == "decode":
+        return main_decode(args)
 
     import torch
     import block_sparse_top_ssa_amd as ssa
@@ -266,6 +285,154 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, k)
+    print(json.dumps(out), flush=True)
+
+
+# ----------------------------------------------------------------------------------
+# decoding with a key/value cache
+# ----------------------------------------------------------------------------------
+def decode_work_model(w: W.DecodeWorkload, pos: np.ndarray) -> dict:
+    """Algorithmic HBM bytes per call of one decoding step (each byte read or written
+    once): the full stream reads k and v rows 0..t of every key/value head; the sparse
+    stream reads the pooled keys of the b_t candidate blocks and k, v of the attended
+    rows of every query head, and writes the kept indices; append writes one row and
+    re-reads the open block; align reads both outputs."""
+    e = 2 if w.dtype == W.BF16 else 4
+    D, s, k = w.D, w.s, w.k
+    full = sparse = append = 0
+    for t in pos.astype(np.int64):
+        bt = t // s
+        m = min(k - 1, bt)
+        att = m * s + t % s + 1
+        full += w.hkv * (t + 1) * D * e * 2 + w.H * (2 * D * e + 4)
+        sparse += w.H * (bt * D * 4 + att * D * e * 2 + 2 * D * e + 4 + k * 4)
+        append += w.hkv * (2 * D * e + (t % s + 1) * D * e + D * 4)
+    return {"append": {"bytes": int(append)}, "sparse": {"bytes": int(sparse)}, "full": {"bytes": int(full)},
+            "align": {"bytes": int(w.B * w.H * (2 * D * e + 4 * 4))}}
+
+
+def cpu_baseline_decode(di: W.DecodeInputs, budget_s: float = 10.0) -> dict:
+    """The CPU oracle's decode_step (both streams) on as many (sequence, head) rows as fit
+    in about `budget_s` seconds; tokens/s counts a token as all H heads of a sequence."""
+    import oracle.ssa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = di.workload
+    scale = 1.0 / math.sqrt(w.D)
+    rows, t_total = 0, 0.0
+    for b in range(w.B):
+        t = int(di.pos[b])
+        for h in range(w.H):
+            kh = h // w.group
+            conv = (lambda a: W.bf16_bits_to_f32(a) if w.dtype == W.BF16 else a)
+            kk = conv(di.k[b, kh, :t + 1]).astype(np.float64)
+            vv = conv(di.v[b, kh, :t + 1]).astype(np.float64)
+            qq = conv(di.q[b, h]).astype(np.float64)
+            t0 = time.perf_counter()
+            O.decode_step(qq, kk, vv, t, w.s, w.k, scale)
+            t_total += time.perf_counter() - t0
+            rows += 1
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    tps = rows / w.H / t_total
+    return {"value": tps, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle decode_step (select, sparse and full attention) on {rows} of "
+                      f"{w.B * w.H} (sequence, head) rows, {t_total:.1f} s; a token = all {w.H} heads of one "
+                      f"sequence"}
+
+
+def main_decode(args):
+    import torch
+    import block_sparse_top_ssa_amd as ssa
+
+    di = W.make_decode(args.decode_workload)
+    w = di.workload
+
+    def dev(a):
+        if w.dtype == W.BF16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    kc, vc, q = dev(di.k), dev(di.v), dev(di.q)
+    pos = torch.from_numpy(di.pos).cuda()
+    ar = torch.arange(w.B, device="cuda")
+    k_new = kc[ar, :, pos.long()].contiguous()   # the new token's key and value (already at row pos)
+    v_new = vc[ar, :, pos.long()].contiguous()
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    km = ssa.block_pool(kc, s)                    # the prompt's pooled keys (outside the timed steps)
+    names = ["append", "sparse", "full", "align"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ssa.decode_append(pos, k_new, v_new, kc, vc, km, s)
+        mark(1)
+        o_s, lse_s, _ = ssa.decode_sparse_fwd(pos, q, kc, vc, km, s, w.k, scale, want_idx=False)
+        mark(2)
+        o_f, lse_f = ssa.decode_full_fwd(pos, q, kc, vc, scale, block=s)
+        mark(3)
+        ssa.align_stats(o_f.unsqueeze(2), o_s.unsqueeze(2), lse_f.unsqueeze(2), lse_s.unsqueeze(2), block=s)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}
+    if args.copy_calib:
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    model = decode_work_model(w, di.pos)
+    traffic = measured_traffic(w.name, DECODE_SOURCES)
+    kernels = {}
+    for nm in names:
+        gb = model[nm]["bytes"] / (per[nm] * 1e-3) / 1e9
+        kernels[nm] = {"ms": round(per[nm], 4), "gbps": round(gb, 1), "frac_peak": round(gb / PEAK_HBM_GBPS, 4),
+                       "algorithmic_bytes": model[nm]["bytes"], "hbm_bytes_measured": traffic[nm]}
+    full_gbps = model["full"]["bytes"] / (per["full"] * 1e-3) / 1e9
+    out = {
+        "metric": "decode tokens/s (one new token per sequence, both streams) at a 32K cache",
+        "value": round(w.B / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) cache and queries, sink key at token 0; no dataset, no weights)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.hkv, "cache": w.L, "D": w.D, "block": s,
+                   "topk": w.k, "positions": [int(x) for x in di.pos],
+                   "step": "append+decode_sparse(select+attend)+decode_full+align"},
+        "roofline": {"kernel": "ssa_decode_full_fwd", "bound": "hbm", "achieved": round(full_gbps, 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(full_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic["full"], "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
+                     "WRITE_SIZE, scaled by a 1 GiB copy; null when the kernel changed since)"},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(di)
     print(json.dumps(out), flush=True)
 
 

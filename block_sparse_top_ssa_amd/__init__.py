@@ -10,6 +10,13 @@ and the stream: each call enqueues on torch's current stream and does not synchr
     o_f, lse_f = full_attn_fwd(q, k, v)
     dist, dropped = align_stats(o_f, o_s, lse_f, lse_s)
 
+Decoding with a key/value cache (one new query per sequence, positions in a device
+int32 tensor `pos`, caches [B, Hkv, L, D] with L the capacity):
+
+    decode_append(pos, k_new, v_new, k_cache, v_cache, k_mean, block)
+    o_s, lse_s, idx = decode_sparse_fwd(pos, q, k_cache, v_cache, k_mean, block, topk)
+    o_f, lse_f = decode_full_fwd(pos, q, k_cache, v_cache)
+
 q is [B, H, L, D]; k and v may have fewer heads, [B, Hkv, L, D] with Hkv dividing H
 (grouped-query attention: query head h uses key/value head h // (H // Hkv)), and
 k_mean then has Hkv heads too.
@@ -26,6 +33,7 @@ import torch
 from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
+           "decode_append", "decode_sparse_fwd", "decode_full_fwd",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
 
 
@@ -147,3 +155,62 @@ def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, bloc
     check(load().ssa_align_stats(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
                                  _ptr(lse_sparse), _ptr(dist), _ptr(drop), _stream(ref)))
     return dist, drop
+
+
+# ---------------------------------------------------------------- decoding
+def _cache_dims(q_like: torch.Tensor, k_cache: torch.Tensor, block: int) -> Dims:
+    """Dims of a decoding call: q_like is [B, H, D], k_cache [B, Hkv, L, D]."""
+    if k_cache.dim() != 4 or q_like.dim() != 3:
+        raise SSAError(2, "expected q [B, H, D] and a cache [B, Hkv, L, D]")
+    B, Hkv, L, D = k_cache.shape
+    if q_like.shape[0] != B or q_like.shape[2] != D or q_like.dtype != k_cache.dtype or q_like.shape[1] % Hkv:
+        raise SSAError(2, f"q {tuple(q_like.shape)}/{q_like.dtype} does not fit the cache "
+                          f"{tuple(k_cache.shape)}/{k_cache.dtype}")
+    return Dims(B, q_like.shape[1], L, D, int(block), _dtype_code(k_cache), Hkv)
+
+
+def _pos(pos: torch.Tensor, B: int) -> torch.Tensor:
+    if pos.dtype != torch.int32 or pos.shape != (B,):
+        raise SSAError(2, "pos must be an int32 [B] device tensor")
+    return pos
+
+
+def decode_append(pos, k_new, v_new, k_cache, v_cache, k_mean, block: int):
+    """Write k_new, v_new ([B, Hkv, D]) at row pos[b] of the caches and refresh the pooled
+    key of that row's block in k_mean ([B, Hkv, L // block, D] float32), in place."""
+    d = _cache_dims(k_new, k_cache, block)
+    _same(k_new, v_new, "k_new/v_new")
+    _same(k_cache, v_cache, "k_cache/v_cache")
+    check(load().ssa_decode_append(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(k_mean), _stream(k_cache)))
+
+
+def decode_sparse_fwd(pos, q, k_cache, v_cache, k_mean, block: int, topk: int, scale: float | None = None,
+                      want_lse: bool = True, want_idx: bool = True):
+    """Selection and sparse attention for the query q[b, h] ([B, H, D]) at position pos[b].
+    Returns (o [B, H, D], lse [B, H] or None, idx [B, H, topk] or None)."""
+    d = _cache_dims(q, k_cache, block)
+    _same(k_cache, v_cache, "k_cache/v_cache")
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((d.B, d.H), dtype=torch.float32, device=q.device) if want_lse else None
+    idx = torch.empty((d.B, d.H, int(topk)), dtype=torch.int32, device=q.device) if want_idx else None
+    check(load().ssa_decode_sparse_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(q), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(k_mean), int(topk), ctypes.c_float(scale), _ptr(o),
+                                       _ptr(lse), _ptr(idx), _stream(q)))
+    return o, lse, idx
+
+
+def decode_full_fwd(pos, q, k_cache, v_cache, scale: float | None = None, want_o: bool = True,
+                    want_lse: bool = True, block: int = 64):
+    """Dense attention for the query q[b, h] at position pos[b] over cache rows 0..pos[b].
+    Returns (o [B, H, D] or None, lse [B, H] or None)."""
+    d = _cache_dims(q, k_cache, block)
+    if v_cache is not None:
+        _same(k_cache, v_cache, "k_cache/v_cache")
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    o = torch.empty_like(q) if want_o else None
+    lse = torch.empty((d.B, d.H), dtype=torch.float32, device=q.device) if want_lse else None
+    check(load().ssa_decode_full_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(q), _ptr(k_cache),
+                                     _ptr(v_cache), ctypes.c_float(scale), _ptr(o), _ptr(lse), _stream(q)))
+    return o, lse

@@ -52,18 +52,21 @@ ssa_status check_device() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-ssa_status check_dims(const ssa_dims* d, ssa::Dims* out) {
+// `blocks` = false for calls that do not use the block partition (ssa_align_stats):
+// then block is not checked and L need not be a multiple of it.
+ssa_status check_dims(const ssa_dims* d, ssa::Dims* out, bool blocks = true) {
   if (!d) return fail(SSA_ERR_NULL, "dims is NULL");
   if (d->dtype != SSA_F32 && d->dtype != SSA_BF16) return fail(SSA_ERR_DTYPE, "unknown dtype %d", d->dtype);
   if (d->B < 1 || d->H < 1 || d->L < 1) return fail(SSA_ERR_SHAPE, "B, H, L must be >= 1 (got %d, %d, %d)", d->B, d->H, d->L);
   if (d->D != 64 && d->D != 128) return fail(SSA_ERR_SHAPE, "head dim D must be 64 or 128 (got %d)", d->D);
-  if (d->block != 64 && d->block != 128) return fail(SSA_ERR_SHAPE, "block size must be 64 or 128 (got %d)", d->block);
-  if (d->L % d->block) return fail(SSA_ERR_SHAPE, "L=%d is not a multiple of the block size %d", d->L, d->block);
+  if (blocks && d->block != 64 && d->block != 128)
+    return fail(SSA_ERR_SHAPE, "block size must be 64 or 128 (got %d)", d->block);
+  if (blocks && d->L % d->block) return fail(SSA_ERR_SHAPE, "L=%d is not a multiple of the block size %d", d->L, d->block);
   const int hkv = d->Hkv == 0 ? d->H : d->Hkv;
   if (hkv < 1 || d->H % hkv) return fail(SSA_ERR_SHAPE, "Hkv=%d must be >= 1 and divide H=%d (0 means H)", d->Hkv, d->H);
   const int64_t tokens = (int64_t)d->B * d->H * d->L;
   if (tokens > (int64_t(1) << 24)) return fail(SSA_ERR_SHAPE, "B*H*L=%lld exceeds 2^24", (long long)tokens);
-  *out = ssa::Dims{d->B, d->H, d->L, d->D, d->block, d->dtype, hkv};
+  *out = ssa::Dims{d->B, d->H, d->L, d->D, blocks ? d->block : 64, d->dtype, hkv};
   return SSA_OK;
 }
 
@@ -167,7 +170,7 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
 ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void* o_sparse, const float* lse_full,
                            const float* lse_sparse, float* l2_dist, float* dropped, void* stream) {
   ssa::Dims d;
-  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_dims(dims, &d, false));
   if (!l2_dist && !dropped) return fail(SSA_ERR_NULL, "ssa_align_stats needs l2_dist or dropped");
   if (l2_dist) {
     SSA_TRY(check_ptr(o_full, "o_full", 16));
@@ -182,6 +185,59 @@ ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void*
   SSA_TRY(check_device());
   return finish(ssa::launch_align(d, o_full, o_sparse, lse_full, lse_sparse, l2_dist, dropped, (hipStream_t)stream),
                 "ssa_align_stats");
+}
+
+ssa_status ssa_decode_append(const ssa_dims* dims, const int32_t* pos, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, float* k_mean, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(pos, "pos", 4));
+  SSA_TRY(check_ptr(k_new, "k_new", 16));
+  SSA_TRY(check_ptr(v_new, "v_new", 16));
+  SSA_TRY(check_ptr(k_cache, "k_cache", 16));
+  SSA_TRY(check_ptr(v_cache, "v_cache", 16));
+  SSA_TRY(check_ptr(k_mean, "k_mean", 16));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_decode_append(d, pos, k_new, v_new, k_cache, v_cache, k_mean, (hipStream_t)stream),
+                "ssa_decode_append");
+}
+
+ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_mean, int32_t topk, float scale, void* o,
+                                 float* lse, int32_t* idx, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(pos, "pos", 4));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k_cache, "k_cache", 16));
+  SSA_TRY(check_ptr(v_cache, "v_cache", 16));
+  SSA_TRY(check_ptr(k_mean, "k_mean", 16));
+  SSA_TRY(check_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  SSA_TRY(check_opt_ptr(idx, "idx", 4));
+  if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_decode_sparse(d, pos, q, k_cache, v_cache, k_mean, topk, scale, o, lse, idx,
+                                          (hipStream_t)stream),
+                "ssa_decode_sparse_fwd");
+}
+
+ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
+                               const void* v_cache, float scale, void* o, float* lse, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(pos, "pos", 4));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k_cache, "k_cache", 16));
+  if (!o && !lse) return fail(SSA_ERR_NULL, "ssa_decode_full_fwd needs o or lse");
+  if (o) SSA_TRY(check_ptr(v_cache, "v_cache", 16));
+  SSA_TRY(check_opt_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_decode_full(d, pos, q, k_cache, v_cache, scale, o, lse, (hipStream_t)stream),
+                "ssa_decode_full_fwd");
 }
 
 const char* ssa_status_str(ssa_status s) {

@@ -1,0 +1,537 @@
+// Decoding with a key/value cache: one new query per sequence per step.
+//
+// The paper's sparse kernel has no key/value cache, which makes its decoding slow (App. E,
+// p. 22).  These kernels are the cached form of the per-layer forward of sec. 3 (pp. 3-4)
+// for the query at position t = pos[b]: the same block selection over the complete
+// blocks before t's own, the same sparse attention over the kept blocks, and dense
+// attention over 0..t, reading a cache of capacity L instead of the whole sequence.
+//
+// Everything here is bound by memory traffic and latency, not arithmetic: one query row
+// per (b, h) makes every product a matrix-vector product, so the kernels use 16-byte
+// coalesced loads of whole key/value rows, float32 vector arithmetic and short
+// xor-shuffle reductions, and spread a row's keys over many workgroups (split keys,
+// combined afterwards through per-split log-sum-exps) so that a small batch still
+// fills the chip.
+#include <cmath>
+
+#include "launch.hpp"
+#include "pool.hpp"
+
+namespace ssa {
+
+namespace {
+
+constexpr int kDecodeMaxBlocks = 8192;  // candidates held in LDS by the selection kernel
+constexpr int kChunk = 64;              // keys per wave step of the attention kernel
+
+// Position of the new token of sequence b, or -1 when it lies outside the cache.
+__device__ __forceinline__ int cache_pos(const int32_t* pos, int b, int L) {
+  const int p = pos[b];
+  return (p >= 0 && p < L) ? p : -1;
+}
+
+// Number of 64-key chunks a row attends and the chunks per split, identical in the
+// attention and combine kernels.  Sparse: the m = min(topk-1, b_t) kept blocks, then the
+// chunks of the own block up to t.  Full: chunks 0 .. t/64.
+template <bool SPARSE>
+__device__ __forceinline__ int row_chunks(int p, int s, int topk) {
+  if (SPARSE) {
+    const int bt = p / s;
+    const int m = min(topk - 1, bt);
+    return m * (s / kChunk) + (p - bt * s) / kChunk + 1;
+  }
+  return p / kChunk + 1;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- append
+// One wave per (b, key/value head): writes the new key and value at p = pos[b] and
+// rewrites the pooled key of block p / s as the mean of the c = p % s + 1 tokens it holds
+// (the new key read from k_new, the others from the cache), summed exactly as the block
+// pooling kernel sums a block, so a block completed by appends holds the same bits as one
+// pooled from the whole sequence.  A sequence whose pos is outside [0, L) is skipped.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_append_kernel(const int32_t* __restrict__ pos,
+                                                            const T* __restrict__ k_new,
+                                                            const T* __restrict__ v_new, T* __restrict__ kc,
+                                                            T* __restrict__ vc, float* __restrict__ km, int B,
+                                                            int Hkv, int L, int s, float inv_s) {
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // flat (b, kv head)
+  if (w >= (int64_t)B * Hkv) return;
+  const int p = cache_pos(pos, (int)(w / Hkv), L);
+  if (p < 0) return;
+  const T* kn = k_new + w * D;
+  const T* vn = v_new + w * D;
+  T* kh = kc + w * (int64_t)L * D;
+  T* vh = vc + w * (int64_t)L * D;
+  if (lane < LPR) {
+    store16(kh + (int64_t)p * D + lane * E, load16(kn + lane * E));
+    store16(vh + (int64_t)p * D + lane * E, load16(vn + lane * E));
+  }
+  const int bt = p / s, c = p - bt * s + 1;
+  float acc[E];
+  block_key_sum<T, D>(kh + (int64_t)bt * s * D, s, c, c - 1, kn, acc);
+  if (lane < LPR) {
+    float* dst = km + (w * (L / s) + bt) * D + lane * E;
+    const float cf = (float)c;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(c == s ? acc[e + i] * inv_s : acc[e + i] / cf);
+      store16(dst + e, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- selection
+// One workgroup per (b, query head).  Scores sigma_j = q . kbar_j of the complete blocks
+// j < b_t in float32 (a kbar row is D/4 lanes wide, several rows per wave-wide load,
+// xor-shuffle sums), held in LDS as order-preserving 32-bit keys.  The m = min(topk-1,
+// b_t) best by (score descending, j ascending) are found by a radix select, 8 bits per
+// pass from the top: a 256-bin histogram of the keys that match the digits chosen so far,
+// then the digit where the running count from the top reaches the wanted rank.  After
+// four passes the m-th key T is known with r = the number of keys equal to T to keep;
+// those are the r lowest indices among the keys equal to T.  A block-wide scan in index
+// order then writes the kept blocks in ascending order, b_t after them, -1 after that.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restrict__ pos, const T* __restrict__ q,
+                                                          const float* __restrict__ km, int32_t* __restrict__ idx,
+                                                          int H, int G, int L, int s, int topk) {
+  __shared__ uint32_t keys[kDecodeMaxBlocks];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wsum[4];
+  __shared__ int sel[2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t bh = blockIdx.x;
+  const int p = cache_pos(pos, (int)(bh / H), L);
+  int32_t* out = idx + bh * topk;
+  if (p < 0) {
+    for (int i = tid; i < topk; i += 256) out[i] = -1;
+    return;
+  }
+  const int bt = p / s;
+  const int m = min(topk - 1, bt);
+  if (m == bt || m == 0) {  // every candidate is kept, or none (topk = 1)
+    for (int i = tid; i < topk; i += 256) out[i] = i < m ? i : (i == m ? bt : -1);
+    return;
+  }
+  // ---- scores (bt >= 1 here)
+  constexpr int LK = D / 4, RK = kWave / LK;  // lanes per kbar row, rows per load
+  const float* kmh = km + (bh / G) * (int64_t)(L / s) * D;
+  float qv[4];
+  {
+    const T* qp = q + bh * D + (lane % LK) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[e] = Elem<T>::load1(qp + e);
+  }
+  const int nc = bt;
+  for (int j0 = wv * RK * 4; j0 < nc; j0 += 4 * RK * 4) {
+    f32x4 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u * RK + lane / LK;
+      x[u] = j < nc ? *reinterpret_cast<const f32x4*>(kmh + (int64_t)j * D + (lane % LK) * 4) : f32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float d = qv[0] * x[u][0];
+      d = fmaf(qv[1], x[u][1], d);
+      d = fmaf(qv[2], x[u][2], d);
+      d = fmaf(qv[3], x[u][3], d);
+#pragma unroll
+      for (int o = 1; o < LK; o <<= 1) d += __shfl_xor(d, o);
+      const int j = j0 + u * RK + lane / LK;
+      if (lane % LK == 0 && j < nc) keys[j] = orderable_f32(d);
+    }
+  }
+  __syncthreads();
+  // ---- radix select of the m-th largest key
+  uint32_t prefix = 0;
+  int rank = m;  // 1-based rank wanted among the keys that match `prefix`
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < nc; j += 256) {
+      const uint32_t u = keys[j];
+      if (pass == 0 || (u >> (shift + 8)) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wv == 0) {
+      // lane l holds digits 255-4l .. 252-4l, so lanes run from the top digit down
+      uint32_t c4[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c4[i] = hist[255 - 4 * lane - i];
+        tot += c4[i];
+      }
+      uint32_t incl = tot;
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      const uint64_t hit = __ballot(incl >= (uint32_t)rank);
+      if (lane == __ffsll((unsigned long long)hit) - 1) {
+        uint32_t before = incl - tot;
+        int digit = 255 - 4 * lane - 3;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (before + c4[i] >= (uint32_t)rank) {
+            digit = 255 - 4 * lane - i;
+            break;
+          }
+          before += c4[i];
+        }
+        sel[0] = digit;
+        sel[1] = rank - (int)before;
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << 8) | (uint32_t)sel[0];
+    rank = sel[1];
+  }
+  const uint32_t kth = prefix;
+  const int take_eq = rank;  // keys equal to kth that are kept (lowest indices first)
+  // ---- write the kept blocks in index order: each thread owns a contiguous range
+  const int C = (nc + 255) / 256;
+  const int jlo = min(tid * C, nc), jhi = min(jlo + C, nc);
+  uint32_t gt = 0, eq = 0;
+  for (int j = jlo; j < jhi; ++j) {
+    const uint32_t u = keys[j];
+    gt += u > kth;
+    eq += u == kth;
+  }
+  // exclusive scan of (gt, eq) packed in 16-bit halves (each total <= 8192)
+  const uint32_t mine = (gt << 16) | eq;
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == kWave - 1) wsum[wv] = incl;
+  __syncthreads();
+  uint32_t excl = incl - mine;
+  for (int i = 0; i < wv; ++i) excl += wsum[i];
+  const int gt_before = (int)(excl >> 16), eq_before = (int)(excl & 0xFFFFu);
+  int o = gt_before + min(eq_before, take_eq);
+  int e = eq_before;
+  for (int j = jlo; j < jhi; ++j) {
+    const uint32_t u = keys[j];
+    if (u > kth) {
+      out[o++] = j;
+    } else if (u == kth) {
+      if (e < take_eq) out[o++] = j;
+      ++e;
+    }
+  }
+  for (int i = m + tid; i < topk; i += 256) out[i] = i == m ? bt : -1;
+}
+
+// ---------------------------------------------------------------- attention (split keys)
+// Grid (splits, B*H), four waves per workgroup.  Split x of a row takes its chunks
+// [x*cps, (x+1)*cps); a wave takes every fourth of them.  Per 64-key chunk a wave loads
+// all keys (and values) at once: a row of D elements is D/E lanes wide, so load i covers
+// keys i*RPW .. i*RPW+RPW-1 of the chunk, 1 KB contiguous.  Each lane forms its part of
+// q . k_i, an xor-shuffle over the row's lanes completes the dot product, and an online
+// softmax in base 2 (running maximum, rescaled sum and o) folds the chunk in.  The four
+// waves' (max, sum, o) are merged through LDS into the split's partial result
+// part[(bh, x)] = {max, sum, o[0..D)} (o not normalised), combined later.
+template <typename T, int D, bool SPARSE, bool WANT_O>
+__global__ __launch_bounds__(256) void decode_attn_kernel(const int32_t* __restrict__ pos, const T* __restrict__ q,
+                                                          const T* __restrict__ kc, const T* __restrict__ vc,
+                                                          const int32_t* __restrict__ idx, float* __restrict__ part,
+                                                          int H, int G, int L, int s, int topk, int cps, float sl2) {
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int LPR = D / E;        // lanes per key row
+  constexpr int RPW = kWave / LPR;  // key rows per wave-wide load
+  constexpr int NI = kChunk / RPW;  // loads per chunk
+  __shared__ float red[4][D + 2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int64_t bh = blockIdx.y;
+  const int p = cache_pos(pos, (int)(bh / H), L);
+  if (p < 0) return;
+  const int nch = row_chunks<SPARSE>(p, s, topk);
+  const int c0 = split * cps, c1 = min(nch, c0 + cps);
+  if (c0 >= nch) return;
+  const int bt = p / s, cpb = s / kChunk;
+  const int m_sel = min(topk - 1, bt);
+  const int32_t* ir = idx + bh * topk;
+  const int64_t kvbh = bh / G;
+  const T* kh = kc + kvbh * (int64_t)L * D;
+  const T* vh = WANT_O ? vc + kvbh * (int64_t)L * D : nullptr;  // v is not read for lse only
+  const int col = (lane % LPR) * E, krow = lane / LPR;
+  float qv[E];
+  Elem<T>::unpack(load16(q + bh * D + col), qv);
+  float mrun = -INFINITY, lrun = 0.f, o[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  for (int ch = c0 + wv; ch < c1; ch += 4) {
+    int key0;
+    if (SPARSE) {
+      const int slot = ch / cpb, sub = ch - slot * cpb;
+      key0 = (slot < m_sel ? ir[slot] : bt) * s + sub * kChunk;
+    } else {
+      key0 = ch * kChunk;
+    }
+    const T* kp = kh + (int64_t)(key0 + krow) * D + col;
+    const T* vp = WANT_O ? vh + (int64_t)(key0 + krow) * D + col : nullptr;
+    u32x4 kr[NI], vr[WANT_O ? NI : 1];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) kr[i] = load16(kp + (int64_t)i * RPW * D);
+    if (WANT_O) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) vr[i] = load16(vp + (int64_t)i * RPW * D);
+    }
+    float sc[NI];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float x[E];
+      Elem<T>::unpack(kr[i], x);
+      float d = qv[0] * x[0];
+#pragma unroll
+      for (int e = 1; e < E; ++e) d = fmaf(qv[e], x[e], d);
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) d += __shfl_xor(d, off);
+      sc[i] = (key0 + i * RPW + krow <= p) ? d * sl2 : -INFINITY;
+      cmax = fmaxf(cmax, sc[i]);
+    }
+#pragma unroll
+    for (int off = LPR; off < kWave; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off));
+    // cmax is finite: the chunk's first key is at or before p
+    const float mnew = fmaxf(mrun, cmax);
+    const float alpha = mrun == -INFINITY ? 0.f : fast_exp2(mrun - mnew);
+    lrun *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const float pr = fast_exp2(sc[i] - mnew);
+      lrun += pr;
+      if (WANT_O) {
+        float y[E];
+        Elem<T>::unpack(vr[WANT_O ? i : 0], y);
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = fmaf(pr, y[e], o[e]);
+      }
+    }
+    mrun = mnew;
+  }
+  // sum over the key rows of the wave (each row group holds one share)
+#pragma unroll
+  for (int off = LPR; off < kWave; off <<= 1) {
+    lrun += __shfl_xor(lrun, off);
+    if (WANT_O) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+  }
+  if (lane == 0) {
+    red[wv][0] = mrun;
+    red[wv][1] = lrun;
+  }
+  if (WANT_O && lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[wv][2 + col + e] = o[e];
+  }
+  __syncthreads();
+  float* pp = part + (bh * nsplit + split) * (int64_t)(D + 2);
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][0]);  // finite: wave 0 has a chunk
+  float wt[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) wt[w] = red[w][0] == -INFINITY ? 0.f : fast_exp2(red[w][0] - M);
+  const int t = threadIdx.x;
+  if (t == 0) {
+    pp[0] = M;
+    pp[1] = wt[0] * red[0][1] + wt[1] * red[1][1] + wt[2] * red[2][1] + wt[3] * red[3][1];
+  }
+  if (WANT_O && t < D)
+    pp[2 + t] = wt[0] * red[0][2 + t] + wt[1] * red[1][2 + t] + wt[2] * red[2][2 + t] + wt[3] * red[3][2 + t];
+}
+
+// ---------------------------------------------------------------- combine
+// One workgroup per (b, h): merges the row's split partials, o = sum_x 2^(m_x - M) o_x /
+// sum_x 2^(m_x - M) l_x, lse = ln 2 * (M + log2 l), with M the largest split maximum (the
+// logits are in base 2).  A sequence whose pos is outside [0, L) gets NaN outputs.
+template <typename T, int D, bool SPARSE, bool WANT_O>
+__global__ __launch_bounds__(256) void decode_combine_kernel(const int32_t* __restrict__ pos,
+                                                             const float* __restrict__ part, T* __restrict__ o,
+                                                             float* __restrict__ lse, int H, int L, int s, int topk,
+                                                             int cps, int nsplit) {
+  __shared__ float red[256];
+  __shared__ float acc[256 / D][D];
+  const int t = threadIdx.x;
+  const int64_t bh = blockIdx.x;
+  const int p = cache_pos(pos, (int)(bh / H), L);
+  if (p < 0) {
+    if (WANT_O && t < D) Elem<T>::store1(o + bh * D + t, NAN);
+    if (t == 0 && lse) lse[bh] = NAN;
+    return;
+  }
+  const int ns = (row_chunks<SPARSE>(p, s, topk) + cps - 1) / cps;  // splits that wrote
+  const float* pr = part + bh * nsplit * (int64_t)(D + 2);
+  float mx = -INFINITY;
+  for (int x = t; x < ns; x += 256) mx = fmaxf(mx, pr[(int64_t)x * (D + 2)]);
+  red[t] = mx;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) red[t] = fmaxf(red[t], red[t + h]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float l = 0.f;
+  for (int x = t; x < ns; x += 256) {
+    const float* px = pr + (int64_t)x * (D + 2);
+    l += fast_exp2(px[0] - M) * px[1];
+  }
+  red[t] = l;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if (t < h) red[t] += red[t + h];
+    __syncthreads();
+  }
+  const float lsum = red[0];
+  if (WANT_O) {
+    constexpr int NG = 256 / D;  // split groups
+    const int c = t % D, g = t / D;
+    float a = 0.f;
+    for (int x = g; x < ns; x += NG) {
+      const float* px = pr + (int64_t)x * (D + 2);
+      a = fmaf(fast_exp2(px[0] - M), px[2 + c], a);
+    }
+    acc[g][c] = a;
+    __syncthreads();
+    if (t < D) {
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) v += acc[i][t];
+      Elem<T>::store1(o + bh * D + t, v / lsum);
+    }
+  }
+  if (t == 0 && lse) lse[bh] = (M + log2f(lsum)) * kLn2;
+}
+
+// ---------------------------------------------------------------- launchers
+namespace {
+
+template <typename T, int D>
+hipError_t run_append(const Dims& d, const int32_t* pos, const void* kn, const void* vn, void* kc, void* vc,
+                      float* km, hipStream_t st) {
+  const int64_t waves = (int64_t)d.B * d.Hkv;
+  hipLaunchKernelGGL((decode_append_kernel<T, D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, pos,
+                     static_cast<const T*>(kn), static_cast<const T*>(vn), static_cast<T*>(kc), static_cast<T*>(vc),
+                     km, d.B, d.Hkv, d.L, d.S, 1.0f / (float)d.S);
+  return hipGetLastError();
+}
+
+// Splits of a row: sparse rows have at most topk * s / 64 chunks, full rows L / 64.
+constexpr int kSparseCps = 4;  // one chunk per wave
+constexpr int kFullCps = 8;    // two chunks per wave
+int max_chunks(const Dims& d, bool sparse, int topk) { return sparse ? topk * (d.S / kChunk) : d.L / kChunk; }
+int splits(const Dims& d, bool sparse, int topk) {
+  const int cps = sparse ? kSparseCps : kFullCps;
+  return (max_chunks(d, sparse, topk) + cps - 1) / cps;
+}
+
+template <typename T, int D, bool SPARSE, bool WANT_O>
+hipError_t run_attn(const Dims& d, const int32_t* pos, const void* q, const void* kc, const void* vc,
+                    const int32_t* idx, int topk, float scale, void* o, float* lse, float* part, hipStream_t st) {
+  const int cps = SPARSE ? kSparseCps : kFullCps;
+  const int ns = splits(d, SPARSE, topk);
+  hipLaunchKernelGGL((decode_attn_kernel<T, D, SPARSE, WANT_O>), dim3((unsigned)ns, (unsigned)d.bh()), dim3(256), 0,
+                     st, pos, static_cast<const T*>(q), static_cast<const T*>(kc), static_cast<const T*>(vc), idx,
+                     part, d.H, d.G(), d.L, d.S, topk, cps, scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<T, D, SPARSE, WANT_O>), dim3((unsigned)d.bh()), dim3(256), 0, st, pos,
+                     part, static_cast<T*>(o), lse, d.H, d.L, d.S, topk, cps, ns);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t run_topk(const Dims& d, const int32_t* pos, const void* q, const float* km, int topk, int32_t* idx,
+                    hipStream_t st) {
+  hipLaunchKernelGGL((decode_topk_kernel<T, D>), dim3((unsigned)d.bh()), dim3(256), 0, st, pos,
+                     static_cast<const T*>(q), km, idx, d.H, d.G(), d.L, d.S, topk);
+  return hipGetLastError();
+}
+
+template <typename F>
+hipError_t dispatch(const Dims& d, F&& f) {
+  if (d.dtype == 1) return d.D == 128 ? f(uint16_t{}, std::integral_constant<int, 128>{})
+                                      : f(uint16_t{}, std::integral_constant<int, 64>{});
+  return d.D == 128 ? f(float{}, std::integral_constant<int, 128>{}) : f(float{}, std::integral_constant<int, 64>{});
+}
+
+}  // namespace
+
+bool decode_sparse_supported(const Dims& d) { return d.n() <= kDecodeMaxBlocks; }
+
+LaunchResult launch_decode_append(const Dims& d, const int32_t* pos, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, float* k_mean, hipStream_t st) {
+  LaunchResult r;
+  r.err = dispatch(d, [&](auto t, auto dd) {
+    return run_append<decltype(t), decltype(dd)::value>(d, pos, k_new, v_new, k_cache, v_cache, k_mean, st);
+  });
+  return r;
+}
+
+LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                  const void* v_cache, const float* k_mean, int topk, float scale, void* o, float* lse,
+                                  int32_t* idx, hipStream_t st) {
+  LaunchResult r;
+  if (!decode_sparse_supported(d)) {
+    r.unsupported = "decoding selects over at most 8192 blocks (L / block)";
+    return r;
+  }
+  const int ns = splits(d, true, topk);
+  const size_t part_bytes = (size_t)d.bh() * ns * (d.D + 2) * sizeof(float);
+  const size_t idx_bytes = idx ? 0 : (size_t)d.bh() * topk * sizeof(int32_t);
+  void* ws = nullptr;
+  r.err = workspace_alloc(part_bytes + idx_bytes, &ws, st);
+  if (r.err != hipSuccess) return r;
+  float* part = static_cast<float*>(ws);
+  int32_t* sel = idx ? idx : reinterpret_cast<int32_t*>(static_cast<char*>(ws) + part_bytes);
+  r.err = dispatch(d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    constexpr int D = decltype(dd)::value;
+    hipError_t e = run_topk<T, D>(d, pos, q, k_mean, topk, sel, st);
+    if (e != hipSuccess) return e;
+    return run_attn<T, D, true, true>(d, pos, q, k_cache, v_cache, sel, topk, scale, o, lse, part, st);
+  });
+  const hipError_t fe = workspace_free(ws, st);
+  if (r.err == hipSuccess) r.err = fe;
+  return r;
+}
+
+LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                const void* v_cache, float scale, void* o, float* lse, hipStream_t st) {
+  LaunchResult r;
+  const int ns = splits(d, false, 1);
+  void* ws = nullptr;
+  r.err = workspace_alloc((size_t)d.bh() * ns * (d.D + 2) * sizeof(float), &ws, st);
+  if (r.err != hipSuccess) return r;
+  float* part = static_cast<float*>(ws);
+  r.err = dispatch(d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    constexpr int D = decltype(dd)::value;
+    return o ? run_attn<T, D, false, true>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st)
+             : run_attn<T, D, false, false>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st);
+  });
+  const hipError_t fe = workspace_free(ws, st);
+  if (r.err == hipSuccess) r.err = fe;
+  return r;
+}
+
+}  // namespace ssa

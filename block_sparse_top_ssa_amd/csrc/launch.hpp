@@ -47,6 +47,21 @@ LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, co
 hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st);
 hipError_t vfrag_release(void* ws, hipStream_t st);
 
+// Transient device memory from the same per-device stream-ordered pool: valid for work
+// enqueued on `st` after the call, given back with workspace_free on the same stream.
+hipError_t workspace_alloc(size_t bytes, void** ws, hipStream_t st);
+hipError_t workspace_free(void* ws, hipStream_t st);
+
+// Decoding with a key/value cache (one query per sequence; d.L = cache capacity).
+bool decode_sparse_supported(const Dims& d);
+LaunchResult launch_decode_append(const Dims& d, const int32_t* pos, const void* k_new, const void* v_new,
+                                  void* k_cache, void* v_cache, float* k_mean, hipStream_t st);
+LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                  const void* v_cache, const float* k_mean, int topk, float scale, void* o, float* lse,
+                                  int32_t* idx, hipStream_t st);
+LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                const void* v_cache, float scale, void* o, float* lse, hipStream_t st);
+
 // MFMA kernels (bf16 only).  *_supported() tells whether the shape fits.
 bool topk_mfma_supported(const Dims& d, int topk);
 LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,

@@ -1,11 +1,10 @@
 // Block mean-pooling of keys: kbar[b,h,j,:] = (1/s) sum_{i=js}^{js+s-1} k[b,h,i,:].
 // Paper sec. 3 (p. 4): contiguous blocks of s tokens, one mean-pooled key per block.
 //
-// HBM-bound: each wave owns one block; lanes read 16-byte pieces of consecutive rows
-// (a row of D elements is D/E lanes wide, E = elements per 16 bytes), so one wave-wide
-// load covers 64/(D/E) whole rows.  Partial sums are kept in float32 per lane and
-// folded across the row groups with xor-shuffles.
+// HBM-bound: each wave owns one block and sums it with block_key_sum (16-byte loads of
+// whole rows, float32 partial sums per lane, xor-shuffle fold).
 #include "launch.hpp"
+#include "pool.hpp"
 
 namespace ssa {
 
@@ -13,38 +12,15 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ k, float* __restrict__ km,
                                                    int64_t nblocks, int s, float inv_s) {
   constexpr int E = Elem<T>::kPer16B;
-  constexpr int LPR = D / E;      // lanes per row
-  constexpr int RPI = kWave / LPR; // rows per wave-wide load
+  constexpr int LPR = D / E;  // lanes per row
   const int lane = threadIdx.x & 63;
   const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (blk >= nblocks) return;
   // Blocks are contiguous in [B,H,L,D] because L = n*s: block blk starts at row blk*s.
-  const T* base = k + blk * (int64_t)s * D;
-  const int r0 = lane / LPR, c = lane % LPR;
   float acc[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int r = r0; r < s; r += RPI * 4) {
-    u32x4 w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int rr = r + u * RPI;
-      w[u] = rr < s ? load16(base + (int64_t)rr * D + c * E) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float x[E];
-      Elem<T>::unpack(w[u], x);
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += x[e];
-    }
-  }
-#pragma unroll
-  for (int o = LPR; o < kWave; o <<= 1)
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], o);
+  block_key_sum<T, D>(k + blk * (int64_t)s * D, s, s, -1, k, acc);
   if (lane < LPR) {
-    float* dst = km + blk * D + c * E;
+    float* dst = km + blk * D + lane * E;
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       u32x4 w;

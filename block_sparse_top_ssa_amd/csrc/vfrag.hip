@@ -80,4 +80,14 @@ hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st
 
 hipError_t vfrag_release(void* ws, hipStream_t st) { return ws ? hipFreeAsync(ws, st) : hipSuccess; }
 
+hipError_t workspace_alloc(size_t bytes, void** ws, hipStream_t st) {
+  *ws = nullptr;
+  hipMemPool_t pool = nullptr;
+  hipError_t e = workspace_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(ws, bytes, pool, st);
+}
+
+hipError_t workspace_free(void* ws, hipStream_t st) { return ws ? hipFreeAsync(ws, st) : hipSuccess; }
+
 }  // namespace ssa

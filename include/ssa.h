@@ -17,12 +17,13 @@
  *               Blocks: block size s = ssa_dims.block, n = L / s blocks per sequence; the
  *               query at position t lies in block b_t = t / s.
  *  Pointers     every data pointer is a DEVICE pointer (hipMalloc'd, or torch CUDA
- *               memory); q, k, v, o and k_mean 16-byte aligned, idx, lse, sel_score,
- *               l2_dist and dropped 4-byte aligned.  The caller owns every buffer it
- *               passes.  The library keeps no pointer to them after a call returns and
- *               writes nothing outside the outputs named by a call.  Two calls allocate:
- *               ssa_sparse_attn_fwd on bf16, and ssa_full_attn_fwd on bf16 with o given,
- *               take a transient workspace (see ssa_sparse_attn_fwd).
+ *               memory); q, k, v, o, k_mean and the caches 16-byte aligned, idx, pos,
+ *               lse, sel_score, l2_dist and dropped 4-byte aligned.  The caller owns every
+ *               buffer it passes.  The library keeps no pointer to them after a call
+ *               returns and writes nothing outside the outputs named by a call.  Four
+ *               calls allocate: ssa_sparse_attn_fwd on bf16, ssa_full_attn_fwd on bf16
+ *               with o given, ssa_decode_sparse_fwd and ssa_decode_full_fwd take a
+ *               transient workspace (see ssa_sparse_attn_fwd).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 2 /* 2: ssa_dims.Hkv (grouped-query attention) */
+#define SSA_ABI_VERSION 3 /* 2: ssa_dims.Hkv (grouped-query attention); 3: decoding calls */
 
 typedef int32_t ssa_status;
 enum {
@@ -153,11 +154,81 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
  *   l2_dist   [B,H,L] float32 or NULL   out: ||o_full(t) - o_sparse(t)||_2 over D (needs the o pair)
  *   dropped   [B,H,L] float32 or NULL   out: clamp(-expm1(lse_sparse - lse_full), 0, 1)
  *                                       (needs the lse pair)
- *   At least one output must be given.
+ *   At least one output must be given.  The block partition is not used: block is not
+ *   checked and L need not be a multiple of it (L = 1 compares one decoding step's
+ *   outputs, [B,H,D] and [B,H]).
  */
 ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void* o_sparse,
                            const float* lse_full, const float* lse_sparse, float* l2_dist,
                            float* dropped, void* stream);
+
+/*
+ * Decoding with a key/value cache -- one new query per sequence per step.
+ *   The paper's sparse kernel has no key/value cache, which makes its decoding slow
+ *   (App. E, p. 22).  These calls are the cached form of the same forward (sec. 3,
+ *   pp. 3-4) for the query at position t = pos[b] of each sequence b: the same
+ *   selection over the complete blocks before t's own, the same sparse attention, and
+ *   dense attention over 0..t.  Their results equal row t of ssa_block_topk,
+ *   ssa_sparse_attn_fwd and ssa_full_attn_fwd run over the whole sequence, up to
+ *   float32 rounding (and, for the selection, score ties within rounding).
+ *
+ *   dims     B sequences, H query heads, Hkv key/value heads, L = cache CAPACITY in
+ *            tokens (a multiple of block), D, block, dtype.  n = L / block.
+ *   pos      [B] int32 DEVICE array: the position t of the new token of each sequence,
+ *            read by the kernels (the host never sees it).  Sequences may be at different
+ *            positions.  An entry outside [0, L) is not an error the call can report:
+ *            that sequence is skipped by ssa_decode_append, gets NaN in o and lse and -1
+ *            in idx from the forward calls, and nothing outside the buffers is touched.
+ *   k_cache, v_cache  [B,Hkv,L,D] (dtype): token i of sequence b at row i.  Rows after
+ *            pos[b] are never read by the forward calls.
+ *   k_mean   [B,Hkv,n,D] float32: pooled keys of the cached blocks.  Block j < pos/block
+ *            must hold the mean of its block keys (ssa_block_pool over a prompt writes it;
+ *            ssa_decode_append maintains it); the entry of the open block is the mean of
+ *            the tokens it holds, written by each ssa_decode_append.
+ */
+
+/*
+ * ssa_decode_append -- store one new token per sequence and update its block's mean.
+ *   k_new, v_new  [B,Hkv,D] (dtype)          in: key and value of the token at pos[b]
+ *   k_cache, v_cache [B,Hkv,L,D] (dtype)     in/out: row pos[b] is written
+ *   k_mean   [B,Hkv,n,D] float32             in/out: entry pos[b]/block is rewritten as the
+ *            mean of rows block*(pos/block) .. pos (summed in float32 in the same order as
+ *            ssa_block_pool, so a block completed by appends holds the same bits)
+ *   Two sequences never share cache rows; calls on one stream run in order.
+ */
+ssa_status ssa_decode_append(const ssa_dims* dims, const int32_t* pos, const void* k_new, const void* v_new,
+                             void* k_cache, void* v_cache, float* k_mean, void* stream);
+
+/*
+ * ssa_decode_sparse_fwd -- selection and sparse attention for one query per sequence.
+ *   q        [B,H,D] (dtype)                 in: the query at pos[b]
+ *   k_cache, v_cache, k_mean                 in (as above; query head h uses key/value head h / G)
+ *   topk     1 <= topk <= n                  blocks kept (own block included)
+ *   scale    softmax scale (> 0, finite)
+ *   o        [B,H,D] (dtype)                 out: sparse-stream output o_s(t)
+ *   lse      [B,H] float32 or NULL           out (optional): log-sum-exp of the sparse stream
+ *   idx      [B,H,topk] int32 or NULL        out (optional): the kept blocks, as ssa_block_topk
+ *            lists them for row t
+ *   Needs n <= 8192 (else SSA_ERR_UNSUPPORTED).
+ *   Workspace: B*H*(ceil(topk*block/256))*(D+2)*4 bytes of split results, plus B*H*topk*4
+ *   bytes for the selection when idx is NULL, from the stream-ordered pool described
+ *   under ssa_sparse_attn_fwd, with the same error behaviour.
+ */
+ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
+                                 const void* v_cache, const float* k_mean, int32_t topk, float scale, void* o,
+                                 float* lse, int32_t* idx, void* stream);
+
+/*
+ * ssa_decode_full_fwd -- dense attention over 0..pos[b] for one query per sequence.
+ *   q        [B,H,D] (dtype)                 in
+ *   k_cache, v_cache                         in (v_cache may be NULL when o is NULL)
+ *   o        [B,H,D] (dtype) or NULL         out: full-stream output o_f(t)
+ *   lse      [B,H] float32 or NULL           out: log-sum-exp of the full stream
+ *   At least one of o, lse must be given; with o == NULL the values are not read.
+ *   Workspace: B*H*ceil(L/512)*(D+2)*4 bytes of split results, from the same pool.
+ */
+ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
+                               const void* v_cache, float scale, void* o, float* lse, void* stream);
 
 /* Text for a status code (static storage). */
 const char* ssa_status_str(ssa_status status);

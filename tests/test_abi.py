@@ -87,6 +87,41 @@ def test_null_and_alignment(libssa):
     assert libssa.ssa_align_stats(ctypes.byref(d), None, None, FAKE, None, None, FAKE, None) == 1
 
 
+def test_decode_argument_checks(libssa):
+    d = _dims()
+    # append: every pointer required, 16-byte aligned tensors, 4-byte aligned pos
+    assert libssa.ssa_decode_append(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert libssa.ssa_decode_append(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert libssa.ssa_decode_append(ctypes.byref(d), FAKE, MISALIGNED, FAKE, FAKE, FAKE, FAKE, None) == 4
+    # sparse: o required; lse, idx optional; topk in [1, n]
+    assert libssa.ssa_decode_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.1,
+                                        None, None, None, None) == 1
+    assert libssa.ssa_decode_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1,
+                                        FAKE, None, None, None) == 2
+    assert libssa.ssa_decode_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 5, 0.1,
+                                        FAKE, None, None, None) == 2
+    assert libssa.ssa_decode_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2, -1.0,
+                                        FAKE, None, None, None) == 4
+    assert libssa.ssa_decode_sparse_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.1,
+                                        FAKE, None, ctypes.c_void_p((1 << 20) + 1), None) == 4
+    # full: o or lse; v_cache only needed with o
+    assert libssa.ssa_decode_full_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 0.1, None, None, None) == 1
+    assert libssa.ssa_decode_full_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, None, 0.1, FAKE, None, None) == 1
+    assert libssa.ssa_decode_full_fwd(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, None,
+                                      None) == 4
+    # the cache capacity follows the block rules
+    bad = _dims(L=200)
+    assert libssa.ssa_decode_append(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path; a GPU is present")
+def test_align_ignores_block(libssa):
+    """ssa_align_stats does not use the block partition, so L = 1 (one decoding step) and
+    an unused block value pass its shape checks and fail only at the device check."""
+    d = _dims(L=1, block=0)
+    assert libssa.ssa_align_stats(ctypes.byref(d), FAKE, FAKE, None, None, FAKE, None, None) == 5
+
+
 @pytest.mark.parametrize("topk", [0, -1, 5])
 def test_topk_range(libssa, topk):
     d = _dims(L=256, block=64)   # n = 4

@@ -220,3 +220,76 @@ def sample_rows(L: int, s: int, k: int, count: int, seed: int) -> np.ndarray:
     must = {r for r in must if 0 <= r < L}
     rest = rng.choice(L, size=max(0, count - len(must)), replace=False)
     return np.array(sorted(must | set(int(r) for r in rest)), dtype=np.int64)
+
+
+# ----------------------------------------------------------------------------------
+# decoding with a key/value cache
+# ----------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One decoding step for B sequences at different positions of a cache of capacity L:
+    the cache holds k, v for every row (rows after a sequence's position are never read
+    by decoding), the queries are [B, H, D], positions are drawn in [L/2, L)."""
+    name: str
+    B: int
+    H: int
+    L: int
+    D: int
+    s: int
+    k: int
+    dtype: str
+    structure: str
+    seed: int
+    Hkv: int = 0
+
+    @property
+    def n(self) -> int:
+        return self.L // self.s
+
+    @property
+    def hkv(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def group(self) -> int:
+        return self.H // self.hkv
+
+
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        # bf16_L32768_sink's head shape, four sequences decoding at once.
+        DecodeWorkload("bf16_L32768_decode", 4, 32, 32768, 128, 64, 32, BF16, "sink", 1007),
+    ]
+}
+
+
+@dataclass
+class DecodeInputs:
+    workload: DecodeWorkload
+    k: np.ndarray      # [B, Hkv, L, D] cache
+    v: np.ndarray      # [B, Hkv, L, D] cache
+    q: np.ndarray      # [B, H, D] queries at pos
+    pos: np.ndarray    # [B] int32
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        return (bf16_bits_to_f32(a) if self.workload.dtype == BF16 else a).astype(np.float64)
+
+
+def make_decode(name: str) -> DecodeInputs:
+    """Draw k, v (the cache), then q, then the positions, from one generator; the sink
+    structure scales token 0's key by 8 as in the prefill workloads."""
+    w = DECODE_WORKLOADS[name]
+    rng = np.random.default_rng(w.seed)
+    Hk = w.hkv
+    k = _draw(rng, (w.B, Hk, w.L, w.D))
+    v = _draw(rng, (w.B, Hk, w.L, w.D))
+    q = _draw(rng, (w.B, w.H, w.D))
+    pos = rng.integers(w.L // 2, w.L, size=w.B).astype(np.int32)
+    if w.structure == "sink":
+        k[:, :, 0, :] *= np.float32(8.0)
+    elif w.structure != "none":
+        raise ValueError(f"unknown structure {w.structure!r}")
+    if w.dtype == BF16:
+        k, v, q = f32_to_bf16_bits(k), f32_to_bf16_bits(v), f32_to_bf16_bits(q)
+    return DecodeInputs(w, k, v, q, pos)
