@@ -23,6 +23,7 @@ namespace {
 
 constexpr int kDecodeMaxBlocks = 8192;  // candidates held in LDS by the selection kernel
 constexpr int kChunk = 64;              // keys per wave step of the attention kernel
+constexpr int kTopkThreads = 1024;      // selection workgroup: 16 waves share the scoring loads
 
 // Position of the new token of sequence b, or -1 when it lies outside the cache.
 __device__ __forceinline__ int cache_pos(const int32_t* pos, int b, int L) {
@@ -89,9 +90,10 @@ __global__ __launch_bounds__(256) void decode_append_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------- selection
-// One workgroup per (b, query head).  Scores sigma_j = q . kbar_j of the complete blocks
-// j < b_t in float32 (a kbar row is D/4 lanes wide, several rows per wave-wide load,
-// xor-shuffle sums), held in LDS as order-preserving 32-bit keys.  The m = min(topk-1,
+// One workgroup of 16 waves per (b, query head).  Scores sigma_j = q . kbar_j of the
+// complete blocks j < b_t in float32 (a kbar row is D/4 lanes wide, several rows per
+// wave-wide load, eight loads in flight per lane, xor-shuffle sums), held in LDS as
+// order-preserving 32-bit keys.  The m = min(topk-1,
 // b_t) best by (score descending, j ascending) are found by a radix select, 8 bits per
 // pass from the top: a 256-bin histogram of the keys that match the digits chosen so far,
 // then the digit where the running count from the top reaches the wanted rank.  After
@@ -99,25 +101,26 @@ __global__ __launch_bounds__(256) void decode_append_kernel(const int32_t* __res
 // those are the r lowest indices among the keys equal to T.  A block-wide scan in index
 // order then writes the kept blocks in ascending order, b_t after them, -1 after that.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restrict__ pos, const T* __restrict__ q,
+__global__ __launch_bounds__(kTopkThreads) void decode_topk_kernel(const int32_t* __restrict__ pos, const T* __restrict__ q,
                                                           const float* __restrict__ km, int32_t* __restrict__ idx,
                                                           int H, int G, int L, int s, int topk) {
   __shared__ uint32_t keys[kDecodeMaxBlocks];
   __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[4];
+  constexpr int NT = kTopkThreads, NW = NT / kWave;
+  __shared__ uint32_t wsum[NW];
   __shared__ int sel[2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t bh = blockIdx.x;
   const int p = cache_pos(pos, (int)(bh / H), L);
   int32_t* out = idx + bh * topk;
   if (p < 0) {
-    for (int i = tid; i < topk; i += 256) out[i] = -1;
+    for (int i = tid; i < topk; i += NT) out[i] = -1;
     return;
   }
   const int bt = p / s;
   const int m = min(topk - 1, bt);
   if (m == bt || m == 0) {  // every candidate is kept, or none (topk = 1)
-    for (int i = tid; i < topk; i += 256) out[i] = i < m ? i : (i == m ? bt : -1);
+    for (int i = tid; i < topk; i += NT) out[i] = i < m ? i : (i == m ? bt : -1);
     return;
   }
   // ---- scores (bt >= 1 here)
@@ -130,15 +133,16 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restr
     for (int e = 0; e < 4; ++e) qv[e] = Elem<T>::load1(qp + e);
   }
   const int nc = bt;
-  for (int j0 = wv * RK * 4; j0 < nc; j0 += 4 * RK * 4) {
-    f32x4 x[4];
+  constexpr int U = 8;  // loads in flight per lane
+  for (int j0 = wv * RK * U; j0 < nc; j0 += NW * RK * U) {
+    f32x4 x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int j = j0 + u * RK + lane / LK;
       x[u] = j < nc ? *reinterpret_cast<const f32x4*>(kmh + (int64_t)j * D + (lane % LK) * 4) : f32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       float d = qv[0] * x[u][0];
       d = fmaf(qv[1], x[u][1], d);
       d = fmaf(qv[2], x[u][2], d);
@@ -155,9 +159,9 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restr
   int rank = m;  // 1-based rank wanted among the keys that match `prefix`
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int j = tid; j < nc; j += 256) {
+    for (int j = tid; j < nc; j += NT) {
       const uint32_t u = keys[j];
       if (pass == 0 || (u >> (shift + 8)) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
     }
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restr
   const uint32_t kth = prefix;
   const int take_eq = rank;  // keys equal to kth that are kept (lowest indices first)
   // ---- write the kept blocks in index order: each thread owns a contiguous range
-  const int C = (nc + 255) / 256;
+  const int C = (nc + NT - 1) / NT;
   const int jlo = min(tid * C, nc), jhi = min(jlo + C, nc);
   uint32_t gt = 0, eq = 0;
   for (int j = jlo; j < jhi; ++j) {
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void decode_topk_kernel(const int32_t* __restr
       ++e;
     }
   }
-  for (int i = m + tid; i < topk; i += 256) out[i] = i == m ? bt : -1;
+  for (int i = m + tid; i < topk; i += NT) out[i] = i == m ? bt : -1;
 }
 
 // ---------------------------------------------------------------- attention (split keys)
@@ -437,7 +441,7 @@ hipError_t run_append(const Dims& d, const int32_t* pos, const void* kn, const v
 
 // Splits of a row: sparse rows have at most topk * s / 64 chunks, full rows L / 64.
 constexpr int kSparseCps = 4;  // one chunk per wave
-constexpr int kFullCps = 8;    // two chunks per wave
+constexpr int kFullCps = 16;   // four chunks per wave (fewer split results to merge)
 int max_chunks(const Dims& d, bool sparse, int topk) { return sparse ? topk * (d.S / kChunk) : d.L / kChunk; }
 int splits(const Dims& d, bool sparse, int topk) {
   const int cps = sparse ? kSparseCps : kFullCps;
@@ -462,7 +466,7 @@ hipError_t run_attn(const Dims& d, const int32_t* pos, const void* q, const void
 template <typename T, int D>
 hipError_t run_topk(const Dims& d, const int32_t* pos, const void* q, const float* km, int topk, int32_t* idx,
                     hipStream_t st) {
-  hipLaunchKernelGGL((decode_topk_kernel<T, D>), dim3((unsigned)d.bh()), dim3(256), 0, st, pos,
+  hipLaunchKernelGGL((decode_topk_kernel<T, D>), dim3((unsigned)d.bh()), dim3(kTopkThreads), 0, st, pos,
                      static_cast<const T*>(q), km, idx, d.H, d.G(), d.L, d.S, topk);
   return hipGetLastError();
 }

@@ -225,7 +225,7 @@ ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const
  *   o        [B,H,D] (dtype) or NULL         out: full-stream output o_f(t)
  *   lse      [B,H] float32 or NULL           out: log-sum-exp of the full stream
  *   At least one of o, lse must be given; with o == NULL the values are not read.
- *   Workspace: B*H*ceil(L/512)*(D+2)*4 bytes of split results, from the same pool.
+ *   Workspace: B*H*ceil(L/1024)*(D+2)*4 bytes of split results, from the same pool.
  */
 ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
                                const void* v_cache, float scale, void* o, float* lse, void* stream);
