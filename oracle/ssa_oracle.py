@@ -33,6 +33,15 @@ Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
   decode_step           one decoding step with a key/value cache: the query at position
                         t against the cached keys and values 0..t, both streams, formed
                         from the cache alone (sec. 3, p. 3-4; App. E, p. 22).
+  attend_full_bwd       gradients of the full stream's output with respect to q, k, v
+  attend_sparse_bwd     and of the sparse stream's (no gradient through the selection):
+                        SSA trains both streams (sec. 5, pp. 6-7; App. C, p. 20); the
+                        formulas are the chain rule through softmax attention.
+  align_loss            the bidirectional alignment objective of sec. 5 (pp. 6-7): a
+                        sparsity term pulling the full output toward the (held) sparse
+                        one and a commitment term pulling the sparse output toward the
+                        (held) full one, both SmoothL1, weighted by alpha; its value and
+                        the gradient it sends to each stream's output.
 
 Readings where the pages are silent (listed in full in the design notes):
   * candidates are the blocks strictly before the query's block; the own block is
@@ -55,7 +64,8 @@ import numpy as np
 __all__ = [
     "block_pool", "block_scores", "block_topk", "attend_full", "attend_sparse",
     "attend_sparse_gather", "dropped_mass", "align_stats", "attended_blocks",
-    "attended_count", "open_block_mean", "decode_step",
+    "attended_count", "open_block_mean", "decode_step", "attend_full_bwd",
+    "attend_sparse_bwd", "smooth_l1", "align_loss",
 ]
 
 
@@ -341,3 +351,70 @@ def decode_step(q_t: np.ndarray, k_bh: np.ndarray, v_bh: np.ndarray, t: int, s: 
     o_f, lse_f = attend(np.arange(t + 1))
     return {"idx": idx, "o_s": o_s, "lse_s": lse_s, "o_f": o_f, "lse_f": lse_f,
             "sigma_m": sigma_m, "sigma_m1": sigma_m1}
+
+
+# ----------------------------------------------------------------------------------
+# sec. 5 / App. C: training both streams -- backward of the attention forward and the
+# bidirectional alignment loss
+# ----------------------------------------------------------------------------------
+def _attend_bwd_masked(q, k, v, do, scale, mask):
+    """Gradients of o = softmax(scale q k^T, masked) v for one (b, h): with P the
+    attention weights, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)),
+    dQ = scale dS K, dK = scale dS^T Q.  (rowsum(dP * P) equals rowsum(dO * O).)"""
+    lg = np.where(mask, scale * (q @ k.T), -np.inf)
+    m = lg.max(axis=1, keepdims=True)
+    e = np.exp(lg - m)
+    p = e / e.sum(axis=1, keepdims=True)
+    dv = p.T @ do
+    dp = do @ v.T
+    ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds.T @ q), dv
+
+
+def attend_full_bwd(q, k, v, do, scale: float):
+    """dq, dk, dv of the full causal stream for an upstream gradient do = dL/do_f
+    ([B,H,L,D] each, float64)."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    B, H, L, D = q.shape
+    mask = np.arange(L)[None, :] <= np.arange(L)[:, None]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = _attend_bwd_masked(q[b, h], k[b, h], v[b, h], do[b, h], scale, mask)
+    return dq, dk, dv
+
+
+def attend_sparse_bwd(q, k, v, do, idx, s: int, scale: float):
+    """dq, dk, dv of the sparse stream with its kept blocks held fixed (the selection
+    has no gradient): attention restricted to A(t) = {i <= t : block of i kept}."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    B, H, L, D = q.shape
+    R = np.arange(L)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            mask = _sparse_key_mask(idx[b, h], R, s, L)
+            dq[b, h], dk[b, h], dv[b, h] = _attend_bwd_masked(q[b, h], k[b, h], v[b, h], do[b, h], scale, mask)
+    return dq, dk, dv
+
+
+def smooth_l1(x, beta: float = 1.0):
+    """Elementwise SmoothL1 (Huber with threshold beta): 0.5 x^2 / beta where |x| < beta,
+    |x| - 0.5 beta elsewhere."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    return np.where(ax < beta, 0.5 * x * x / beta, ax - 0.5 * beta)
+
+
+def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0):
+    """alpha * [mean SmoothL1(o_f - sg(o_s)) + mean SmoothL1(o_s - sg(o_f))] over every
+    element.  Returns (loss, dL/do_f, dL/do_s): each term sends gradient only to its own
+    first argument (the other is held), the derivative of SmoothL1 being x / beta
+    clipped to [-1, 1], divided by the element count."""
+    of = np.asarray(o_full, dtype=np.float64)
+    os_ = np.asarray(o_sparse, dtype=np.float64)
+    N = of.size
+    loss = alpha * (smooth_l1(of - os_, beta).mean() + smooth_l1(os_ - of, beta).mean())
+    g_f = alpha * np.clip((of - os_) / beta, -1.0, 1.0) / N
+    g_s = alpha * np.clip((os_ - of) / beta, -1.0, 1.0) / N
+    return loss, g_f, g_s

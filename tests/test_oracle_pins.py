@@ -560,3 +560,132 @@ def test_decode_planted_mistakes_are_caught(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, f"planted slip {fake.__name__} went unnoticed"
+
+
+# ----------------------------------------------------------------------------------
+# training: attention backward and the alignment loss, pinned by finite differences
+# ----------------------------------------------------------------------------------
+def _fd_grad(f, x, h=1e-5):
+    """Central finite differences of the scalar f at x (float64), element by element."""
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        i = it.multi_index
+        old = x[i]
+        x[i] = old + h
+        fp = f()
+        x[i] = old - h
+        fm = f()
+        x[i] = old
+        g[i] = (fp - fm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("stream", ["full", "sparse"])
+def test_attention_bwd_matches_finite_differences(stream):
+    """dq, dk, dv against central differences of F = sum(do * o) through the forward
+    oracle (the sparse stream with its selection held fixed)."""
+    B, H, L, D, s, topk, scale = 1, 2, 24, 4, 4, 3, 0.7
+    q, k, v, do = (_rand((B, H, L, D), 80 + i) for i in range(4))
+    idx = O.block_topk(q, O.block_pool(k, s), s, topk)
+
+    def F():
+        if stream == "full":
+            o, _ = O.attend_full(q, k, v, scale)
+        else:
+            o, _ = O.attend_sparse(q, k, v, idx, s, scale)
+        return float((o * do).sum())
+
+    if stream == "full":
+        dq, dk, dv = O.attend_full_bwd(q, k, v, do, scale)
+    else:
+        dq, dk, dv = O.attend_sparse_bwd(q, k, v, do, idx, s, scale)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        np.testing.assert_allclose(g, _fd_grad(F, x), rtol=1e-6, atol=1e-8, err_msg=f"d{name}")
+
+
+def test_attention_bwd_q_zero_closed_form():
+    """q = 0: each row's weights are uniform over its attended keys, so
+    dv_i = sum over rows t attending i of do_t / |A(t)|, and dk = 0 (every logit
+    is 0 whatever k is, and stays so to first order in k)."""
+    B, H, L, D, s, topk, scale = 1, 1, 40, 3, 4, 3, 0.9
+    _, k, v, do = (_rand((B, H, L, D), 90 + i) for i in range(4))
+    q = np.zeros((B, H, L, D))
+    idx = O.block_topk(q, O.block_pool(k, s), s, topk)
+    for stream in ("full", "sparse"):
+        if stream == "full":
+            _, dk, dv = O.attend_full_bwd(q, k, v, do, scale)
+            sets = [list(range(t + 1)) for t in range(L)]
+        else:
+            _, dk, dv = O.attend_sparse_bwd(q, k, v, do, idx, s, scale)
+            sets = [[i for j in O.attended_blocks(idx[0, 0, t], t, s) for i in range(j * s, min(j * s + s, t + 1))]
+                    for t in range(L)]
+        ref = np.zeros((L, D))
+        for t in range(L):
+            for i in sets[t]:
+                ref[i] += do[0, 0, t] / len(sets[t])
+        np.testing.assert_allclose(dv[0, 0], ref, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dk, 0.0, atol=1e-13)
+
+
+def test_align_loss_closed_forms_and_gradient():
+    """SmoothL1: 0.5 x^2 / beta inside the threshold, |x| - beta/2 outside; the loss is
+    alpha times the two equal means; each gradient matches central differences of its
+    own term with the other output held; identical outputs give zero loss and zero
+    gradients."""
+    beta, alpha = 0.5, 0.3
+    x = np.array([-2.0, -0.5, -0.2, 0.0, 0.1, 0.49, 0.5, 3.0])
+    np.testing.assert_allclose(O.smooth_l1(x, beta), [1.75, 0.25, 0.04, 0.0, 0.01, 0.2401, 0.25, 2.75], rtol=1e-14)
+    of, os_ = _rand((1, 2, 5, 3), 95), _rand((1, 2, 5, 3), 96) * 0.4
+    loss, gf, gs = O.align_loss(of, os_, alpha, beta)
+    N = of.size
+    manual = 0.0
+    for a, b in zip(of.ravel(), os_.ravel()):
+        d = abs(a - b)
+        manual += 0.5 * d * d / beta if d < beta else d - 0.5 * beta
+    assert math.isclose(loss, 2 * alpha * manual / N, rel_tol=1e-13)
+    held = os_.copy()
+    gf_fd = _fd_grad(lambda: alpha * float(O.smooth_l1(of - held, beta).mean()), of, h=1e-7)
+    np.testing.assert_allclose(gf, gf_fd, rtol=1e-5, atol=1e-9)
+    held_f = of.copy()
+    gs_fd = _fd_grad(lambda: alpha * float(O.smooth_l1(os_ - held_f, beta).mean()), os_, h=1e-7)
+    np.testing.assert_allclose(gs, gs_fd, rtol=1e-5, atol=1e-9)
+    l0, g0f, g0s = O.align_loss(of, of, alpha, beta)
+    assert l0 == 0.0 and not g0f.any() and not g0s.any()
+
+
+def test_bwd_planted_mistakes_are_caught(monkeypatch):
+    """Slips planted in the backward (the softmax term dropped, the scale left out of
+    dq, dS used untransposed for dk) fail the finite-difference pin."""
+    orig = O._attend_bwd_masked
+
+    def no_delta(q, k, v, do, scale, mask):
+        lg = np.where(mask, scale * (q @ k.T), -np.inf)
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ds = p * (do @ v.T)
+        return scale * (ds @ k), scale * (ds.T @ q), p.T @ do
+
+    def no_scale_dq(q, k, v, do, scale, mask):
+        dq, dk, dv = orig(q, k, v, do, scale, mask)
+        return dq / scale, dk, dv
+
+    def dk_untransposed(q, k, v, do, scale, mask):
+        dq, dk, dv = orig(q, k, v, do, scale, mask)
+        lg = np.where(mask, scale * (q @ k.T), -np.inf)
+        p = np.exp(lg - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        dp = do @ v.T
+        ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+        return dq, scale * (ds @ q), dv
+
+    for fake in (no_delta, no_scale_dq, dk_untransposed):
+        with monkeypatch.context() as mp:
+            mp.setattr(O, "_attend_bwd_masked", fake)
+            failed = 0
+            for stream in ("full", "sparse"):
+                try:
+                    test_attention_bwd_matches_finite_differences(stream)
+                except AssertionError:
+                    failed += 1
+            assert failed > 0, f"planted slip {fake.__name__} went unnoticed"
