@@ -17,6 +17,12 @@ int32 tensor `pos`, caches [B, Hkv, L, D] with L the capacity):
     o_s, lse_s, idx = decode_sparse_fwd(pos, q, k_cache, v_cache, k_mean, block, topk)
     o_f, lse_f = decode_full_fwd(pos, q, k_cache, v_cache)
 
+Training (gradients added into float32 buffers, the selection held fixed):
+
+    loss, g_f, g_s = align_loss(o_f, o_s, alpha)
+    full_attn_bwd(q, k, v, o_f, lse_f, do_f, dq, dk, dv)
+    sparse_attn_bwd(q, k, v, o_s, lse_s, do_s, idx, block, dq, dk, dv)
+
 q is [B, H, L, D]; k and v may have fewer heads, [B, Hkv, L, D] with Hkv dividing H
 (grouped-query attention: query head h uses key/value head h // (H // Hkv)), and
 k_mean then has Hkv heads too.
@@ -34,6 +40,7 @@ from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
            "decode_append", "decode_sparse_fwd", "decode_full_fwd",
+           "full_attn_bwd", "sparse_attn_bwd", "align_loss",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
 
 
@@ -214,3 +221,58 @@ def decode_full_fwd(pos, q, k_cache, v_cache, scale: float | None = None, want_o
     check(load().ssa_decode_full_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(q), _ptr(k_cache),
                                      _ptr(v_cache), ctypes.c_float(scale), _ptr(o), _ptr(lse), _stream(q)))
     return o, lse
+
+
+# ---------------------------------------------------------------- training
+def _grad_bufs(q, k, dq, dk, dv):
+    if dq is None:
+        dq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    for t, ref, what in ((dq, q, "dq"), (dk, k, "dk"), (dv, k, "dv")):
+        if t.dtype != torch.float32 or t.shape != ref.shape:
+            raise SSAError(2, f"{what} must be float32 of shape {tuple(ref.shape)}")
+    return dq, dk, dv
+
+
+def full_attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale: float | None = None, block: int = 64):
+    """Adds the full stream's gradients into dq, dk, dv (float32; zero-filled when not
+    given) and returns them.  o, lse: the forward's outputs; dout: dL/do (q's dtype)."""
+    d = _dims(q, block, _kv_heads(q, k, v))
+    _same(o, q, "o/q")
+    _same(dout, q, "dout/q")
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    dq, dk, dv = _grad_bufs(q, k, dq, dk, dv)
+    check(load().ssa_full_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                   ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _stream(q)))
+    return dq, dk, dv
+
+
+def sparse_attn_bwd(q, k, v, o, lse, dout, idx, block: int, dq=None, dk=None, dv=None, scale: float | None = None):
+    """Adds the sparse stream's gradients (kept blocks idx held fixed) into dq, dk, dv."""
+    d = _dims(q, block, _kv_heads(q, k, v))
+    _same(o, q, "o/q")
+    _same(dout, q, "dout/q")
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
+        raise SSAError(2, "idx must be int32 [B, H, L, topk]")
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    dq, dk, dv = _grad_bufs(q, k, dq, dk, dv)
+    check(load().ssa_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                     _ptr(idx), int(idx.shape[3]), ctypes.c_float(scale), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), _stream(q)))
+    return dq, dk, dv
+
+
+def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0, want_grads: bool = True):
+    """Returns (loss [1] float32, dloss/do_full, dloss/do_sparse) of the bidirectional
+    SmoothL1 alignment objective; the gradients are float32 tensors shaped like o."""
+    _same(o_full, o_sparse, "o_full/o_sparse")
+    d = _dims(o_full, 64)
+    loss = torch.empty((1,), dtype=torch.float32, device=o_full.device)
+    gf = torch.empty(o_full.shape, dtype=torch.float32, device=o_full.device) if want_grads else None
+    gs = torch.empty(o_full.shape, dtype=torch.float32, device=o_full.device) if want_grads else None
+    check(load().ssa_align_loss(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), ctypes.c_float(alpha),
+                                ctypes.c_float(beta), _ptr(loss), _ptr(gf), _ptr(gs), _stream(o_full)))
+    return loss, gf, gs

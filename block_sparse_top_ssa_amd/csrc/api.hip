@@ -240,6 +240,60 @@ ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const v
                 "ssa_decode_full_fwd");
 }
 
+static ssa_status attn_bwd(const char* what, bool sparse, const ssa_dims* dims, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* dout, const int32_t* idx,
+                           int32_t topk, float scale, float* dq, float* dk, float* dv, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(v, "v", 16));
+  SSA_TRY(check_ptr(o, "o", 16));
+  SSA_TRY(check_ptr(lse, "lse", 4));
+  SSA_TRY(check_ptr(dout, "dout", 16));
+  SSA_TRY(check_ptr(dq, "dq", 16));
+  SSA_TRY(check_ptr(dk, "dk", 16));
+  SSA_TRY(check_ptr(dv, "dv", 16));
+  if (sparse) {
+    SSA_TRY(check_ptr(idx, "idx", 4));
+    if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  }
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_attn_bwd(d, sparse, q, k, v, o, lse, dout, idx, sparse ? topk : 1, scale, dq, dk, dv,
+                                     (hipStream_t)stream),
+                what);
+}
+
+ssa_status ssa_full_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float scale, float* dq, float* dk, float* dv,
+                             void* stream) {
+  return attn_bwd("ssa_full_attn_bwd", false, dims, q, k, v, o, lse, dout, nullptr, 1, scale, dq, dk, dv, stream);
+}
+
+ssa_status ssa_sparse_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, const int32_t* idx, int32_t topk, float scale,
+                               float* dq, float* dk, float* dv, void* stream) {
+  return attn_bwd("ssa_sparse_attn_bwd", true, dims, q, k, v, o, lse, dout, idx, topk, scale, dq, dk, dv, stream);
+}
+
+ssa_status ssa_align_loss(const ssa_dims* dims, const void* o_full, const void* o_sparse, float alpha, float beta,
+                          float* loss, float* grad_full, float* grad_sparse, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d, false));
+  SSA_TRY(check_ptr(o_full, "o_full", 16));
+  SSA_TRY(check_ptr(o_sparse, "o_sparse", 16));
+  SSA_TRY(check_ptr(loss, "loss", 4));
+  SSA_TRY(check_opt_ptr(grad_full, "grad_full", 16));
+  SSA_TRY(check_opt_ptr(grad_sparse, "grad_sparse", 16));
+  if (!std::isfinite(alpha) || !std::isfinite(beta) || !(beta > 0.f))
+    return fail(SSA_ERR_UNSUPPORTED, "alpha must be finite and beta finite and > 0");
+  SSA_TRY(check_device());
+  return finish(ssa::launch_align_loss(d, o_full, o_sparse, alpha, beta, loss, grad_full, grad_sparse,
+                                       (hipStream_t)stream),
+                "ssa_align_loss");
+}
+
 const char* ssa_status_str(ssa_status s) {
   switch (s) {
     case SSA_OK: return "SSA_OK";

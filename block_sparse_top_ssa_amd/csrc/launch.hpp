@@ -62,6 +62,14 @@ LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void*
 LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
                                 const void* v_cache, float scale, void* o, float* lse, hipStream_t st);
 
+// Training: backward of one stream's attention forward (gradients accumulated into the
+// float32 dq [B,H,L,D], dk and dv [B,Hkv,L,D]) and the SmoothL1 alignment loss.
+LaunchResult launch_attn_bwd(const Dims& d, bool sparse, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, const int32_t* idx, int topk, float scale,
+                             float* dq, float* dk, float* dv, hipStream_t st);
+LaunchResult launch_align_loss(const Dims& d, const void* of, const void* os, float alpha, float beta, float* loss,
+                               float* gf, float* gs, hipStream_t st);
+
 // MFMA kernels (bf16 only).  *_supported() tells whether the shape fits.
 bool topk_mfma_supported(const Dims& d, int topk);
 LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,

@@ -497,15 +497,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (w < 4) publish(0, my_items > 0);
   __syncthreads();
   // Round rd: the value waves fold slot set rd % 2 while the score waves score their
-  // next tile and publish it in the other set; one barrier per round.
-  for (int rd = 0; rd < rounds; ++rd) {
-    const Slot* const cs = slots + (rd & 1) * 4;
-    if (w < 4) {
+  // next tile and publish it in the other set; one barrier per round.  Each role runs
+  // its own loop (same number of rounds, so the barriers pair up), which keeps the
+  // compiler's load counting of one role free of the other's pending loads.
+  if (w < 4) {
+    for (int rd = 0; rd < rounds; ++rd) {
       // ------------------------------------------------------------ score wave: next tile
       const bool more = rd + 1 < my_items;
       if (more) score_item();
       publish((rd + 1) & 1, more);
-    } else {
+      __syncthreads();
+    }
+  } else {
+    for (int rd = 0; rd < rounds; ++rd) {
+      // ------------------------------------------------------------ value wave
+      const Slot* const cs = slots + (rd & 1) * 4;
       // ------------------------------------------------------------ value wave
       // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
       // loaded a round ahead); (3) all products; (4) next round's V^T loads (registers
@@ -566,8 +572,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   // ---------------------------------------------------------------- 4. finalize

@@ -22,8 +22,8 @@
  *               buffer it passes.  The library keeps no pointer to them after a call
  *               returns and writes nothing outside the outputs named by a call.  Four
  *               calls allocate: ssa_sparse_attn_fwd on bf16, ssa_full_attn_fwd on bf16
- *               with o given, ssa_decode_sparse_fwd and ssa_decode_full_fwd take a
- *               transient workspace (see ssa_sparse_attn_fwd).
+ *               with o given, the two decoding forward calls, the two backward calls
+ *               and ssa_align_loss take a transient workspace (see ssa_sparse_attn_fwd).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 3 /* 2: ssa_dims.Hkv (grouped-query attention); 3: decoding calls */
+#define SSA_ABI_VERSION 4 /* 2: ssa_dims.Hkv; 3: decoding calls; 4: backward and alignment loss */
 
 typedef int32_t ssa_status;
 enum {
@@ -229,6 +229,51 @@ ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const
  */
 ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
                                const void* v_cache, float scale, void* o, float* lse, void* stream);
+
+/*
+ * Training both streams -- backward of the attention forward, and the alignment loss.
+ *   SSA trains the full and the sparse stream of every layer (sec. 5, pp. 6-7; App. C,
+ *   p. 20): the sampled main stream carries the language-model gradient and both carry
+ *   the gradient of the bidirectional alignment loss.  The backward calls give the
+ *   gradients of one stream's forward (as computed by ssa_full_attn_fwd /
+ *   ssa_sparse_attn_fwd) with respect to q, k and v, for an upstream gradient dout of
+ *   that stream's output; the selection idx is held fixed (it has no gradient).
+ *
+ *   q, o, dout  [B,H,L,D] (dtype)     in: the forward's inputs, its output o, and dL/do
+ *   k, v        [B,Hkv,L,D] (dtype)   in
+ *   lse         [B,H,L] float32       in: the forward's log-sum-exp (same stream)
+ *   dq          [B,H,L,D] float32     in/out: dq += dL/dq
+ *   dk, dv      [B,Hkv,L,D] float32   in/out: dk += dL/dk, dv += dL/dv (all query heads of
+ *               a group add into their key/value head)
+ *   The gradients are ADDED to dq, dk, dv, so the two streams' calls can share them;
+ *   clear them first.  The softmax term uses delta_t = sum_d dout_t,d o_t,d with the
+ *   stored o.  Workspace: B*H*L*4 bytes (delta); the sparse call adds an inverted index
+ *   (block -> rows that kept it) of B*H*(2n+1)*4 + B*H*L*topk*4 bytes; both from the
+ *   pool described under ssa_sparse_attn_fwd.  The sparse call accumulates dk, dv over
+ *   rows in an order that can differ between runs (last-bit float32 differences).
+ */
+ssa_status ssa_full_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float scale, float* dq, float* dk, float* dv,
+                             void* stream);
+ssa_status ssa_sparse_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, const int32_t* idx, int32_t topk, float scale,
+                               float* dq, float* dk, float* dv, void* stream);
+
+/*
+ * ssa_align_loss -- the bidirectional alignment objective of sec. 5 (pp. 6-7): a
+ *   sparsity term SmoothL1(o_full, held o_sparse) pulling the full output toward the
+ *   sparse one, and a commitment term SmoothL1(o_sparse, held o_full), each the mean over
+ *   all B*H*L*D elements, weighted by alpha.  SmoothL1(x) = 0.5 x^2 / beta for |x| < beta,
+ *   |x| - beta/2 otherwise.
+ *   o_full, o_sparse  [B,H,L,D] (dtype)   in
+ *   loss        float32 [1]               out: alpha * (mean + mean), summed in a fixed order
+ *   grad_full   [B,H,L,D] float32 or NULL out: dloss/do_full (the sparsity term only)
+ *   grad_sparse [B,H,L,D] float32 or NULL out: dloss/do_sparse (the commitment term only)
+ *   alpha finite, beta finite and > 0.  The block partition is not used (as for
+ *   ssa_align_stats).  Workspace: 4 bytes per 256 16-byte groups of o.
+ */
+ssa_status ssa_align_loss(const ssa_dims* dims, const void* o_full, const void* o_sparse, float alpha, float beta,
+                          float* loss, float* grad_full, float* grad_sparse, void* stream);
 
 /* Text for a status code (static storage). */
 const char* ssa_status_str(ssa_status status);

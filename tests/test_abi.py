@@ -114,6 +114,23 @@ def test_decode_argument_checks(libssa):
     assert libssa.ssa_decode_append(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 2
 
 
+def test_training_argument_checks(libssa):
+    d = _dims()
+    F = FAKE
+    # backward: every tensor required, dq/dk/dv 16-byte aligned float32, scale checked
+    assert libssa.ssa_full_attn_bwd(ctypes.byref(d), F, F, F, F, F, F, 0.1, F, F, None, None) == 1
+    assert libssa.ssa_full_attn_bwd(ctypes.byref(d), F, F, F, None, F, F, 0.1, F, F, F, None) == 1
+    assert libssa.ssa_full_attn_bwd(ctypes.byref(d), F, F, F, F, F, F, 0.0, F, F, F, None) == 4
+    assert libssa.ssa_full_attn_bwd(ctypes.byref(d), F, F, F, F, F, MISALIGNED, 0.1, F, F, F, None) == 4
+    assert libssa.ssa_sparse_attn_bwd(ctypes.byref(d), F, F, F, F, F, F, None, 2, 0.1, F, F, F, None) == 1
+    assert libssa.ssa_sparse_attn_bwd(ctypes.byref(d), F, F, F, F, F, F, F, 9, 0.1, F, F, F, None) == 2
+    # loss: o pair and loss required, gradients optional, beta > 0
+    assert libssa.ssa_align_loss(ctypes.byref(d), F, F, 1.0, 1.0, None, None, None, None) == 1
+    assert libssa.ssa_align_loss(ctypes.byref(d), F, None, 1.0, 1.0, F, None, None, None) == 1
+    assert libssa.ssa_align_loss(ctypes.byref(d), F, F, 1.0, 0.0, F, None, None, None) == 4
+    assert libssa.ssa_align_loss(ctypes.byref(d), F, F, float("inf"), 1.0, F, None, None, None) == 4
+
+
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path; a GPU is present")
 def test_align_ignores_block(libssa):
     """ssa_align_stats does not use the block partition, so L = 1 (one decoding step) and
