@@ -21,6 +21,13 @@ token for each of B sequences (at different positions of a 32768-token cache): a
 (cache rows + open block's pooled key) -> selection + sparse attention -> full attention
 -> alignment statistics; `value` is tokens/s (B / step time) and `roofline` is given
 for the dominant kernel, the full-stream attention, against HBM bandwidth.
+
+`--path train` measures one layer's training step of both streams on the same workload:
+pool -> top-k -> sparse and full forward -> alignment loss -> backward of the full
+stream (upstream gradient = a synthetic language-model gradient + the loss's gradient)
+and of the sparse stream (the loss's gradient) into shared float32 dq, dk, dv; `value` is
+tokens/s (B*L / step time) and `roofline` is for the full stream's backward against the
+MFMA bf16 peak (its algorithmic FLOPs 10*D per attended (query, key) pair).
 """
 from __future__ import annotations
 
@@ -160,8 +167,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
-    ap.add_argument("--path", default="prefill", choices=["prefill", "decode"],
-                    help="prefill: the whole-sequence forward (default); decode: one cached decoding step")
+    ap.add_argument("--path", default="prefill", choices=["prefill", "decode", "train"],
+                    help="prefill: the whole-sequence forward (default); decode: one cached decoding step; "
+                         "train: forward, alignment loss and backward of both streams")
     ap.add_argument("--decode-workload", default="bf16_L32768_decode", choices=sorted(W.DECODE_WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,6 +178,8 @@ def main():
         sys.exit(2)
     if args.path == "decode":
         return main_decode(args)
+    if args.path == "train":
+        return main_train(args)
 
     import torch
     import block_sparse_top_ssa_amd as ssa
@@ -433,6 +443,135 @@ def main_decode(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(di)
+    print(json.dumps(out), flush=True)
+
+
+# ----------------------------------------------------------------------------------
+# training step of both streams
+# ----------------------------------------------------------------------------------
+def cpu_baseline_train(inp: W.Inputs, k: int, Lc: int = 8192) -> dict:
+    """The CPU oracle's backward of both streams on the first Lc positions of head 0 (the
+    oracle forms the whole L x L weights, so the sample is a prefix, not a row subset)."""
+    import oracle.ssa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = inp.workload
+    s, scale = w.s, 1.0 / math.sqrt(w.D)
+    conv = (lambda a: W.bf16_bits_to_f32(a) if w.dtype == W.BF16 else a)
+    q = conv(inp.q[:1, :1, :Lc]).astype(np.float64)
+    kk = conv(inp.k[:1, :1, :Lc]).astype(np.float64)
+    vv = conv(inp.v[:1, :1, :Lc]).astype(np.float64)
+    do = np.random.default_rng(7).standard_normal(q.shape)
+    t0 = time.perf_counter()
+    idx = O.block_topk(q, O.block_pool(kk, s), s, min(k, Lc // s))
+    O.attend_full_bwd(q, kk, vv, do, scale)
+    O.attend_sparse_bwd(q, kk, vv, do, idx, s, scale)
+    dt = time.perf_counter() - t0
+    return {"value": Lc / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle backward of both streams (plus its selection) on the first {Lc} "
+                      f"positions of one head, {dt:.1f} s; tokens/s = {Lc} / wall time (one head; the oracle's "
+                      f"cost grows as L^2, so this overstates its rate at L = {w.L})"}
+
+
+def main_train(args):
+    import torch
+    import block_sparse_top_ssa_amd as ssa
+
+    w = W.WORKLOADS[args.workload]
+    k = args.topk or w.ks[0]
+    inp = W.make_workload(args.workload)
+
+    def dev(a):
+        if w.dtype == W.BF16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    q, kk, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    s, scale, alpha = w.s, 1.0 / math.sqrt(w.D), 1.0
+    B, H, L, D = w.B, w.H, w.L, w.D
+    up = torch.randn(q.shape, generator=torch.Generator(device="cuda").manual_seed(11), device="cuda",
+                     dtype=torch.float32).mul_(1e-3)   # stand-in for the language-model gradient
+    km = torch.empty((B, w.hkv, w.n, D), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, H, L, k), dtype=torch.int32, device="cuda")
+    o_s, o_f = torch.empty_like(q), torch.empty_like(q)
+    lse_s = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    lse_f = torch.empty_like(lse_s)
+    dq = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(kk.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty_like(dk)
+    names = ["forward", "loss", "full_bwd", "sparse_bwd"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ssa.block_pool(kk, s, out=km)
+        ssa.block_topk(q, km, s, k, out=idx)
+        ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s)
+        ssa.full_attn_fwd(q, kk, v, scale, block=s, out=o_f, lse=lse_f)
+        mark(1)
+        loss, g_f, g_s = ssa.align_loss(o_f, o_s, alpha)
+        do_f = (up + g_f).to(q.dtype)        # main stream: language-model gradient + alignment
+        do_s = g_s.to(q.dtype)               # auxiliary stream: alignment only
+        dq.zero_()
+        dk.zero_()
+        dv.zero_()
+        mark(2)
+        ssa.full_attn_bwd(q, kk, v, o_f, lse_f, do_f, dq, dk, dv, scale=scale, block=s)
+        mark(3)
+        ssa.sparse_attn_bwd(q, kk, v, o_s, lse_s, do_s, idx, s, dq, dk, dv, scale=scale)
+        mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}
+    pairs_full = B * H * (L * (L + 1) // 2)
+    pairs_sparse = B * H * attended_total(L, s, k)
+    flops = {"full_bwd": 10 * D * pairs_full, "sparse_bwd": 10 * D * pairs_sparse}
+    kernels = {nm: {"ms": round(per[nm], 4)} for nm in names}
+    for nm, f in flops.items():
+        tf = f / (per[nm] * 1e-3) / 1e12
+        kernels[nm].update({"tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                            "algorithmic_flops": f})
+    kernels["loss"]["note"] = "alignment loss + upstream gradient composition (torch add/cast) + zeroing dq, dk, dv"
+    tf_full = flops["full_bwd"] / (per["full_bwd"] * 1e-3) / 1e12
+    out = {
+        "metric": "training step tokens/s (forward, alignment loss, backward of both streams) at L=32K",
+        "value": round(B * L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) q, k, v with the workload's key structure, N(0,1e-6) upstream gradient)",
+        "config": {"workload": w.name, "B": B, "H": H, "Hkv": w.hkv, "L": L, "D": D, "block": s, "topk": k,
+                   "alpha": alpha, "step": "pool+topk+sparse_fwd+full_fwd+align_loss+full_bwd+sparse_bwd"},
+        "roofline": {"kernel": "ssa_full_attn_bwd", "bound": "mfma", "achieved": round(tf_full, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf_full / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "note": "matrix-core kernels (bf16 products, float32 accumulation)"},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_train(inp, k)
     print(json.dumps(out), flush=True)
 
 

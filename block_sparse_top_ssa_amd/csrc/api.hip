@@ -260,8 +260,8 @@ static ssa_status attn_bwd(const char* what, bool sparse, const ssa_dims* dims, 
   }
   SSA_TRY(check_scale(scale));
   SSA_TRY(check_device());
-  return finish(ssa::launch_attn_bwd(d, sparse, q, k, v, o, lse, dout, idx, sparse ? topk : 1, scale, dq, dk, dv,
-                                     (hipStream_t)stream),
+  return finish(ssa::launch_attn_bwd(d, sparse, use_mfma(), q, k, v, o, lse, dout, idx, sparse ? topk : 1, scale,
+                                     dq, dk, dv, (hipStream_t)stream),
                 what);
 }
 

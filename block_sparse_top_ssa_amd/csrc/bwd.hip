@@ -11,8 +11,10 @@
 //     dq_t += scale sum_i ds_ti k_i,   dk_i += scale ds_ti q_t.
 // p is recomputed from the forward's log-sum-exp: p_ti = exp(scale q_t . k_i - lse_t).
 //
-// Kernels (vector ALU, float32 arithmetic; every key or query row is read with 16-byte
-// coalesced loads, a row of D elements being D/E lanes wide):
+// The dense stream in bf16 runs on the matrix cores (bwd_mfma.hip); the kernels here
+// (vector ALU, float32 arithmetic; every key or query row is read with 16-byte coalesced
+// loads, a row of D elements being D/E lanes wide) serve the sparse stream, fp32, and
+// shapes the matrix-core kernels do not take:
 //   delta:  delta_t from the forward output o and do;
 //   dq:     one wave per query row walks the row's 64-key chunks (as the forward does)
 //           and accumulates scale sum_i ds_ti k_i;
@@ -398,9 +400,9 @@ hipError_t run_attn_bwd(const Dims& d, const void* q, const void* k, const void*
 
 }  // namespace
 
-LaunchResult launch_attn_bwd(const Dims& d, bool sparse, const void* q, const void* k, const void* v, const void* o,
-                             const float* lse, const void* dout, const int32_t* idx, int topk, float scale,
-                             float* dq, float* dk, float* dv, hipStream_t st) {
+LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout, const int32_t* idx, int topk,
+                             float scale, float* dq, float* dk, float* dv, hipStream_t st) {
   LaunchResult r;
   const int64_t rows = d.tokens();
   const int n = d.n();
@@ -430,6 +432,8 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, const void* q, const vo
     hipError_t e = run_delta<T, D>(d, o, dout, delta, st);
     if (e != hipSuccess || !sparse) {
       if (e != hipSuccess) return e;
+      if (mfma && full_bwd_mfma_supported(d))
+        return launch_full_bwd_mfma(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
       return run_attn_bwd<T, D, false>(d, q, k, v, dout, lse, delta, nullptr, 1, nullptr, nullptr, scale, dq, dk, dv,
                                        st);
     }

@@ -1,0 +1,401 @@
+// Backward of the dense causal stream on MFMA (bf16 in, float32 accumulate); the chain
+// rule is the one stated in bwd.hip (training both streams, paper sec. 5, pp. 6-7).
+//
+// Two kernels, each keeping one side resident and streaming the other through LDS:
+//
+//  dk, dv (key-stationary): a workgroup of four waves owns 128 keys of a key/value
+//  head, wave w keys 32w .. 32w+31 (two 16-key column tiles).  For every query head of
+//  the group and every 64-row query chunk at or after the keys, per 32-row pair of row
+//  tiles:
+//      S  = Q K^T,  dP = dO V^T            (A = Q / dO rows from LDS, B = K / V rows held
+//                                            in registers; lane = key column)
+//      P  = exp2(S sl2 - lse2_row), dS = P (dP - delta_row)     (vector ALU)
+//      dV^T += dO^T P,  dK^T += Q^T dS     (A = dO, Q in fragment order, B = P, dS packed
+//                                            to bf16 straight from the S layout)
+//  The fragment order (rows kappa-permuted, as in the forward's V^T) makes the S layout
+//  of two row tiles exactly the B operand of the second pair of products, so P and dS
+//  need no lane movement.
+//
+//  dq (query-stationary): a workgroup of four waves owns 128 query rows, wave w rows
+//  32w .. 32w+31 (two 16-row column tiles), and walks the 64-key chunks 0 .. its last
+//  row's chunk:
+//      S^T = K Q^T, dP^T = V dO^T          (A = K / V rows from LDS, B = Q / dO rows held)
+//      P^T, dS^T as above
+//      dQ^T += K^T dS^T                    (A = K in fragment order from LDS)
+//
+//  Operands of the next chunk are loaded into registers while the current one is
+//  multiplied, then written to the other LDS stage (last read before the previous
+//  barrier): one barrier per chunk.
+#include "launch.hpp"
+#include "mfma.hpp"
+
+namespace ssa {
+
+namespace {
+
+constexpr int kRows = 64;  // query rows per chunk (kernel dk/dv) and keys per chunk (kernel dq)
+
+// A fragment of a row-major [.., D] bf16 matrix for lane l (any lane may load it):
+// row key0 + l%16, columns 32 cc + 8 (l/16) .. +7.
+template <int D>
+__device__ __forceinline__ u32x4 load_k_frag_lane(const uint16_t* __restrict__ base, int key0, int cc, int l) {
+  return load16(base + (int64_t)(key0 + (l & 15)) * D + 32 * cc + 8 * (l >> 4));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- dk, dv
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const u32x4* __restrict__ qt, const u32x4* __restrict__ dot,
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+    int L, int G, int BHkv, float sl2, float scale) {
+  constexpr int NC = D / 32, NDT = D / 16;
+  constexpr int FQ = 4 * NC;          // A fragments of Q (and of dO) per 64-row chunk: 4 row tiles x NC
+  constexpr int FT = 2 * NDT;         // fragment-order fragments per chunk: NDT x 2 row halves
+  constexpr int NF = 2 * FQ + 2 * FT;  // per stage
+  constexpr int PT = NF * 64 / 256;    // 16-byte pieces per thread per stage
+  extern __shared__ __align__(16) unsigned char smem_kv[];
+  u32x4* st = reinterpret_cast<u32x4*>(smem_kv);                     // [2][NF][64]
+  float* sv = reinterpret_cast<float*>(smem_kv + 2 * NF * 64 * 16);  // [2][2][64]: lse2, delta
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int nkb = L / 128, nqc = L / kRows;
+  const int kb = (int)(blockIdx.x / BHkv);  // key blocks with the most query rows first
+  const int64_t kvbh = blockIdx.x - (int64_t)kb * BHkv;
+  const int kw0 = kb * 128 + 32 * w;        // this wave's first key
+  const uint16_t* kh = k + kvbh * (int64_t)L * D;
+  const uint16_t* vh = v + kvbh * (int64_t)L * D;
+
+  u32x4 kf[2][NC], vf[2][NC];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      kf[kt][cc] = load_k_frag<D>(kh, kw0 + 16 * kt, cc);
+      vf[kt][cc] = load_k_frag<D>(vh, kw0 + 16 * kt, cc);
+    }
+  f32x4 dva[2][NDT], dka[2][NDT];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dva[kt][dt] = dka[kt][dt] = f32x4{0, 0, 0, 0};
+
+  const int qc0 = kb * 2;                 // first query chunk that sees these keys
+  const int per_head = nqc - qc0;
+  const int items = G * per_head;
+  (void)nkb;
+  // staging registers of the next item, filled and stored in two halves (one per pair of
+  // row tiles) to keep register pressure down
+  constexpr int PH = PT / 2;
+  u32x4 pr[PH];
+  float ps = 0.f;
+  auto load_half = [&](int it, int half) {
+    const int gq = it / per_head, qc = qc0 + (it - gq * per_head);
+    const int64_t bh = kvbh * G + gq;
+    const int r0 = qc * kRows;
+    const uint16_t* qh = q + bh * (int64_t)L * D;
+    const uint16_t* dh = dout + bh * (int64_t)L * D;
+    const int64_t fbase = (bh * nqc + qc) * (int64_t)FT;  // fragment-order index of (head, chunk)
+#pragma unroll
+    for (int i = 0; i < PH; ++i) {
+      const int p = tid + 256 * (half * PH + i), f = p >> 6, ll = p & 63;
+      if (f < 2 * FQ) {
+        const int ff = f < FQ ? f : f - FQ, rt = ff / NC, cc = ff % NC;
+        const uint16_t* src = (f < FQ ? qh : dh) + (int64_t)(r0 + 16 * rt + (ll & 15)) * D + 32 * cc + 8 * (ll >> 4);
+        pr[i] = load16(src);
+      } else {
+        const int ff = f - 2 * FQ;
+        pr[i] = ff < FT ? qt[(fbase + ff) * 64 + ll] : dot[(fbase + ff - FT) * 64 + ll];
+      }
+    }
+    if (half == 0 && tid < 2 * kRows) {
+      const int64_t row = bh * L + r0 + (tid & (kRows - 1));
+      ps = tid < kRows ? lse[row] * kLog2e : delta[row];
+    }
+  };
+  auto store_half = [&](int b, int half) {
+#pragma unroll
+    for (int i = 0; i < PH; ++i) st[(b * NF) * 64 + tid + 256 * (half * PH + i)] = pr[i];
+    if (half == 0 && tid < 2 * kRows) sv[b * 2 * kRows + tid] = ps;
+  };
+  // rows 32 rc .. 32 rc + 31 of the chunk in stage b against this wave's keys
+  auto compute_rc = [&](int b, int r0, int rc) {
+    const u32x4* sb = st + b * NF * 64;
+    const float* lse2 = sv + b * 2 * kRows;
+    const float* dl = lse2 + kRows;
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[h][kt] = dp[h][kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rt = 2 * rc + h;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const u32x4 aq = sb[(rt * NC + cc) * 64 + lane];
+        const u32x4 ad = sb[(FQ + rt * NC + cc) * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          s[h][kt] = mfma_bf16(aq, kf[kt][cc], s[h][kt]);
+          dp[h][kt] = mfma_bf16(ad, vf[kt][cc], dp[h][kt]);
+        }
+      }
+    }
+    // element i of s[h][kt]: row r0 + 32 rc + 16 h + 4 g + i, key kw0 + 16 kt + n
+    float pv[2][2][4], dsv[2][2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 32 * rc + 16 * h + 4 * g + i;
+        const float l2 = lse2[rl], de = dl[rl];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bool live = r0 + rl >= kw0 + 16 * kt + n;
+          const float p = live ? fast_exp2(fmaf(s[h][kt][i], sl2, -l2)) : 0.f;
+          pv[h][kt][i] = p;
+          dsv[h][kt][i] = p * (dp[h][kt][i] - de);
+        }
+      }
+    u32x4 pb[2], sbf[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      pb[kt] = pack_p(pv[0][kt], pv[1][kt]);
+      sbf[kt] = pack_p(dsv[0][kt], dsv[1][kt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 aqt = sb[(2 * FQ + dt * 2 + rc) * 64 + lane];
+      const u32x4 adt = sb[(2 * FQ + FT + dt * 2 + rc) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        dva[kt][dt] = mfma_bf16(adt, pb[kt], dva[kt][dt]);
+        dka[kt][dt] = mfma_bf16(aqt, sbf[kt], dka[kt][dt]);
+      }
+    }
+  };
+
+  load_half(0, 0);
+  store_half(0, 0);
+  load_half(0, 1);
+  store_half(0, 1);
+  __syncthreads();
+  for (int it = 0; it < items; ++it) {
+    const int b = it & 1;
+    const int nxt = min(it + 1, items - 1);  // unconditional loads (a repeat on the last item)
+    const int gq = it / per_head, qc = qc0 + (it - gq * per_head);
+    const int r0 = qc * kRows;
+    const bool live = r0 + kRows - 1 >= kw0;  // some row of the chunk sees some key of this wave
+    // stage b ^ 1 was last read in the previous iteration, before its barrier
+#pragma unroll
+    for (int rc = 0; rc < 2; ++rc) {
+      load_half(nxt, rc);
+      if (live) compute_rc(b, r0, rc);
+      store_half(b ^ 1, rc);
+    }
+    __syncthreads();
+  }
+  // dva[kt][dt] element i: d = 16 dt + 4 g + i, key kw0 + 16 kt + n
+  float* dkh = dk + kvbh * (int64_t)L * D;
+  float* dvh = dv + kvbh * (int64_t)L * D;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int64_t key = kw0 + 16 * kt + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f32x4* pk = reinterpret_cast<f32x4*>(dkh + key * D + 16 * dt + 4 * g);
+      f32x4* pv = reinterpret_cast<f32x4*>(dvh + key * D + 16 * dt + 4 * g);
+      *pk = *pk + dka[kt][dt] * scale;
+      *pv = *pv + dva[kt][dt];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dq
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_q_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const u32x4* __restrict__ kt_frag, const float* __restrict__ lse,
+    const float* __restrict__ delta, float* __restrict__ dq, int L, int G, int BH, float sl2, float scale) {
+  constexpr int NC = D / 32, NDT = D / 16;
+  constexpr int FK = 4 * NC;          // A fragments of K (and of V) per 64-key chunk
+  constexpr int FT = 2 * NDT;         // fragment-order K^T fragments per chunk
+  constexpr int NF = 2 * FK + FT;
+  constexpr int PT = NF * 64 / 256;
+  extern __shared__ __align__(16) unsigned char smem_q[];
+  u32x4* st = reinterpret_cast<u32x4*>(smem_q);  // [2][NF][64]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int nqb = L / 128, nck = L / 64;
+  const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // row blocks with the most keys first
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t kvbh = bh / G;
+  const int rw0 = qb * 128 + 32 * w;  // this wave's first row
+  const uint16_t* qh = q + bh * (int64_t)L * D;
+  const uint16_t* dh = dout + bh * (int64_t)L * D;
+  const uint16_t* kh = k + kvbh * (int64_t)L * D;
+  const uint16_t* vh = v + kvbh * (int64_t)L * D;
+
+  u32x4 qf[2][NC], df[2][NC];
+  float l2[2], de[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t row = rw0 + 16 * nt + n;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      qf[nt][cc] = load_q_frag<D>(qh + row * D, cc);
+      df[nt][cc] = load_q_frag<D>(dh + row * D, cc);
+    }
+    l2[nt] = lse[bh * L + row] * kLog2e;
+    de[nt] = delta[bh * L + row];
+  }
+  f32x4 dqa[2][NDT];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dqa[nt][dt] = f32x4{0, 0, 0, 0};
+
+  const int items = (qb * 128 + 127) / 64 + 1;  // key chunks 0 .. the block's last row's chunk
+  u32x4 pr[PT];
+  auto load_item = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const int p = tid + 256 * i, f = p >> 6, ll = p & 63;
+      if (f < 2 * FK) {
+        const int ff = f < FK ? f : f - FK, kt = ff / NC, cc = ff % NC;
+        pr[i] = load_k_frag_lane<D>(f < FK ? kh : vh, c * 64 + 16 * kt, cc, ll);
+      } else {
+        pr[i] = kt_frag[((kvbh * nck + c) * (int64_t)FT + (f - 2 * FK)) * 64 + ll];
+      }
+    }
+  };
+  auto store_item = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) st[(b * NF) * 64 + tid + 256 * i] = pr[i];
+  };
+  load_item(0);
+  store_item(0);
+  __syncthreads();
+  for (int c = 0; c < items; ++c) {
+    const int b = c & 1;
+    load_item(min(c + 1, items - 1));
+    const u32x4* sb = st + b * NF * 64;
+    const int k0 = c * 64;
+    if (k0 <= rw0 + 31) {  // some key of the chunk is at or before some row of this wave
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 s[4], dp[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) s[kt] = dp[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) {
+            s[kt] = mfma_bf16(sb[(kt * NC + cc) * 64 + lane], qf[nt][cc], s[kt]);
+            dp[kt] = mfma_bf16(sb[(FK + kt * NC + cc) * 64 + lane], df[nt][cc], dp[kt]);
+          }
+        // element i of s[kt]: key k0 + 16 kt + 4 g + i, row rw0 + 16 nt + n
+        const int row = rw0 + 16 * nt + n;
+        float dsv[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool live = k0 + 16 * kt + 4 * g + i <= row;
+            const float p = live ? fast_exp2(fmaf(s[kt][i], sl2, -l2[nt])) : 0.f;
+            dsv[kt][i] = p * (dp[kt][i] - de[nt]);
+          }
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const u32x4 bs = pack_p(dsv[2 * kc], dsv[2 * kc + 1]);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            dqa[nt][dt] = mfma_bf16(sb[(2 * FK + dt * 2 + kc) * 64 + lane], bs, dqa[nt][dt]);
+        }
+      }
+    }
+    store_item(b ^ 1);
+    __syncthreads();
+  }
+  // dqa[nt][dt] element i: d = 16 dt + 4 g + i, row rw0 + 16 nt + n
+  float* dqh = dq + bh * (int64_t)L * D;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t row = rw0 + 16 * nt + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f32x4* pq = reinterpret_cast<f32x4*>(dqh + row * D + 16 * dt + 4 * g);
+      *pq = *pq + dqa[nt][dt] * scale;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launcher
+bool full_bwd_mfma_supported(const Dims& d) {
+  return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 128 == 0;
+}
+
+template <int D>
+static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
+                                    const float* lse, const float* delta, float scale, float* dq, float* dk,
+                                    float* dv, u32x4* qt, u32x4* dot, u32x4* ktf, hipStream_t st) {
+  constexpr int NC = D / 32, NDT = D / 16;
+  const Dims kv = d.kv();
+  hipError_t e = frag_order_into(d, q, qt, st);
+  if (e == hipSuccess) e = frag_order_into(d, dout, dot, st);
+  if (e == hipSuccess) e = frag_order_into(kv, k, ktf, st);
+  if (e != hipSuccess) return e;
+  const float sl2 = scale * kLog2e;
+  {
+    constexpr int NF = 2 * (4 * NC) + 2 * (2 * NDT);
+    const int lds = 2 * NF * 64 * 16 + 2 * 2 * 64 * 4;
+    auto kern = bwd_kv_mfma_kernel<D>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    const int64_t grid = (int64_t)kv.bh() * (d.L / 128);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(dout), qt, dot, lse, delta, dk, dv, d.L, d.G(), (int)kv.bh(), sl2,
+                       scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    constexpr int NF = 2 * (4 * NC) + 2 * NDT;
+    const int lds = 2 * NF * 64 * 16;
+    auto kern = bwd_q_mfma_kernel<D>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    const int64_t grid = d.bh() * (d.L / 128);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(dout), ktf, lse, delta, dq, d.L, d.G(), (int)d.bh(), sl2, scale);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, float scale, float* dq, float* dk, float* dv,
+                                hipStream_t st) {
+  // fragment-order copies of Q, dO (query heads) and K (key/value heads)
+  const size_t qbytes = (size_t)d.tokens() * d.D * 2, kbytes = (size_t)d.kv().tokens() * d.D * 2;
+  void* ws = nullptr;
+  hipError_t e = workspace_alloc(2 * qbytes + kbytes, &ws, st);
+  if (e != hipSuccess) return e;
+  char* base = static_cast<char*>(ws);
+  u32x4* qt = reinterpret_cast<u32x4*>(base);
+  u32x4* dot = reinterpret_cast<u32x4*>(base + qbytes);
+  u32x4* ktf = reinterpret_cast<u32x4*>(base + 2 * qbytes);
+  e = d.D == 128 ? run_full_bwd_mfma<128>(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, qt, dot, ktf, st)
+                 : run_full_bwd_mfma<64>(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, qt, dot, ktf, st);
+  const hipError_t fe = workspace_free(ws, st);
+  return e != hipSuccess ? e : fe;
+}
+
+}  // namespace ssa

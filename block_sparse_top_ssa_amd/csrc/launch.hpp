@@ -46,6 +46,8 @@ LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, co
 // pool kept per device; give it back with vfrag_release on the same stream.
 hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st);
 hipError_t vfrag_release(void* ws, hipStream_t st);
+// The same rewrite of any bf16 [B,H,L,D] tensor (d.H heads) into a caller-given buffer.
+hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st);
 
 // Transient device memory from the same per-device stream-ordered pool: valid for work
 // enqueued on `st` after the call, given back with workspace_free on the same stream.
@@ -64,9 +66,14 @@ LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q
 
 // Training: backward of one stream's attention forward (gradients accumulated into the
 // float32 dq [B,H,L,D], dk and dv [B,Hkv,L,D]) and the SmoothL1 alignment loss.
-LaunchResult launch_attn_bwd(const Dims& d, bool sparse, const void* q, const void* k, const void* v, const void* o,
-                             const float* lse, const void* dout, const int32_t* idx, int topk, float scale,
-                             float* dq, float* dk, float* dv, hipStream_t st);
+LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const void* dout, const int32_t* idx, int topk,
+                             float scale, float* dq, float* dk, float* dv, hipStream_t st);
+// MFMA backward of the dense stream (bf16): dq, dk, dv += ..., given delta [B*H*L].
+bool full_bwd_mfma_supported(const Dims& d);
+hipError_t launch_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, float scale, float* dq, float* dk, float* dv,
+                                hipStream_t st);
 LaunchResult launch_align_loss(const Dims& d, const void* of, const void* os, float alpha, float beta, float* loss,
                                float* gf, float* gs, hipStream_t st);
 

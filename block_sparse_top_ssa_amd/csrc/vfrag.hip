@@ -80,6 +80,11 @@ hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st
 
 hipError_t vfrag_release(void* ws, hipStream_t st) { return ws ? hipFreeAsync(ws, st) : hipSuccess; }
 
+hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st) {
+  return d.D == 128 ? run_vfrag<128>(d, x, static_cast<u32x4*>(out), st)
+                    : run_vfrag<64>(d, x, static_cast<u32x4*>(out), st);
+}
+
 hipError_t workspace_alloc(size_t bytes, void** ws, hipStream_t st) {
   *ws = nullptr;
   hipMemPool_t pool = nullptr;

@@ -68,9 +68,16 @@ def forward_backward(inp, s, topk, do_f, do_s, tag=""):
     return dict(idx=idx.cpu().numpy(), full=[to_f64(t) for t in g_full], both=[to_f64(t) for t in (dq, dk, dv)])
 
 
+@pytest.fixture(params=[0, 1], ids=["mfma", "portable"])
+def variant(request):
+    prev = ssa.set_kernel_variant(request.param)
+    yield request.param
+    ssa.set_kernel_variant(prev)
+
+
 @pytest.mark.parametrize("dtype,D,s,Hkv", [(W.BF16, 128, 64, 4), (W.BF16, 64, 128, 2), (W.F32, 128, 64, 4),
-                                           (W.F32, 64, 64, 1)])
-def test_attention_bwd_both_streams(dtype, D, s, Hkv):
+                                           (W.F32, 64, 64, 1), (W.BF16, 128, 64, 1)])
+def test_attention_bwd_both_streams(variant, dtype, D, s, Hkv):
     B, H, L, topk = 1, 4, 512, 3
     inp = W.make_qkv(B, H, L, D, s, dtype, "sink", seed=3100 + D + s + Hkv, hkv=Hkv)
     rng = np.random.default_rng(3200 + D)
@@ -93,7 +100,7 @@ def test_attention_bwd_both_streams(dtype, D, s, Hkv):
         ref_both = rf[i] + rs[i] if i == 0 else _kv_sum(rf[i] + rs[i], H, Hkv)
         errs[nm + "_full"] = close_rel(g["full"][i], ref_f, tol, nm + " (full stream)")
         errs[nm + "_both"] = close_rel(g["both"][i], ref_both, tol, nm + " (full + sparse)")
-    say(f"[oracle] train D={D} s={s} Hkv={Hkv} {dtype}: {errs}")
+    say(f"[oracle] train D={D} s={s} Hkv={Hkv} {dtype} variant={variant}: {errs}")
 
 
 def test_sparse_bwd_alone_matches_oracle():
