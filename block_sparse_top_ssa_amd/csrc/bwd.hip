@@ -433,10 +433,12 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* 
     if (e != hipSuccess || !sparse) {
       if (e != hipSuccess) return e;
       if (mfma && full_bwd_mfma_supported(d))
-        return launch_full_bwd_mfma(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
+        return launch_full_bwd_mfma(d, nullptr, 0, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
       return run_attn_bwd<T, D, false>(d, q, k, v, dout, lse, delta, nullptr, 1, nullptr, nullptr, scale, dq, dk, dv,
                                        st);
     }
+    if (mfma && sparse_bwd_mfma_supported(d))
+      return launch_full_bwd_mfma(d, idx, topk, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
     const int64_t ncnt = d.bh() * n;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((ncnt + 255) / 256)), dim3(256), 0, st, cnt, ncnt);
     const unsigned g = (unsigned)((rows + 255) / 256);

@@ -26,6 +26,12 @@
 //  Operands of the next chunk are loaded into registers while the current one is
 //  multiplied, then written to the other LDS stage (last read before the previous
 //  barrier): one barrier per chunk.
+//
+//  The sparse stream runs the same kernels with a per-row bit mask of attended blocks
+//  (the kept blocks and the own block, built from idx): a weight whose key's block is
+//  not in the row's mask is zero.  This does the dense stream's work for the sparse
+//  stream's result; the kept blocks of neighbouring rows cover most earlier blocks, so
+//  skipping by tile would save little.
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -45,12 +51,12 @@ __device__ __forceinline__ u32x4 load_k_frag_lane(const uint16_t* __restrict__ b
 }  // namespace
 
 // ---------------------------------------------------------------- dk, dv
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const u32x4* __restrict__ qt, const u32x4* __restrict__ dot,
-    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
-    int L, int G, int BHkv, float sl2, float scale) {
+    const float* __restrict__ lse, const float* __restrict__ delta, const uint32_t* __restrict__ mask, int W, int s,
+    float* __restrict__ dk, float* __restrict__ dv, int L, int G, int BHkv, float sl2, float scale) {
   constexpr int NC = D / 32, NDT = D / 16;
   constexpr int FQ = 4 * NC;          // A fragments of Q (and of dO) per 64-row chunk: 4 row tiles x NC
   constexpr int FT = 2 * NDT;         // fragment-order fragments per chunk: NDT x 2 row halves
@@ -59,6 +65,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   extern __shared__ __align__(16) unsigned char smem_kv[];
   u32x4* st = reinterpret_cast<u32x4*>(smem_kv);                     // [2][NF][64]
   float* sv = reinterpret_cast<float*>(smem_kv + 2 * NF * 64 * 16);  // [2][2][64]: lse2, delta
+  uint32_t* sm = reinterpret_cast<uint32_t*>(sv + 2 * 2 * 64);       // [2][64]: rows' mask words
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -66,6 +73,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int kb = (int)(blockIdx.x / BHkv);  // key blocks with the most query rows first
   const int64_t kvbh = blockIdx.x - (int64_t)kb * BHkv;
   const int kw0 = kb * 128 + 32 * w;        // this wave's first key
+  // sparse: the mask word holding the workgroup's blocks, and this wave's bit in it
+  const int mword = SPARSE ? (kb * 128 / s) / 32 : 0;
+  const int mbit = SPARSE ? (kw0 / s) % 32 : 0;
   const uint16_t* kh = k + kvbh * (int64_t)L * D;
   const uint16_t* vh = v + kvbh * (int64_t)L * D;
 
@@ -92,6 +102,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int PH = PT / 2;
   u32x4 pr[PH];
   float ps = 0.f;
+  uint32_t pm = 0;
   auto load_half = [&](int it, int half) {
     const int gq = it / per_head, qc = qc0 + (it - gq * per_head);
     const int64_t bh = kvbh * G + gq;
@@ -115,11 +126,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int64_t row = bh * L + r0 + (tid & (kRows - 1));
       ps = tid < kRows ? lse[row] * kLog2e : delta[row];
     }
+    if (SPARSE && half == 0 && tid >= 2 * kRows && tid < 3 * kRows)
+      pm = mask[(bh * L + r0 + (tid - 2 * kRows)) * (int64_t)W + mword];
   };
   auto store_half = [&](int b, int half) {
 #pragma unroll
     for (int i = 0; i < PH; ++i) st[(b * NF) * 64 + tid + 256 * (half * PH + i)] = pr[i];
     if (half == 0 && tid < 2 * kRows) sv[b * 2 * kRows + tid] = ps;
+    if (SPARSE && half == 0 && tid >= 2 * kRows && tid < 3 * kRows) sm[b * kRows + tid - 2 * kRows] = pm;
   };
   // rows 32 rc .. 32 rc + 31 of the chunk in stage b against this wave's keys
   auto compute_rc = [&](int b, int r0, int rc) {
@@ -153,9 +167,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int i = 0; i < 4; ++i) {
         const int rl = 32 * rc + 16 * h + 4 * g + i;
         const float l2 = lse2[rl], de = dl[rl];
+        const bool kept = !SPARSE || ((sm[b * kRows + rl] >> mbit) & 1u);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bool live = r0 + rl >= kw0 + 16 * kt + n;
+          const bool live = kept && r0 + rl >= kw0 + 16 * kt + n;
           const float p = live ? fast_exp2(fmaf(s[h][kt][i], sl2, -l2)) : 0.f;
           pv[h][kt][i] = p;
           dsv[h][kt][i] = p * (dp[h][kt][i] - de);
@@ -216,11 +231,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------- dq
-template <int D>
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_q_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const u32x4* __restrict__ kt_frag, const float* __restrict__ lse,
-    const float* __restrict__ delta, float* __restrict__ dq, int L, int G, int BH, float sl2, float scale) {
+    const float* __restrict__ delta, const uint32_t* __restrict__ mask, int W, int s, float* __restrict__ dq, int L,
+    int G, int BH, float sl2, float scale) {
   constexpr int NC = D / 32, NDT = D / 16;
   constexpr int FK = 4 * NC;          // A fragments of K (and of V) per 64-key chunk
   constexpr int FT = 2 * NDT;         // fragment-order K^T fragments per chunk
@@ -261,6 +277,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int dt = 0; dt < NDT; ++dt) dqa[nt][dt] = f32x4{0, 0, 0, 0};
 
   const int items = (qb * 128 + 127) / 64 + 1;  // key chunks 0 .. the block's last row's chunk
+  // sparse: whether each of this lane's two rows attends the block of the current chunk
+  // (its mask bit), fetched one chunk ahead
+  auto row_keeps = [&](int nt, int c) -> bool {
+    if (!SPARSE) return true;
+    const int j = c * 64 / s;
+    const uint32_t word = mask[(bh * L + rw0 + 16 * nt + n) * (int64_t)W + j / 32];
+    return (word >> (j % 32)) & 1u;
+  };
+  bool keep_cur[2] = {row_keeps(0, 0), row_keeps(1, 0)};
   u32x4 pr[PT];
   auto load_item = [&](int c) {
 #pragma unroll
@@ -284,6 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int c = 0; c < items; ++c) {
     const int b = c & 1;
     load_item(min(c + 1, items - 1));
+    const bool keep_next[2] = {row_keeps(0, min(c + 1, items - 1)), row_keeps(1, min(c + 1, items - 1))};
     const u32x4* sb = st + b * NF * 64;
     const int k0 = c * 64;
     if (k0 <= rw0 + 31) {  // some key of the chunk is at or before some row of this wave
@@ -306,7 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool live = k0 + 16 * kt + 4 * g + i <= row;
+            const bool live = keep_cur[nt] && k0 + 16 * kt + 4 * g + i <= row;
             const float p = live ? fast_exp2(fmaf(s[kt][i], sl2, -l2[nt])) : 0.f;
             dsv[kt][i] = p * (dp[kt][i] - de[nt]);
           }
@@ -320,6 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
     store_item(b ^ 1);
+    keep_cur[0] = keep_next[0];
+    keep_cur[1] = keep_next[1];
     __syncthreads();
   }
   // dqa[nt][dt] element i: d = 16 dt + 4 g + i, row rw0 + 16 nt + n
@@ -340,10 +368,40 @@ bool full_bwd_mfma_supported(const Dims& d) {
   return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 128 == 0;
 }
 
-template <int D>
+bool sparse_bwd_mfma_supported(const Dims& d) { return full_bwd_mfma_supported(d) && d.n() <= 4096; }
+
+// Bit j of word j / 32 of row t's mask: the sparse stream attends block j (a valid kept
+// entry of idx, or the own block).  One thread per (row, word).
+__global__ __launch_bounds__(256) void bwd_mask_kernel(const int32_t* __restrict__ idx, int topk,
+                                                       uint32_t* __restrict__ mask, int64_t rows, int W, int L,
+                                                       int s) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * W) return;
+  const int64_t row = i / W;
+  const int wd = (int)(i - row * W);
+  const int t = (int)(row % L), bt = t / s;
+  uint32_t m = 0;
+  auto set = [&](int j) {
+    if (j / 32 == wd) m |= 1u << (j % 32);
+  };
+  set(bt);
+  const int32_t* ir = idx + row * topk;
+  int prev = -1;
+  for (int e = 0; e < topk; ++e) {
+    const int j = ir[e];
+    if (j > prev && j < bt) {
+      prev = j;
+      set(j);
+    }
+  }
+  mask[i] = m;
+}
+
+template <int D, bool SPARSE>
 static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
-                                    const float* lse, const float* delta, float scale, float* dq, float* dk,
-                                    float* dv, u32x4* qt, u32x4* dot, u32x4* ktf, hipStream_t st) {
+                                    const float* lse, const float* delta, const uint32_t* mask, int W, float scale,
+                                    float* dq, float* dk, float* dv, u32x4* qt, u32x4* dot, u32x4* ktf,
+                                    hipStream_t st) {
   constexpr int NC = D / 32, NDT = D / 16;
   const Dims kv = d.kv();
   hipError_t e = frag_order_into(d, q, qt, st);
@@ -353,47 +411,68 @@ static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k,
   const float sl2 = scale * kLog2e;
   {
     constexpr int NF = 2 * (4 * NC) + 2 * (2 * NDT);
-    const int lds = 2 * NF * 64 * 16 + 2 * 2 * 64 * 4;
-    auto kern = bwd_kv_mfma_kernel<D>;
+    const int lds = 2 * NF * 64 * 16 + 3 * 2 * 64 * 4;
+    auto kern = bwd_kv_mfma_kernel<D, SPARSE>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     const int64_t grid = (int64_t)kv.bh() * (d.L / 128);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), qt, dot, lse, delta, dk, dv, d.L, d.G(), (int)kv.bh(), sl2,
-                       scale);
+                       static_cast<const uint16_t*>(dout), qt, dot, lse, delta, mask, W, d.S, dk, dv, d.L, d.G(),
+                       (int)kv.bh(), sl2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   {
     constexpr int NF = 2 * (4 * NC) + 2 * NDT;
     const int lds = 2 * NF * 64 * 16;
-    auto kern = bwd_q_mfma_kernel<D>;
+    auto kern = bwd_q_mfma_kernel<D, SPARSE>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     const int64_t grid = d.bh() * (d.L / 128);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), ktf, lse, delta, dq, d.L, d.G(), (int)d.bh(), sl2, scale);
+                       static_cast<const uint16_t*>(dout), ktf, lse, delta, mask, W, d.S, dq, d.L, d.G(), (int)d.bh(),
+                       sl2, scale);
     e = hipGetLastError();
   }
   return e;
 }
 
-hipError_t launch_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
-                                const float* lse, const float* delta, float scale, float* dq, float* dk, float* dv,
-                                hipStream_t st) {
-  // fragment-order copies of Q, dO (query heads) and K (key/value heads)
+hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const void* q, const void* k,
+                                const void* v, const void* dout, const float* lse, const float* delta, float scale,
+                                float* dq, float* dk, float* dv, hipStream_t st) {
+  // fragment-order copies of Q, dO (query heads) and K (key/value heads); sparse: the
+  // rows' block masks
   const size_t qbytes = (size_t)d.tokens() * d.D * 2, kbytes = (size_t)d.kv().tokens() * d.D * 2;
+  const int W = (d.n() + 31) / 32;
+  const size_t mbytes = idx ? (size_t)d.tokens() * W * 4 : 0;
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(2 * qbytes + kbytes, &ws, st);
+  hipError_t e = workspace_alloc(2 * qbytes + kbytes + mbytes, &ws, st);
   if (e != hipSuccess) return e;
   char* base = static_cast<char*>(ws);
   u32x4* qt = reinterpret_cast<u32x4*>(base);
   u32x4* dot = reinterpret_cast<u32x4*>(base + qbytes);
   u32x4* ktf = reinterpret_cast<u32x4*>(base + 2 * qbytes);
-  e = d.D == 128 ? run_full_bwd_mfma<128>(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, qt, dot, ktf, st)
-                 : run_full_bwd_mfma<64>(d, q, k, v, dout, lse, delta, scale, dq, dk, dv, qt, dot, ktf, st);
+  uint32_t* mask = reinterpret_cast<uint32_t*>(base + 2 * qbytes + kbytes);
+  if (idx) {
+    const int64_t n = d.tokens() * W;
+    hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, topk, mask,
+                       d.tokens(), W, d.L, d.S);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    if (idx)
+      e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, mask, W, scale, dq, dk, dv, qt, dot,
+                                                    ktf, st)
+                     : run_full_bwd_mfma<64, true>(d, q, k, v, dout, lse, delta, mask, W, scale, dq, dk, dv, qt, dot,
+                                                   ktf, st);
+    else
+      e = d.D == 128 ? run_full_bwd_mfma<128, false>(d, q, k, v, dout, lse, delta, nullptr, 0, scale, dq, dk, dv, qt,
+                                                     dot, ktf, st)
+                     : run_full_bwd_mfma<64, false>(d, q, k, v, dout, lse, delta, nullptr, 0, scale, dq, dk, dv, qt,
+                                                    dot, ktf, st);
+  }
   const hipError_t fe = workspace_free(ws, st);
   return e != hipSuccess ? e : fe;
 }
