@@ -174,6 +174,49 @@ __global__ __launch_bounds__(256) void bwd_index_count_kernel(const int32_t* __r
   for_kept(idx + row * topk, topk, t / s, [&](int j) { atomicAdd(&c[j], 1); });
 }
 
+// The same count and fill with the counting done in LDS first: a workgroup takes 1024
+// rows of one (b, h), counts its entries per block in LDS and adds each nonzero count to
+// the global counter once (fill: reserves its range with one global atomic per block,
+// then places its rows with LDS cursors).  For n <= kIndexLdsBlocks.
+constexpr int kIndexLdsBlocks = 4096;
+constexpr int kIndexRows = 1024;
+
+__global__ __launch_bounds__(256) void bwd_index_count_lds_kernel(const int32_t* __restrict__ idx, int topk,
+                                                                  int* __restrict__ cnt, int L, int s, int n) {
+  __shared__ int lc[kIndexLdsBlocks];
+  const int tiles = (L + kIndexRows - 1) / kIndexRows;
+  const int64_t bh = blockIdx.x / tiles;
+  const int t0 = (int)(blockIdx.x - bh * tiles) * kIndexRows;
+  for (int j = threadIdx.x; j < n; j += 256) lc[j] = 0;
+  __syncthreads();
+  for (int t = t0 + threadIdx.x; t < min(L, t0 + kIndexRows); t += 256)
+    for_kept(idx + (bh * L + t) * topk, topk, t / s, [&](int j) { atomicAdd(&lc[j], 1); });
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256)
+    if (lc[j]) atomicAdd(&cnt[bh * n + j], lc[j]);
+}
+
+__global__ __launch_bounds__(256) void bwd_index_fill_lds_kernel(const int32_t* __restrict__ idx, int topk,
+                                                                 int* __restrict__ cur, int* __restrict__ list, int L,
+                                                                 int s, int n) {
+  __shared__ int lc[kIndexLdsBlocks];
+  const int tiles = (L + kIndexRows - 1) / kIndexRows;
+  const int64_t bh = blockIdx.x / tiles;
+  const int t0 = (int)(blockIdx.x - bh * tiles) * kIndexRows;
+  const int t1 = min(L, t0 + kIndexRows);
+  int* li = list + bh * (int64_t)L * topk;
+  for (int j = threadIdx.x; j < n; j += 256) lc[j] = 0;
+  __syncthreads();
+  for (int t = t0 + threadIdx.x; t < t1; t += 256)
+    for_kept(idx + (bh * L + t) * topk, topk, t / s, [&](int j) { atomicAdd(&lc[j], 1); });
+  __syncthreads();
+  for (int j = threadIdx.x; j < n; j += 256)
+    if (lc[j]) lc[j] = atomicAdd(&cur[bh * n + j], lc[j]);  // this workgroup's first slot of block j
+  __syncthreads();
+  for (int t = t0 + threadIdx.x; t < t1; t += 256)
+    for_kept(idx + (bh * L + t) * topk, topk, t / s, [&](int j) { li[atomicAdd(&lc[j], 1)] = t; });
+}
+
 // Exclusive prefix sum of cnt over the n blocks of one (b, h); cnt becomes the fill
 // cursor.  One workgroup per (b, h).
 __global__ __launch_bounds__(256) void bwd_index_scan_kernel(int* __restrict__ cnt, int* __restrict__ off, int n) {
@@ -433,20 +476,28 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* 
     if (e != hipSuccess || !sparse) {
       if (e != hipSuccess) return e;
       if (mfma && full_bwd_mfma_supported(d))
-        return launch_full_bwd_mfma(d, nullptr, 0, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
+        return launch_full_bwd_mfma(d, nullptr, 0, nullptr, nullptr, q, k, v, dout, lse, delta, scale, dq, dk, dv,
+                                    st);
       return run_attn_bwd<T, D, false>(d, q, k, v, dout, lse, delta, nullptr, 1, nullptr, nullptr, scale, dq, dk, dv,
                                        st);
     }
-    if (mfma && sparse_bwd_mfma_supported(d))
-      return launch_full_bwd_mfma(d, idx, topk, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
     const int64_t ncnt = d.bh() * n;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((ncnt + 255) / 256)), dim3(256), 0, st, cnt, ncnt);
     const unsigned g = (unsigned)((rows + 255) / 256);
-    hipLaunchKernelGGL(bwd_index_count_kernel, dim3(g), dim3(256), 0, st, idx, topk, cnt, rows, d.L, d.S, n);
+    const unsigned gl = (unsigned)(d.bh() * ((d.L + kIndexRows - 1) / kIndexRows));
+    if (n <= kIndexLdsBlocks)
+      hipLaunchKernelGGL(bwd_index_count_lds_kernel, dim3(gl), dim3(256), 0, st, idx, topk, cnt, d.L, d.S, n);
+    else
+      hipLaunchKernelGGL(bwd_index_count_kernel, dim3(g), dim3(256), 0, st, idx, topk, cnt, rows, d.L, d.S, n);
     hipLaunchKernelGGL(bwd_index_scan_kernel, dim3((unsigned)d.bh()), dim3(256), 0, st, cnt, off, n);
-    hipLaunchKernelGGL(bwd_index_fill_kernel, dim3(g), dim3(256), 0, st, idx, topk, cnt, list, rows, d.L, d.S, n);
+    if (n <= kIndexLdsBlocks)
+      hipLaunchKernelGGL(bwd_index_fill_lds_kernel, dim3(gl), dim3(256), 0, st, idx, topk, cnt, list, d.L, d.S, n);
+    else
+      hipLaunchKernelGGL(bwd_index_fill_kernel, dim3(g), dim3(256), 0, st, idx, topk, cnt, list, rows, d.L, d.S, n);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (mfma && sparse_bwd_mfma_supported(d))
+      return launch_full_bwd_mfma(d, idx, topk, off, list, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
     return run_attn_bwd<T, D, true>(d, q, k, v, dout, lse, delta, idx, topk, off, list, scale, dq, dk, dv, st);
   });
   const hipError_t fe = workspace_free(ws, st);

@@ -27,11 +27,13 @@
 //  multiplied, then written to the other LDS stage (last read before the previous
 //  barrier): one barrier per chunk.
 //
-//  The sparse stream runs the same kernels with a per-row bit mask of attended blocks
-//  (the kept blocks and the own block, built from idx): a weight whose key's block is
-//  not in the row's mask is zero.  This does the dense stream's work for the sparse
-//  stream's result; the kept blocks of neighbouring rows cover most earlier blocks, so
-//  skipping by tile would save little.
+//  The sparse stream: dk, dv visit only the rows that attend each block -- a workgroup
+//  per (key/value head, block) walks the block's own rows (causally) and the rows that
+//  kept it (an inverted index block -> rows), gathered 64 at a time; dq runs the
+//  query-stationary kernel with a per-row bit mask of attended blocks (kept blocks and
+//  the own block, built from idx), a weight whose key's block is not in the mask being
+//  zero.  That does the dense amount of work for dq: the kept blocks of 32 neighbouring
+//  rows cover most earlier blocks, so a row tile skips few chunks.
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -51,12 +53,12 @@ __device__ __forceinline__ u32x4 load_k_frag_lane(const uint16_t* __restrict__ b
 }  // namespace
 
 // ---------------------------------------------------------------- dk, dv
-template <int D, bool SPARSE>
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const u32x4* __restrict__ qt, const u32x4* __restrict__ dot,
-    const float* __restrict__ lse, const float* __restrict__ delta, const uint32_t* __restrict__ mask, int W, int s,
-    float* __restrict__ dk, float* __restrict__ dv, int L, int G, int BHkv, float sl2, float scale) {
+    const float* __restrict__ lse, const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+    int L, int G, int BHkv, float sl2, float scale) {
   constexpr int NC = D / 32, NDT = D / 16;
   constexpr int FQ = 4 * NC;          // A fragments of Q (and of dO) per 64-row chunk: 4 row tiles x NC
   constexpr int FT = 2 * NDT;         // fragment-order fragments per chunk: NDT x 2 row halves
@@ -65,7 +67,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   extern __shared__ __align__(16) unsigned char smem_kv[];
   u32x4* st = reinterpret_cast<u32x4*>(smem_kv);                     // [2][NF][64]
   float* sv = reinterpret_cast<float*>(smem_kv + 2 * NF * 64 * 16);  // [2][2][64]: lse2, delta
-  uint32_t* sm = reinterpret_cast<uint32_t*>(sv + 2 * 2 * 64);       // [2][64]: rows' mask words
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -73,9 +74,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int kb = (int)(blockIdx.x / BHkv);  // key blocks with the most query rows first
   const int64_t kvbh = blockIdx.x - (int64_t)kb * BHkv;
   const int kw0 = kb * 128 + 32 * w;        // this wave's first key
-  // sparse: the mask word holding the workgroup's blocks, and this wave's bit in it
-  const int mword = SPARSE ? (kb * 128 / s) / 32 : 0;
-  const int mbit = SPARSE ? (kw0 / s) % 32 : 0;
   const uint16_t* kh = k + kvbh * (int64_t)L * D;
   const uint16_t* vh = v + kvbh * (int64_t)L * D;
 
@@ -102,7 +100,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int PH = PT / 2;
   u32x4 pr[PH];
   float ps = 0.f;
-  uint32_t pm = 0;
   auto load_half = [&](int it, int half) {
     const int gq = it / per_head, qc = qc0 + (it - gq * per_head);
     const int64_t bh = kvbh * G + gq;
@@ -126,14 +123,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int64_t row = bh * L + r0 + (tid & (kRows - 1));
       ps = tid < kRows ? lse[row] * kLog2e : delta[row];
     }
-    if (SPARSE && half == 0 && tid >= 2 * kRows && tid < 3 * kRows)
-      pm = mask[(bh * L + r0 + (tid - 2 * kRows)) * (int64_t)W + mword];
   };
   auto store_half = [&](int b, int half) {
 #pragma unroll
     for (int i = 0; i < PH; ++i) st[(b * NF) * 64 + tid + 256 * (half * PH + i)] = pr[i];
     if (half == 0 && tid < 2 * kRows) sv[b * 2 * kRows + tid] = ps;
-    if (SPARSE && half == 0 && tid >= 2 * kRows && tid < 3 * kRows) sm[b * kRows + tid - 2 * kRows] = pm;
   };
   // rows 32 rc .. 32 rc + 31 of the chunk in stage b against this wave's keys
   auto compute_rc = [&](int b, int r0, int rc) {
@@ -167,10 +161,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int i = 0; i < 4; ++i) {
         const int rl = 32 * rc + 16 * h + 4 * g + i;
         const float l2 = lse2[rl], de = dl[rl];
-        const bool kept = !SPARSE || ((sm[b * kRows + rl] >> mbit) & 1u);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bool live = kept && r0 + rl >= kw0 + 16 * kt + n;
+          const bool live = r0 + rl >= kw0 + 16 * kt + n;
           const float p = live ? fast_exp2(fmaf(s[h][kt][i], sl2, -l2)) : 0.f;
           pv[h][kt][i] = p;
           dsv[h][kt][i] = p * (dp[h][kt][i] - de);
@@ -363,6 +356,219 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+
+// ---------------------------------------------------------------- sparse dk, dv (gathered rows)
+// One workgroup per (key/value head, block j): wave w owns keys j*S + (S/4) w .. +S/4-1
+// (S/64 column tiles).  The rows that attend block j are the rows of the block itself
+// (causally) and the rows that kept it (from the inverted index); they are processed 64 at
+// a time for every query head of the group.  The staging builds, for each gathered 64-row
+// item, the A fragments of Q and dO (row-major rows) and of Q^T and dO^T in the kappa row
+// order (16-byte loads of the gathered rows, then an 8x8 transpose of 16-bit values across
+// 8 lanes), so the products are those of the dense kernel with gathered rows.
+template <int D, int S>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_kv_sparse_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    const int* __restrict__ off, const int* __restrict__ list, int topk, float* __restrict__ dk,
+    float* __restrict__ dv, int L, int G, int BHkv, float sl2, float scale) {
+  constexpr int NC = D / 32, NDT = D / 16, NKT = S / 64;
+  constexpr int FQ = 4 * NC, FT = 2 * NDT, NF = 2 * FQ + 2 * FT, PT = NF * 64 / 256, PH = PT / 2;
+  extern __shared__ __align__(16) unsigned char smem_ks[];
+  u32x4* st = reinterpret_cast<u32x4*>(smem_ks);                     // [2][NF][64]
+  float* sv = reinterpret_cast<float*>(smem_ks + 2 * NF * 64 * 16);  // [2][2][64]: lse2, delta
+  int* srow = reinterpret_cast<int*>(sv + 2 * 2 * 64);               // [3][64]: row ids of items it % 3
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int nb = L / S;
+  const int j = (int)(blockIdx.x / BHkv);
+  const int64_t kvbh = blockIdx.x - (int64_t)j * BHkv;
+  const int kw0 = j * S + (S / 4) * w;
+  const uint16_t* kh = k + kvbh * (int64_t)L * D;
+  const uint16_t* vh = v + kvbh * (int64_t)L * D;
+  u32x4 kf[NKT][NC], vf[NKT][NC];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      kf[kt][cc] = load_k_frag<D>(kh, kw0 + 16 * kt, cc);
+      vf[kt][cc] = load_k_frag<D>(vh, kw0 + 16 * kt, cc);
+    }
+  f32x4 dva[NKT][NDT], dka[NKT][NDT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) dva[kt][dt] = dka[kt][dt] = f32x4{0, 0, 0, 0};
+
+  // items of query head gq: S/64 items of the block's own rows, then the kept-by list
+  constexpr int OWN = S / 64;
+  auto list_count = [&](int gq) {
+    const int* o = off + (kvbh * G + gq) * (int64_t)(nb + 1);
+    return o[j + 1] - o[j];
+  };
+  int items = 0;
+  for (int gq = 0; gq < G; ++gq) items += OWN + (list_count(gq) + 63) / 64;
+  struct Item {
+    int64_t bh;
+    int ii, first, cnt;  // item index within the head, first list entry, list length
+  };
+  auto item_of = [&](int it) {
+    Item x;
+    int gq = 0;
+    for (;; ++gq) {
+      const int c = list_count(gq), ni = OWN + (c + 63) / 64;
+      if (it < ni || gq == G - 1) {
+        x.bh = kvbh * G + gq;
+        x.ii = it;
+        x.cnt = c;
+        x.first = off[(kvbh * G + gq) * (int64_t)(nb + 1) + j];
+        return x;
+      }
+      it -= ni;
+    }
+  };
+  // row of position r (0..63) of an item; -1 past the end of the list.  The row ids of
+  // item it + 2 are fetched during item it and kept in LDS (srow[(it + 2) % 3]), so the
+  // operand loads of item it + 1 read their rows from LDS, not behind a list lookup.
+  auto row_of = [&](const Item& x, int r) -> int {
+    if (x.ii < OWN) return j * S + 64 * x.ii + r;
+    const int e = (x.ii - OWN) * 64 + r;
+    return e < x.cnt ? list[x.bh * (int64_t)L * topk + x.first + e] : -1;
+  };
+
+  u32x4 pr[PH];  // staging registers for one half of the next item
+  float ps = 0.f;
+  auto load_half = [&](const Item& x, const int* rows, int half) {
+    const uint16_t* qh = q + x.bh * (int64_t)L * D;
+    const uint16_t* dh = dout + x.bh * (int64_t)L * D;
+#pragma unroll
+    for (int i = 0; i < PH; ++i) {
+      const int f = (tid >> 6) + 4 * (half * PH + i);  // uniform per wave; lane = tid & 63
+      if (f < 2 * FQ) {
+        const int ff = f < FQ ? f : f - FQ, rt = ff / NC, cc = ff % NC;
+        const int row = max(rows[16 * rt + n], 0);
+        pr[i] = load16((f < FQ ? qh : dh) + (int64_t)row * D + 32 * cc + 8 * g);
+      } else {
+        const int ff = (f - 2 * FQ) % FT, dt = ff >> 1, rc = ff & 1;
+        const int h8 = (lane >> 3) & 1, p8 = lane & 7;
+        const int row = max(rows[kappa(rc, g, p8)], 0);
+        pr[i] = transpose8x8_b16_dpp(
+            load16((f < 2 * FQ + FT ? qh : dh) + (int64_t)row * D + 16 * dt + 8 * h8));
+      }
+    }
+    if (half == 0 && tid < 128) {
+      const int row = rows[tid & 63];
+      const int64_t gr = x.bh * L + max(row, 0);
+      if (tid < 64) ps = row < 0 ? __builtin_huge_valf() : lse[gr] * kLog2e;
+      else ps = row < 0 ? 0.f : delta[gr];
+    }
+  };
+  auto store_half = [&](int b, int half) {
+#pragma unroll
+    for (int i = 0; i < PH; ++i) st[(b * NF + (tid >> 6) + 4 * (half * PH + i)) * 64 + lane] = pr[i];
+    if (half == 0 && tid < 128) sv[b * 128 + tid] = ps;
+  };
+  auto compute_rc = [&](int b, const int* rows, int rc, bool causal) {
+    const u32x4* sb = st + b * NF * 64;
+    const float* lse2 = sv + b * 128;
+    const float* dl = lse2 + 64;
+    f32x4 sa[2][NKT], dp[2][NKT];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) sa[h][kt] = dp[h][kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rt = 2 * rc + h;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const u32x4 aq = sb[(rt * NC + cc) * 64 + lane];
+        const u32x4 ad = sb[(FQ + rt * NC + cc) * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          sa[h][kt] = mfma_bf16(aq, kf[kt][cc], sa[h][kt]);
+          dp[h][kt] = mfma_bf16(ad, vf[kt][cc], dp[h][kt]);
+        }
+      }
+    }
+    float pv[2][NKT][4], dsv[2][NKT][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rl = 32 * rc + 16 * h + 4 * g + i;
+        const int row = rows[rl];
+        const float l2 = lse2[rl], de = dl[rl];
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt) {
+          const bool live = row >= 0 && (!causal || row >= kw0 + 16 * kt + n);
+          const float p = live ? fast_exp2(fmaf(sa[h][kt][i], sl2, -l2)) : 0.f;
+          pv[h][kt][i] = p;
+          dsv[h][kt][i] = p * (dp[h][kt][i] - de);
+        }
+      }
+    u32x4 pb[NKT], sbf[NKT];
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) {
+      pb[kt] = pack_p(pv[0][kt], pv[1][kt]);
+      sbf[kt] = pack_p(dsv[0][kt], dsv[1][kt]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const u32x4 aqt = sb[(2 * FQ + dt * 2 + rc) * 64 + lane];
+      const u32x4 adt = sb[(2 * FQ + FT + dt * 2 + rc) * 64 + lane];
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+        dva[kt][dt] = mfma_bf16(adt, pb[kt], dva[kt][dt]);
+        dka[kt][dt] = mfma_bf16(aqt, sbf[kt], dka[kt][dt]);
+      }
+    }
+  };
+
+  {
+    const Item x0 = item_of(0), x1 = item_of(min(1, items - 1));
+    if (tid < 64) srow[tid] = row_of(x0, tid);
+    else if (tid < 128) srow[64 + tid - 64] = row_of(x1, tid - 64);
+    __syncthreads();
+    load_half(x0, srow, 0);
+    store_half(0, 0);
+    load_half(x0, srow, 1);
+    store_half(0, 1);
+  }
+  __syncthreads();
+  for (int it = 0; it < items; ++it) {
+    const int b = it & 1;
+    const Item cur = item_of(it);
+    const Item nxt = item_of(min(it + 1, items - 1));  // unconditional (a repeat at the end)
+    int nid = -1;
+    if (tid >= 192) nid = row_of(item_of(min(it + 2, items - 1)), tid - 192);
+    const int* rows_cur = srow + (it % 3) * 64;
+    const int* rows_nxt = srow + ((it + 1) % 3) * 64;
+#pragma unroll
+    for (int rc = 0; rc < 2; ++rc) {
+      load_half(nxt, rows_nxt, rc);
+      compute_rc(b, rows_cur, rc, cur.ii < OWN);
+      store_half(b ^ 1, rc);
+    }
+    // srow[(it + 2) % 3] held item it - 1's rows, last read before the previous barrier
+    if (tid >= 192) srow[((it + 2) % 3) * 64 + tid - 192] = nid;
+    __syncthreads();
+  }
+  float* dkh = dk + kvbh * (int64_t)L * D;
+  float* dvh = dv + kvbh * (int64_t)L * D;
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    const int64_t key = kw0 + 16 * kt + n;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      f32x4* pk = reinterpret_cast<f32x4*>(dkh + key * D + 16 * dt + 4 * g);
+      f32x4* pv = reinterpret_cast<f32x4*>(dvh + key * D + 16 * dt + 4 * g);
+      *pk = *pk + dka[kt][dt] * scale;
+      *pv = *pv + dva[kt][dt];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 bool full_bwd_mfma_supported(const Dims& d) {
   return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 128 == 0;
@@ -399,27 +605,43 @@ __global__ __launch_bounds__(256) void bwd_mask_kernel(const int32_t* __restrict
 
 template <int D, bool SPARSE>
 static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
-                                    const float* lse, const float* delta, const uint32_t* mask, int W, float scale,
-                                    float* dq, float* dk, float* dv, u32x4* qt, u32x4* dot, u32x4* ktf,
-                                    hipStream_t st) {
+                                    const float* lse, const float* delta, const uint32_t* mask, int W,
+                                    const int* off, const int* list, int topk, float scale, float* dq, float* dk,
+                                    float* dv, u32x4* qt, u32x4* dot, u32x4* ktf, hipStream_t st) {
   constexpr int NC = D / 32, NDT = D / 16;
   const Dims kv = d.kv();
-  hipError_t e = frag_order_into(d, q, qt, st);
-  if (e == hipSuccess) e = frag_order_into(d, dout, dot, st);
+  hipError_t e = hipSuccess;
+  if (!SPARSE) {
+    e = frag_order_into(d, q, qt, st);
+    if (e == hipSuccess) e = frag_order_into(d, dout, dot, st);
+  }
   if (e == hipSuccess) e = frag_order_into(kv, k, ktf, st);
   if (e != hipSuccess) return e;
   const float sl2 = scale * kLog2e;
-  {
+  if constexpr (SPARSE) {  // dk, dv over the gathered rows of each block
     constexpr int NF = 2 * (4 * NC) + 2 * (2 * NDT);
-    const int lds = 2 * NF * 64 * 16 + 3 * 2 * 64 * 4;
-    auto kern = bwd_kv_mfma_kernel<D, SPARSE>;
+    const int lds = 2 * NF * 64 * 16 + 2 * 2 * 64 * 4 + 3 * 64 * 4;
+    auto kern = d.S == 64 ? bwd_kv_sparse_mfma_kernel<D, 64> : bwd_kv_sparse_mfma_kernel<D, 128>;
+    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    const int64_t grid = (int64_t)kv.bh() * d.n();
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                       static_cast<const uint16_t*>(dout), lse, delta, off, list, topk, dk, dv, d.L, d.G(),
+                       (int)kv.bh(), sl2, scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    constexpr int NF = 2 * (4 * NC) + 2 * (2 * NDT);
+    const int lds = 2 * NF * 64 * 16 + 2 * 2 * 64 * 4;
+    auto kern = bwd_kv_mfma_kernel<D>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     const int64_t grid = (int64_t)kv.bh() * (d.L / 128);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), qt, dot, lse, delta, mask, W, d.S, dk, dv, d.L, d.G(),
-                       (int)kv.bh(), sl2, scale);
+                       static_cast<const uint16_t*>(dout), qt, dot, lse, delta, dk, dv, d.L, d.G(), (int)kv.bh(),
+                       sl2, scale);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -439,9 +661,9 @@ static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k,
   return e;
 }
 
-hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const void* q, const void* k,
-                                const void* v, const void* dout, const float* lse, const float* delta, float scale,
-                                float* dq, float* dk, float* dv, hipStream_t st) {
+hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const int* off, const int* list,
+                                const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* delta, float scale, float* dq, float* dk, float* dv, hipStream_t st) {
   // fragment-order copies of Q, dO (query heads) and K (key/value heads); sparse: the
   // rows' block masks
   const size_t qbytes = (size_t)d.tokens() * d.D * 2, kbytes = (size_t)d.kv().tokens() * d.D * 2;
@@ -463,15 +685,15 @@ hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, con
   }
   if (e == hipSuccess) {
     if (idx)
-      e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, mask, W, scale, dq, dk, dv, qt, dot,
-                                                    ktf, st)
-                     : run_full_bwd_mfma<64, true>(d, q, k, v, dout, lse, delta, mask, W, scale, dq, dk, dv, qt, dot,
-                                                   ktf, st);
+      e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, mask, W, off, list, topk, scale, dq,
+                                                    dk, dv, qt, dot, ktf, st)
+                     : run_full_bwd_mfma<64, true>(d, q, k, v, dout, lse, delta, mask, W, off, list, topk, scale, dq,
+                                                   dk, dv, qt, dot, ktf, st);
     else
-      e = d.D == 128 ? run_full_bwd_mfma<128, false>(d, q, k, v, dout, lse, delta, nullptr, 0, scale, dq, dk, dv, qt,
-                                                     dot, ktf, st)
-                     : run_full_bwd_mfma<64, false>(d, q, k, v, dout, lse, delta, nullptr, 0, scale, dq, dk, dv, qt,
-                                                    dot, ktf, st);
+      e = d.D == 128 ? run_full_bwd_mfma<128, false>(d, q, k, v, dout, lse, delta, nullptr, 0, nullptr, nullptr, 1,
+                                                     scale, dq, dk, dv, qt, dot, ktf, st)
+                     : run_full_bwd_mfma<64, false>(d, q, k, v, dout, lse, delta, nullptr, 0, nullptr, nullptr, 1,
+                                                    scale, dq, dk, dv, qt, dot, ktf, st);
   }
   const hipError_t fe = workspace_free(ws, st);
   return e != hipSuccess ? e : fe;

@@ -70,12 +70,13 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* 
                              const void* o, const float* lse, const void* dout, const int32_t* idx, int topk,
                              float scale, float* dq, float* dk, float* dv, hipStream_t st);
 // MFMA backward (bf16): dq, dk, dv += ..., given delta [B*H*L]; with idx (the sparse
-// stream) the weights are masked to each row's attended blocks.
+// stream) dq uses each row's block mask and dk, dv the inverted index off/list (block ->
+// rows that kept it, as built in bwd.hip).
 bool full_bwd_mfma_supported(const Dims& d);
 bool sparse_bwd_mfma_supported(const Dims& d);
-hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const void* q, const void* k,
-                                const void* v, const void* dout, const float* lse, const float* delta, float scale,
-                                float* dq, float* dk, float* dv, hipStream_t st);
+hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const int* off, const int* list,
+                                const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* delta, float scale, float* dq, float* dk, float* dv, hipStream_t st);
 LaunchResult launch_align_loss(const Dims& d, const void* of, const void* os, float alpha, float beta, float* loss,
                                float* gf, float* gs, hipStream_t st);
 
