@@ -37,6 +37,10 @@ Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
   attend_sparse_bwd     and of the sparse stream's (no gradient through the selection):
                         SSA trains both streams (sec. 5, pp. 6-7; App. C, p. 20); the
                         formulas are the chain rule through softmax attention.
+  attention_stats       attention-pattern measurements the pages report (App. H, Table
+                        A9: sparsity; App. K.2, p. 31: entropy and distance histograms):
+                        each row's attention entropy and, per head, the attention mass
+                        by block distance in powers of two.
   align_loss            the bidirectional alignment objective of sec. 5 (pp. 6-7): a
                         sparsity term pulling the full output toward the (held) sparse
                         one and a commitment term pulling the sparse output toward the
@@ -65,7 +69,7 @@ __all__ = [
     "block_pool", "block_scores", "block_topk", "attend_full", "attend_sparse",
     "attend_sparse_gather", "dropped_mass", "align_stats", "attended_blocks",
     "attended_count", "open_block_mean", "decode_step", "attend_full_bwd",
-    "attend_sparse_bwd", "smooth_l1", "align_loss",
+    "attend_sparse_bwd", "smooth_l1", "align_loss", "attention_stats", "distance_bucket",
 ]
 
 
@@ -418,3 +422,44 @@ def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0):
     g_f = alpha * np.clip((of - os_) / beta, -1.0, 1.0) / N
     g_s = alpha * np.clip((os_ - of) / beta, -1.0, 1.0) / N
     return loss, g_f, g_s
+
+
+# ----------------------------------------------------------------------------------
+# App. H / App. K.2: attention-pattern measurements
+# ----------------------------------------------------------------------------------
+N_DIST_BUCKETS = 16
+
+
+def distance_bucket(d: int) -> int:
+    """Bucket of a block distance d = b_t - b_i >= 0: 0 for the own block, 1 + floor(log2 d)
+    otherwise, the last bucket collecting everything from 2^14 on."""
+    if d <= 0:
+        return 0
+    return min(1 + int(d).bit_length() - 1, N_DIST_BUCKETS - 1)
+
+
+def attention_stats(q, k, s: int, scale: float, idx=None):
+    """For each row t, the entropy -sum_i p_ti ln p_ti of its attention weights over A(t)
+    (all i <= t for the full stream, the kept blocks' tokens when idx is given), and per
+    (b, h) the attention mass by block distance: hist[b, h, m] = sum_t sum_{i in A(t)}
+    p_ti [distance_bucket(t // s - i // s) = m].  Returns (entropy [B,H,L], hist [B,H,16])."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, L, D = q.shape
+    R = np.arange(L)
+    causal = R[None, :] <= R[:, None]
+    bucket = np.array([[distance_bucket(t // s - i // s) for i in range(L)] for t in range(L)])
+    ent = np.zeros((B, H, L))
+    hist = np.zeros((B, H, N_DIST_BUCKETS))
+    for b in range(B):
+        for h in range(H):
+            kk = np.asarray(k[b, h], dtype=np.float64)
+            mask = causal if idx is None else _sparse_key_mask(idx[b, h], R, s, L)
+            lg = np.where(mask, scale * (q[b, h] @ kk.T), -np.inf)
+            m = lg.max(axis=1, keepdims=True)
+            e = np.exp(lg - m)
+            p = e / e.sum(axis=1, keepdims=True)
+            logp = np.where(mask, lg - m - np.log(e.sum(axis=1, keepdims=True)), 0.0)
+            ent[b, h] = -(p * logp).sum(axis=1)
+            for m_ in range(N_DIST_BUCKETS):
+                hist[b, h, m_] = p[bucket == m_].sum()
+    return ent, hist

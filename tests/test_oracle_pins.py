@@ -689,3 +689,49 @@ def test_bwd_planted_mistakes_are_caught(monkeypatch):
                 except AssertionError:
                     failed += 1
             assert failed > 0, f"planted slip {fake.__name__} went unnoticed"
+
+
+# ----------------------------------------------------------------------------------
+# attention-pattern measurements
+# ----------------------------------------------------------------------------------
+def test_distance_bucket_values():
+    assert [O.distance_bucket(d) for d in (0, 1, 2, 3, 4, 7, 8, 1023, 1024)] == [0, 1, 2, 2, 3, 3, 4, 10, 11]
+    assert O.distance_bucket(1 << 20) == O.N_DIST_BUCKETS - 1
+
+
+def test_attention_stats_q_zero_closed_form():
+    """q = 0: weights uniform over A(t), so entropy = log |A(t)| and the histogram is the
+    count of attended keys per bucket divided by |A(t)|, summed over rows; every row's
+    mass is 1, so each head's histogram sums to L."""
+    B, H, L, D, s, topk = 1, 2, 96, 4, 8, 3
+    k = _rand((B, H, L, D), 101)
+    q = np.zeros((B, H, L, D))
+    idx = O.block_topk(q, O.block_pool(k, s), s, topk)
+    for sparse in (False, True):
+        ent, hist = O.attention_stats(q, k, s, 0.5, idx if sparse else None)
+        ref = np.zeros(O.N_DIST_BUCKETS)
+        for t in range(L):
+            blocks = O.attended_blocks(idx[0, 0, t], t, s) if sparse else list(range(t // s + 1))
+            keys = [i for j in blocks for i in range(j * s, min(j * s + s, t + 1))]
+            assert math.isclose(ent[0, 0, t], math.log(len(keys)), rel_tol=1e-12, abs_tol=1e-15)
+            for i in keys:
+                ref[O.distance_bucket(t // s - i // s)] += 1.0 / len(keys)
+        np.testing.assert_allclose(hist[0, 0], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(hist.sum(axis=-1), L, rtol=1e-12)
+
+
+def test_attention_stats_brute_force():
+    """Entropy and histogram against a per-row loop over the forward oracle's weights
+    (recovered from o with one-hot values: v = identity picks each weight)."""
+    B, H, L, s, scale = 1, 1, 20, 4, 0.3
+    q, k = _rand((B, H, L, L), 111), _rand((B, H, L, L), 112)   # head dim = L for the one-hot v
+    v = np.eye(L)[None, None]            # o_t = (p_t0, ..., p_t,L-1)
+    o, _ = O.attend_full(q, k, v, scale)
+    ent, hist = O.attention_stats(q, k, s, scale)
+    ref_h = np.zeros(O.N_DIST_BUCKETS)
+    for t in range(L):
+        p = o[0, 0, t, :t + 1]
+        assert math.isclose(ent[0, 0, t], float(-(p * np.log(p)).sum()), rel_tol=1e-12)
+        for i in range(t + 1):
+            ref_h[O.distance_bucket(t // s - i // s)] += p[i]
+    np.testing.assert_allclose(hist[0, 0], ref_h, rtol=1e-12, atol=1e-14)
