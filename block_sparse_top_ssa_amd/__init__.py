@@ -40,7 +40,7 @@ from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
            "decode_append", "decode_sparse_fwd", "decode_full_fwd",
-           "full_attn_bwd", "sparse_attn_bwd", "align_loss",
+           "full_attn_bwd", "sparse_attn_bwd", "align_loss", "attn_stats",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
 
 
@@ -276,3 +276,18 @@ def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0, want_grads: bo
     check(load().ssa_align_loss(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), ctypes.c_float(alpha),
                                 ctypes.c_float(beta), _ptr(loss), _ptr(gf), _ptr(gs), _stream(o_full)))
     return loss, gf, gs
+
+
+# ---------------------------------------------------------------- measurements
+def attn_stats(q, k, lse, block: int, idx=None, scale: float | None = None, want_entropy: bool = True,
+               want_hist: bool = True):
+    """Row entropy [B, H, L] and attention mass by block distance [B, H, 16] of the full
+    stream (idx None) or the sparse stream (its idx), given that stream's lse."""
+    d = _dims(q, block, k.shape[1] if k.dim() == 4 else 0)
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
+    hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
+    topk = int(idx.shape[3]) if idx is not None else 0
+    check(load().ssa_attn_stats(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(lse), _ptr(idx), topk,
+                                ctypes.c_float(scale), _ptr(ent), _ptr(hist), _stream(q)))
+    return ent, hist

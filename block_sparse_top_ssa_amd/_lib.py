@@ -39,6 +39,7 @@ PROTOTYPES = {
     "ssa_full_attn_bwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP]),
     "ssa_sparse_attn_bwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),
     "ssa_align_loss": (_I32, [_DP, _VP, _VP, _F, _F, _VP, _VP, _VP, _VP]),
+    "ssa_attn_stats": (_I32, [_DP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP]),
     "ssa_status_str": (ctypes.c_char_p, [_I32]),
     "ssa_last_error": (ctypes.c_char_p, []),
     "ssa_abi_version": (_I32, []),

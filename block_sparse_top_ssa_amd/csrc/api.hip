@@ -277,6 +277,25 @@ ssa_status ssa_sparse_attn_bwd(const ssa_dims* dims, const void* q, const void* 
   return attn_bwd("ssa_sparse_attn_bwd", true, dims, q, k, v, o, lse, dout, idx, topk, scale, dq, dk, dv, stream);
 }
 
+ssa_status ssa_attn_stats(const ssa_dims* dims, const void* q, const void* k, const float* lse, const int32_t* idx,
+                          int32_t topk, float scale, float* entropy, float* dist_hist, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(lse, "lse", 4));
+  if (!entropy && !dist_hist) return fail(SSA_ERR_NULL, "ssa_attn_stats needs entropy or dist_hist");
+  SSA_TRY(check_opt_ptr(entropy, "entropy", 4));
+  SSA_TRY(check_opt_ptr(dist_hist, "dist_hist", 4));
+  SSA_TRY(check_opt_ptr(idx, "idx", 4));
+  if (idx && (topk < 1 || topk > d.n())) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  return finish(ssa::launch_attn_stats(d, use_mfma(), q, k, lse, idx, idx ? topk : 1, scale, entropy, dist_hist,
+                                       (hipStream_t)stream),
+                "ssa_attn_stats");
+}
+
 ssa_status ssa_align_loss(const ssa_dims* dims, const void* o_full, const void* o_sparse, float alpha, float beta,
                           float* loss, float* grad_full, float* grad_sparse, void* stream) {
   ssa::Dims d;

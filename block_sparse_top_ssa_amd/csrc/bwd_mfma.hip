@@ -603,6 +603,14 @@ __global__ __launch_bounds__(256) void bwd_mask_kernel(const int32_t* __restrict
   mask[i] = m;
 }
 
+hipError_t build_block_mask(const Dims& d, const int32_t* idx, int topk, uint32_t* mask, hipStream_t st) {
+  const int W = (d.n() + 31) / 32;
+  const int64_t n = d.tokens() * W;
+  hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, topk, mask, d.tokens(),
+                     W, d.L, d.S);
+  return hipGetLastError();
+}
+
 template <int D, bool SPARSE>
 static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
                                     const float* lse, const float* delta, const uint32_t* mask, int W,
@@ -677,12 +685,7 @@ hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, con
   u32x4* dot = reinterpret_cast<u32x4*>(base + qbytes);
   u32x4* ktf = reinterpret_cast<u32x4*>(base + 2 * qbytes);
   uint32_t* mask = reinterpret_cast<uint32_t*>(base + 2 * qbytes + kbytes);
-  if (idx) {
-    const int64_t n = d.tokens() * W;
-    hipLaunchKernelGGL(bwd_mask_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, idx, topk, mask,
-                       d.tokens(), W, d.L, d.S);
-    e = hipGetLastError();
-  }
+  if (idx) e = build_block_mask(d, idx, topk, mask, st);
   if (e == hipSuccess) {
     if (idx)
       e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, mask, W, off, list, topk, scale, dq,

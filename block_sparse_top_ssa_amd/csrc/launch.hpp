@@ -77,6 +77,14 @@ bool sparse_bwd_mfma_supported(const Dims& d);
 hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const int* off, const int* list,
                                 const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* delta, float scale, float* dq, float* dk, float* dv, hipStream_t st);
+// Per-row bit masks of the blocks the sparse stream attends (word j / 32, bit j % 32 of
+// row t: a valid kept entry of idx, or the own block); [B*H*L][ceil(n/32)] words.
+hipError_t build_block_mask(const Dims& d, const int32_t* idx, int topk, uint32_t* mask, hipStream_t st);
+
+// Attention-pattern measurements: row entropy and attention mass by block distance.
+LaunchResult launch_attn_stats(const Dims& d, bool mfma, const void* q, const void* k, const float* lse,
+                               const int32_t* idx, int topk, float scale, float* entropy, float* hist,
+                               hipStream_t st);
 LaunchResult launch_align_loss(const Dims& d, const void* of, const void* os, float alpha, float beta, float* loss,
                                float* gf, float* gs, hipStream_t st);
 

@@ -22,8 +22,9 @@
  *               buffer it passes.  The library keeps no pointer to them after a call
  *               returns and writes nothing outside the outputs named by a call.  Four
  *               calls allocate: ssa_sparse_attn_fwd on bf16, ssa_full_attn_fwd on bf16
- *               with o given, the two decoding forward calls, the two backward calls
- *               and ssa_align_loss take a transient workspace (see ssa_sparse_attn_fwd).
+ *               with o given, the two decoding forward calls, the two backward calls,
+ *               ssa_attn_stats and ssa_align_loss take a transient workspace (see
+ *               ssa_sparse_attn_fwd).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 4 /* 2: ssa_dims.Hkv; 3: decoding calls; 4: backward and alignment loss */
+#define SSA_ABI_VERSION 5 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats */
 
 typedef int32_t ssa_status;
 enum {
@@ -258,6 +259,29 @@ ssa_status ssa_full_attn_bwd(const ssa_dims* dims, const void* q, const void* k,
 ssa_status ssa_sparse_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, const int32_t* idx, int32_t topk, float scale,
                                float* dq, float* dk, float* dv, void* stream);
+
+/*
+ * ssa_attn_stats -- attention-pattern measurements of one stream.
+ *   The pages compare methods by attention sparsity and entropy (App. H, Table A9) and by
+ *   histograms of attention distance (App. K.2, p. 31).  For the full stream (idx NULL)
+ *   or the sparse stream (idx as given to ssa_sparse_attn_fwd) and that stream's lse:
+ *   q          [B,H,L,D] (dtype)          in
+ *   k          [B,Hkv,L,D] (dtype)        in
+ *   lse        [B,H,L] float32            in: the stream's log-sum-exp (from its forward call)
+ *   idx, topk  as for ssa_sparse_attn_fwd, or idx NULL for the full stream
+ *   entropy    [B,H,L] float32 or NULL    out: -sum_i p_ti ln p_ti over the stream's keys
+ *   dist_hist  [B,H,16] float32 or NULL   out: sum_t sum_i p_ti over keys whose block distance
+ *              b_t - b_i falls in bucket m: 0 for the own block, 1 + floor(log2 d) for
+ *              d >= 1, bucket 15 also collecting everything beyond; each head's buckets sum
+ *              to L (summed in a fixed order)
+ *   At least one output must be given.  The sparse stream's dropped mass and the
+ *   divergence KL(p_sparse || p_full) = lse_full - lse_sparse follow from the two
+ *   log-sum-exps (ssa_align_stats gives the first).  Workspace: B*H*(L/128 or L/4)*64
+ *   bytes of partial sums, plus the sparse rows' block masks (B*H*L*ceil(n/32)*4 bytes),
+ *   from the pool.
+ */
+ssa_status ssa_attn_stats(const ssa_dims* dims, const void* q, const void* k, const float* lse, const int32_t* idx,
+                          int32_t topk, float scale, float* entropy, float* dist_hist, void* stream);
 
 /*
  * ssa_align_loss -- the bidirectional alignment objective of sec. 5 (pp. 6-7): a

@@ -131,6 +131,15 @@ def test_training_argument_checks(libssa):
     assert libssa.ssa_align_loss(ctypes.byref(d), F, F, float("inf"), 1.0, F, None, None, None) == 4
 
 
+def test_stats_argument_checks(libssa):
+    d = _dims()
+    F = FAKE
+    assert libssa.ssa_attn_stats(ctypes.byref(d), F, F, F, None, 0, 0.1, None, None, None) == 1
+    assert libssa.ssa_attn_stats(ctypes.byref(d), F, None, F, None, 0, 0.1, F, None, None) == 1
+    assert libssa.ssa_attn_stats(ctypes.byref(d), F, F, F, F, 9, 0.1, F, None, None) == 2
+    assert libssa.ssa_attn_stats(ctypes.byref(d), F, F, F, None, 0, -0.1, F, None, None) == 4
+
+
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path; a GPU is present")
 def test_align_ignores_block(libssa):
     """ssa_align_stats does not use the block partition, so L = 1 (one decoding step) and
