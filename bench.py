@@ -540,6 +540,18 @@ def main_train(args):
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
     per = {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, nm in enumerate(names)}
+    # the attention-pattern measurements of both streams, timed apart from the step
+    st_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    st_ms = {"stats_full": [], "stats_sparse": []}
+    for _ in range(3):
+        st_ev[0].record()
+        ssa.attn_stats(q, kk, lse_f, s, scale=scale)
+        st_ev[1].record()
+        ssa.attn_stats(q, kk, lse_s, s, idx=idx, scale=scale)
+        st_ev[2].record()
+        torch.cuda.synchronize()
+        st_ms["stats_full"].append(st_ev[0].elapsed_time(st_ev[1]))
+        st_ms["stats_sparse"].append(st_ev[1].elapsed_time(st_ev[2]))
     pairs_full = B * H * (L * (L + 1) // 2)
     pairs_sparse = B * H * attended_total(L, s, k)
     flops = {"full_bwd": 10 * D * pairs_full, "sparse_bwd": 10 * D * pairs_sparse}
@@ -549,6 +561,11 @@ def main_train(args):
         kernels[nm].update({"tflops": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                             "algorithmic_flops": f})
     kernels["loss"]["note"] = "alignment loss + upstream gradient composition (torch add/cast) + zeroing dq, dk, dv"
+    for nm, pairs in (("stats_full", pairs_full), ("stats_sparse", pairs_sparse)):
+        ms = float(np.median(st_ms[nm]))
+        kernels[nm] = {"ms": round(ms, 4), "tflops": round(2 * D * pairs / (ms * 1e-3) / 1e12, 2),
+                       "note": "entropy + distance histogram (ssa_attn_stats), not part of the step; "
+                               "2*D FLOP per attended pair"}
     tf_full = flops["full_bwd"] / (per["full_bwd"] * 1e-3) / 1e12
     out = {
         "metric": "training step tokens/s (forward, alignment loss, backward of both streams) at L=32K",
