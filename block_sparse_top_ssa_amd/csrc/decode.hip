@@ -15,6 +15,7 @@
 #include <cmath>
 
 #include "launch.hpp"
+#include "mfma.hpp"
 #include "pool.hpp"
 
 namespace ssa {
@@ -363,6 +364,141 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const int32_t* __restr
     pp[2 + t] = wt[0] * red[0][2 + t] + wt[1] * red[1][2 + t] + wt[2] * red[2][2 + t] + wt[3] * red[3][2 + t];
 }
 
+
+// ---------------------------------------------------------------- dense stream, grouped heads
+// With G query heads per key/value head, the dense stream's G rows of one sequence read the
+// same keys and values, so they are one small matrix product on the matrix cores: the
+// group's heads are the N (column) dimension, S^T (64 keys x 16 heads) = K Q^T, an online
+// softmax per column, O^T (D x 16 heads) += V^T P^T with V^T fragments formed from the
+// cache rows on the fly (8x8 transposes of 16-bit values across 8 lanes, the kappa key
+// order in which the S^T layout is the B operand).  Each key/value row is read once per
+// group instead of once per query head.  Up to 16 heads per pass; columns past G hold no
+// query.  Split partials as in decode_attn_kernel (same layout, merged by the same
+// combine kernel).
+template <int D, bool WANT_O>
+__global__ __launch_bounds__(256) void decode_full_group_kernel(const int32_t* __restrict__ pos,
+                                                                const uint16_t* __restrict__ q,
+                                                                const uint16_t* __restrict__ kc,
+                                                                const uint16_t* __restrict__ vc,
+                                                                float* __restrict__ part, int H, int G, int L,
+                                                                int cps, float sl2) {
+  constexpr int NC = D / 32, NDT = D / 16;
+  __shared__ float red[4][16][D + 2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int split = blockIdx.x, nsplit = gridDim.x;
+  const int nhg = (G + 15) / 16;
+  const int64_t kvbh = blockIdx.y / nhg;
+  const int hg = (int)(blockIdx.y - kvbh * nhg);
+  const int Hkv = H / G;
+  const int b = (int)(kvbh / Hkv), kvh = (int)(kvbh - (int64_t)b * Hkv);
+  const int p = cache_pos(pos, b, L);
+  if (p < 0) return;
+  const int nch = p / kChunk + 1;
+  const int c0 = split * cps, c1 = min(nch, c0 + cps);
+  if (c0 >= nch) return;
+  const int hl = 16 * hg + n;  // this lane's head within the group (column n)
+  const bool hv = hl < G;
+  const int64_t bhq = (int64_t)b * H + kvh * G + (hv ? hl : 0);
+  const uint16_t* kh = kc + kvbh * (int64_t)L * D;
+  const uint16_t* vh = vc + kvbh * (int64_t)L * D;
+  u32x4 qf[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) qf[cc] = hv ? load_q_frag<D>(q + bhq * D, cc) : u32x4{0, 0, 0, 0};
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0, 0, 0, 0};
+  for (int ch = c0 + wv; ch < c1; ch += 4) {
+    const int key0 = ch * kChunk;
+    u32x4 kf[4][NC], vt[WANT_O ? NDT : 1][2];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, key0 + 16 * kt, cc);
+    if (WANT_O) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) vt[WANT_O ? dt : 0][c2] = load_v_raw<D>(vh, key0, dt, c2);
+    }
+    f32x4 sa[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sa[kt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) sa[kt] = mfma_bf16(kf[kt][cc], qf[cc], sa[kt]);
+    }
+    // element i of sa[kt]: key key0 + 16 kt + 4 g + i, head column n
+    float sc[4][4], cmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sc[kt][i] = key0 + 16 * kt + 4 * g + i <= p ? sa[kt][i] * sl2 : -INFINITY;
+        cmax = fmaxf(cmax, sc[kt][i]);
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float mnew = fmaxf(mrun, cmax);  // finite: the chunk's first key is at or before p
+    const float alpha = mrun == -INFINITY ? 0.f : fast_exp2(mrun - mnew);
+    float pr[4][4], ps = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[kt][i] = fast_exp2(sc[kt][i] - mnew);
+        ps += pr[kt][i];
+      }
+    lrun = lrun * alpha + ps;
+    if (WANT_O) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] = oacc[dt] * alpha;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const u32x4 pb = pack_p(pr[2 * c2], pr[2 * c2 + 1]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          oacc[dt] = mfma_bf16(transpose8x8_b16_dpp(vt[WANT_O ? dt : 0][c2]), pb, oacc[dt]);
+      }
+    }
+    mrun = mnew;
+  }
+  lrun += __shfl_xor(lrun, 16);
+  lrun += __shfl_xor(lrun, 32);
+  if (g == 0) {
+    red[wv][n][0] = mrun;
+    red[wv][n][1] = lrun;
+  }
+  if (WANT_O) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wv][n][2 + 16 * dt + 4 * g + i] = oacc[dt][i];
+  }
+  __syncthreads();
+  // merge the four waves per head; part[(query head, split)] = {max, sum, o}
+  for (int e = threadIdx.x; e < 16 * (D + 2); e += 256) {
+    const int hn = e / (D + 2), c = e - hn * (D + 2);
+    if (16 * hg + hn >= G || (!WANT_O && c >= 2)) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, red[w][hn][0]);
+    float x = 0.f;
+    if (c == 0) {
+      x = M;
+    } else {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = red[w][hn][0];
+        if (mw != -INFINITY) x += fast_exp2(mw - M) * red[w][hn][c];
+      }
+    }
+    const int64_t bq = (int64_t)b * H + kvh * G + 16 * hg + hn;
+    part[(bq * nsplit + split) * (int64_t)(D + 2) + c] = x;
+  }
+}
+
 // ---------------------------------------------------------------- combine
 // One workgroup per (b, h): merges the row's split partials, o = sum_x 2^(m_x - M) o_x /
 // sum_x 2^(m_x - M) l_x, lse = ln 2 * (M + log2 l), with M the largest split maximum (the
@@ -463,6 +599,21 @@ hipError_t run_attn(const Dims& d, const int32_t* pos, const void* q, const void
   return hipGetLastError();
 }
 
+template <int D, bool WANT_O>
+hipError_t run_group(const Dims& d, const int32_t* pos, const void* q, const void* kc, const void* vc, float scale,
+                     void* o, float* lse, float* part, hipStream_t st) {
+  const int ns = splits(d, false, 1);
+  const int nhg = (d.G() + 15) / 16;
+  hipLaunchKernelGGL((decode_full_group_kernel<D, WANT_O>), dim3((unsigned)ns, (unsigned)(d.kv().bh() * nhg)),
+                     dim3(256), 0, st, pos, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                     static_cast<const uint16_t*>(vc), part, d.H, d.G(), d.L, kFullCps, scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D, false, WANT_O>), dim3((unsigned)d.bh()), dim3(256), 0, st,
+                     pos, part, static_cast<uint16_t*>(o), lse, d.H, d.L, d.S, 1, kFullCps, ns);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t run_topk(const Dims& d, const int32_t* pos, const void* q, const float* km, int topk, int32_t* idx,
                     hipStream_t st) {
@@ -527,12 +678,19 @@ LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q
   r.err = workspace_alloc((size_t)d.bh() * ns * (d.D + 2) * sizeof(float), &ws, st);
   if (r.err != hipSuccess) return r;
   float* part = static_cast<float*>(ws);
-  r.err = dispatch(d, [&](auto t, auto dd) {
-    using T = decltype(t);
-    constexpr int D = decltype(dd)::value;
-    return o ? run_attn<T, D, false, true>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st)
-             : run_attn<T, D, false, false>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st);
-  });
+  if (d.dtype == 1 && d.G() > 1) {  // grouped heads: one pass over K/V per group on the matrix cores
+    r.err = d.D == 128 ? (o ? run_group<128, true>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st)
+                            : run_group<128, false>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st))
+                       : (o ? run_group<64, true>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st)
+                            : run_group<64, false>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st));
+  } else {
+    r.err = dispatch(d, [&](auto t, auto dd) {
+      using T = decltype(t);
+      constexpr int D = decltype(dd)::value;
+      return o ? run_attn<T, D, false, true>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st)
+               : run_attn<T, D, false, false>(d, pos, q, k_cache, v_cache, nullptr, 1, scale, o, lse, part, st);
+    });
+  }
   const hipError_t fe = workspace_free(ws, st);
   if (r.err == hipSuccess) r.err = fe;
   return r;

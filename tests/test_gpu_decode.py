@@ -121,6 +121,17 @@ def test_decode_step(dtype, D, s, Hkv, topk):
     run_and_check(inp.k, inp.v, q, pos, s, topk, dtype, Hkv, tag=f"step n={n}")
 
 
+@pytest.mark.parametrize("H,Hkv", [(32, 2), (32, 1), (8, 8), (12, 4)])
+def test_decode_grouped_heads(H, Hkv):
+    """Many query heads per key/value head (the dense stream then runs on the matrix cores,
+    16 heads per pass: G = 16, 32 (two passes), 1 and 3)."""
+    B, L, D, s, topk = 2, 2048, 128, 64, 6
+    inp = W.make_qkv(B, Hkv, L, D, s, W.BF16, "sink", seed=2900 + H + Hkv, hkv=Hkv)
+    q = W.make_qkv(B, H, 1, D, 1, W.BF16, "none", seed=2950 + H).q[:, :, 0]
+    pos = np.array([1500, 777], dtype=np.int32)
+    run_and_check(inp.k, inp.v, q, pos, s, topk, W.BF16, Hkv, tag=f"G={H // Hkv}")
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_decode_all_blocks_equals_full(dtype):
     """topk = n keeps every earlier block: the sparse stream equals the full stream."""

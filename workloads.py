@@ -259,6 +259,9 @@ DECODE_WORKLOADS = {
     w.name: w for w in [
         # bf16_L32768_sink's head shape, four sequences decoding at once.
         DecodeWorkload("bf16_L32768_decode", 4, 32, 32768, 128, 64, 32, BF16, "sink", 1007),
+        # the same with two key/value heads (the paper's model, App. C): 16 query heads per
+        # cached key/value head.
+        DecodeWorkload("bf16_L32768_decode_gqa2", 4, 32, 32768, 128, 64, 32, BF16, "sink", 1008, Hkv=2),
     ]
 }
 
