@@ -578,6 +578,7 @@ hipError_t run_append(const Dims& d, const int32_t* pos, const void* kn, const v
 // Splits of a row: sparse rows have at most topk * s / 64 chunks, full rows L / 64.
 constexpr int kSparseCps = 4;  // one chunk per wave
 constexpr int kFullCps = 16;   // four chunks per wave (fewer split results to merge)
+constexpr int kGroupCps = 16;  // grouped heads (4 measured slower: more partials to merge)
 int max_chunks(const Dims& d, bool sparse, int topk) { return sparse ? topk * (d.S / kChunk) : d.L / kChunk; }
 int splits(const Dims& d, bool sparse, int topk) {
   const int cps = sparse ? kSparseCps : kFullCps;
@@ -602,15 +603,15 @@ hipError_t run_attn(const Dims& d, const int32_t* pos, const void* q, const void
 template <int D, bool WANT_O>
 hipError_t run_group(const Dims& d, const int32_t* pos, const void* q, const void* kc, const void* vc, float scale,
                      void* o, float* lse, float* part, hipStream_t st) {
-  const int ns = splits(d, false, 1);
+  const int ns = (max_chunks(d, false, 1) + kGroupCps - 1) / kGroupCps;
   const int nhg = (d.G() + 15) / 16;
   hipLaunchKernelGGL((decode_full_group_kernel<D, WANT_O>), dim3((unsigned)ns, (unsigned)(d.kv().bh() * nhg)),
                      dim3(256), 0, st, pos, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), part, d.H, d.G(), d.L, kFullCps, scale * kLog2e);
+                     static_cast<const uint16_t*>(vc), part, d.H, d.G(), d.L, kGroupCps, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<uint16_t, D, false, WANT_O>), dim3((unsigned)d.bh()), dim3(256), 0, st,
-                     pos, part, static_cast<uint16_t*>(o), lse, d.H, d.L, d.S, 1, kFullCps, ns);
+                     pos, part, static_cast<uint16_t*>(o), lse, d.H, d.L, d.S, 1, kGroupCps, ns);
   return hipGetLastError();
 }
 
@@ -673,12 +674,13 @@ LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void*
 LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
                                 const void* v_cache, float scale, void* o, float* lse, hipStream_t st) {
   LaunchResult r;
-  const int ns = splits(d, false, 1);
+  const bool group = d.dtype == 1 && d.G() > 1;
+  const int ns = group ? (max_chunks(d, false, 1) + kGroupCps - 1) / kGroupCps : splits(d, false, 1);
   void* ws = nullptr;
   r.err = workspace_alloc((size_t)d.bh() * ns * (d.D + 2) * sizeof(float), &ws, st);
   if (r.err != hipSuccess) return r;
   float* part = static_cast<float*>(ws);
-  if (d.dtype == 1 && d.G() > 1) {  // grouped heads: one pass over K/V per group on the matrix cores
+  if (group) {  // grouped heads: one pass over K/V per group on the matrix cores
     r.err = d.D == 128 ? (o ? run_group<128, true>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st)
                             : run_group<128, false>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st))
                        : (o ? run_group<64, true>(d, pos, q, k_cache, v_cache, scale, o, lse, part, st)
