@@ -496,7 +496,7 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* 
       hipLaunchKernelGGL(bwd_index_fill_kernel, dim3(g), dim3(256), 0, st, idx, topk, cnt, list, rows, d.L, d.S, n);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (mfma && sparse_bwd_mfma_supported(d))
+    if (mfma && sparse_bwd_mfma_supported(d, topk))
       return launch_full_bwd_mfma(d, idx, topk, off, list, q, k, v, dout, lse, delta, scale, dq, dk, dv, st);
     return run_attn_bwd<T, D, true>(d, q, k, v, dout, lse, delta, idx, topk, off, list, scale, dq, dk, dv, st);
   });

@@ -29,11 +29,8 @@
 //
 //  The sparse stream: dk, dv visit only the rows that attend each block -- a workgroup
 //  per (key/value head, block) walks the block's own rows (causally) and the rows that
-//  kept it (an inverted index block -> rows), gathered 64 at a time; dq runs the
-//  query-stationary kernel with a per-row bit mask of attended blocks (kept blocks and
-//  the own block, built from idx), a weight whose key's block is not in the mask being
-//  zero.  That does the dense amount of work for dq: the kept blocks of 32 neighbouring
-//  rows cover most earlier blocks, so a row tile skips few chunks.
+//  kept it (an inverted index block -> rows), gathered 64 at a time; dq visits, for a
+//  tile of rows, each attended block once with the rows that attend it (bwd_dq_gather.hip).
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -224,12 +221,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------- dq
-template <int D, bool SPARSE>
+template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_q_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const u32x4* __restrict__ kt_frag, const float* __restrict__ lse,
-    const float* __restrict__ delta, const uint32_t* __restrict__ mask, int W, int s, float* __restrict__ dq, int L,
-    int G, int BH, float sl2, float scale) {
+    const float* __restrict__ delta, float* __restrict__ dq, int L, int G, int BH, float sl2, float scale) {
   constexpr int NC = D / 32, NDT = D / 16;
   constexpr int FK = 4 * NC;          // A fragments of K (and of V) per 64-key chunk
   constexpr int FT = 2 * NDT;         // fragment-order K^T fragments per chunk
@@ -270,15 +266,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int dt = 0; dt < NDT; ++dt) dqa[nt][dt] = f32x4{0, 0, 0, 0};
 
   const int items = (qb * 128 + 127) / 64 + 1;  // key chunks 0 .. the block's last row's chunk
-  // sparse: whether each of this lane's two rows attends the block of the current chunk
-  // (its mask bit), fetched one chunk ahead
-  auto row_keeps = [&](int nt, int c) -> bool {
-    if (!SPARSE) return true;
-    const int j = c * 64 / s;
-    const uint32_t word = mask[(bh * L + rw0 + 16 * nt + n) * (int64_t)W + j / 32];
-    return (word >> (j % 32)) & 1u;
-  };
-  bool keep_cur[2] = {row_keeps(0, 0), row_keeps(1, 0)};
   u32x4 pr[PT];
   auto load_item = [&](int c) {
 #pragma unroll
@@ -302,7 +289,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int c = 0; c < items; ++c) {
     const int b = c & 1;
     load_item(min(c + 1, items - 1));
-    const bool keep_next[2] = {row_keeps(0, min(c + 1, items - 1)), row_keeps(1, min(c + 1, items - 1))};
     const u32x4* sb = st + b * NF * 64;
     const int k0 = c * 64;
     if (k0 <= rw0 + 31) {  // some key of the chunk is at or before some row of this wave
@@ -325,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const bool live = keep_cur[nt] && k0 + 16 * kt + 4 * g + i <= row;
+            const bool live = k0 + 16 * kt + 4 * g + i <= row;
             const float p = live ? fast_exp2(fmaf(s[kt][i], sl2, -l2[nt])) : 0.f;
             dsv[kt][i] = p * (dp[kt][i] - de[nt]);
           }
@@ -339,8 +325,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
     store_item(b ^ 1);
-    keep_cur[0] = keep_next[0];
-    keep_cur[1] = keep_next[1];
     __syncthreads();
   }
   // dqa[nt][dt] element i: d = 16 dt + 4 g + i, row rw0 + 16 nt + n
@@ -574,7 +558,9 @@ bool full_bwd_mfma_supported(const Dims& d) {
   return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 128 == 0;
 }
 
-bool sparse_bwd_mfma_supported(const Dims& d) { return full_bwd_mfma_supported(d) && d.n() <= 4096; }
+bool sparse_bwd_mfma_supported(const Dims& d, int topk) {
+  return full_bwd_mfma_supported(d) && dq_gather_supported(d, topk);
+}
 
 // Bit j of word j / 32 of row t's mask: the sparse stream attends block j (a valid kept
 // entry of idx, or the own block).  One thread per (row, word).
@@ -613,9 +599,9 @@ hipError_t build_block_mask(const Dims& d, const int32_t* idx, int topk, uint32_
 
 template <int D, bool SPARSE>
 static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
-                                    const float* lse, const float* delta, const uint32_t* mask, int W,
-                                    const int* off, const int* list, int topk, float scale, float* dq, float* dk,
-                                    float* dv, u32x4* qt, u32x4* dot, u32x4* ktf, hipStream_t st) {
+                                    const float* lse, const float* delta, const int32_t* idx, const int* off,
+                                    const int* list, int topk, float scale, float* dq, float* dk, float* dv,
+                                    u32x4* qt, u32x4* dot, u32x4* ktf, hipStream_t st) {
   constexpr int NC = D / 32, NDT = D / 16;
   const Dims kv = d.kv();
   hipError_t e = hipSuccess;
@@ -653,17 +639,18 @@ static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k,
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if constexpr (SPARSE) {
+    e = launch_dq_gather(d, q, k, v, dout, ktf, lse, delta, idx, topk, scale, dq, st);
+  } else {
     constexpr int NF = 2 * (4 * NC) + 2 * NDT;
     const int lds = 2 * NF * 64 * 16;
-    auto kern = bwd_q_mfma_kernel<D, SPARSE>;
+    auto kern = bwd_q_mfma_kernel<D>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     const int64_t grid = d.bh() * (d.L / 128);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                       static_cast<const uint16_t*>(dout), ktf, lse, delta, mask, W, d.S, dq, d.L, d.G(), (int)d.bh(),
-                       sl2, scale);
+                       static_cast<const uint16_t*>(dout), ktf, lse, delta, dq, d.L, d.G(), (int)d.bh(), sl2, scale);
     e = hipGetLastError();
   }
   return e;
@@ -672,32 +659,25 @@ static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k,
 hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const int* off, const int* list,
                                 const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* delta, float scale, float* dq, float* dk, float* dv, hipStream_t st) {
-  // fragment-order copies of Q, dO (query heads) and K (key/value heads); sparse: the
-  // rows' block masks
-  const size_t qbytes = (size_t)d.tokens() * d.D * 2, kbytes = (size_t)d.kv().tokens() * d.D * 2;
-  const int W = (d.n() + 31) / 32;
-  const size_t mbytes = idx ? (size_t)d.tokens() * W * 4 : 0;
+  // fragment-order copies of K (key/value heads) and, for the dense stream, of Q and dO
+  const size_t qbytes = idx ? 0 : (size_t)d.tokens() * d.D * 2, kbytes = (size_t)d.kv().tokens() * d.D * 2;
   void* ws = nullptr;
-  hipError_t e = workspace_alloc(2 * qbytes + kbytes + mbytes, &ws, st);
+  hipError_t e = workspace_alloc(2 * qbytes + kbytes, &ws, st);
   if (e != hipSuccess) return e;
   char* base = static_cast<char*>(ws);
   u32x4* qt = reinterpret_cast<u32x4*>(base);
   u32x4* dot = reinterpret_cast<u32x4*>(base + qbytes);
   u32x4* ktf = reinterpret_cast<u32x4*>(base + 2 * qbytes);
-  uint32_t* mask = reinterpret_cast<uint32_t*>(base + 2 * qbytes + kbytes);
-  if (idx) e = build_block_mask(d, idx, topk, mask, st);
-  if (e == hipSuccess) {
-    if (idx)
-      e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, mask, W, off, list, topk, scale, dq,
-                                                    dk, dv, qt, dot, ktf, st)
-                     : run_full_bwd_mfma<64, true>(d, q, k, v, dout, lse, delta, mask, W, off, list, topk, scale, dq,
-                                                   dk, dv, qt, dot, ktf, st);
-    else
-      e = d.D == 128 ? run_full_bwd_mfma<128, false>(d, q, k, v, dout, lse, delta, nullptr, 0, nullptr, nullptr, 1,
-                                                     scale, dq, dk, dv, qt, dot, ktf, st)
-                     : run_full_bwd_mfma<64, false>(d, q, k, v, dout, lse, delta, nullptr, 0, nullptr, nullptr, 1,
-                                                    scale, dq, dk, dv, qt, dot, ktf, st);
-  }
+  if (idx)
+    e = d.D == 128 ? run_full_bwd_mfma<128, true>(d, q, k, v, dout, lse, delta, idx, off, list, topk, scale, dq, dk,
+                                                  dv, qt, dot, ktf, st)
+                   : run_full_bwd_mfma<64, true>(d, q, k, v, dout, lse, delta, idx, off, list, topk, scale, dq, dk,
+                                                 dv, qt, dot, ktf, st);
+  else
+    e = d.D == 128 ? run_full_bwd_mfma<128, false>(d, q, k, v, dout, lse, delta, nullptr, nullptr, nullptr, 1, scale,
+                                                   dq, dk, dv, qt, dot, ktf, st)
+                   : run_full_bwd_mfma<64, false>(d, q, k, v, dout, lse, delta, nullptr, nullptr, nullptr, 1, scale,
+                                                  dq, dk, dv, qt, dot, ktf, st);
   const hipError_t fe = workspace_free(ws, st);
   return e != hipSuccess ? e : fe;
 }

@@ -70,13 +70,19 @@ LaunchResult launch_attn_bwd(const Dims& d, bool sparse, bool mfma, const void* 
                              const void* o, const float* lse, const void* dout, const int32_t* idx, int topk,
                              float scale, float* dq, float* dk, float* dv, hipStream_t st);
 // MFMA backward (bf16): dq, dk, dv += ..., given delta [B*H*L]; with idx (the sparse
-// stream) dq uses each row's block mask and dk, dv the inverted index off/list (block ->
-// rows that kept it, as built in bwd.hip).
+// stream) dk, dv use the inverted index off/list (block -> rows that kept it, as built in
+// bwd.hip) and dq the gathered-row kernel, which builds its own per-tile index from idx.
 bool full_bwd_mfma_supported(const Dims& d);
-bool sparse_bwd_mfma_supported(const Dims& d);
+bool sparse_bwd_mfma_supported(const Dims& d, int topk);
 hipError_t launch_full_bwd_mfma(const Dims& d, const int32_t* idx, int topk, const int* off, const int* list,
                                 const void* q, const void* k, const void* v, const void* dout, const float* lse,
                                 const float* delta, float scale, float* dq, float* dk, float* dv, hipStream_t st);
+// Sparse-stream dq on MFMA over gathered rows: dq += scale sum ds k over each row's kept
+// blocks and own block; ktf is K in fragment order (frag_order_into of the K/V heads).
+bool dq_gather_supported(const Dims& d, int topk);
+hipError_t launch_dq_gather(const Dims& d, const void* q, const void* k, const void* v, const void* dout,
+                            const u32x4* ktf, const float* lse, const float* delta, const int32_t* idx, int topk,
+                            float scale, float* dq, hipStream_t st);
 // Per-row bit masks of the blocks the sparse stream attends (word j / 32, bit j % 32 of
 // row t: a valid kept entry of idx, or the own block); [B*H*L][ceil(n/32)] words.
 hipError_t build_block_mask(const Dims& d, const int32_t* idx, int topk, uint32_t* mask, hipStream_t st);

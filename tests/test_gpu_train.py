@@ -128,6 +128,43 @@ def test_sparse_bwd_alone_matches_oracle():
                 np.testing.assert_allclose(r1, r2, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("B,H,Hkv,L,D,s,topk,padded", [
+    (1, 2, 2, 384, 128, 64, 5, False),    # last tile of rows ragged (128 of 256)
+    (1, 2, 1, 384, 64, 128, 2, True),     # 128-token blocks, grouped heads, padded rows
+    (2, 2, 1, 2048, 128, 64, 16, True),   # several tiles, grouped heads, padded rows
+    (1, 1, 1, 4096, 128, 64, 32, False),  # 32 entries per row, as in the long-context workload
+])
+def test_sparse_bwd_gathered_rows(B, H, Hkv, L, D, s, topk, padded):
+    """The sparse stream's gradients alone on shapes that exercise the gathered-row dq:
+    a ragged last row tile, several tiles, grouped K/V heads, 32 entries per row, and idx
+    rows where some kept entries are replaced by -1 or by a block index past the end
+    (skipped, like the forward skips them)."""
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "sink", seed=3600 + L + topk, hkv=Hkv)
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    rng = np.random.default_rng(3700 + L)
+    do = W.f32_to_bf16_bits(rng.standard_normal((B, H, L, D), dtype=np.float32) * np.float32(0.1))
+    dod = to_device(do, W.BF16)
+    scale = 1.0 / math.sqrt(D)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, topk)
+    if padded:
+        g = idx.cpu().numpy()
+        hit = rng.random(g.shape) < 0.25
+        g = np.where(hit, np.where(rng.random(g.shape) < 0.5, -1, L // s + 7), g).astype(np.int32)
+        idx = torch.from_numpy(g).to(idx.device)
+    say(f"[gpu] sparse bwd B={B} H={H} Hkv={Hkv} L={L} D={D} s={s} topk={topk} padded={padded}")
+    o_s, lse_s = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+    dq, dk, dv = ssa.sparse_attn_bwd(q, k, v, o_s, lse_s, dod, idx, s, scale=scale)
+    torch.cuda.synchronize()
+    q64 = inp.as_f64("q")
+    k64, v64 = (inp.kv_per_query_head(inp.as_f64(n)) for n in ("k", "v"))
+    ref = O.attend_sparse_bwd(q64, k64, v64, W.bf16_bits_to_f32(do).astype(np.float64), idx.cpu().numpy(), s, scale)
+    errs = {}
+    for i, (got, nm) in enumerate(zip((dq, dk, dv), ("dq", "dk", "dv"))):
+        r = ref[i] if i == 0 else _kv_sum(ref[i], H, Hkv)
+        errs[nm] = close_rel(to_f64(got), r, TOL[W.BF16], f"{nm} L={L} topk={topk}")
+    say(f"[oracle] sparse bwd L={L} topk={topk} padded={padded}: {errs}")
+
+
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 def test_align_loss(dtype):
     B, H, L, D = 2, 3, 256, 128
