@@ -16,9 +16,11 @@
 //  of two row tiles exactly the B operand of the second pair of products, so P and dS
 //  need no lane movement.
 //
-//  dq (query-stationary): a workgroup of four waves owns 128 query rows, wave w rows
-//  32w .. 32w+31 (two 16-row column tiles), and walks the 64-key chunks 0 .. its last
-//  row's chunk:
+//  dq (query-stationary): a workgroup of eight waves (two per SIMD; four where L is not a
+//  multiple of 256) owns 256 (128) query rows, wave w rows 32w .. 32w+31 (two 16-row
+//  column tiles), and walks the 64-key chunks 0 .. its last row's chunk; each K / V
+//  fragment read from LDS serves both row tiles, and the next chunk is staged in two
+//  halves around the two groups of products:
 //      S^T = K Q^T, dP^T = V dO^T          (A = K / V rows from LDS, B = Q / dO rows held)
 //      P^T, dS^T as above
 //      dQ^T += K^T dS^T                    (A = K in fragment order from LDS)
@@ -221,8 +223,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------- dq
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void bwd_q_mfma_kernel(
+// NW waves of 32 rows each (NW / 4 waves per SIMD)
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void bwd_q_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const u32x4* __restrict__ kt_frag, const float* __restrict__ lse,
     const float* __restrict__ delta, float* __restrict__ dq, int L, int G, int BH, float sl2, float scale) {
@@ -230,17 +233,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int FK = 4 * NC;          // A fragments of K (and of V) per 64-key chunk
   constexpr int FT = 2 * NDT;         // fragment-order K^T fragments per chunk
   constexpr int NF = 2 * FK + FT;
-  constexpr int PT = NF * 64 / 256;
+  constexpr int NTH = 64 * NW, RB = 32 * NW;  // threads, rows per workgroup
+  constexpr int PT = NF * 64 / NTH;  // staging pieces per thread: PH0 in the first half, the rest in the second
+  constexpr int PH0 = (PT + 1) / 2;
+  static_assert(NF * 64 % NTH == 0, "staging pieces per thread");
   extern __shared__ __align__(16) unsigned char smem_q[];
   u32x4* st = reinterpret_cast<u32x4*>(smem_q);  // [2][NF][64]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int nqb = L / 128, nck = L / 64;
+  const int nqb = L / RB, nck = L / 64;
   const int qb = nqb - 1 - (int)(blockIdx.x / BH);  // row blocks with the most keys first
   const int64_t bh = blockIdx.x % BH;
   const int64_t kvbh = bh / G;
-  const int rw0 = qb * 128 + 32 * w;  // this wave's first row
+  const int rw0 = qb * RB + 32 * w;  // this wave's first row
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const uint16_t* dh = dout + bh * (int64_t)L * D;
   const uint16_t* kh = k + kvbh * (int64_t)L * D;
@@ -265,12 +271,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) dqa[nt][dt] = f32x4{0, 0, 0, 0};
 
-  const int items = (qb * 128 + 127) / 64 + 1;  // key chunks 0 .. the block's last row's chunk
-  u32x4 pr[PT];
-  auto load_item = [&](int c) {
+  const int items = (qb * RB + RB - 1) / 64 + 1;  // key chunks 0 .. the block's last row's chunk
+  // The next chunk is staged in two halves, each loaded before and stored after one group
+  // of products, so only half of the staging registers are live at a time.
+  u32x4 pr[PH0];
+  auto load_half = [&](int c, int half) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int p = tid + 256 * i, f = p >> 6, ll = p & 63;
+    for (int i = 0; i < (half ? PT - PH0 : PH0); ++i) {
+      const int p = tid + NTH * (half * PH0 + i), f = p >> 6, ll = p & 63;
       if (f < 2 * FK) {
         const int ff = f < FK ? f : f - FK, kt = ff / NC, cc = ff % NC;
         pr[i] = load_k_frag_lane<D>(f < FK ? kh : vh, c * 64 + 16 * kt, cc, ll);
@@ -279,32 +287,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
   };
-  auto store_item = [&](int b) {
+  auto store_half = [&](int b, int half) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) st[(b * NF) * 64 + tid + 256 * i] = pr[i];
+    for (int i = 0; i < (half ? PT - PH0 : PH0); ++i) st[(b * NF) * 64 + tid + NTH * (half * PH0 + i)] = pr[i];
   };
-  load_item(0);
-  store_item(0);
+  load_half(0, 0);
+  store_half(0, 0);
+  load_half(0, 1);
+  store_half(0, 1);
   __syncthreads();
   for (int c = 0; c < items; ++c) {
     const int b = c & 1;
-    load_item(min(c + 1, items - 1));
+    const int cn = min(c + 1, items - 1);  // unconditional loads (a repeat at the end)
     const u32x4* sb = st + b * NF * 64;
     const int k0 = c * 64;
-    if (k0 <= rw0 + 31) {  // some key of the chunk is at or before some row of this wave
+    const bool act = k0 <= rw0 + 31;  // some key of the chunk is at or before some row of this wave
+    // S^T and dP^T: each fragment read from LDS feeds the products of both row tiles
+    load_half(cn, 0);
+    f32x4 sa[2][4], dp[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) sa[nt][kt] = dp[nt][kt] = f32x4{0, 0, 0, 0};
+    if (act) {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4 ak = sb[(kt * NC + cc) * 64 + lane];
+          const u32x4 av = sb[(FK + kt * NC + cc) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            sa[nt][kt] = mfma_bf16(ak, qf[nt][cc], sa[nt][kt]);
+            dp[nt][kt] = mfma_bf16(av, df[nt][cc], dp[nt][kt]);
+          }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    store_half(b ^ 1, 0);
+    // dS^T (element i of sa[nt][kt]: key k0 + 16 kt + 4 g + i, row rw0 + 16 nt + n), then
+    // dQ^T += K^T dS^T
+    load_half(cn, 1);
+    if (act) {
+      u32x4 bs[2][2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        f32x4 s[4], dp[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) s[kt] = dp[kt] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt) {
-            s[kt] = mfma_bf16(sb[(kt * NC + cc) * 64 + lane], qf[nt][cc], s[kt]);
-            dp[kt] = mfma_bf16(sb[(FK + kt * NC + cc) * 64 + lane], df[nt][cc], dp[kt]);
-          }
-        // element i of s[kt]: key k0 + 16 kt + 4 g + i, row rw0 + 16 nt + n
         const int row = rw0 + 16 * nt + n;
         float dsv[4][4];
 #pragma unroll
@@ -312,19 +339,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const bool live = k0 + 16 * kt + 4 * g + i <= row;
-            const float p = live ? fast_exp2(fmaf(s[kt][i], sl2, -l2[nt])) : 0.f;
-            dsv[kt][i] = p * (dp[kt][i] - de[nt]);
+            const float p = live ? fast_exp2(fmaf(sa[nt][kt][i], sl2, -l2[nt])) : 0.f;
+            dsv[kt][i] = p * (dp[nt][kt][i] - de[nt]);
           }
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const u32x4 bs = pack_p(dsv[2 * kc], dsv[2 * kc + 1]);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            dqa[nt][dt] = mfma_bf16(sb[(2 * FK + dt * 2 + kc) * 64 + lane], bs, dqa[nt][dt]);
-        }
+        for (int kc = 0; kc < 2; ++kc) bs[nt][kc] = pack_p(dsv[2 * kc], dsv[2 * kc + 1]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x4 at = sb[(2 * FK + dt * 2 + kc) * 64 + lane];
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) dqa[nt][dt] = mfma_bf16(at, bs[nt][kc], dqa[nt][dt]);
+        }
     }
-    store_item(b ^ 1);
+    store_half(b ^ 1, 1);
     __syncthreads();
   }
   // dqa[nt][dt] element i: d = 16 dt + 4 g + i, row rw0 + 16 nt + n
@@ -644,11 +675,13 @@ static hipError_t run_full_bwd_mfma(const Dims& d, const void* q, const void* k,
   } else {
     constexpr int NF = 2 * (4 * NC) + 2 * NDT;
     const int lds = 2 * NF * 64 * 16;
-    auto kern = bwd_q_mfma_kernel<D>;
+    // 256 rows (two waves per SIMD) where L allows, else 128
+    const bool wide = d.L % 256 == 0;
+    auto kern = wide ? bwd_q_mfma_kernel<D, 8> : bwd_q_mfma_kernel<D, 4>;
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    const int64_t grid = d.bh() * (d.L / 128);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, static_cast<const uint16_t*>(q),
+    const int64_t grid = d.bh() * (d.L / (wide ? 256 : 128));
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(wide ? 512 : 256), lds, st, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
                        static_cast<const uint16_t*>(dout), ktf, lse, delta, dq, d.L, d.G(), (int)d.bh(), sl2, scale);
     e = hipGetLastError();
