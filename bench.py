@@ -14,7 +14,14 @@ FLOPs 4*D*sum_t |A(t)|.  `cpu_baseline` times the CPU oracle's sparse stream on 
 bounded sample of the same workload (rank 0, this process).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                    [--no-cpu-baseline] [--copy-calib]
+                    [--no-cpu-baseline] [--copy-calib] [--per-call N] [--no-peaks]
+
+`--per-call N` also times every C-ABI call of the step alone (3 warm-ups, then N
+repetitions, median), writing a 1 GiB scratch buffer between repetitions when the
+workload's inputs fit in the 256 MB last-level cache (so no repetition starts warm).
+After the timed region the prefill path measures the device's own peaks with the probe
+library (libssa_probe.so): back-to-back bf16 MFMA from registers and a streaming read of
+4 GiB; they are reported beside the published peaks (`--no-peaks` skips this).
 
 `--path decode` measures decoding with a key/value cache instead: one step = one new
 token for each of B sequences (at different positions of a 32768-token cache): append
@@ -48,6 +55,7 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+LLC_BYTES = 256 << 20       # MI355X last-level (Infinity) cache
 METRIC = "sparse-attn fwd tokens/s and TFLOP/s (% MFMA bf16 peak) at L=32K"
 
 
@@ -157,6 +165,74 @@ def cpu_baseline(inp: W.Inputs, k: int, budget_s: float = 15.0) -> dict:
             "cpu_model": cpu}
 
 
+def time_calls(torch, calls: dict, reps: int, inputs_bytes: int) -> dict:
+    """Each call alone on torch's current stream: 3 warm-ups, then `reps` repetitions timed
+    with HIP events, median; a 1 GiB buffer is written before every repetition when the
+    inputs fit in the last-level cache."""
+    flush = inputs_bytes < LLC_BYTES
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+    res = {}
+    for nm, fn in calls.items():
+        for _ in range(3):
+            fn()
+        ts = []
+        for r in range(reps):
+            if flush:
+                scratch.fill_(float(r))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ts.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ts]
+        res[nm] = {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(np.min(ms)), 4), "reps": reps}
+    return {"calls": res, "llc_flush_1GiB": flush, "inputs_bytes": int(inputs_bytes)}
+
+
+def measure_peaks(torch) -> dict:
+    """The device's reachable peaks (libssa_probe.so), best of 3, beside the published ones:
+    bf16 MFMA issued back to back from registers (4 waves per SIMD, 8 independent chains
+    each) and a 16-byte streaming read of 4 GiB (16x the last-level cache; 4, 8 and 16
+    workgroups per CU, best taken)."""
+    import ctypes
+    from block_sparse_top_ssa_amd import _lib
+    lib = _lib.load_probe()
+    st = torch.cuda.current_stream()
+    blocks, iters = 1024, 20000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    flops = blocks * 4 * iters * 8 * 16384
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    rgrids = (256 * 4, 256 * 8, 256 * 16)  # workgroups of the read probe (4, 8, 16 per CU)
+    rout = torch.empty(max(rgrids) * 256 * 4, dtype=torch.int32, device="cuda")
+    best_mfma, best_rd = 0.0, 0.0
+    for _ in range(3):
+        e0, e1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        e0.record()
+        rc = lib.ssa_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        e1.record()
+        torch.cuda.synchronize()
+        if rc:
+            raise RuntimeError(f"MFMA peak probe launch failed ({rc})")
+        best_mfma = max(best_mfma, flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        for rb in rgrids:
+            e0.record()
+            rc = lib.ssa_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rb, ctypes.c_void_p(rout.data_ptr()),
+                                        ctypes.c_void_p(st.cuda_stream))
+            e1.record()
+            torch.cuda.synchronize()
+            if rc:
+                raise RuntimeError(f"HBM read probe launch failed ({rc})")
+            best_rd = max(best_rd, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return {"mfma_bf16_tflops": round(best_mfma, 1), "mfma_bf16_published": PEAK_BF16_TFLOPS,
+            "hbm_read_gbps": round(best_rd, 1), "hbm_published_gbps": PEAK_HBM_GBPS,
+            "note": "libssa_probe.so: back-to-back v_mfma_f32_16x16x32_bf16 from registers (4 waves per SIMD); "
+                    "16-byte streaming read of 4 GiB; best of 3"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +241,9 @@ def main():
     ap.add_argument("--workload", default=W.BENCH_WORKLOAD, choices=sorted(W.WORKLOADS))
     ap.add_argument("--topk", type=int, default=0, help="blocks per query (default: the workload's first k)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-call", type=int, default=0, metavar="N",
+                    help="also time each call alone: 3 warm-ups, N repetitions, median")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the peak microbenchmarks")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (for HBM counter scaling)")
     ap.add_argument("--path", default="prefill", choices=["prefill", "decode", "train"],
@@ -245,6 +324,18 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
 
+    per_call = None
+    if args.per_call > 0:
+        calls = {
+            "pool": lambda: ssa.block_pool(kk, s, out=km),
+            "topk": lambda: ssa.block_topk(q, km, s, k, out=idx),
+            "sparse": lambda: ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s),
+            "full": lambda: ssa.full_attn_fwd(q, kk, v, scale, want_o=o_f is not None, block=s, out=o_f, lse=lse_f),
+            "align": (lambda: ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)) if o_f is not None
+            else (lambda: ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)),
+        }
+        per_call = time_calls(torch, calls, args.per_call, inputs_bytes=q.nbytes + kk.nbytes + v.nbytes)
+
     model = work_model(w, k)
     traffic = measured_traffic(w.name)
     kernels = {}
@@ -293,6 +384,10 @@ def main():
                      "WRITE_SIZE, scaled by a 1 GiB copy; null when the kernel changed since)"},
         "kernels": kernels,
     }
+    if per_call is not None:
+        out["per_call"] = per_call
+    if not args.no_peaks:
+        out["peaks_measured"] = measure_peaks(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, k)
     print(json.dumps(out), flush=True)

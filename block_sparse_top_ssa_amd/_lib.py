@@ -73,6 +73,26 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+PROBE_PATH = os.path.join(_PKG, "libssa_probe.so")
+# include/ssa_probe.h (peak microbenchmarks, a separate library)
+PROBE_PROTOTYPES = {
+    "ssa_probe_mfma_bf16": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _VP, _VP]),
+    "ssa_probe_hbm_read": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _VP, _VP]),
+}
+
+
+def load_probe(path: str = PROBE_PATH) -> ctypes.CDLL:
+    """Load libssa_probe.so (raises if it has not been built)."""
+    if not os.path.exists(path):
+        raise ImportError(f"libssa_probe.so is not built at {path}; run `python -m block_sparse_top_ssa_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in PROBE_PROTOTYPES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def check(code: int) -> None:
     if code != 0:
         raise SSAError(code, load().ssa_last_error().decode(errors="replace"))

@@ -61,7 +61,23 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
     os.replace(tmp, LIB)
+    build_probe()
     return LIB
+
+
+PROBE_SRC = os.path.join(PKG, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libssa_probe.so")
+
+
+def build_probe() -> str:
+    """libssa_probe.so: the peak microbenchmarks of include/ssa_probe.h (measurement aid)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [_hipcc(), *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on peaks.hip:\n{p.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

@@ -29,6 +29,23 @@ def test_exports_every_declared_symbol(libssa):
     assert not missing, f"not exported: {missing}"
 
 
+def test_probe_library_exports_its_header():
+    """libssa_probe.so (peak microbenchmarks, include/ssa_probe.h) exports what its header
+    declares, and rejects bad arguments before launching anything."""
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ssa_probe.h")).read(), flags=re.S)
+    names = set(re.findall(r"\b(ssa_probe_[a-z_0-9]+)\s*\(", text))
+    assert names == set(_lib.PROBE_PROTOTYPES), "probe prototypes and header disagree"
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.PROBE_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert names <= exported, f"not exported: {sorted(names - exported)}"
+    if gpu_available():
+        return
+    lib = _lib.load_probe()
+    bad = 1  # hipErrorInvalidValue
+    assert lib.ssa_probe_mfma_bf16(0, 10, FAKE, None) == bad
+    assert lib.ssa_probe_hbm_read(FAKE, 24, 4, FAKE, None) == bad  # not a multiple of 16
+
+
 def test_version_and_status_strings(libssa):
     v = int(re.search(r"#define SSA_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
     assert libssa.ssa_abi_version() == v
