@@ -87,6 +87,11 @@ hipError_t launch_dq_gather(const Dims& d, const void* q, const void* k, const v
 // row t: a valid kept entry of idx, or the own block); [B*H*L][ceil(n/32)] words.
 hipError_t build_block_mask(const Dims& d, const int32_t* idx, int topk, uint32_t* mask, hipStream_t st);
 
+// Sparse-stream measurements over gathered rows: the tile (512 or 256 rows) whose index fits
+// in LDS, 0 if none; part gets ceil(L / tile) histogram partials per (b, h), in order.
+int stats_gather_tile(const Dims& d, int topk);
+hipError_t launch_stats_gather(const Dims& d, const void* q, const void* k, const float* lse, const int32_t* idx,
+                               int topk, float scale, float* entropy, float* part, hipStream_t st);
 // Attention-pattern measurements: row entropy and attention mass by block distance.
 LaunchResult launch_attn_stats(const Dims& d, bool mfma, const void* q, const void* k, const float* lse,
                                const int32_t* idx, int topk, float scale, float* entropy, float* hist,

@@ -7,7 +7,9 @@
 //   p_ti = exp(scale q_t . k_i - lse_t),  entropy_t = lse_t - sum_i p_ti scale q_t . k_i,
 //   hist[m] += p_ti for m = bucket(b_t - b_i), bucket(0) = 0, bucket(d) = 1 + floor(log2 d)
 // (the last of the 16 buckets collects the rest).  Only the scores are needed, so the
-// matrix-core kernel (bf16) is the query-stationary backward kernel's first product alone:
+// matrix-core kernel (bf16) of the full stream is the query-stationary backward kernel's
+// first product alone (the sparse stream visits only its kept blocks: stats_gather.hip;
+// the masked form below remains for tiles whose index does not fit in LDS):
 // four waves x 32 rows, 64-key chunks of K streamed through two LDS stages.  Every row of a
 // wave lies in one block, so a chunk's distance bucket is the same for the whole wave.
 // Histogram partials go to one slot per (b, h, row group) and are summed in a fixed order.
@@ -262,8 +264,10 @@ LaunchResult launch_attn_stats(const Dims& d, bool mfma, const void* q, const vo
                                const int32_t* idx, int topk, float scale, float* entropy, float* hist,
                                hipStream_t st) {
   LaunchResult r;
-  const bool use_mfma = mfma && d.dtype == 1 && d.L % 128 == 0 && (!idx || d.n() <= 4096);
-  const int P = use_mfma ? d.L / 128 : d.L / 4;  // histogram partials per (b, h)
+  // the sparse stream over gathered rows (stats_gather.hip) where its tile index fits in LDS
+  const int gT = mfma && idx ? stats_gather_tile(d, topk) : 0;
+  const bool use_mfma = gT == 0 && mfma && d.dtype == 1 && d.L % 128 == 0 && (!idx || d.n() <= 4096);
+  const int P = gT ? (d.L + gT - 1) / gT : use_mfma ? d.L / 128 : d.L / 4;  // histogram partials per (b, h)
   const int W = (d.n() + 31) / 32;
   const size_t pbytes = hist ? (size_t)d.bh() * P * kBuckets * sizeof(float) : 0;
   const size_t mbytes = use_mfma && idx ? (size_t)d.tokens() * W * sizeof(uint32_t) : 0;
@@ -276,6 +280,7 @@ LaunchResult launch_attn_stats(const Dims& d, bool mfma, const void* q, const vo
   uint32_t* mask = mbytes ? reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + pbytes) : nullptr;
   const float sl2 = scale * kLog2e;
   auto go = [&]() -> hipError_t {
+    if (gT) return launch_stats_gather(d, q, k, lse, idx, topk, scale, entropy, part, st);
     if (use_mfma) {
       if (idx) {
         hipError_t e = build_block_mask(d, idx, topk, mask, st);

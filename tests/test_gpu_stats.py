@@ -58,3 +58,36 @@ def test_attn_stats(variant, dtype, D, s, Hkv, stream):
     assert err_e <= 1e-3, err_e
     assert err_h <= 1e-4 * L, err_h
     np.testing.assert_allclose(gh.sum(axis=-1), L, rtol=1e-4)
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,D,s,topk,padded", [
+    (1, 2, 1, 1152, 128, 64, 8, True),   # last tile of rows ragged (128 of 512), grouped heads
+    (2, 1, 1, 640, 64, 128, 3, True),    # 128-token blocks, two sequences
+    (1, 1, 1, 4096, 128, 64, 32, False),  # 32 entries per row, as in the long-context workload
+])
+def test_sparse_stats_gathered_rows(B, H, Hkv, L, D, s, topk, padded):
+    """The sparse stream's measurements on shapes that exercise the gathered-row kernel,
+    including idx rows where a quarter of the entries are -1 or a block past the end."""
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "sink", seed=4300 + L + topk, hkv=Hkv)
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, topk)
+    if padded:
+        rng = np.random.default_rng(4400 + L)
+        g = idx.cpu().numpy()
+        hit = rng.random(g.shape) < 0.25
+        g = np.where(hit, np.where(rng.random(g.shape) < 0.5, -1, L // s + 7), g).astype(np.int32)
+        idx = torch.from_numpy(g).to(idx.device)
+    _, lse = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+    ent, hist = ssa.attn_stats(q, k, lse, s, idx=idx, scale=scale)
+    torch.cuda.synchronize()
+    q64 = inp.as_f64("q")
+    k64 = inp.kv_per_query_head(inp.as_f64("k"))
+    ref_e, ref_h = O.attention_stats(q64, k64, s, scale, idx.cpu().numpy())
+    ge, gh = to_f64(ent), to_f64(hist)
+    err_e = float(np.abs(ge - ref_e).max())
+    err_h = float(np.abs(gh - ref_h).max())
+    print(f"[oracle] sparse stats L={L} topk={topk} padded={padded}: entropy {err_e:.2e} hist {err_h:.2e}", flush=True)
+    assert err_e <= 1e-3, err_e
+    assert err_h <= 1e-4 * L, err_h
+    np.testing.assert_allclose(gh.sum(axis=-1), L, rtol=1e-4)
