@@ -193,14 +193,14 @@ def time_calls(torch, calls: dict, reps: int, inputs_bytes: int) -> dict:
 
 def measure_peaks(torch) -> dict:
     """The device's reachable peaks (libssa_probe.so), best of 3, beside the published ones:
-    bf16 MFMA issued back to back from registers (4 waves per SIMD, 8 independent chains
+    bf16 MFMA issued back to back from registers (8 waves per SIMD, 8 independent chains
     each) and a 16-byte streaming read of 4 GiB (16x the last-level cache; 4, 8 and 16
     workgroups per CU, best taken)."""
     import ctypes
     from block_sparse_top_ssa_amd import _lib
     lib = _lib.load_probe()
     st = torch.cuda.current_stream()
-    blocks, iters = 1024, 20000
+    blocks, iters = 2048, 10000  # 8 waves per SIMD
     out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     flops = blocks * 4 * iters * 8 * 16384
     nbytes = 4 << 30
@@ -229,7 +229,7 @@ def measure_peaks(torch) -> dict:
     del buf
     return {"mfma_bf16_tflops": round(best_mfma, 1), "mfma_bf16_published": PEAK_BF16_TFLOPS,
             "hbm_read_gbps": round(best_rd, 1), "hbm_published_gbps": PEAK_HBM_GBPS,
-            "note": "libssa_probe.so: back-to-back v_mfma_f32_16x16x32_bf16 from registers (4 waves per SIMD); "
+            "note": "libssa_probe.so: back-to-back v_mfma_f32_16x16x32_bf16 from registers (8 waves per SIMD); "
                     "16-byte streaming read of 4 GiB; best of 3"}
 
 
