@@ -249,9 +249,12 @@ ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const v
  *   The gradients are ADDED to dq, dk, dv, so the two streams' calls can share them;
  *   clear them first.  The softmax term uses delta_t = sum_d dout_t,d o_t,d with the
  *   stored o.  Workspace: B*H*L*4 bytes (delta); the sparse call adds an inverted index
- *   (block -> rows that kept it) of B*H*(2n+1)*4 + B*H*L*topk*4 bytes; both from the
- *   pool described under ssa_sparse_attn_fwd.  The sparse call accumulates dk, dv over
- *   rows in an order that can differ between runs (last-bit float32 differences).
+ *   (block -> rows that kept it) of B*H*(2n+1)*4 + B*H*L*topk*4 bytes; on bf16 the
+ *   matrix-core path adds fragment-order copies of Q, dO and K for the full call
+ *   (2*B*H*L*D*2 + B*Hkv*L*D*2 bytes) and of K for the sparse call (B*Hkv*L*D*2 bytes);
+ *   all from the pool described under ssa_sparse_attn_fwd.  The sparse call accumulates
+ *   dq, dk and dv in an order that can differ between runs (last-bit float32
+ *   differences).
  */
 ssa_status ssa_full_attn_bwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, float scale, float* dq, float* dk, float* dv,
@@ -276,9 +279,13 @@ ssa_status ssa_sparse_attn_bwd(const ssa_dims* dims, const void* q, const void* 
  *              to L (summed in a fixed order)
  *   At least one output must be given.  The sparse stream's dropped mass and the
  *   divergence KL(p_sparse || p_full) = lse_full - lse_sparse follow from the two
- *   log-sum-exps (ssa_align_stats gives the first).  Workspace: B*H*(L/128 or L/4)*64
- *   bytes of partial sums, plus the sparse rows' block masks (B*H*L*ceil(n/32)*4 bytes),
- *   from the pool.
+ *   log-sum-exps (ssa_align_stats gives the first).  Workspace, from the pool: 64 bytes
+ *   of histogram partials per (b, h) and row group -- L/128 groups for the full stream
+ *   on bf16, ceil(L/512) (or ceil(L/256)) tiles for the sparse stream on bf16, L/4
+ *   otherwise; when a sparse tile's block index does not fit in LDS (very large n or
+ *   topk) the bf16 path scores under per-row block masks instead and adds them
+ *   (B*H*L*ceil(n/32)*4 bytes).  The sparse stream's bf16 entropies are summed in an
+ *   order that can differ between runs (last-bit float32 differences).
  */
 ssa_status ssa_attn_stats(const ssa_dims* dims, const void* q, const void* k, const float* lse, const int32_t* idx,
                           int32_t topk, float scale, float* entropy, float* dist_hist, void* stream);
