@@ -103,6 +103,23 @@ def test_pool_closed_forms():
     assert np.all(km <= blocks.max(axis=3)) and np.all(km >= blocks.min(axis=3))
 
 
+def test_block_scores_are_mean_token_scores():
+    """By linearity a query's score against a block mean is the mean of its dot products
+    with the block's keys, computed here token by token with explicit loops (no matrix
+    product), on small integer inputs where both sides are exact in float64."""
+    L, D, s, R = 32, 4, 8, 5
+    k = W.integer_tensor((1, 1, L, D), -6, 6, seed=21).astype(float)
+    q = W.integer_tensor((R, D), -5, 5, seed=22).astype(float)
+    got = O.block_scores(q, O.block_pool(k, s)[0, 0])
+    assert got.shape == (R, L // s)
+    for r in range(R):
+        for j in range(L // s):
+            tot = 0.0
+            for i in range(j * s, (j + 1) * s):
+                tot += sum(q[r, d] * k[0, 0, i, d] for d in range(D))
+            assert got[r, j] == tot / s, (r, j, got[r, j], tot / s)
+
+
 def test_pool_rejects_ragged_length():
     with pytest.raises(ValueError):
         O.block_pool(np.zeros((1, 1, 10, 4)), 4)
