@@ -13,15 +13,16 @@
 // causally.
 // Grid order: head-major, tiles with the most chunks first, remapped so that each XCD
 // works through a contiguous range (one head at a time), keeping that head's K/V in its
-// L2.  The softmax exponent reference trails the running row max by up to 2^8, so the
-// O accumulators are rescaled only when the max jumps (rare after the first chunks).
+// L2.  The softmax exponent reference is set by the first chunk and moves only when a
+// chunk's probabilities would pass 2^64 (seen from their row sums, so no per-element row
+// maximum is formed off the diagonal), so the O accumulators are rarely rescaled.
 // With o == NULL only the running max and sums are kept (log-sum-exp only).
 #include "launch.hpp"
 #include "mfma.hpp"
 
 namespace ssa {
 
-constexpr float kLag = 8.f;  // log2 units the exponent reference may trail the row max
+constexpr float kLag = 8.f;  // max path: log2 units the row max may pass the reference before it moves
 
 // Each wave owns NT = 2 column tiles of 16 rows; waves w and w + 4 share a SIMD and own
 // the two 32-row halves of the same 64-row block.  Per 64-key chunk a wave does three
@@ -139,43 +140,59 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int nt = 0; nt < NT; ++nt) sacc[kt][nt] = mfma_bf16(kf[f], qf[nt][cc], sacc[kt][nt]);
     }
   };
-  // X: online softmax of sacc into pf (bf16 P^T fragments), m, lsum and O rescaling
+  // X: online softmax of sacc into pf (bf16 P^T fragments), m, lsum and O rescaling.
+  // Off the diagonal the exponents are taken against the current reference m straight
+  // away, and the row sums of the result show whether that was safe: a first chunk
+  // (m = -inf gives p = +inf) or a chunk whose p would pass 2^64 redoes the chunk on the
+  // max path, as does the diagonal chunk (masked).  The max path moves m only when the
+  // row maximum passes it by more than kLag (the row maximum across the four lanes of a
+  // row is formed only when some lane's own maximum passes), rescaling O and l.  p up to
+  // 2^64 keeps O and l far from the float32 range even over the longest rows.
   auto softmax = [&](bool diag) __attribute__((always_inline)) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float sr[16];
-      float mx = -__builtin_huge_valf();
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = sacc[kt][nt][i];
-          if (diag && (16 * kt + 4 * g + i > rq + 16 * nt + n)) x = -__builtin_huge_valf();
-          sr[kt * 4 + i] = x;
-          mx = fmaxf(mx, x);
-        }
-      // The exponent reference m[nt] only moves when this chunk's max passes it by
-      // more than kLag (p stays <= 2^kLag), so O and l are rescaled rarely; the row
-      // maximum across the four lanes of a row is formed only when some lane's own
-      // maximum passes (the decision per row is the same).
-      if (__builtin_amdgcn_ballot_w64(mx * sl2 > m[nt] + kLag)) {
-        const float mxs = max_over_rows(mx) * sl2;
-        const bool need = mxs > m[nt] + kLag;
-        const float mnew = need ? mxs : m[nt];
-        const float alpha = fast_exp2(m[nt] - mnew);
-        lsum[nt] *= alpha;
-        if (WANT_O) {
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
-        }
-        m[nt] = mnew;
-      }
-      const float mneg = -m[nt];
       float ps = 0.f;
+      if (!diag) {
+        const float mneg = -m[nt];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
-        ps += sr[i];
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sr[kt * 4 + i] = fast_exp2(fmaf(sacc[kt][nt][i], sl2, mneg));
+            ps += sr[kt * 4 + i];
+          }
+      }
+      if (diag || __builtin_amdgcn_ballot_w64(!(ps <= 0x1p64f))) {
+        float mx = -__builtin_huge_valf();
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x = sacc[kt][nt][i];
+            if (diag && (16 * kt + 4 * g + i > rq + 16 * nt + n)) x = -__builtin_huge_valf();
+            sr[kt * 4 + i] = x;
+            mx = fmaxf(mx, x);
+          }
+        if (__builtin_amdgcn_ballot_w64(mx * sl2 > m[nt] + kLag)) {
+          const float mxs = max_over_rows(mx) * sl2;
+          const bool need = mxs > m[nt] + kLag;
+          const float mnew = need ? mxs : m[nt];
+          const float alpha = fast_exp2(m[nt] - mnew);
+          lsum[nt] *= alpha;
+          if (WANT_O) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) oacc[dt][nt] *= alpha;
+          }
+          m[nt] = mnew;
+        }
+        const float mneg = -m[nt];
+        ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
+          ps += sr[i];
+        }
       }
       lsum[nt] += ps;
       if (WANT_O) {

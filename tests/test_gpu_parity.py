@@ -292,6 +292,29 @@ def test_huge_logit_row_recomputed(variant):
     _oracle_checks(inp, g, 4, rows=np.array([0, 130, 899, 900, 901, 1023]))
 
 
+def test_full_stream_growing_logits(variant):
+    """Logits that rise steadily along the sequence (about 170 log2 units from the first
+    key to the last), so every row's later chunks outgrow the exponent reference set by
+    its first chunk many times over: the dense stream's rescaling (and, on matrix cores,
+    its recovery from row sums past 2^64) must still give the exact softmax."""
+    B, H, L, D, s = 1, 2, 2048, 128, 64
+    rng = np.random.default_rng(4501)
+    a = np.linspace(0.0, 10.6, L)  # key strength along the sequence
+    q = 1.0 + 0.1 * rng.standard_normal((B, H, L, D))
+    k = a[None, None, :, None] * (1.0 + 0.05 * rng.standard_normal((B, H, L, D)))
+    v = rng.standard_normal((B, H, L, D))
+    qb, kb, vb = (W.f32_to_bf16_bits(x.astype(np.float32)) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = ssa.full_attn_fwd(to_device(qb, W.BF16), to_device(kb, W.BF16), to_device(vb, W.BF16), scale, block=s)
+    torch.cuda.synchronize()
+    R = np.array([0, 1, 63, 64, 65, 700, 1023, 1024, 1500, 2047])
+    q64, k64, v64 = (W.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb))
+    ro, rl = O.attend_full(q64, k64, v64, scale, rows=R)
+    eo = assert_close(to_f64(o)[:, :, R], ro, TOL[W.BF16], "o_full")
+    el = assert_close(to_f64(lse)[:, :, R], rl, 1e-3 * max(1.0, float(np.abs(rl).max())), "lse_full")
+    say(f"[oracle] growing logits (lse up to {float(np.abs(rl).max()):.1f}) variant={variant}: o {eo:.2e} lse {el:.2e}")
+
+
 # ----------------------------------------------------------------------------------
 # long-context workloads: sampled rows for outputs, selection on every row
 # ----------------------------------------------------------------------------------
