@@ -64,6 +64,7 @@ def test_attn_stats(variant, dtype, D, s, Hkv, stream):
     (1, 2, 1, 1152, 128, 64, 8, True),   # last tile of rows ragged (128 of 512), grouped heads
     (2, 1, 1, 640, 64, 128, 3, True),    # 128-token blocks, two sequences
     (1, 1, 1, 4096, 128, 64, 32, False),  # 32 entries per row, as in the long-context workload
+    (1, 2, 2, 4096, 64, 64, 48, True),    # more than 32 entries per row, D = 64
 ])
 def test_sparse_stats_gathered_rows(B, H, Hkv, L, D, s, topk, padded):
     """The sparse stream's measurements on shapes that exercise the gathered-row kernel,

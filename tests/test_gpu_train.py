@@ -133,6 +133,7 @@ def test_sparse_bwd_alone_matches_oracle():
     (1, 2, 1, 384, 64, 128, 2, True),     # 128-token blocks, grouped heads, padded rows
     (2, 2, 1, 2048, 128, 64, 16, True),   # several tiles, grouped heads, padded rows
     (1, 1, 1, 4096, 128, 64, 32, False),  # 32 entries per row, as in the long-context workload
+    (1, 2, 2, 4096, 64, 64, 48, True),    # more than 32 entries per row (idx walked from memory), D = 64
 ])
 def test_sparse_bwd_gathered_rows(B, H, Hkv, L, D, s, topk, padded):
     """The sparse stream's gradients alone on shapes that exercise the gathered-row dq:
