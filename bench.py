@@ -252,7 +252,7 @@ def main():
     ap.add_argument("--decode-workload", default="bf16_L32768_decode", choices=sorted(W.DECODE_WORKLOADS))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: there is no multi-GPU path "
               "(the kernels shard by head with no exchange; see the design notes).", file=sys.stderr)
         sys.exit(2)
     if args.path == "decode":
