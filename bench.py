@@ -253,7 +253,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path "
-              "(the kernels shard by head with no exchange; see the design notes).", file=sys.stderr)
+              "(every kernel is independent per (b, h), so the path would shard by head with no exchange).",
+              file=sys.stderr)
         sys.exit(2)
     if args.path == "decode":
         return main_decode(args)
