@@ -47,7 +47,7 @@ Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
                         (held) full one, both SmoothL1, weighted by alpha; its value and
                         the gradient it sends to each stream's output.
 
-Readings where the pages are silent (listed in full in the design notes):
+Readings where the pages are silent (the main ones):
   * candidates are the blocks strictly before the query's block; the own block is
     always attended (causal inside) and counts toward k;
   * fewer candidates than k-1: all of them are kept;
