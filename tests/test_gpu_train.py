@@ -128,6 +128,29 @@ def test_sparse_bwd_alone_matches_oracle():
                 np.testing.assert_allclose(r1, r2, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("D,Hkv", [(128, 2), (64, 1)])
+def test_full_bwd_length_not_multiple_of_256(D, Hkv):
+    """The full stream's gradients at L = 384, where the dense dq kernel takes its 128-row
+    form (four waves per workgroup: L is not a multiple of 256)."""
+    B, H, L, s = 1, 2, 384, 64
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "sink", seed=3800 + D, hkv=Hkv)
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    do = W.f32_to_bf16_bits(np.random.default_rng(3801 + D).standard_normal((B, H, L, D), dtype=np.float32)
+                            * np.float32(0.1))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = ssa.full_attn_fwd(q, k, v, scale, block=s)
+    dq, dk, dv = ssa.full_attn_bwd(q, k, v, o, lse, to_device(do, W.BF16), scale=scale, block=s)
+    torch.cuda.synchronize()
+    q64 = inp.as_f64("q")
+    k64, v64 = (inp.kv_per_query_head(inp.as_f64(n)) for n in ("k", "v"))
+    ref = O.attend_full_bwd(q64, k64, v64, W.bf16_bits_to_f32(do).astype(np.float64), scale)
+    errs = {}
+    for i, (got, nm) in enumerate(zip((dq, dk, dv), ("dq", "dk", "dv"))):
+        r = ref[i] if i == 0 else _kv_sum(ref[i], H, Hkv)
+        errs[nm] = close_rel(to_f64(got), r, TOL[W.BF16], f"{nm} L={L} D={D}")
+    say(f"[oracle] full bwd L={L} D={D} Hkv={Hkv}: {errs}")
+
+
 @pytest.mark.parametrize("B,H,Hkv,L,D,s,topk,padded", [
     (1, 2, 2, 384, 128, 64, 5, False),    # last tile of rows ragged (128 of 256)
     (1, 2, 1, 384, 64, 128, 2, True),     # 128-token blocks, grouped heads, padded rows
