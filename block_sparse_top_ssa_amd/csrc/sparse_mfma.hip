@@ -616,9 +616,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 static constexpr int kMaxLds = 160 * 1024 - 256;  // leave room for the static LDS (scan partials)
 
+// Rows per tile: the most (so each visited block serves the most rows) whose LDS fits.
 template <int D>
 static int pick_tile(const Dims& d, int topk) {
-  for (int T : {256, 128}) {
+  for (int T : {256, 192, 128}) {
     const int nb = d.n();  // upper bound on candidate blocks of any tile
     if (sparse_lds_layout<D>(T, nb, topk).total <= kMaxLds) return T;
   }
@@ -650,6 +651,7 @@ static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const 
                              const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int T = pick_tile<D>(d, topk);
   if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  if (T == 192) return run_sparse<D, S, 192>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
   return run_sparse<D, S, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
 }
 
