@@ -130,4 +130,22 @@ __device__ __forceinline__ uint64_t make_key(float score, int j) {
 __device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
 __device__ __forceinline__ float key_score(uint64_t key) { return unorderable_f32((uint32_t)(key >> 32)); }
 
+// ---------------------------------------------------------------- sparse rows that are full rows
+// Whether one row's idx list keeps every block below its own block b_t: its valid
+// entries (ascending, each in [0, b_t) and above the entry used before it -- the entries
+// the sparse kernels use) number b_t.  The sparse stream of such a row is plain causal
+// attention (paper sec. 3, p. 4: with every preceding block kept, nothing is dropped).
+__device__ __forceinline__ bool row_keeps_all(const int32_t* __restrict__ ir, int topk, int bt) {
+  if (bt > topk) return false;
+  int prev = -1, kept = 0;
+  for (int e = 0; e < topk; ++e) {
+    const int j = ir[e];
+    if (j > prev && j < bt) {
+      prev = j;
+      ++kept;
+    }
+  }
+  return kept == bt;
+}
+
 }  // namespace ssa

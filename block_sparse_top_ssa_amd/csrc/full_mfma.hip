@@ -17,6 +17,11 @@
 // chunk's probabilities would pass 2^64 (seen from their row sums, so no per-element row
 // maximum is formed off the diagonal), so the O accumulators are rarely rescaled.
 // With o == NULL only the running max and sums are kept (log-sum-exp only).
+// Given a sparse stream's idx (full rows of the sparse stream), a workgroup writes only
+// the 64-row query chunks whose rows all keep every earlier block -- those rows of the
+// sparse stream are exactly causal attention -- and leaves the rest to the sparse kernel.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -34,7 +39,8 @@ constexpr float kLag = 8.f;  // max path: log2 units the row max may pass the re
 template <int D, bool WANT_O>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void full_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2, int G) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2, int G,
+    const int32_t* __restrict__ didx, int dtopk, int dS) {
   constexpr int NT = 2;        // 16-row column tiles per wave
   constexpr int NW = 8;        // waves per workgroup (256 rows)
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
@@ -57,6 +63,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t kvh = bh / G;  // K/V head of this query head
   const uint16_t* kh = k + kvh * (int64_t)L * D;
   const u32x4* vth = vt + kvh * (int64_t)(L / 64) * VF * 64;  // per chunk: VF fragments of 64 lanes
+  __shared__ int chunk_full[4];  // with didx: 64-row query chunks this workgroup writes
+  if (didx) {
+    if (threadIdx.x < 4) chunk_full[threadIdx.x] = 1;
+    __syncthreads();
+    const int t = tile * 256 + (int)threadIdx.x;
+    if (threadIdx.x < 256 && t < L && !row_keeps_all(didx + (bh * (int64_t)L + t) * dtopk, dtopk, t / dS))
+      chunk_full[threadIdx.x / 64] = 0;
+    __syncthreads();
+    if (!(chunk_full[0] | chunk_full[1] | chunk_full[2] | chunk_full[3])) return;  // uniform
+  }
   const int rq = late ? 32 : 0;              // row offset inside the diagonal chunk
   const int r0 = tile * 256 + 64 * (w & 3) + rq;  // first row of this wave
   const bool active = r0 < L;
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (c + 1 <= cmax + 1) interval(c + 1, kB, vB, kA, vA);
   }
 
-  if (!active) return;
+  if (!active || (didx && !chunk_full[w & 3])) return;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = lsum[nt];
@@ -351,14 +367,23 @@ bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d
 
 template <int D, bool WANT_O>
 static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
-                           float* lse, hipStream_t st) {
-  const int ntile = (d.L + 255) / 256;
+                           float* lse, hipStream_t st, const int32_t* didx = nullptr, int dtopk = 0) {
+  // with didx only the leading rows t < topk * s can keep every earlier block
+  const int rows = didx ? (int)std::min<int64_t>(d.L, (int64_t)dtopk * d.S) : d.L;
+  const int ntile = (rows + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
   hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
-                     scale * kLog2e, d.G());
+                     scale * kLog2e, d.G(), didx, dtopk, d.S);
   return hipGetLastError();
+}
+
+hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* k, const u32x4* vt,
+                                      const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                      hipStream_t st) {
+  return d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st, idx, topk)
+                    : run_full<64, true>(d, q, k, vt, scale, o, lse, st, idx, topk);
 }
 
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,

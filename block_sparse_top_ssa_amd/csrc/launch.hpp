@@ -106,6 +106,11 @@ LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean,
 bool full_mfma_supported(const Dims& d);
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale,
                               void* o, float* lse, hipStream_t st);
+// The dense kernel over the sparse stream's full rows: writes o and lse of the 64-row
+// query chunks whose rows all keep every earlier block (row_keeps_all), nothing else.
+hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* k, const u32x4* vt,
+                                      const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                      hipStream_t st);
 bool sparse_mfma_supported(const Dims& d, int topk);
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v,
                                 const int32_t* idx, int topk, float scale, void* o, float* lse,

@@ -30,6 +30,10 @@
 //     Because every row uses the fixed reference m_ref, partial sums from different
 //     blocks simply add, in any order, with no rescaling.
 //  4. finalize: o = O / l (bf16), lse = m_ref + log l.
+// A 64-row query chunk whose rows all keep every block below their own (the leading
+// rows t < topk * s, or every row when topk covers all blocks) is plain causal
+// attention; this kernel skips it and the dense kernel, launched next on the same
+// stream, writes it (it keeps each row's O in registers, which gathered rows cannot).
 //
 // m_ref is an attained logit of the row, so l >= 1 and nothing underflows.  If any
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass
@@ -58,7 +62,7 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
   s.lse2 = o;  o += T * 4;   // row sums of the float32 p (log-sum-exp)
   s.mref = o;  o += T * 4;
   s.off = o;   o += (nb + 1) * 4;
-  s.misc = o;  o += 32;
+  s.misc = o;  o += 48;  // 4 item counts, 4 chunk flags
   o = (o + 15) & ~15;
   s.slots = o;  // 2 sets x 4 slots; the per-block counters of the index build live here first
   o += 8 * kSlotBytes > nb * 4 ? 8 * kSlotBytes : nb * 4;
@@ -118,6 +122,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int* cnt = reinterpret_cast<int*>(smem + lay.slots);  // index build only
   int* off = reinterpret_cast<int*>(smem + lay.off);
   int* misc = reinterpret_cast<int*>(smem + lay.misc);
+  int* chunk_full = misc + 4;  // per 64-row query chunk: its rows all keep every earlier block
   Slot* slots = reinterpret_cast<Slot*>(smem + lay.slots);  // [2][4]: set, score wave
   uint8_t* flag = smem + lay.flag;
   uint8_t* list = smem + lay.list;
@@ -216,10 +221,24 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (32 * w < rows && w < T / 32) own_load(w);
 
   // ---------------------------------------------------------------- 1. inverted index
+  // A row whose kept blocks are all the blocks below its own block is plain causal
+  // attention.  A 64-row query chunk made only of such rows is left to the dense kernel
+  // (launched after this one, it applies the same test) and takes no part here.
   for (int j = tid; j < nb; j += NTH) cnt[j] = 0;
   for (int r = tid; r < T; r += NTH) flag[r] = 0;
+  if (tid < 4) chunk_full[tid] = 1;
   __syncthreads();
-  if (tid < rows) for_each_entry(t0 + tid, [&](int j) { atomicAdd(&cnt[j], 1); });
+  if (tid < rows) {
+    int kept = 0;
+    for_each_entry(t0 + tid, [&](int) { ++kept; });
+    if (kept != (t0 + tid) / S) chunk_full[tid / 64] = 0;
+  }
+  __syncthreads();
+  bool tile_full = true;
+  for (int c = 0; c < rows / 64; ++c) tile_full = tile_full && chunk_full[c];
+  if (tile_full) return;  // uniform: the dense kernel writes every row of this tile
+  auto row_here = [&](int r) { return !chunk_full[r / 64]; };
+  if (tid < rows && row_here(tid)) for_each_entry(t0 + tid, [&](int j) { atomicAdd(&cnt[j], 1); });
   __syncthreads();
   {  // exclusive prefix sum of cnt[0..nb) into off[0..nb]; thread-contiguous segments
     const int seg = (nb + NTH - 1) / NTH;
@@ -247,7 +266,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   for (int j = tid; j < nb; j += NTH) cnt[j] = off[j];  // cnt becomes the fill cursor
   __syncthreads();
-  if (tid < rows) for_each_entry(t0 + tid, [&](int j) { list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid; });
+  if (tid < rows && row_here(tid)) for_each_entry(t0 + tid, [&](int j) { list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid; });
 
   // ---------------------------------------------------------------- 2. own-block phase
   // Unit = 32 rows (two 16-row column tiles) of one 64-row query chunk against the
@@ -255,6 +274,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int u = w; u < T / 32; u += NW) {
     const int r0 = 32 * u;  // tile-relative first row of the unit
     if (r0 >= rows) break;
+    if (!row_here(r0)) continue;
     const int qc = r0 / 64, rq = r0 % 64;  // query chunk and row offset inside it
     const int c_diag = (t0 + 64 * qc) / 64;
     if (u != w) own_load(u);  // the first unit's operands were loaded before phase 1
@@ -579,7 +599,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // ---------------------------------------------------------------- 4. finalize
   for (int it = tid; it < rows * (D / 8); it += NTH) {
     const int r = it / (D / 8), c8 = it % (D / 8);
-    if (flag[r]) continue;
+    if (flag[r] || !row_here(r)) continue;
     const float inv = 1.f / lst[r];
     const f32x4 a = *reinterpret_cast<const f32x4*>(ost + ost_granule<D>(r, 8 * c8));
     const f32x4 b = *reinterpret_cast<const f32x4*>(ost + ost_granule<D>(r, 8 * c8 + 4));
@@ -588,7 +608,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   if (lse)
     for (int r = tid; r < rows; r += NTH)
-      if (!flag[r]) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lsx[r])) * kLn2;
+      if (!flag[r] && row_here(r)) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lsx[r])) * kLn2;
 
   // ---------------------------------------------------------------- 5. exact recompute of flagged rows
   int any = 0;
@@ -668,6 +688,7 @@ LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, con
   else
     r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
                       : dispatch_t<64, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st);
   const hipError_t ef = vfrag_release(ws, st);
   if (r.err == hipSuccess) r.err = ef;
   return r;
