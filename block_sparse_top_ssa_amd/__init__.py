@@ -80,6 +80,28 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, shape, dtype, device, what):
+    """The C ABI cannot see buffer sizes, so every tensor passed down is checked here:
+    shape, dtype, device and contiguity, before any launch."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise SSAError(1, f"{what} must be a tensor")
+    if t.dtype != dtype:
+        raise SSAError(3, f"{what} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise SSAError(2, f"{what} must have shape {tuple(int(x) for x in shape)} (got {tuple(t.shape)})")
+    if t.device != device:
+        raise SSAError(4, f"{what} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise SSAError(4, f"{what} must be contiguous")
+    return t
+
+
+def _kmean_shape(d: Dims):
+    return (d.B, d.Hkv or d.H, d.L // d.block, d.D)
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -102,15 +124,21 @@ def block_pool(k: torch.Tensor, block: int, out: torch.Tensor | None = None) -> 
     d = _dims(k, block)
     if out is None:
         out = torch.empty((d.B, d.H, d.L // d.block, d.D), dtype=torch.float32, device=k.device)
+    _expect(out, (d.B, d.H, d.L // d.block, d.D), torch.float32, k.device, "block_pool out")
     check(load().ssa_block_pool(ctypes.byref(d), _ptr(k), _ptr(out), _stream(k)))
     return out
 
 
 def block_topk(q: torch.Tensor, k_mean: torch.Tensor, block: int, topk: int, want_scores: bool = False,
                out: torch.Tensor | None = None):
-    d = _dims(q, block, k_mean.shape[1] if k_mean.dim() == 4 else 0)
+    if not isinstance(k_mean, torch.Tensor) or k_mean.dim() != 4 or k_mean.shape[1] < 1 or q.dim() != 4 \
+            or q.shape[1] % k_mean.shape[1]:
+        raise SSAError(2, "k_mean must be float32 [B, Hkv, L // block, D] with Hkv dividing q's heads")
+    d = _dims(q, block, k_mean.shape[1])
+    _expect(k_mean, _kmean_shape(d), torch.float32, q.device, "k_mean")
     if out is None:
         out = torch.empty((d.B, d.H, d.L, topk), dtype=torch.int32, device=q.device)
+    _expect(out, (d.B, d.H, d.L, topk), torch.int32, q.device, "block_topk out")
     sel = torch.empty((d.B, d.H, d.L, topk), dtype=torch.float32, device=q.device) if want_scores else None
     check(load().ssa_block_topk(ctypes.byref(d), _ptr(q), _ptr(k_mean), int(topk), _ptr(out), _ptr(sel),
                                 _stream(q)))
@@ -123,11 +151,15 @@ def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_l
     if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
         raise SSAError(2, "idx must be int32 [B, H, L, topk]")
     topk = idx.shape[3]
+    _expect(idx, idx.shape, torch.int32, q.device, "idx")
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, q.shape, q.dtype, q.device, "sparse_attn_fwd out")
     if want_lse and lse is None:
         lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "sparse_attn_fwd lse")
     check(load().ssa_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(topk),
                                      ctypes.c_float(scale), _ptr(out), _ptr(lse if want_lse else None),
                                      _stream(q)))
@@ -140,8 +172,12 @@ def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if want_o and out is None:
         out = torch.empty_like(q)
+    if want_o:
+        _expect(out, q.shape, q.dtype, q.device, "full_attn_fwd out")
     if want_lse and lse is None:
         lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "full_attn_fwd lse")
     check(load().ssa_full_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale),
                                    _ptr(out if want_o else None), _ptr(lse if want_lse else None),
                                    _stream(q)))
@@ -155,8 +191,16 @@ def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, bloc
     if ref is None:
         raise SSAError(1, "align_stats needs o_full or dims_like to know [B, H, L, D]")
     if o_full is not None:
+        if o_sparse is None:
+            raise SSAError(1, "align_stats needs both o_full and o_sparse")
         _same(o_full, o_sparse, "o_full/o_sparse")
+        if o_sparse.device != o_full.device:
+            raise SSAError(4, "o_full and o_sparse are on different devices")
     d = _dims(ref, block)
+    if (lse_full is None) != (lse_sparse is None):
+        raise SSAError(1, "align_stats needs both lse_full and lse_sparse")
+    _expect(lse_full, (d.B, d.H, d.L), torch.float32, ref.device, "lse_full")
+    _expect(lse_sparse, (d.B, d.H, d.L), torch.float32, ref.device, "lse_sparse")
     dist = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if o_full is not None else None
     drop = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if lse_full is not None else None
     check(load().ssa_align_stats(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
@@ -176,10 +220,21 @@ def _cache_dims(q_like: torch.Tensor, k_cache: torch.Tensor, block: int) -> Dims
     return Dims(B, q_like.shape[1], L, D, int(block), _dtype_code(k_cache), Hkv)
 
 
-def _pos(pos: torch.Tensor, B: int) -> torch.Tensor:
-    if pos.dtype != torch.int32 or pos.shape != (B,):
+def _pos(pos: torch.Tensor, B: int, device) -> torch.Tensor:
+    if not isinstance(pos, torch.Tensor) or pos.dtype != torch.int32 or pos.shape != (B,):
         raise SSAError(2, "pos must be an int32 [B] device tensor")
-    return pos
+    return _expect(pos, (B,), torch.int32, device, "pos")
+
+
+def _decode_operands(d: Dims, q, k_cache, v_cache, k_mean):
+    """Checks the caches (same shape and dtype), k_mean ([B, Hkv, L // block, D] float32)
+    and that everything sits on q's device."""
+    if v_cache is not None:
+        _same(k_cache, v_cache, "k_cache/v_cache")
+        _expect(v_cache, k_cache.shape, k_cache.dtype, q.device, "v_cache")
+    _expect(k_cache, k_cache.shape, k_cache.dtype, q.device, "k_cache")
+    if k_mean is not None:
+        _expect(k_mean, _kmean_shape(d), torch.float32, q.device, "k_mean")
 
 
 def decode_append(pos, k_new, v_new, k_cache, v_cache, k_mean, block: int):
@@ -187,8 +242,11 @@ def decode_append(pos, k_new, v_new, k_cache, v_cache, k_mean, block: int):
     key of that row's block in k_mean ([B, Hkv, L // block, D] float32), in place."""
     d = _cache_dims(k_new, k_cache, block)
     _same(k_new, v_new, "k_new/v_new")
-    _same(k_cache, v_cache, "k_cache/v_cache")
-    check(load().ssa_decode_append(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(k_new), _ptr(v_new),
+    if d.H != d.Hkv:
+        raise SSAError(2, "k_new and v_new must have the cache's key/value heads [B, Hkv, D]")
+    _expect(v_new, k_new.shape, k_new.dtype, k_new.device, "v_new")
+    _decode_operands(d, k_new, k_cache, v_cache, k_mean)
+    check(load().ssa_decode_append(ctypes.byref(d), _ptr(_pos(pos, d.B, k_new.device)), _ptr(k_new), _ptr(v_new),
                                    _ptr(k_cache), _ptr(v_cache), _ptr(k_mean), _stream(k_cache)))
 
 
@@ -196,15 +254,32 @@ def decode_sparse_fwd(pos, q, k_cache, v_cache, k_mean, block: int, topk: int, s
                       want_lse: bool = True, want_idx: bool = True):
     """Selection and sparse attention for the query q[b, h] ([B, H, D]) at position pos[b].
     Returns (o [B, H, D], lse [B, H] or None, idx [B, H, topk] or None)."""
+    return _decode_sparse("ssa_decode_sparse_fwd", pos, q, k_cache, v_cache, k_mean, block, topk, scale,
+                          want_lse, want_idx, None, None, None)
+
+
+def _decode_sparse(entry, pos, q, k_cache, v_cache, k_mean, block, topk, scale, want_lse, want_idx, o, lse, idx):
     d = _cache_dims(q, k_cache, block)
-    _same(k_cache, v_cache, "k_cache/v_cache")
+    _decode_operands(d, q, k_cache, v_cache, k_mean)
+    if k_mean is None or v_cache is None:
+        raise SSAError(1, "decode_sparse_fwd needs v_cache and k_mean")
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
-    o = torch.empty_like(q)
-    lse = torch.empty((d.B, d.H), dtype=torch.float32, device=q.device) if want_lse else None
-    idx = torch.empty((d.B, d.H, int(topk)), dtype=torch.int32, device=q.device) if want_idx else None
-    check(load().ssa_decode_sparse_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(q), _ptr(k_cache),
-                                       _ptr(v_cache), _ptr(k_mean), int(topk), ctypes.c_float(scale), _ptr(o),
-                                       _ptr(lse), _ptr(idx), _stream(q)))
+    if o is None:
+        o = torch.empty_like(q)
+    _expect(o, q.shape, q.dtype, q.device, "o")
+    if want_lse and lse is None:
+        lse = torch.empty((d.B, d.H), dtype=torch.float32, device=q.device)
+    if not want_lse:
+        lse = None
+    _expect(lse, (d.B, d.H), torch.float32, q.device, "lse")
+    if want_idx and idx is None:
+        idx = torch.empty((d.B, d.H, int(topk)), dtype=torch.int32, device=q.device)
+    if not want_idx:
+        idx = None
+    _expect(idx, (d.B, d.H, int(topk)), torch.int32, q.device, "idx")
+    check(getattr(load(), entry)(ctypes.byref(d), _ptr(_pos(pos, d.B, q.device)), _ptr(q), _ptr(k_cache),
+                                 _ptr(v_cache), _ptr(k_mean), int(topk), ctypes.c_float(scale), _ptr(o),
+                                 _ptr(lse), _ptr(idx), _stream(q)))
     return o, lse, idx
 
 
@@ -213,12 +288,13 @@ def decode_full_fwd(pos, q, k_cache, v_cache, scale: float | None = None, want_o
     """Dense attention for the query q[b, h] at position pos[b] over cache rows 0..pos[b].
     Returns (o [B, H, D] or None, lse [B, H] or None)."""
     d = _cache_dims(q, k_cache, block)
-    if v_cache is not None:
-        _same(k_cache, v_cache, "k_cache/v_cache")
+    _decode_operands(d, q, k_cache, v_cache, None)
+    if want_o and v_cache is None:
+        raise SSAError(1, "decode_full_fwd needs v_cache for o")
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     o = torch.empty_like(q) if want_o else None
     lse = torch.empty((d.B, d.H), dtype=torch.float32, device=q.device) if want_lse else None
-    check(load().ssa_decode_full_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B)), _ptr(q), _ptr(k_cache),
+    check(load().ssa_decode_full_fwd(ctypes.byref(d), _ptr(_pos(pos, d.B, q.device)), _ptr(q), _ptr(k_cache),
                                      _ptr(v_cache), ctypes.c_float(scale), _ptr(o), _ptr(lse), _stream(q)))
     return o, lse
 
@@ -232,9 +308,16 @@ def _grad_bufs(q, k, dq, dk, dv):
     if dv is None:
         dv = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
     for t, ref, what in ((dq, q, "dq"), (dk, k, "dk"), (dv, k, "dv")):
-        if t.dtype != torch.float32 or t.shape != ref.shape:
-            raise SSAError(2, f"{what} must be float32 of shape {tuple(ref.shape)}")
+        _expect(t, ref.shape, torch.float32, q.device, what)
     return dq, dk, dv
+
+
+def _bwd_operands(d: Dims, q, k, v, o, lse, dout):
+    for t, what in ((k, "k"), (v, "v")):
+        _expect(t, k.shape, q.dtype, q.device, what)
+    for t, what in ((o, "o"), (dout, "dout")):
+        _expect(t, q.shape, q.dtype, q.device, what)
+    _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "lse")
 
 
 def full_attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale: float | None = None, block: int = 64):
@@ -243,6 +326,7 @@ def full_attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, scale: float
     d = _dims(q, block, _kv_heads(q, k, v))
     _same(o, q, "o/q")
     _same(dout, q, "dout/q")
+    _bwd_operands(d, q, k, v, o, lse, dout)
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     dq, dk, dv = _grad_bufs(q, k, dq, dk, dv)
     check(load().ssa_full_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
@@ -257,6 +341,8 @@ def sparse_attn_bwd(q, k, v, o, lse, dout, idx, block: int, dq=None, dk=None, dv
     _same(dout, q, "dout/q")
     if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
         raise SSAError(2, "idx must be int32 [B, H, L, topk]")
+    _expect(idx, idx.shape, torch.int32, q.device, "idx")
+    _bwd_operands(d, q, k, v, o, lse, dout)
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     dq, dk, dv = _grad_bufs(q, k, dq, dk, dv)
     check(load().ssa_sparse_attn_bwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
@@ -269,6 +355,7 @@ def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0, want_grads: bo
     """Returns (loss [1] float32, dloss/do_full, dloss/do_sparse) of the bidirectional
     SmoothL1 alignment objective; the gradients are float32 tensors shaped like o."""
     _same(o_full, o_sparse, "o_full/o_sparse")
+    _expect(o_sparse, o_full.shape, o_full.dtype, o_full.device, "o_sparse")
     d = _dims(o_full, 64)
     loss = torch.empty((1,), dtype=torch.float32, device=o_full.device)
     gf = torch.empty(o_full.shape, dtype=torch.float32, device=o_full.device) if want_grads else None
@@ -283,7 +370,15 @@ def attn_stats(q, k, lse, block: int, idx=None, scale: float | None = None, want
                want_hist: bool = True):
     """Row entropy [B, H, L] and attention mass by block distance [B, H, 16] of the full
     stream (idx None) or the sparse stream (its idx), given that stream's lse."""
-    d = _dims(q, block, k.shape[1] if k.dim() == 4 else 0)
+    if not isinstance(k, torch.Tensor) or k.dim() != 4 or q.dim() != 4 or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise SSAError(2, "k must be [B, Hkv, L, D] with Hkv dividing q's heads")
+    d = _dims(q, block, k.shape[1])
+    _expect(k, (d.B, k.shape[1], d.L, d.D), q.dtype, q.device, "k")
+    _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "lse")
+    if idx is not None:
+        if idx.dim() != 4:
+            raise SSAError(2, "idx must be int32 [B, H, L, topk]")
+        _expect(idx, (d.B, d.H, d.L, idx.shape[3]), torch.int32, q.device, "idx")
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
     hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
