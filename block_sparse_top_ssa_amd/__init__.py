@@ -39,7 +39,7 @@ import torch
 from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
-           "decode_append", "decode_sparse_fwd", "decode_full_fwd",
+           "decode_append", "decode_sparse_fwd", "decode_sparse_fwd_noalloc", "decode_full_fwd",
            "full_attn_bwd", "sparse_attn_bwd", "align_loss", "attn_stats",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
 
@@ -256,6 +256,16 @@ def decode_sparse_fwd(pos, q, k_cache, v_cache, k_mean, block: int, topk: int, s
     Returns (o [B, H, D], lse [B, H] or None, idx [B, H, topk] or None)."""
     return _decode_sparse("ssa_decode_sparse_fwd", pos, q, k_cache, v_cache, k_mean, block, topk, scale,
                           want_lse, want_idx, None, None, None)
+
+
+def decode_sparse_fwd_noalloc(pos, q, k_cache, v_cache, k_mean, block: int, topk: int, scale: float | None = None,
+                              out=None, lse=None, idx=None, want_lse: bool = True, want_idx: bool = True):
+    """decode_sparse_fwd through the library entry point that allocates nothing (its
+    scratch is a fixed 16 MiB device array; calls overlapping on one device race).  Pass
+    out ([B, H, D]), lse ([B, H] float32) and idx ([B, H, topk] int32) to allocate nothing
+    here either; the ones left None are created."""
+    return _decode_sparse("ssa_decode_sparse_fwd_noalloc", pos, q, k_cache, v_cache, k_mean, block, topk, scale,
+                          want_lse, want_idx, out, lse, idx)
 
 
 def _decode_sparse(entry, pos, q, k_cache, v_cache, k_mean, block, topk, scale, want_lse, want_idx, o, lse, idx):

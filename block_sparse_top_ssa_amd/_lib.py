@@ -35,6 +35,7 @@ PROTOTYPES = {
     "ssa_align_stats": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_decode_append": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_decode_sparse_fwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),
+    "ssa_decode_sparse_fwd_noalloc": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),
     "ssa_decode_full_fwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP]),
     "ssa_full_attn_bwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP]),
     "ssa_sparse_attn_bwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),

@@ -223,6 +223,31 @@ ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const
                 "ssa_decode_sparse_fwd");
 }
 
+ssa_status ssa_decode_sparse_fwd_noalloc(const ssa_dims* dims, const int32_t* pos, const void* q,
+                                         const void* k_cache, const void* v_cache, const float* k_mean, int32_t topk,
+                                         float scale, void* o, float* lse, int32_t* idx, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(pos, "pos", 4));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k_cache, "k_cache", 16));
+  SSA_TRY(check_ptr(v_cache, "v_cache", 16));
+  SSA_TRY(check_ptr(k_mean, "k_mean", 16));
+  SSA_TRY(check_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  SSA_TRY(check_opt_ptr(idx, "idx", 4));
+  if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_scale(scale));
+  const size_t need = ssa::decode_sparse_scratch_bytes(d, topk, idx != nullptr);
+  if (need > ssa::kDecodeScratchMax)
+    return fail(SSA_ERR_SHAPE, "ssa_decode_sparse_fwd_noalloc: needs %zu bytes of scratch, above its %zu-byte limit",
+                need, ssa::kDecodeScratchMax);
+  SSA_TRY(check_device());
+  return finish(ssa::launch_decode_sparse_noalloc(d, pos, q, k_cache, v_cache, k_mean, topk, scale, o, lse, idx,
+                                                  (hipStream_t)stream),
+                "ssa_decode_sparse_fwd_noalloc");
+}
+
 ssa_status ssa_decode_full_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
                                const void* v_cache, float scale, void* o, float* lse, void* stream) {
   ssa::Dims d;

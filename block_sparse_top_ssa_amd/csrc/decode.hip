@@ -14,6 +14,8 @@
 // fills the chip.
 #include <cmath>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 #include "pool.hpp"
@@ -643,6 +645,30 @@ LaunchResult launch_decode_append(const Dims& d, const int32_t* pos, const void*
   return r;
 }
 
+size_t decode_sparse_scratch_bytes(const Dims& d, int topk, bool own_idx) {
+  const int ns = splits(d, true, topk);
+  const size_t part_bytes = (size_t)d.bh() * ns * (d.D + 2) * sizeof(float);
+  return part_bytes + (own_idx ? 0 : (size_t)d.bh() * topk * sizeof(int32_t));
+}
+
+// Selection, split attention and combine; `ws` holds the split results and, when the
+// caller passes no idx, the kept blocks.  The combine reads only the splits the same
+// call wrote, so ws needs no clearing.
+static hipError_t decode_sparse_into(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                     const void* v_cache, const float* k_mean, int topk, float scale, void* o,
+                                     float* lse, int32_t* idx, void* ws, hipStream_t st) {
+  const size_t part_bytes = decode_sparse_scratch_bytes(d, topk, true);
+  float* part = static_cast<float*>(ws);
+  int32_t* sel = idx ? idx : reinterpret_cast<int32_t*>(static_cast<char*>(ws) + part_bytes);
+  return dispatch(d, [&](auto t, auto dd) {
+    using T = decltype(t);
+    constexpr int D = decltype(dd)::value;
+    hipError_t e = run_topk<T, D>(d, pos, q, k_mean, topk, sel, st);
+    if (e != hipSuccess) return e;
+    return run_attn<T, D, true, true>(d, pos, q, k_cache, v_cache, sel, topk, scale, o, lse, part, st);
+  });
+}
+
 LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
                                   const void* v_cache, const float* k_mean, int topk, float scale, void* o, float* lse,
                                   int32_t* idx, hipStream_t st) {
@@ -651,23 +677,57 @@ LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void*
     r.unsupported = "decoding selects over at most 8192 blocks (L / block)";
     return r;
   }
-  const int ns = splits(d, true, topk);
-  const size_t part_bytes = (size_t)d.bh() * ns * (d.D + 2) * sizeof(float);
-  const size_t idx_bytes = idx ? 0 : (size_t)d.bh() * topk * sizeof(int32_t);
   void* ws = nullptr;
-  r.err = workspace_alloc(part_bytes + idx_bytes, &ws, st);
+  r.err = workspace_alloc(decode_sparse_scratch_bytes(d, topk, idx != nullptr), &ws, st);
   if (r.err != hipSuccess) return r;
-  float* part = static_cast<float*>(ws);
-  int32_t* sel = idx ? idx : reinterpret_cast<int32_t*>(static_cast<char*>(ws) + part_bytes);
-  r.err = dispatch(d, [&](auto t, auto dd) {
-    using T = decltype(t);
-    constexpr int D = decltype(dd)::value;
-    hipError_t e = run_topk<T, D>(d, pos, q, k_mean, topk, sel, st);
-    if (e != hipSuccess) return e;
-    return run_attn<T, D, true, true>(d, pos, q, k_cache, v_cache, sel, topk, scale, o, lse, part, st);
-  });
+  r.err = decode_sparse_into(d, pos, q, k_cache, v_cache, k_mean, topk, scale, o, lse, idx, ws, st);
   const hipError_t fe = workspace_free(ws, st);
   if (r.err == hipSuccess) r.err = fe;
+  return r;
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// The same work with its scratch in a fixed device array instead of the pool, for
+// callers that cannot allocate (graph capture, serving loops).  Each device holds its
+// own copy of the array, at an address found once per device with that device current;
+// host code uses that address, never the array's name (a host-side stand-in).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchMax];
+
+static hipError_t scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+LaunchResult launch_decode_sparse_noalloc(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                          const void* v_cache, const float* k_mean, int topk, float scale, void* o,
+                                          float* lse, int32_t* idx, hipStream_t st) {
+  LaunchResult r;
+  if (!decode_sparse_supported(d)) {
+    r.unsupported = "decoding selects over at most 8192 blocks (L / block)";
+    return r;
+  }
+  if (decode_sparse_scratch_bytes(d, topk, idx != nullptr) > kDecodeScratchMax) {
+    r.unsupported = "needs more than the 16 MiB of fixed scratch (B*H*ceil(topk*block/256)*(D+2)*4 bytes, plus "
+                    "B*H*topk*4 when idx is NULL)";
+    return r;
+  }
+  void* ws = nullptr;
+  r.err = scratch_address(&ws);
+  if (r.err != hipSuccess) return r;
+  r.err = decode_sparse_into(d, pos, q, k_cache, v_cache, k_mean, topk, scale, o, lse, idx, ws, st);
   return r;
 }
 

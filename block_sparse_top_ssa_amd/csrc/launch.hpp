@@ -61,6 +61,13 @@ LaunchResult launch_decode_append(const Dims& d, const int32_t* pos, const void*
 LaunchResult launch_decode_sparse(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
                                   const void* v_cache, const float* k_mean, int topk, float scale, void* o, float* lse,
                                   int32_t* idx, hipStream_t st);
+// The same selection and sparse attention with its scratch in a fixed 16 MiB device array
+// (no allocation); bytes it needs (decode_sparse_scratch_bytes) above that are refused.
+constexpr size_t kDecodeScratchMax = size_t(16) << 20;
+size_t decode_sparse_scratch_bytes(const Dims& d, int topk, bool own_idx);
+LaunchResult launch_decode_sparse_noalloc(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
+                                          const void* v_cache, const float* k_mean, int topk, float scale, void* o,
+                                          float* lse, int32_t* idx, hipStream_t st);
 LaunchResult launch_decode_full(const Dims& d, const int32_t* pos, const void* q, const void* k_cache,
                                 const void* v_cache, float scale, void* o, float* lse, hipStream_t st);
 

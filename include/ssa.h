@@ -53,7 +53,8 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 5 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats */
+#define SSA_ABI_VERSION 6 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
+                             6: allocation-free sparse decoding */
 
 typedef int32_t ssa_status;
 enum {
@@ -218,6 +219,24 @@ ssa_status ssa_decode_append(const ssa_dims* dims, const int32_t* pos, const voi
 ssa_status ssa_decode_sparse_fwd(const ssa_dims* dims, const int32_t* pos, const void* q, const void* k_cache,
                                  const void* v_cache, const float* k_mean, int32_t topk, float scale, void* o,
                                  float* lse, int32_t* idx, void* stream);
+
+/*
+ * ssa_decode_sparse_fwd_noalloc -- ssa_decode_sparse_fwd with no allocation.
+ *   For callers that cannot allocate device memory during the call: code under HIP
+ *   graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ *   checks, kernels and results as ssa_decode_sparse_fwd; its scratch (the split results,
+ *   plus the kept blocks when idx is NULL) lives in a fixed 16 MiB device array that the
+ *   library holds on each device it runs on until the process ends, instead of the pool.
+ *   Limit: B*H*ceil(topk*block/256)*(D+2)*4 bytes, plus B*H*topk*4 when idx is NULL, at
+ *   most 16 MiB (16777216); larger calls return SSA_ERR_SHAPE before any work.  Nothing
+ *   in the array needs to start cleared: each call reads only what it has written.
+ *   Every call on one device shares that device's array, so calls that overlap on one
+ *   device (different streams, or different host threads) race and must be serialised
+ *   by the caller.
+ */
+ssa_status ssa_decode_sparse_fwd_noalloc(const ssa_dims* dims, const int32_t* pos, const void* q,
+                                         const void* k_cache, const void* v_cache, const float* k_mean, int32_t topk,
+                                         float scale, void* o, float* lse, int32_t* idx, void* stream);
 
 /*
  * ssa_decode_full_fwd -- dense attention over 0..pos[b] for one query per sequence.

@@ -184,3 +184,20 @@ def test_valid_call_without_device_reports_device_error(libssa):
     d = _dims()
     assert libssa.ssa_block_pool(ctypes.byref(d), FAKE, FAKE, None) == 5
     assert "device" in libssa.ssa_last_error().decode().lower() or libssa.ssa_last_error()
+
+
+def test_decode_noalloc_argument_checks(libssa):
+    """The allocation-free sparse decoding call checks like ssa_decode_sparse_fwd and
+    refuses, before any device work, a shape whose scratch would pass its 16 MiB array."""
+    d = _dims()
+    assert libssa.ssa_decode_sparse_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0.1,
+                                                None, None, None, None) == 1
+    assert libssa.ssa_decode_sparse_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1,
+                                                FAKE, None, None, None) == 2
+    assert libssa.ssa_decode_sparse_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 2, -1.0,
+                                                FAKE, None, None, None) == 4
+    # B*H*ceil(topk*block/256)*(D+2)*4 = 4096*8*130*4 = 17039360 bytes > 16 MiB
+    big = _dims(B=32, H=128, L=2048, block=128, D=128)
+    assert libssa.ssa_decode_sparse_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1,
+                                                FAKE, None, FAKE, None) == 2
+    assert "scratch" in libssa.ssa_last_error().decode()

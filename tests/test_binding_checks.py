@@ -52,6 +52,10 @@ QKV = dict(q=bf(B, H, L, D), k=bf(B, H, L, D), v=bf(B, H, L, D))
     (lambda: ssa.decode_sparse_fwd(i32(B), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D), bf(B, H, N, D), S, 2), 3),
     (lambda: ssa.decode_sparse_fwd(torch.zeros(B, dtype=torch.int64), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D),
                                    f32(B, H, N, D), S, 2), 2),
+    (lambda: ssa.decode_sparse_fwd_noalloc(i32(B), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D), f32(B, H, N, D), S, 2,
+                                           idx=i32(B, H, 3)), 2),
+    (lambda: ssa.decode_sparse_fwd_noalloc(i32(B), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D), f32(B, H, N, D), S, 2,
+                                           out=f32(B, H, D)), 3),
     (lambda: ssa.decode_append(i32(B), bf(B, H, D), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D), f32(B, H, N - 1, D),
                                S), 2),
     (lambda: ssa.decode_full_fwd(i32(B), bf(B, H, D), bf(B, H, L, D), bf(B, H, L, D + 8)), 2),
