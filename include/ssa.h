@@ -20,11 +20,15 @@
  *               memory); q, k, v, o, k_mean and the caches 16-byte aligned, idx, pos,
  *               lse, sel_score, l2_dist and dropped 4-byte aligned.  The caller owns every
  *               buffer it passes.  The library keeps no pointer to them after a call
- *               returns and writes nothing outside the outputs named by a call.  Four
- *               calls allocate: ssa_sparse_attn_fwd on bf16, ssa_full_attn_fwd on bf16
- *               with o given, the two decoding forward calls, the two backward calls,
- *               ssa_attn_stats and ssa_align_loss take a transient workspace (see
- *               ssa_sparse_attn_fwd).
+ *               returns and writes nothing outside the outputs named by a call.  These
+ *               calls take a transient workspace from a per-device stream-ordered pool
+ *               (sizes and error behaviour under ssa_sparse_attn_fwd and each call):
+ *                 - ssa_sparse_attn_fwd (bf16)
+ *                 - ssa_full_attn_fwd (bf16, with o given)
+ *                 - ssa_decode_sparse_fwd, ssa_decode_full_fwd
+ *                 - ssa_full_attn_bwd, ssa_sparse_attn_bwd
+ *                 - ssa_attn_stats, ssa_align_loss
+ *               ssa_decode_sparse_fwd_noalloc allocates nothing (a fixed device array).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -36,9 +40,12 @@
  *               B*H*L <= 2^24; the current device is gfx950.  A failed launch returns
  *               SSA_ERR_LAUNCH.  ssa_last_error() gives a thread-local message for the
  *               last failing call.  The library never prints, aborts or throws.
- *  Threads      stateless apart from a per-device properties cache and a per-device
- *               workspace pool, each created once under a lock; calls from several
- *               threads are safe.
+ *  Threads      stateless apart from a per-device properties cache, a per-device
+ *               workspace pool and the per-device address of the allocation-free
+ *               call's scratch array, each created once under a lock, and the
+ *               process-wide kernel choice of ssa_set_kernel_variant (an atomic read
+ *               by every call).  Calls from several threads are safe, except that
+ *               ssa_decode_sparse_fwd_noalloc calls overlapping on one device race.
  *  Determinism  ssa_block_pool, ssa_block_topk, ssa_full_attn_fwd and ssa_align_stats
  *               are deterministic.  ssa_sparse_attn_fwd accumulates partial sums in an
  *               order that can differ between runs (last-bit fp32 differences, which

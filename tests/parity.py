@@ -5,8 +5,22 @@
     may differ only in blocks whose oracle score lies in that tied band, and both must
     hold the same number of blocks and the own block;
   * float outputs: max abs error <= 2e-2 for bf16 and 1e-4 for fp32 I/O;
-  * L2 distance computed end to end: |error| <= 2 * tol * sqrt(D) (per-element tolerance
-    through the triangle inequality); from identical inputs: 1e-5 relative.
+  * log-sum-exps (float32 outputs) within TOL_LSE: 1e-3 for bf16 inputs, 1e-4 for fp32.
+    Derivation: the logits are float32 dot products of the same input values the
+    oracle reads (error <= D * 2^-24 * sum |q_d k_d|, ~1e-5 at these magnitudes); the
+    row sum is formed in blocks whose longest float32 addition chain is <= L/64 + 64
+    (< 600 at L = 32768), so its relative error is <= 600 * 2^-24 = 3.6e-5, and log
+    and exp add ~1e-7; 1e-3 leaves a wide margin over these and over what is measured
+    (~5e-6), yet is 20x tighter than the bf16 output bar.  The dropped mass
+    -expm1(lse_s - lse_f) moves by at most the two lse errors: 2 * TOL_LSE;
+  * L2 distance row by row: |dist_gpu - dist| <= ||o_f,gpu - o_f|| + ||o_s,gpu - o_s||
+    (triangle inequality, from each row's own output errors); from identical inputs:
+    1e-5 relative;
+  * the dropped-mass bound on the GPU's outputs, ||o_f - o_s|| <= 2 delta M_t with
+    M_t = max_{j<=t} ||v_j||, up to BOUND_SLACK * M_t: with bf16, P is rounded to bf16
+    before the value products (each weight moves by <= 2^-9 relative, each stream's
+    normalised weights by <= 2^-8 in total, so its output by <= 2^-8 M_t) and the output
+    is rounded to bf16 (<= 2^-9 M_t): 3 * 2^-8 M_t for the two streams, below 2^-6 M_t.
 """
 from __future__ import annotations
 
@@ -17,6 +31,8 @@ import workloads as W
 
 TIE_REL = 1e-5
 TOL = {W.BF16: 2e-2, W.F32: 1e-4}
+TOL_LSE = {W.BF16: 1e-3, W.F32: 1e-4}
+BOUND_SLACK = {W.BF16: 2.0 ** -6, W.F32: 1e-5}
 
 
 def to_device(a: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:

@@ -752,3 +752,33 @@ def test_attention_stats_brute_force():
         for i in range(t + 1):
             ref_h[O.distance_bucket(t // s - i // s)] += p[i]
     np.testing.assert_allclose(hist[0, 0], ref_h, rtol=1e-12, atol=1e-14)
+
+
+def test_topk_sigma_bounds_hand_worked():
+    """block_topk's sigma_m (score of the last kept candidate) and sigma_m1 (best score
+    left out), which bound the tie band the parity rule allows, worked by hand.  q = e_0
+    and the pooled keys' first components are the block scores; s = 2, query row t = 10
+    (block 5) so blocks 0..4 compete.
+      scores [5, 3, 9, 1, 7], topk 3 (m = 2): order 9 (j2), 7 (j4), 5 (j0), 3, 1 ->
+        kept {2, 4}, sigma_m = 7, sigma_m1 = 5;
+      scores [5, 7, 7, 1, 0], topk 2 (m = 1): equal scores by lower index -> kept {1},
+        sigma_m = 7 (j1), sigma_m1 = 7 (j2);
+      topk 6 (m = 5 = b_t, every candidate kept): sigma_m = 1 (the smallest),
+        sigma_m1 = NaN (nothing left out);
+      a row in block 0 has no candidate: both NaN."""
+    L, s, D = 12, 2, 4
+    q = np.zeros((1, 1, L, D))
+    q[0, 0, :, 0] = 1.0
+    for scores, topk, kept, sm, sm1 in (([5, 3, 9, 1, 7], 3, [2, 4], 7.0, 5.0),
+                                        ([5, 7, 7, 1, 0], 2, [1], 7.0, 7.0),
+                                        ([5, 3, 9, 1, 7], 6, [0, 1, 2, 3, 4], 1.0, np.nan)):
+        km = np.zeros((1, 1, L // s, D))
+        km[0, 0, :5, 0] = scores
+        idx, ex = O.block_topk(q, km, s, topk, rows=np.array([10, 1]), return_scores=True)
+        assert idx[0, 0, 0].tolist() == kept + [5] + [-1] * (topk - len(kept) - 1)
+        assert ex["sigma_m"][0, 0, 0] == sm
+        if np.isnan(sm1):
+            assert np.isnan(ex["sigma_m1"][0, 0, 0])
+        else:
+            assert ex["sigma_m1"][0, 0, 0] == sm1
+        assert np.isnan(ex["sigma_m"][0, 0, 1]) and np.isnan(ex["sigma_m1"][0, 0, 1])
