@@ -46,6 +46,11 @@ LaunchResult launch_full_generic(const Dims& d, const void* q, const void* k, co
 // pool kept per device; give it back with vfrag_release on the same stream.
 hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st);
 hipError_t vfrag_release(void* ws, hipStream_t st);
+// K of a bf16 [B,H,L,D] tensor in MFMA fragment order (the A operand of S^T = K Q^T):
+// per (b,h), 64-key chunk c, key tile kt and contraction chunk cc, 64 lanes x 16 bytes,
+// lane 16 g + i holding K[64 c + 16 kt + i][32 cc + 8 g .. +7]; B*H*L*D*2 bytes from the
+// same pool (d holds the key/value head count in H), given back with vfrag_release.
+hipError_t kfrag_acquire(const Dims& d, const void* k, void** ws, hipStream_t st);
 // The same rewrite of any bf16 [B,H,L,D] tensor (d.H heads) into a caller-given buffer.
 hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st);
 

@@ -8,8 +8,11 @@
 // each key block that any of its rows kept exactly once, multiplying only the rows
 // that kept it (gathered into 16-row MFMA column tiles):
 //
-//  0. (separate pass) V is rewritten once into MFMA fragment order, so the PV operand
-//     V^T is loaded with one coalesced 16-byte load per lane and no lane transposes;
+//  0. (separate passes) V and K are rewritten once into MFMA fragment order, so the PV
+//     operand V^T is loaded with one coalesced 16-byte load per lane and no lane
+//     transposes, and every K fragment is one contiguous 1 KB load (8 full cache lines
+//     instead of 16 half lines: the CU's address unit, the busiest resource here, pays
+//     per line);
 //  1. inverted index: from idx, count per block the rows that kept it, prefix-sum,
 //     and list the row ids per block (LDS, one byte per entry);
 //  2. own-block phase: each 64-row query chunk against its own 64-key chunk (causal)
@@ -97,7 +100,8 @@ __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
 template <int D, int S, int T>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const u32x4* __restrict__ vt, const int32_t* __restrict__ idx, int topk, uint16_t* __restrict__ o,
+    const u32x4* __restrict__ vt, const u32x4* __restrict__ ktf, const int32_t* __restrict__ idx, int topk,
+    uint16_t* __restrict__ o,
     float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G) {
   constexpr int NW = 8, NTH = 512;
   constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
@@ -134,6 +138,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const u32x4* vth = vt + kvh * (int64_t)(L / 64) * NDT * 2 * 64;
   const int32_t* ih = idx + bh * (int64_t)L * topk;
   auto vt_frag = [&](int c, int dt, int kc) -> u32x4 { return vth[((int64_t)(c * NDT + dt) * 2 + kc) * 64 + lane]; };
+  const u32x4* kth = ktf + kvh * (int64_t)(L / 64) * 4 * NC * 64;
+  // K fragment (key tile kt4, contraction chunk cc) of chunk c: one contiguous 1 KB load
+  auto k_frag = [&](int c, int kt4, int cc) -> u32x4 { return kth[((int64_t)(c * 4 + kt4) * NC + cc) * 64 + lane]; };
 
   // Walk the valid entries of one row's idx list: distinct blocks below b_t, each
   // greater than the entry used before it.  Entries are loaded 32 at a time.
@@ -207,7 +214,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) okf[kt][cc] = load_k_frag<D>(kh, c_diag * 64 + 16 * kt, cc);
+      for (int cc = 0; cc < NC; ++cc) okf[kt][cc] = k_frag(c_diag, kt, cc);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
+        for (int cc = 0; cc < NC; ++cc) kf[kt][cc] = k_frag(c, kt, cc);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -431,7 +438,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) ra[kt * NC + cc] = load_k_frag<D>(kh, c * 64 + 16 * kt, cc);
+        for (int cc = 0; cc < NC; ++cc) ra[kt * NC + cc] = k_frag(c, kt, cc);
     }
     const uint16_t* qrow = qh + (int64_t)(t0 + (r_cur < 0 ? 0 : r_cur)) * D;
 #pragma unroll
@@ -653,7 +660,8 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
 
 template <int D, int S, int T>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
-                             const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
+                             const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse,
+                             hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
   const int lds = sparse_lds_layout<D>(T, d.n(), topk).total;
@@ -661,18 +669,18 @@ static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const 
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
-                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, idx, topk,
+                     static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, kt, idx, topk,
                      static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G());
   return hipGetLastError();
 }
 
 template <int D, int S>
 static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
-                             const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
+                             const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
   const int T = pick_tile<D>(d, topk);
-  if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
-  if (T == 192) return run_sparse<D, S, 192>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
-  return run_sparse<D, S, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+  if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  if (T == 192) return run_sparse<D, S, 192>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  return run_sparse<D, S, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
 }
 
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -681,16 +689,24 @@ LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, con
   void* ws = nullptr;
   r.err = vfrag_acquire(d.kv(), v, &ws, st);
   if (r.err != hipSuccess) return r;
+  void* kws = nullptr;
+  r.err = kfrag_acquire(d.kv(), k, &kws, st);
+  if (r.err != hipSuccess) {
+    (void)vfrag_release(ws, st);
+    return r;
+  }
   const u32x4* vt = static_cast<const u32x4*>(ws);
+  const u32x4* kt = static_cast<const u32x4*>(kws);
   if (d.D == 128)
-    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<128, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<128, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
   else
-    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<64, 128>(d, q, k, v, vt, idx, topk, scale, o, lse, st);
+    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<64, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
   if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st);
   const hipError_t ef = vfrag_release(ws, st);
-  if (r.err == hipSuccess) r.err = ef;
+  const hipError_t ek = vfrag_release(kws, st);
+  if (r.err == hipSuccess) r.err = ef != hipSuccess ? ef : ek;
   return r;
 }
 

@@ -1,6 +1,7 @@
-// V rewritten once into the MFMA fragment order the attention kernels read as the A
-// operand of O^T = V^T P^T (paper sec. 3, p. 3-4: both streams multiply the attention
-// weights with V), and the stream-ordered workspace that holds it.
+// V (and, for the sparse stream, K) rewritten once into the MFMA fragment order the
+// attention kernels read as A operands -- of O^T = V^T P^T and S^T = K Q^T (paper sec. 3,
+// pp. 3-4: both streams score the keys against the query and weight V) -- and the
+// stream-ordered workspace that holds them.
 #include <mutex>
 
 #include "launch.hpp"
@@ -23,6 +24,23 @@ __global__ __launch_bounds__(256) void vfrag_kernel(const uint16_t* __restrict__
   const uint16_t* vh = v + bh * (int64_t)L * D;
   for (int f = w; f < F; f += 4)
     vt[(chunk * F + f) * 64 + lane] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, f >> 1, f & 1));
+}
+
+// ---------------------------------------------------------------- K in fragment order
+// Fragment (chunk c, key tile kt, contraction chunk cc) of a head: 64 lanes x 16 bytes;
+// lane l = 16 g + i holds K[64 c + 16 kt + i][32 cc + 8 g .. + 7], the A operand of
+// S^T = K Q^T.  Read from here a fragment is one contiguous 1 KB load (8 full cache
+// lines) instead of 16 half lines of K's rows.  One workgroup per 64-key chunk.
+template <int D>
+__global__ __launch_bounds__(256) void kfrag_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt, int L) {
+  constexpr int F = 4 * (D / 32);  // fragments per chunk
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t chunk = blockIdx.x;  // over B*H*(L/64), head-major
+  const int nck = L / 64;
+  const int64_t bh = chunk / nck;
+  const int c = (int)(chunk % nck);
+  const uint16_t* kh = k + bh * (int64_t)L * D;
+  for (int f = w; f < F; f += 4) kt[(chunk * F + f) * 64 + lane] = load_k_frag<D>(kh, c * 64 + 16 * (f / (D / 32)), f % (D / 32));
 }
 
 // ---------------------------------------------------------------- workspace
@@ -79,6 +97,30 @@ hipError_t vfrag_acquire(const Dims& d, const void* v, void** ws, hipStream_t st
 }
 
 hipError_t vfrag_release(void* ws, hipStream_t st) { return ws ? hipFreeAsync(ws, st) : hipSuccess; }
+
+template <int D>
+static hipError_t run_kfrag(const Dims& d, const void* k, u32x4* kt, hipStream_t st) {
+  const int64_t grid = d.bh() * (d.L / 64);
+  hipLaunchKernelGGL((kfrag_kernel<D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const uint16_t*>(k), kt,
+                     d.L);
+  return hipGetLastError();
+}
+
+hipError_t kfrag_acquire(const Dims& d, const void* k, void** ws, hipStream_t st) {
+  *ws = nullptr;
+  hipMemPool_t pool = nullptr;
+  hipError_t e = workspace_pool(&pool);
+  if (e != hipSuccess) return e;
+  e = hipMallocFromPoolAsync(ws, (size_t)d.tokens() * d.D * 2, pool, st);
+  if (e != hipSuccess) return e;
+  e = d.D == 128 ? run_kfrag<128>(d, k, static_cast<u32x4*>(*ws), st)
+                 : run_kfrag<64>(d, k, static_cast<u32x4*>(*ws), st);
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(*ws, st);
+    *ws = nullptr;
+  }
+  return e;
+}
 
 hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st) {
   return d.D == 128 ? run_vfrag<128>(d, x, static_cast<u32x4*>(out), st)
