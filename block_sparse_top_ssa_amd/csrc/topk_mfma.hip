@@ -7,24 +7,26 @@
 // of 64.  Scores are on MFMA: sigma = q . kbar with kbar (float32) split exactly into
 // three bf16 terms hi + mid + lo (each the bf16 rounding of what is left), so three
 // bf16 products per element give the float32 dot product (bf16 x bf16 products are
-// exact in the float32 accumulator).  Each wave scores 16 candidates against all rows
+// exact in the float32 accumulator).  Each wave scores 16 candidates against 64 rows
 // of the block and leaves the scores in LDS.  Candidates are ordered by 64-bit keys
 // (score, then lower block index first), so all keys of a row are distinct.
 //
-// Selection of the m = topk - 1 best keys per row (one wave per row at a time):
-//  * m <= 40 (two passes over the scores, computed twice):
-//    1. every lane keeps the largest score (as order-preserving bits) among the
-//       candidates it sees (j = lane mod 64); the m-th largest t of these 64 lane
-//       maxima gives a lower bound (t, 0) on the row's m-th largest key, because m of
-//       its keys have score bits >= t;
+// Selection of the m = topk - 1 best keys per row:
+//  * m <= 40 (two passes over the scores, computed twice; kbar is split once, ahead,
+//    into MFMA fragments).  A row's 64 candidates of a chunk go to the four lanes of a
+//    quad, 16 consecutive ones each:
+//    1. every lane keeps the largest score of each of its 16 candidate classes (block
+//       index mod 64); the m-th largest t of the row's 64 class maxima gives a lower
+//       bound (t, any block) on the row's m-th largest key, because m of its keys have
+//       scores >= t;
 //    2. the keys at or above that bound are collected in index order (about 31-45 for
 //       m = 31 on unstructured scores); their m-th largest is exactly the row's m-th
 //       largest key, and the keys at or above it are emitted in index order.  If more
 //       than 64 keys reach the bound, the m-th largest of the first 64 collected is a
 //       strictly higher bound and pass 2 runs again (only for such rows).
-//    Both m-th largest values come from a 32-bit sort of the score bits across the
-//    wave; equal scores at the cut are then settled by index with a ballot, which is
-//    exact because the collected keys sit in index order;
+//    Both m-th largest values come from a 32-bit sort of the score bits (a quad's 64
+//    values sorted in registers); equal scores at the cut are then settled by index
+//    with a ballot, which is exact because the collected keys sit in index order;
 //  * m > 40: each chunk's 64 keys are sorted across the wave with a bitonic network and
 //    merged into the row's running list of the best 64*E keys in LDS; the result is
 //    re-sorted by block index.  (For m close to 64 the first pass's bound is weak: rows
@@ -132,14 +134,11 @@ __device__ __forceinline__ uint64_t kth_key_index_ordered(uint64_t y, int m, uin
   return shfl_u64(y, src);
 }
 
-// ---------------------------------------------------------------- m-th largest of 16 rows at once
-// A wave holds 16 rows of 64 values (row r's value of lane l in v[r]).  Moved through
-// LDS so that lanes 4r .. 4r+3 hold row r's 64 values, 16 each, one sorting network in
-// registers then orders all 16 rows together: each lane sorts its 16 values, and two
-// bitonic merges with the partner lane's values in reverse order (lanes p^1, then p^3
-// and p^1) join them into the row's 64 values in descending order, element 16 p + i in
-// register i of lane 4r + p.  About 30 instructions per row, against about 125 for a
-// 64-lane network per row.
+// ---------------------------------------------------------------- m-th largest of 64 values per quad
+// With a row's 64 values spread over the four lanes of a quad, 16 each, one sorting
+// network in registers orders all 16 rows a wave holds at once: each lane sorts its 16
+// values, and two bitonic merges with the partner lane's values in reverse order join
+// them into the row's 64 values in descending order.
 __device__ __forceinline__ void minmax_u32(uint32_t& hi, uint32_t& lo) {
   const uint32_t a = hi, b = lo;
   hi = a > b ? a : b;
@@ -171,24 +170,13 @@ template <int PERM>
 __device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, PERM, 0xF, 0xF, false);
 }
-// out[r] = the m-th largest (1 <= m <= 64) of row r's 64 values, wave-uniform.
-// tmp: 1024 words of LDS owned by this wave.
-__device__ __forceinline__ void mth_largest_16rows(const uint32_t (&v)[16], int m, uint32_t* tmp,
-                                                   uint32_t (&out)[16]) {
+// The m-th largest (1 <= m <= 64) of the 64 values a quad holds (16 per lane), in
+// every lane of the quad.  The lane's 16 are sorted by an in-register network, then
+// bitonic merges with the partner lanes (p^1, then p^3 and p^1) join them into the
+// quad's 64 values in descending order, element 16 p + i in register i of lane p.
+// About 30 instructions per quad, against about 125 for a 64-lane network.
+__device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
   const int lane = threadIdx.x & 63, p = lane & 3;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) tmp[r * 64 + lane] = v[r];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint32_t x[16];
-  const u32x4* src = reinterpret_cast<const u32x4*>(tmp + (lane >> 2) * 64 + 16 * p);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 w4 = src[c];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * c + e] = w4[e];
-  }
   sort16_desc(x);
   {  // lanes p, p^1: two descending 16-lists into one descending 32-list over the pair
     uint32_t y[16];
@@ -199,7 +187,7 @@ __device__ __forceinline__ void mth_largest_16rows(const uint32_t (&v)[16], int 
     for (int i = 0; i < 16; ++i) x[i] = first ? (x[i] > y[i] ? x[i] : y[i]) : (x[i] > y[i] ? y[i] : x[i]);
     clean16_desc(x);
   }
-  {  // lanes 0,1 and 2,3: two descending 32-lists into the row's descending 64
+  {  // lanes 0,1 and 2,3: two descending 32-lists into the quad's descending 64
     uint32_t y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = quad_lane<0x1B>(x[15 - i]);  // quad_perm 3,2,1,0
@@ -217,9 +205,43 @@ __device__ __forceinline__ void mth_largest_16rows(const uint32_t (&v)[16], int 
   uint32_t sel = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) sel = i == ii ? x[i] : sel;
+  return (uint32_t)__shfl((int)sel, (lane & ~3) | (e >> 4));
+}
+// out[r] = the m-th largest (1 <= m <= 64) of row r's 64 values, wave-uniform, where
+// lane l holds element l of every row in v.  tmp: 1024 words of LDS owned by this wave.
+__device__ __forceinline__ void mth_largest_16rows(const uint32_t (&v)[16], int m, uint32_t* tmp,
+                                                   uint32_t (&out)[16]) {
+  const int lane = threadIdx.x & 63, p = lane & 3;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) out[r] = (uint32_t)__builtin_amdgcn_readlane((int)sel, 4 * r + (e >> 4));
+  for (int r = 0; r < 16; ++r) tmp[r * 64 + lane] = v[r];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint32_t x[16];
+  const u32x4* src = reinterpret_cast<const u32x4*>(tmp + (lane >> 2) * 64 + 16 * p);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 w4 = src[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[4 * c + e] = w4[e];
+  }
+  const uint32_t t = mth_largest_quad(x, m);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) out[r] = (uint32_t)__builtin_amdgcn_readlane((int)t, 4 * r);
   __builtin_amdgcn_wave_barrier();  // tmp may be reused by the caller
+}
+
+// Exclusive prefix sum of x over the lanes of a quad (in lane order), and the quad's
+// total in *total.
+__device__ __forceinline__ int quad_excl_sum(int x, int* total) {
+  const int p = threadIdx.x & 3;
+  int s = x;
+  int y = (int)quad_lane<0x90>((uint32_t)s);  // quad_perm 0,0,1,2: lane p - 1
+  s += p >= 1 ? y : 0;
+  y = (int)quad_lane<0x40>((uint32_t)s);  // quad_perm 0,0,0,1: lane p - 2
+  s += p >= 2 ? y : 0;
+  *total = (int)quad_lane<0xFF>((uint32_t)s);  // quad_perm 3,3,3,3
+  return s - x;
 }
 
 // bitonic merge (half-cleaners) of KP = 64*E values laid out as p = e*64 + lane,
@@ -435,98 +457,95 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restr
 }
 
 
-// The float32 kbar values a lane needs for one 64-candidate chunk (wave w takes the
-// candidates cb + 16 w .. +15; lane (nn, g) the columns 32 cc + 8 g .. +7).  The row
-// index is clamped into the pooled keys, so rows past the candidates load valid memory;
-// their scores are never used.
+// kbar split into its three bf16 terms once per launch and stored as the MFMA A
+// fragments the selection kernel reads: fragment (chunk, w, cc, term) of a K/V head
+// gives lane (nn, g) that term's 8 values of candidate 64 chunk + 16 w + nn, columns
+// 32 cc + 8 g .. +7 (term 0 = hi, 1 = mid, 2 = lo; rows past the pooled keys are zero).
+// Each fragment is one contiguous 1 KB load, and the selection kernel, which scores
+// every chunk at least twice, does no splitting.
 template <int D>
-__device__ __forceinline__ void load_kchunk(const float* __restrict__ kmh, int cb, int n, float (&xk)[D / 32][8]) {
+__global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ km, u32x4* __restrict__ ks, int n,
+                                                     int nck) {
   constexpr int NC = D / 32;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nn = lane & 15, g = lane >> 4;
-  const int j = min(cb + 16 * w + nn, n - 1);
+  const int64_t ch = blockIdx.x;  // (K/V head, chunk)
+  const int64_t kvh = ch / nck;
+  const int j = (int)(ch % nck) * 64 + 16 * w + nn;
+  const float* src = km + (kvh * n + j) * (int64_t)D + 8 * g;
+  u32x4* out = ks + (ch * 4 + w) * (3 * NC * 64) + lane;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
-    const float* src = kmh + (int64_t)j * D + 32 * cc + 8 * g;
-    const u32x4 w0 = load16(src), w1 = load16(src + 4);
+    u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
+    if (j < n) {
+      w0 = load16(src + 32 * cc);
+      w1 = load16(src + 32 * cc + 4);
+    }
+    u32x4 h, md, lo;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      xk[cc][e] = __uint_as_float(w0[e]);
-      xk[cc][4 + e] = __uint_as_float(w1[e]);
+      const uint32_t a = e < 2 ? w0[2 * e] : w1[2 * e - 4], b = e < 2 ? w0[2 * e + 1] : w1[2 * e - 3];
+      uint32_t th, tm, tl;
+      split3x2(__uint_as_float(a), __uint_as_float(b), th, tm, tl);
+      h[e] = th;
+      md[e] = tm;
+      lo[e] = tl;
     }
+    out[(3 * cc + 0) * 64] = h;
+    out[(3 * cc + 1) * 64] = md;
+    out[(3 * cc + 2) * 64] = lo;
   }
 }
 
-// Scores of one 64-candidate chunk (its kbar values in xk) against all S rows of the
-// block into sc.
-template <int D, int S>
-__device__ __forceinline__ void score_chunk(const u32x4 (&qf)[S / 16][D / 32], const float (&xk)[D / 32][8],
-                                            float (*sc)[65]) {
-  constexpr int NC = D / 32, NT = S / 16;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int nn = lane & 15, g = lane >> 4;
-  u32x4 ah[NC], am[NC], al[NC];
-#pragma unroll
-  for (int cc = 0; cc < NC; ++cc) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t h, md, lo;
-      split3x2(xk[cc][2 * e], xk[cc][2 * e + 1], h, md, lo);
-      ah[cc][e] = h;
-      am[cc][e] = md;
-      al[cc][e] = lo;
-    }
-  }
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    f32x4 acc = f32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      acc = mfma_bf16(al[cc], qf[nt][cc], acc);
-      acc = mfma_bf16(am[cc], qf[nt][cc], acc);
-      acc = mfma_bf16(ah[cc], qf[nt][cc], acc);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[16 * nt + nn][16 * w + 4 * g + i] = acc[i];
-  }
+// The selection key of an entry (raw score bits, 0xFFFFFFFF - j).
+__device__ __forceinline__ uint64_t raw_key(uint64_t e) {
+  return ((uint64_t)orderable_f32(__uint_as_float((uint32_t)(e >> 32))) << 32) | (uint32_t)e;
 }
-
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 // Two-pass selection, exact for m = topk - 1 <= 64; dispatched for m <= kSelectMaxM
-// (see the top of the file).
+// (see the top of the file).  S / 16 waves: for scoring, wave w takes candidates
+// 16 (w & 3) .. +15 of each chunk against rows 64 (w >> 2) .. +63; for selection, lane
+// (r, p) = (lane >> 2, lane & 3) of wave w takes row 16 w + r and, of each chunk, the
+// 16 candidates 16 p .. +15, so a row's 64 candidates sit in one quad and every
+// selection step is per-lane arithmetic or a move inside the quad.
 template <int D, int S>
-__global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __restrict__ q, const float* __restrict__ km,
-                                                          int32_t* __restrict__ idx, float* __restrict__ sel, int L,
-                                                          int n, int BH, int topk, int G) {
-  constexpr int NC = D / 32, NT = S / 16, RPW = S / 4;  // rows per wave
+__global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __restrict__ q,
+                                                            const u32x4* __restrict__ ks,
+                                                            const float* __restrict__ km, int32_t* __restrict__ idx,
+                                                            float* __restrict__ sel, int L, int n, int nck, int topk,
+                                                            int G) {
+  constexpr int NC = D / 32, NF = 3 * NC, NT = 4, NTH = S * 4, SCS = 68;
   // Scores of a chunk go to one of two buffers (chunk parity), so scoring the next chunk
-  // never overwrites scores other waves may still read: one barrier per chunk.
-  __shared__ float scb[2][S][65];
+  // never overwrites scores other waves may still read: one barrier per chunk.  Rows are
+  // 68 words apart: 16-byte aligned, and the quads' 16-byte reads fall in distinct banks.
+  __shared__ float scb[2][S][SCS];
   __shared__ uint64_t buf[S][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
-  const int nn = lane & 15;
+  const int nn = lane & 15, g = lane >> 4;
+  const int cw = w & 3, rh = w >> 2;
+  const int rq = lane >> 2, p = lane & 3, row = 16 * w + rq;
   const int64_t wg = xcd_logical(blockIdx.x, (int64_t)gridDim.x);  // one head per XCD at a time
   const int64_t bh = wg / n;
   const int qb = n - 1 - (int)(wg % n);
   const int m = min(topk - 1, qb);
   const uint16_t* qh = q + (bh * L + (int64_t)qb * S) * D;
-  const float* kmh = km + (bh / G) * (int64_t)n * D;  // pooled keys of this head's K/V head
+  const int64_t kvh = bh / G;  // this head's K/V head
   int32_t* ih = idx + (bh * L + (int64_t)qb * S) * topk;
   float* sh = sel ? sel + (bh * L + (int64_t)qb * S) * topk : nullptr;
   const float inf = __builtin_huge_valf();
 
   if (m == qb || m == 0) {
     // every candidate kept (or none to keep): no selection needed
-    for (int it = tid; it < S * topk; it += 256) {
-      const int r = it / topk, p = it % topk;
-      ih[it] = p < qb && m == qb ? p : (p == m ? qb : -1);
+    const float* kmh = km + kvh * (int64_t)n * D;
+    for (int it = tid; it < S * topk; it += NTH) {
+      const int r = it / topk, pp = it % topk;
+      ih[it] = pp < qb && m == qb ? pp : (pp == m ? qb : -1);
       if (sh) {
-        float v = p == m ? inf : -inf;
-        if (p < m) {
+        float v = pp == m ? inf : -inf;
+        if (pp < m) {
           float acc = 0.f;
           const uint16_t* qr = qh + (int64_t)r * D;
-          const float* kr = kmh + (int64_t)p * D;
+          const float* kr = kmh + (int64_t)pp * D;
           for (int d = 0; d < D; ++d) acc = fmaf(bf16_bits_to_f32(qr[d]), kr[d], acc);
           v = acc;
         }
@@ -540,125 +559,169 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(16 * nt + nn) * D, cc);
+    for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(64 * rh + 16 * nt + nn) * D, cc);
+  const u32x4* kst = ks + ((kvh * nck) * 4 + cw) * (NF * 64) + lane;
   const int nchunks = (qb + 63) / 64;
-  // kbar of the next chunk to score, loaded one chunk ahead (after the last chunk of a
-  // pass, chunk 0 again for the next pass)
-  float xk[NC][8];
-  load_kchunk<D>(kmh, 0, n, xk);
-
-  // ---- pass 1: lane maxima of the score bits, and from them a lower bound on each
-  // row's m-th key (the m lanes whose maximum reaches the m-th largest lane maximum t
-  // hold m distinct keys with score bits >= t, so (t, 0) is at most the m-th key)
-  uint32_t lmax[RPW];
+  // kbar fragments of the next chunk to score, loaded one chunk ahead (after the last
+  // chunk of a pass, chunk 0 again for the next pass)
+  u32x4 kf[NF];
+  auto load_frags = [&](int c) {
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) lmax[i] = 0;
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    const int cb = chunk * 64;
-    float (*sc)[65] = scb[chunk & 1];
-    score_chunk<D, S>(qf, xk, sc);
-    load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
-    __syncthreads();
-    const int j = cb + lane;
+    for (int f = 0; f < NF; ++f) kf[f] = kst[((int64_t)c * 4 * NF + f) * 64];
+  };
+  // scores of chunk cb against this wave's 64 rows into sc; candidates past the block's
+  // own score -inf, below every real score
+  auto score = [&](int cb, float (*sc)[SCS]) {
+    const bool tail = cb + 64 > qb;
 #pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = w + 4 * i;
-      const uint32_t h = j < qb ? orderable_f32(sc[r][lane]) : 0u;
-      lmax[i] = lmax[i] > h ? lmax[i] : h;
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        acc = mfma_bf16(kf[3 * cc + 2], qf[nt][cc], acc);
+        acc = mfma_bf16(kf[3 * cc + 1], qf[nt][cc], acc);
+        acc = mfma_bf16(kf[3 * cc], qf[nt][cc], acc);
+      }
+      if (tail) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = cb + 16 * cw + 4 * g + i < qb ? acc[i] : -inf;
+      }
+      *reinterpret_cast<f32x4*>(&sc[64 * rh + 16 * nt + nn][16 * cw + 4 * g]) = acc;
     }
+  };
+  auto read_scores = [&](const float (*sc)[SCS], float (&v)[16]) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(&sc[row][16 * p]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v4 = src[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * k + e] = v4[e];
+    }
+  };
+  load_frags(0);
+
+  // ---- pass 1: the largest score of each of the row's 64 candidate classes (block
+  // index mod 64, 16 per lane), and from them a lower bound on the row's m-th key (the
+  // m classes whose maximum reaches the m-th largest class maximum t hold m distinct
+  // keys with score >= t, so (t, any block) is at most the m-th key)
+  float cmax[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) cmax[s] = -inf;
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    float (*sc)[SCS] = scb[chunk & 1];
+    score(chunk * 64, sc);
+    load_frags(chunk + 1 < nchunks ? chunk + 1 : 0);
+    __syncthreads();
+    float v[16];
+    read_scores(sc, v);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) cmax[s] = fmaxf(cmax[s], v[s]);
   }
   __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
-  uint64_t thr[RPW];
-  bool act[RPW];
-  uint32_t* tmpw = reinterpret_cast<uint32_t*>(&buf[0][0]) + w * 1024;  // buf is not used before pass 2
+  // The bound as a float tf and a block limit jmax: key (x, j) is at or above it iff
+  // x > tf, or x == tf and j <= jmax (float comparison folds -0 onto +0 as the keys do).
+  float tf;
+  int jmax = 0x7FFFFFFF;
+  {
+    uint32_t u[16];
 #pragma unroll
-  for (int i0 = 0; i0 < RPW; i0 += 16) {
-    uint32_t vv[16], tt[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) vv[i] = lmax[i0 + i];
-    mth_largest_16rows(vv, m, tmpw, tt);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      thr[i0 + i] = (uint64_t)tt[i] << 32;
-      act[i0 + i] = true;
-    }
+    for (int s = 0; s < 16; ++s) u[s] = orderable_f32(cmax[s]);
+    tf = unorderable_f32(mth_largest_quad(u, m));
   }
-  __syncthreads();  // buf is written by pass 2
+  bool act = true;
 
   // ---- pass 2: collect the keys at or above the bound, in index order
-  int cnt[RPW];
-  for (;;) {
-#pragma unroll
-    for (int i = 0; i < RPW; ++i)
-      if (act[i]) cnt[i] = 0;
+  int cnt = 0;
+  for (bool first = true;; first = false) {
+    if (act) cnt = 0;
     for (int chunk = 0; chunk < nchunks; ++chunk) {
       const int cb = chunk * 64;
-      float (*sc)[65] = scb[chunk & 1];
-      score_chunk<D, S>(qf, xk, sc);
-      load_kchunk<D>(kmh, chunk + 1 < nchunks ? cb + 64 : 0, n, xk);
+      float (*sc)[SCS] = scb[chunk & 1];
+      score(cb, sc);
+      load_frags(chunk + 1 < nchunks ? chunk + 1 : 0);
       __syncthreads();
-      const int j = cb + lane;
+      float v[16];
+      read_scores(sc, v);
+      const int j0 = cb + 16 * p;
+      // bit s: candidate j0 + s is at or above the bound (bitwise logic, no branches)
+      uint32_t pm = 0;
+      if (first) {  // every block index at tf qualifies
 #pragma unroll
-      for (int i = 0; i < RPW; ++i) {
-        if (!act[i]) continue;
-        const int r = w + 4 * i;
-        const uint64_t key = j < qb ? make_key(sc[r][lane], j) : 0ull;
-        const bool pass = key >= thr[i];
-        const uint64_t mask = __builtin_amdgcn_ballot_w64(pass);
-        const int pos = cnt[i] + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-        if (pass && pos < 64) buf[r][pos] = key;
-        cnt[i] += __builtin_popcountll(mask);
+        for (int s = 0; s < 16; ++s) pm |= (uint32_t)(v[s] >= tf) << s;
+      } else {
+        const int lim = jmax - j0;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) pm |= (uint32_t)((v[s] > tf) | ((v[s] == tf) & (s <= lim))) << s;
       }
+      pm = act ? pm : 0u;
+      int tot;
+      int pos = cnt + quad_excl_sum(__builtin_popcount(pm), &tot);
+      // entries hold the raw score bits and 0xFFFFFFFF - j; the order-preserving key is
+      // formed when they are read (raw_key)
+      uint64_t* brow = &buf[row][0];
+      const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)j0;
+      if (__builtin_amdgcn_ballot_w64(cnt + tot > 64) == 0) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if ((pm >> s) & 1u) brow[pos++] = ((uint64_t)__float_as_uint(v[s]) << 32) | (lo0 - s);
+      } else {  // some row of the wave overflows: keep its first 64 entries
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+          if ((pm >> s) & 1u) {
+            if (pos < 64) brow[pos] = ((uint64_t)__float_as_uint(v[s]) << 32) | (lo0 - s);
+            ++pos;
+          }
+      }
+      cnt += tot;
     }
     __syncthreads();  // buf complete; a repeated pass scores chunk 0 into buffer 0 again
     // rows that collected more than 64 keys: raise the bound to the m-th largest of
     // the first 64 collected (a strictly higher bound) and collect again
     bool again = false;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      if (!act[i]) continue;
-      if (cnt[i] > 64) {
-        const int r = w + 4 * i;
+    for (int i = 0; i < 16; ++i) {
+      const int ci = __builtin_amdgcn_readlane(act ? cnt : 0, 4 * i);
+      if (ci > 64) {
         uint32_t t;
         int need;
         uint64_t eq;
-        thr[i] = kth_key_index_ordered(buf[r][lane], m, &t, &need, &eq);  // the first 64, index order
+        const uint64_t thr = kth_key_index_ordered(raw_key(buf[16 * w + i][lane]), m, &t, &need, &eq);
+        if (rq == i) {
+          tf = key_score(thr);
+          jmax = key_index(thr);
+        }
         again = true;
-      } else {
-        act[i] = false;
+      } else if (rq == i) {
+        act = false;
       }
     }
     if (!__syncthreads_or(again)) break;
   }
 
   // ---- output: the m keys at or above the row's exact m-th key, in index order.  The
-  // m-th largest score bits t of each row's collected keys come from the 16-row
-  // network; equal scores at t are settled by index (the keys sit in index order).
+  // m-th largest score bits t of each row's collected keys come from the quad network;
+  // equal scores at t are settled by index (the keys sit in index order).
   uint32_t* tmpo = reinterpret_cast<uint32_t*>(&scb[0][0][0]) + w * 1024;  // scores no longer needed
-#pragma unroll
-  for (int i0 = 0; i0 < RPW; i0 += 16) {
   uint64_t yy[16];
   uint32_t hv[16], tt[16];
+  int cr[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    yy[i] = lane < cnt[i0 + i] ? buf[w + 4 * (i0 + i)][lane] : 0ull;
+    cr[i] = __builtin_amdgcn_readlane(cnt, 4 * i);
+    yy[i] = lane < cr[i] ? raw_key(buf[16 * w + i][lane]) : 0ull;
     hv[i] = (uint32_t)(yy[i] >> 32);
   }
   mth_largest_16rows(hv, m, tmpo, tt);
 #pragma unroll
-  for (int ii = 0; ii < 16; ++ii) {
-    const int i = i0 + ii;
-    const int r = w + 4 * i;
-    const int c = cnt[i];
-    const uint64_t y = yy[ii];
-    const uint32_t t = tt[ii];
+  for (int i = 0; i < 16; ++i) {
+    const int r = 16 * w + i;
+    const uint64_t y = yy[i];
+    const uint32_t t = tt[i];
     const uint32_t hi = (uint32_t)(y >> 32);
     const int need = m - __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));  // >= 1
     const uint64_t eq = __builtin_amdgcn_ballot_w64(hi == t);
     // all keys with score bits above t, and the first `need` (lowest blocks) at t
     const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
-    const bool take = lane < c && (hi > t || (hi == t && rank < need));
+    const bool take = lane < cr[i] && (hi > t || (hi == t && rank < need));
     const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
     const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
     int32_t* orow = ih + (int64_t)r * topk;
@@ -667,11 +730,10 @@ __global__ __launch_bounds__(256) void topk_select_kernel(const uint16_t* __rest
       orow[pos] = key_index(y);
       if (srow) srow[pos] = key_score(y);
     }
-    for (int p = m + lane; p < topk; p += 64) {
-      orow[p] = p == m ? qb : -1;
-      if (srow) srow[p] = p == m ? inf : -inf;
+    for (int pp = m + lane; pp < topk; pp += 64) {
+      orow[pp] = pp == m ? qb : -1;
+      if (srow) srow[pp] = pp == m ? inf : -inf;
     }
-  }
   }
 }
 
@@ -693,10 +755,22 @@ bool topk_mfma_supported(const Dims& d, int topk) {
 template <int D, int S>
 static hipError_t run_select(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                              hipStream_t st) {
-  const int64_t grid = (int64_t)d.n() * d.bh();
-  hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(q), km, idx, sel, d.L, d.n(), (int)d.bh(), topk, d.G());
-  return hipGetLastError();
+  const int n = d.n(), nck = (n + 63) / 64;
+  const int64_t kvheads = (int64_t)d.B * d.Hkv;
+  void* ws = nullptr;
+  hipError_t e = workspace_alloc((size_t)kvheads * nck * 4 * 3 * (D / 32) * 64 * sizeof(u32x4), &ws, st);
+  if (e != hipSuccess) return e;
+  u32x4* ks = static_cast<u32x4*>(ws);
+  hipLaunchKernelGGL((ksplit_kernel<D>), dim3((unsigned)(kvheads * nck)), dim3(256), 0, st, km, ks, n, nck);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    const int64_t grid = (int64_t)n * d.bh();
+    hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(S * 4), 0, st,
+                       static_cast<const uint16_t*>(q), ks, km, idx, sel, d.L, n, nck, topk, d.G());
+    e = hipGetLastError();
+  }
+  const hipError_t ef = vfrag_release(ws, st);
+  return e != hipSuccess ? e : ef;
 }
 
 template <int D, int S, int E>
