@@ -32,6 +32,8 @@
 //    re-sorted by block index.  (For m close to 64 the first pass's bound is weak: rows
 //    would collect far more than 64 keys and refine many times.)
 // Output per row: the selected blocks in ascending order, then b_t, then -1.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 
@@ -166,6 +168,18 @@ __device__ __forceinline__ void clean16_desc(uint32_t (&x)[16]) {
     for (int i = 0; i < 16; ++i)
       if ((i & j) == 0) minmax_u32(x[i], x[i ^ j]);
 }
+// v_max_f32 / v_med3_u32 as single instructions (the library max of floats adds a
+// quieting step per operand; the scores are never NaN)
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 template <int PERM>
 __device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, PERM, 0xF, 0xF, false);
@@ -182,23 +196,23 @@ __device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
     uint32_t y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = quad_lane<0xB1>(x[15 - i]);  // quad_perm 1,0,3,2
-    const bool first = (p & 1) == 0;
+    const uint32_t keep = (p & 1) == 0 ? 0xFFFFFFFFu : 0u;  // med3 with it: max, else min
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = first ? (x[i] > y[i] ? x[i] : y[i]) : (x[i] > y[i] ? y[i] : x[i]);
+    for (int i = 0; i < 16; ++i) x[i] = med3_u32(x[i], y[i], keep);
     clean16_desc(x);
   }
   {  // lanes 0,1 and 2,3: two descending 32-lists into the quad's descending 64
     uint32_t y[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = quad_lane<0x1B>(x[15 - i]);  // quad_perm 3,2,1,0
-    const bool top = p < 2;
+    const uint32_t top = p < 2 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = top ? (x[i] > y[i] ? x[i] : y[i]) : (x[i] > y[i] ? y[i] : x[i]);
+    for (int i = 0; i < 16; ++i) x[i] = med3_u32(x[i], y[i], top);
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = quad_lane<0xB1>(x[i]);
-    const bool first = (p & 1) == 0;
+    const uint32_t keep = (p & 1) == 0 ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = first ? (x[i] > y[i] ? x[i] : y[i]) : (x[i] > y[i] ? y[i] : x[i]);
+    for (int i = 0; i < 16; ++i) x[i] = med3_u32(x[i], y[i], keep);
     clean16_desc(x);
   }
   const int e = m - 1, ii = e & 15;
@@ -207,30 +221,6 @@ __device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
   for (int i = 1; i < 16; ++i) sel = i == ii ? x[i] : sel;
   return (uint32_t)__shfl((int)sel, (lane & ~3) | (e >> 4));
 }
-// out[r] = the m-th largest (1 <= m <= 64) of row r's 64 values, wave-uniform, where
-// lane l holds element l of every row in v.  tmp: 1024 words of LDS owned by this wave.
-__device__ __forceinline__ void mth_largest_16rows(const uint32_t (&v)[16], int m, uint32_t* tmp,
-                                                   uint32_t (&out)[16]) {
-  const int lane = threadIdx.x & 63, p = lane & 3;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) tmp[r * 64 + lane] = v[r];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  uint32_t x[16];
-  const u32x4* src = reinterpret_cast<const u32x4*>(tmp + (lane >> 2) * 64 + 16 * p);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 w4 = src[c];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * c + e] = w4[e];
-  }
-  const uint32_t t = mth_largest_quad(x, m);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) out[r] = (uint32_t)__builtin_amdgcn_readlane((int)t, 4 * r);
-  __builtin_amdgcn_wave_barrier();  // tmp may be reused by the caller
-}
-
 // Exclusive prefix sum of x over the lanes of a quad (in lane order), and the quad's
 // total in *total.
 __device__ __forceinline__ int quad_excl_sum(int x, int* total) {
@@ -519,7 +509,7 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
   // never overwrites scores other waves may still read: one barrier per chunk.  Rows are
   // 68 words apart: 16-byte aligned, and the quads' 16-byte reads fall in distinct banks.
   __shared__ float scb[2][S][SCS];
-  __shared__ uint64_t buf[S][64];
+  __shared__ uint64_t buf[S][65];  // 65: rows start in different banks
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   const int nn = lane & 15, g = lane >> 4;
   const int cw = w & 3, rh = w >> 2;
@@ -571,22 +561,48 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
   };
   // scores of chunk cb against this wave's 64 rows into sc; candidates past the block's
   // own score -inf, below every real score
-  auto score = [&](int cb, float (*sc)[SCS]) {
+  // Scores of one chunk against this wave's 64 rows: four independent accumulation
+  // chains (one per 16 rows), each in the order lo, mid, hi per 32 columns.  The MFMAs
+  // of the next chunk are issued before the current chunk is selected, so they run
+  // under the selection's vector work.
+  f32x4 acc[NT];
+  auto mfma_chunk = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int t = 2; t >= 0; --t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(kf[3 * cc + t], qf[nt][cc], acc[nt]);
+  };
+  // the scores into sc; candidates past the block's own score -inf, below every real score
+  auto store_scores = [&](int cb, float (*sc)[SCS]) {
     const bool tail = cb + 64 > qb;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      f32x4 acc = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        acc = mfma_bf16(kf[3 * cc + 2], qf[nt][cc], acc);
-        acc = mfma_bf16(kf[3 * cc + 1], qf[nt][cc], acc);
-        acc = mfma_bf16(kf[3 * cc], qf[nt][cc], acc);
-      }
+      f32x4 a4 = acc[nt];
       if (tail) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = cb + 16 * cw + 4 * g + i < qb ? acc[i] : -inf;
+        for (int i = 0; i < 4; ++i) a4[i] = cb + 16 * cw + 4 * g + i < qb ? a4[i] : -inf;
       }
-      *reinterpret_cast<f32x4*>(&sc[64 * rh + 16 * nt + nn][16 * cw + 4 * g]) = acc;
+      *reinterpret_cast<f32x4*>(&sc[64 * rh + 16 * nt + nn][16 * cw + 4 * g]) = a4;
+    }
+  };
+  // One pass over the chunks: select(cb, sc) sees each chunk's scores in turn.  On
+  // entry kf holds chunk 0, and on return again (the last prefetch wraps to chunk 0).
+  auto pass = [&](auto&& select) {
+    mfma_chunk();
+    load_frags(nchunks > 1 ? 1 : 0);
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+      float (*sc)[SCS] = scb[chunk & 1];
+      store_scores(chunk * 64, sc);
+      if (chunk + 1 < nchunks) {
+        mfma_chunk();
+        load_frags(chunk + 2 < nchunks ? chunk + 2 : 0);
+      }
+      __syncthreads();
+      select(chunk * 64, sc);
     }
   };
   auto read_scores = [&](const float (*sc)[SCS], float (&v)[16]) {
@@ -607,16 +623,12 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
   float cmax[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) cmax[s] = -inf;
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    float (*sc)[SCS] = scb[chunk & 1];
-    score(chunk * 64, sc);
-    load_frags(chunk + 1 < nchunks ? chunk + 1 : 0);
-    __syncthreads();
+  pass([&](int, const float (*sc)[SCS]) {
     float v[16];
     read_scores(sc, v);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) cmax[s] = fmaxf(cmax[s], v[s]);
-  }
+    for (int s = 0; s < 16; ++s) cmax[s] = max_f32(cmax[s], v[s]);
+  });
   __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
   // The bound as a float tf and a block limit jmax: key (x, j) is at or above it iff
   // x > tf, or x == tf and j <= jmax (float comparison folds -0 onto +0 as the keys do).
@@ -628,52 +640,59 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
     for (int s = 0; s < 16; ++s) u[s] = orderable_f32(cmax[s]);
     tf = unorderable_f32(mth_largest_quad(u, m));
   }
-  bool act = true;
+  bool act = true;  // rows done keep tf = +inf, so that nothing reaches their bound
 
   // ---- pass 2: collect the keys at or above the bound, in index order
   int cnt = 0;
-  for (bool first = true;; first = false) {
-    if (act) cnt = 0;
-    for (int chunk = 0; chunk < nchunks; ++chunk) {
-      const int cb = chunk * 64;
-      float (*sc)[SCS] = scb[chunk & 1];
-      score(cb, sc);
-      load_frags(chunk + 1 < nchunks ? chunk + 1 : 0);
-      __syncthreads();
+  auto collect = [&](auto first_c) {
+    constexpr bool kFirst = decltype(first_c)::value;  // every block index at tf qualifies
+    pass([&](int cb, const float (*sc)[SCS]) {
       float v[16];
       read_scores(sc, v);
       const int j0 = cb + 16 * p;
-      // bit s: candidate j0 + s is at or above the bound (bitwise logic, no branches)
-      uint32_t pm = 0;
-      if (first) {  // every block index at tf qualifies
+      // f[s]: candidate j0 + s is at or above the bound (lane masks, no branches)
+      bool f[16];
+      if constexpr (kFirst) {
 #pragma unroll
-        for (int s = 0; s < 16; ++s) pm |= (uint32_t)(v[s] >= tf) << s;
+        for (int s = 0; s < 16; ++s) f[s] = v[s] >= tf;
       } else {
         const int lim = jmax - j0;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) pm |= (uint32_t)((v[s] > tf) | ((v[s] == tf) & (s <= lim))) << s;
+        for (int s = 0; s < 16; ++s) f[s] = (v[s] > tf) | ((v[s] == tf) & (s <= lim));
       }
-      pm = act ? pm : 0u;
+      int c = 0;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) c += f[s];
       int tot;
-      int pos = cnt + quad_excl_sum(__builtin_popcount(pm), &tot);
-      // entries hold the raw score bits and 0xFFFFFFFF - j; the order-preserving key is
+      int pos = cnt + quad_excl_sum(c, &tot);
+      // entries hold 0xFFFFFFFF - j and the raw score bits; the order-preserving key is
       // formed when they are read (raw_key)
-      uint64_t* brow = &buf[row][0];
+      uint32_t* b32 = reinterpret_cast<uint32_t*>(&buf[row][0]);
       const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)j0;
       if (__builtin_amdgcn_ballot_w64(cnt + tot > 64) == 0) {
 #pragma unroll
         for (int s = 0; s < 16; ++s)
-          if ((pm >> s) & 1u) brow[pos++] = ((uint64_t)__float_as_uint(v[s]) << 32) | (lo0 - s);
+          if (f[s]) {
+            b32[2 * pos] = lo0 - s;
+            b32[2 * pos + 1] = __float_as_uint(v[s]);
+            ++pos;
+          }
       } else {  // some row of the wave overflows: keep its first 64 entries
 #pragma unroll
         for (int s = 0; s < 16; ++s)
-          if ((pm >> s) & 1u) {
-            if (pos < 64) brow[pos] = ((uint64_t)__float_as_uint(v[s]) << 32) | (lo0 - s);
+          if (f[s]) {
+            if (pos < 64) {
+              b32[2 * pos] = lo0 - s;
+              b32[2 * pos + 1] = __float_as_uint(v[s]);
+            }
             ++pos;
           }
       }
       cnt += tot;
-    }
+    });
+  };
+  collect(std::true_type{});
+  for (;;) {
     __syncthreads();  // buf complete; a repeated pass scores chunk 0 into buffer 0 again
     // rows that collected more than 64 keys: raise the bound to the m-th largest of
     // the first 64 collected (a strictly higher bound) and collect again
@@ -692,25 +711,34 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
         again = true;
       } else if (rq == i) {
         act = false;
+        tf = inf;
       }
     }
     if (!__syncthreads_or(again)) break;
+    if (act) cnt = 0;
+    collect(std::false_type{});
   }
 
   // ---- output: the m keys at or above the row's exact m-th key, in index order.  The
   // m-th largest score bits t of each row's collected keys come from the quad network;
   // equal scores at t are settled by index (the keys sit in index order).
-  uint32_t* tmpo = reinterpret_cast<uint32_t*>(&scb[0][0][0]) + w * 1024;  // scores no longer needed
+  uint32_t tt[16];
+  {  // t for the lane's row, from its entries 16 p .. +15 (absent ones 0)
+    uint32_t hq[16];
+    const uint64_t* bq = &buf[row][16 * p];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) hq[k] = 16 * p + k < cnt ? (uint32_t)(raw_key(bq[k]) >> 32) : 0u;
+    const uint32_t t = mth_largest_quad(hq, m);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tt[i] = (uint32_t)__builtin_amdgcn_readlane((int)t, 4 * i);
+  }
   uint64_t yy[16];
-  uint32_t hv[16], tt[16];
   int cr[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     cr[i] = __builtin_amdgcn_readlane(cnt, 4 * i);
     yy[i] = lane < cr[i] ? raw_key(buf[16 * w + i][lane]) : 0ull;
-    hv[i] = (uint32_t)(yy[i] >> 32);
   }
-  mth_largest_16rows(hv, m, tmpo, tt);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = 16 * w + i;
