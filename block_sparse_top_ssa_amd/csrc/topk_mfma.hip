@@ -452,11 +452,13 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const uint16_t* __restr
 // gives lane (nn, g) that term's 8 values of candidate 64 chunk + 16 w + nn, columns
 // 32 cc + 8 g .. +7 (term 0 = hi, 1 = mid, 2 = lo; rows past the pooled keys are zero).
 // Each fragment is one contiguous 1 KB load, and the selection kernel, which scores
-// every chunk at least twice, does no splitting.
+// every chunk at least twice, does no splitting.  kn2[chunk] gets the largest squared
+// norm of the chunk's pooled keys (rounded up), for the first pass's error margin.
 template <int D>
-__global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ km, u32x4* __restrict__ ks, int n,
-                                                     int nck) {
+__global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ km, u32x4* __restrict__ ks,
+                                                     float* __restrict__ kn2, int n, int nck) {
   constexpr int NC = D / 32;
+  __shared__ float wmax[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int nn = lane & 15, g = lane >> 4;
   const int64_t ch = blockIdx.x;  // (K/V head, chunk)
@@ -464,6 +466,7 @@ __global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ k
   const int j = (int)(ch % nck) * 64 + 16 * w + nn;
   const float* src = km + (kvh * n + j) * (int64_t)D + 8 * g;
   u32x4* out = ks + (ch * 4 + w) * (3 * NC * 64) + lane;
+  float ss = 0.f;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
@@ -480,11 +483,20 @@ __global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ k
       h[e] = th;
       md[e] = tm;
       lo[e] = tl;
+      ss = fmaf(__uint_as_float(a), __uint_as_float(a), ss);
+      ss = fmaf(__uint_as_float(b), __uint_as_float(b), ss);
     }
     out[(3 * cc + 0) * 64] = h;
     out[(3 * cc + 1) * 64] = md;
     out[(3 * cc + 2) * 64] = lo;
   }
+  ss += __shfl_xor(ss, 16);  // the four lanes of candidate nn
+  ss += __shfl_xor(ss, 32);
+  ss = wave_max(ss);
+  if (lane == 0) wmax[w] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0)  // rounded up past the float sums' error
+    kn2[ch] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) * (1.f + 0x1p-16f);
 }
 
 // The selection key of an entry (raw score bits, 0xFFFFFFFF - j).
@@ -499,8 +511,9 @@ __device__ __forceinline__ uint64_t raw_key(uint64_t e) {
 // 16 candidates 16 p .. +15, so a row's 64 candidates sit in one quad and every
 // selection step is per-lane arithmetic or a move inside the quad.
 template <int D, int S>
-__global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* __restrict__ q,
                                                             const u32x4* __restrict__ ks,
+                                                            const float* __restrict__ kn2,
                                                             const float* __restrict__ km, int32_t* __restrict__ idx,
                                                             float* __restrict__ sel, int L, int n, int nck, int topk,
                                                             int G) {
@@ -614,31 +627,79 @@ __global__ __launch_bounds__(S * 4) void topk_select_kernel(const uint16_t* __re
       for (int e = 0; e < 4; ++e) v[4 * k + e] = v4[e];
     }
   };
-  load_frags(0);
-
-  // ---- pass 1: the largest score of each of the row's 64 candidate classes (block
-  // index mod 64, 16 per lane), and from them a lower bound on the row's m-th key (the
-  // m classes whose maximum reaches the m-th largest class maximum t hold m distinct
-  // keys with score >= t, so (t, any block) is at most the m-th key)
+  // ---- pass 1: approximate scores from the hi term alone (a third of the loads and
+  // MFMAs).  The largest of each of the row's 64 candidate classes (block index mod
+  // 64, 16 per lane) and the m-th largest t of those mean that m distinct keys have
+  // approximate scores >= t.  An approximate score is within eps of the float32 score
+  // used for the keys, so (t - eps, any block) is at most the row's m-th key.
+  //   The hi term differs from kbar by at most 2^-8 |kbar| per element (nearest-even
+  // rounding to 8 significant bits); the float32 accumulations add at most D 2^-24
+  // (approximate score) and 3 D 2^-24 (score) of sum_d |q_d kbar_d|, below
+  // 2^-8 (2^-9 + 2^-7.4) of it for D <= 128; so with Cauchy-Schwarz
+  // |approx - score| <= 1.008 2^-8 |q| |kbar|, and eps = 1.02 2^-8 |q| max|kbar|
+  // (the norms' own float32 rounding is far inside the difference).
+  u32x4 kh[NC];
+  auto load_hi = [&](int c) {
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) kh[cc] = kst[((int64_t)c * 4 * NF + 3 * cc) * 64];
+  };
+  auto mfma_hi = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(kh[cc], qf[nt][cc], acc[nt]);
+  };
   float cmax[16];
 #pragma unroll
   for (int s = 0; s < 16; ++s) cmax[s] = -inf;
-  pass([&](int, const float (*sc)[SCS]) {
+  load_hi(0);
+  mfma_hi();
+  if (nchunks > 1) load_hi(1);
+  else load_frags(0);
+  for (int chunk = 0; chunk < nchunks; ++chunk) {
+    float (*sc)[SCS] = scb[chunk & 1];
+    store_scores(chunk * 64, sc);
+    if (chunk + 1 < nchunks) {
+      mfma_hi();
+      if (chunk + 2 < nchunks) load_hi(chunk + 2);
+      else load_frags(0);  // pass 2 starts with chunk 0
+    }
+    __syncthreads();
     float v[16];
     read_scores(sc, v);
 #pragma unroll
     for (int s = 0; s < 16; ++s) cmax[s] = max_f32(cmax[s], v[s]);
-  });
+  }
   __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
   // The bound as a float tf and a block limit jmax: key (x, j) is at or above it iff
   // x > tf, or x == tf and j <= jmax (float comparison folds -0 onto +0 as the keys do).
   float tf;
   int jmax = 0x7FFFFFFF;
   {
+    // |q| of the lane's row (its quad sums the squares of D / 4 elements each)
+    float qq = 0.f;
+    const uint16_t* qr = qh + (int64_t)row * D + (D / 4) * p;
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) {
+      const u32x4 w4 = load16(qr + 8 * k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = lo_bf16(w4[e]), b = hi_bf16(w4[e]);
+        qq = fmaf(a, a, fmaf(b, b, qq));
+      }
+    }
+    qq += __shfl_xor(qq, 1);
+    qq += __shfl_xor(qq, 2);
+    float kk = 0.f;  // largest squared norm of the block's pooled keys
+    const float* kn2h = kn2 + kvh * nck;
+    for (int c = 0; c < nchunks; ++c) kk = fmaxf(kk, kn2h[c]);
+    const float eps = 1.02f * 0x1p-8f * __builtin_sqrtf(qq * kk);
     uint32_t u[16];
 #pragma unroll
     for (int s = 0; s < 16; ++s) u[s] = orderable_f32(cmax[s]);
-    tf = unorderable_f32(mth_largest_quad(u, m));
+    tf = unorderable_f32(mth_largest_quad(u, m)) - eps;
   }
   bool act = true;  // rows done keep tf = +inf, so that nothing reaches their bound
 
@@ -786,15 +847,17 @@ static hipError_t run_select(const Dims& d, const void* q, const float* km, int 
   const int n = d.n(), nck = (n + 63) / 64;
   const int64_t kvheads = (int64_t)d.B * d.Hkv;
   void* ws = nullptr;
-  hipError_t e = workspace_alloc((size_t)kvheads * nck * 4 * 3 * (D / 32) * 64 * sizeof(u32x4), &ws, st);
+  const size_t frag_bytes = (size_t)kvheads * nck * 4 * 3 * (D / 32) * 64 * sizeof(u32x4);
+  hipError_t e = workspace_alloc(frag_bytes + (size_t)kvheads * nck * sizeof(float), &ws, st);
   if (e != hipSuccess) return e;
   u32x4* ks = static_cast<u32x4*>(ws);
-  hipLaunchKernelGGL((ksplit_kernel<D>), dim3((unsigned)(kvheads * nck)), dim3(256), 0, st, km, ks, n, nck);
+  float* kn2 = reinterpret_cast<float*>(static_cast<char*>(ws) + frag_bytes);
+  hipLaunchKernelGGL((ksplit_kernel<D>), dim3((unsigned)(kvheads * nck)), dim3(256), 0, st, km, ks, kn2, n, nck);
   e = hipGetLastError();
   if (e == hipSuccess) {
     const int64_t grid = (int64_t)n * d.bh();
     hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(S * 4), 0, st,
-                       static_cast<const uint16_t*>(q), ks, km, idx, sel, d.L, n, nck, topk, d.G());
+                       static_cast<const uint16_t*>(q), ks, kn2, km, idx, sel, d.L, n, nck, topk, d.G());
     e = hipGetLastError();
   }
   const hipError_t ef = vfrag_release(ws, st);
