@@ -88,54 +88,6 @@ struct SortStages {
 // full bitonic sort of 64 lane values; ascending if `asc`
 __device__ __forceinline__ uint64_t sort64(uint64_t x, bool asc) { return SortStages<2, 1>::run(x, asc); }
 
-// The same network on 32-bit values (one lane move and a min/max per stage).
-template <int K2, int J>
-struct SortStages32 {
-  __device__ static __forceinline__ uint32_t run(uint32_t x, bool asc) {
-    const int lane = threadIdx.x & 63;
-    const bool blk_asc = ((lane & K2) == 0) == asc;
-    const bool keep_max = ((lane & J) == 0) == !blk_asc;
-    uint32_t a, y;
-    if constexpr (J >= 16) {
-      // the row swaps leave the lane's value and its partner's in the two results
-      const auto pr = J == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
-                              : __builtin_amdgcn_permlane32_swap(x, x, false, false);
-      a = pr[0];
-      y = pr[1];
-    } else {
-      a = x;
-      y = xor_lane<J>(x);
-    }
-    x = keep_max ? (a > y ? a : y) : (a < y ? a : y);
-    if constexpr (J > 1) return SortStages32<K2, J / 2>::run(x, asc);
-    else if constexpr (K2 < 64) return SortStages32<K2 * 2, K2>::run(x, asc);
-    else return x;
-  }
-};
-__device__ __forceinline__ uint32_t sort64_u32(uint32_t x, bool asc) { return SortStages32<2, 1>::run(x, asc); }
-
-// The m-th largest (1 <= m <= 64) of the 64-bit keys held by the lanes, where absent
-// lanes hold 0, at least m keys are present, and the present keys with equal score
-// bits sit in ascending block order along the lanes (true of keys collected in index
-// order).  Only the 32 score bits are sorted: with t the m-th largest of them, the
-// m-th key is the (m - #{score > t})-th key with score t in lane order.  Returns the
-// key; *t_out and *need_out describe the cut for the caller.
-__device__ __forceinline__ uint64_t kth_key_index_ordered(uint64_t y, int m, uint32_t* t_out, int* need_out,
-                                                          uint64_t* eq_out) {
-  const uint32_t hi = (uint32_t)(y >> 32);
-  const uint32_t t = (uint32_t)__shfl((int)sort64_u32(hi, false), m - 1);  // descending
-  const int n_gt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));
-  const int need = m - n_gt;  // >= 1
-  const uint64_t eq = __builtin_amdgcn_ballot_w64(hi == t);
-  const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
-  const uint64_t pick = __builtin_amdgcn_ballot_w64(hi == t && rank == need - 1);
-  const int src = (int)__builtin_ctzll(pick);
-  *t_out = t;
-  *need_out = need;
-  *eq_out = eq;
-  return shfl_u64(y, src);
-}
-
 // ---------------------------------------------------------------- m-th largest of 64 values per quad
 // With a row's 64 values spread over the four lanes of a quad, 16 each, one sorting
 // network in registers orders all 16 rows a wave holds at once: each lane sorts its 16
@@ -175,6 +127,11 @@ __device__ __forceinline__ float max_f32(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+__device__ __forceinline__ float med3_f32(float a, float b, float c) {
+  float r;
+  asm("v_med3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t r;
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
@@ -184,13 +141,12 @@ template <int PERM>
 __device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, PERM, 0xF, 0xF, false);
 }
-// The m-th largest (1 <= m <= 64) of the 64 values a quad holds (16 per lane), in
-// every lane of the quad.  The lane's 16 are sorted by an in-register network, then
-// bitonic merges with the partner lanes (p^1, then p^3 and p^1) join them into the
-// quad's 64 values in descending order, element 16 p + i in register i of lane p.
-// About 30 instructions per quad, against about 125 for a 64-lane network.
-__device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
-  const int lane = threadIdx.x & 63, p = lane & 3;
+// Sorts the 64 values a quad holds (16 per lane) into descending order, element
+// 16 p + i in register i of lane p: each lane sorts its 16 by an in-register network,
+// then bitonic merges with the partner lanes (p^1, then p^3 and p^1) join them.  About
+// 30 instructions per quad, against about 125 for a 64-lane network.
+__device__ __forceinline__ void sort64_quad_desc(uint32_t (&x)[16]) {
+  const int p = threadIdx.x & 3;
   sort16_desc(x);
   {  // lanes p, p^1: two descending 16-lists into one descending 32-list over the pair
     uint32_t y[16];
@@ -215,12 +171,50 @@ __device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
     for (int i = 0; i < 16; ++i) x[i] = med3_u32(x[i], y[i], keep);
     clean16_desc(x);
   }
-  const int e = m - 1, ii = e & 15;
+}
+// Element e (0 <= e < 64) of a quad's sorted 64, in every lane of the quad.
+__device__ __forceinline__ uint32_t quad_element(const uint32_t (&x)[16], int e) {
+  const int lane = threadIdx.x & 63, ii = e & 15;
   uint32_t sel = x[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) sel = i == ii ? x[i] : sel;
   return (uint32_t)__shfl((int)sel, (lane & ~3) | (e >> 4));
 }
+// The m-th largest (1 <= m <= 64) of the 64 values a quad holds, in every lane of it.
+__device__ __forceinline__ uint32_t mth_largest_quad(uint32_t (&x)[16], int m) {
+  sort64_quad_desc(x);
+  return quad_element(x, m - 1);
+}
+// The m-th largest (1 <= m <= 64) of the 128 values a quad holds (a and b, 16 + 16
+// per lane): both sorted, the top 64 of the two lists is max(a[e], b[63 - e]) (a
+// bitonic sequence), put in order by half-cleaners 32 (lanes p^2), 16 (lanes p^1)
+// and 8 .. 1 (registers).
+__device__ __forceinline__ uint32_t mth_largest_quad128(uint32_t (&a)[16], uint32_t (&b)[16], int m) {
+  const int p = threadIdx.x & 3;
+  sort64_quad_desc(a);
+  sort64_quad_desc(b);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t y = quad_lane<0x1B>(b[15 - i]);  // element 63 - e: lane 3 - p, register 15 - i
+    a[i] = a[i] > y ? a[i] : y;
+  }
+  {
+    uint32_t y[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = quad_lane<0x4E>(a[i]);  // quad_perm 2,3,0,1
+    const uint32_t top = p < 2 ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = med3_u32(a[i], y[i], top);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = quad_lane<0xB1>(a[i]);
+    const uint32_t keep = (p & 1) == 0 ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = med3_u32(a[i], y[i], keep);
+    clean16_desc(a);
+  }
+  return quad_element(a, m - 1);
+}
+
 // Exclusive prefix sum of x over the lanes of a quad (in lane order), and the quad's
 // total in *total.
 __device__ __forceinline__ int quad_excl_sum(int x, int* total) {
@@ -499,30 +493,31 @@ __global__ __launch_bounds__(256) void ksplit_kernel(const float* __restrict__ k
     kn2[ch] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3])) * (1.f + 0x1p-16f);
 }
 
-// The selection key of an entry (raw score bits, 0xFFFFFFFF - j).
-__device__ __forceinline__ uint64_t raw_key(uint64_t e) {
-  return ((uint64_t)orderable_f32(__uint_as_float((uint32_t)(e >> 32))) << 32) | (uint32_t)e;
-}
-
-// Two-pass selection, exact for m = topk - 1 <= 64; dispatched for m <= kSelectMaxM
-// (see the top of the file).  S / 16 waves: for scoring, wave w takes candidates
-// 16 (w & 3) .. +15 of each chunk against rows 64 (w >> 2) .. +63; for selection, lane
-// (r, p) = (lane >> 2, lane & 3) of wave w takes row 16 w + r and, of each chunk, the
-// 16 candidates 16 p .. +15, so a row's 64 candidates sit in one quad and every
-// selection step is per-lane arithmetic or a move inside the quad.
-template <int D, int S>
+// Two-pass selection, exact for m = topk - 1 <= 64 (see the top of the file).
+// S / 16 waves: for scoring, wave w takes candidates 16 (w & 3) .. +15 of each chunk
+// against rows 64 (w >> 2) .. +63; for selection, lane (r, p) = (lane >> 2, lane & 3)
+// of wave w takes row 16 w + r and, of each chunk, the 16 candidates 16 p .. +15, so a
+// row's 64 candidates sit in one quad and every selection step is per-lane arithmetic
+// or a move inside the quad.
+//   T: approximate scores kept per candidate class in the first pass (1: the largest,
+// for m <= 40; 2: the two largest, so that the bound stays tight up to m = 64).
+//   CAP: entries collected per row (64 or 128); NB: score buffers (2: one barrier per
+// chunk; 1: two, for the larger workgroups).
+template <int D, int S, int T, int CAP, int NB>
 __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* __restrict__ q,
                                                             const u32x4* __restrict__ ks,
                                                             const float* __restrict__ kn2,
                                                             const float* __restrict__ km, int32_t* __restrict__ idx,
                                                             float* __restrict__ sel, int L, int n, int nck, int topk,
                                                             int G) {
-  constexpr int NC = D / 32, NF = 3 * NC, NT = 4, NTH = S * 4, SCS = 68;
-  // Scores of a chunk go to one of two buffers (chunk parity), so scoring the next chunk
-  // never overwrites scores other waves may still read: one barrier per chunk.  Rows are
-  // 68 words apart: 16-byte aligned, and the quads' 16-byte reads fall in distinct banks.
-  __shared__ float scb[2][S][SCS];
-  __shared__ uint64_t buf[S][65];  // 65: rows start in different banks
+  constexpr int NC = D / 32, NF = 3 * NC, NT = 4, NTH = S * 4, SCS = 68, NH = CAP / 64;
+  // Scores of a chunk; rows 68 words apart: 16-byte aligned, and the quads' 16-byte
+  // reads fall in distinct banks.
+  __shared__ float scb[NB][S][SCS];
+  // Collected entries, in index order: raw score and block index (rows start in
+  // different banks).
+  __shared__ float esc[S][CAP + 1];
+  __shared__ uint16_t eix[S][CAP + 2];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, tid = threadIdx.x;
   const int nn = lane & 15, g = lane >> 4;
   const int cw = w & 3, rh = w >> 2;
@@ -565,15 +560,12 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
     for (int cc = 0; cc < NC; ++cc) qf[nt][cc] = load_q_frag<D>(qh + (int64_t)(64 * rh + 16 * nt + nn) * D, cc);
   const u32x4* kst = ks + ((kvh * nck) * 4 + cw) * (NF * 64) + lane;
   const int nchunks = (qb + 63) / 64;
-  // kbar fragments of the next chunk to score, loaded one chunk ahead (after the last
-  // chunk of a pass, chunk 0 again for the next pass)
+  // kbar fragments of the next chunk to score, loaded one chunk ahead
   u32x4 kf[NF];
   auto load_frags = [&](int c) {
 #pragma unroll
     for (int f = 0; f < NF; ++f) kf[f] = kst[((int64_t)c * 4 * NF + f) * 64];
   };
-  // scores of chunk cb against this wave's 64 rows into sc; candidates past the block's
-  // own score -inf, below every real score
   // Scores of one chunk against this wave's 64 rows: four independent accumulation
   // chains (one per 16 rows), each in the order lo, mid, hi per 32 columns.  The MFMAs
   // of the next chunk are issued before the current chunk is selected, so they run
@@ -589,7 +581,7 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(kf[3 * cc + t], qf[nt][cc], acc[nt]);
   };
-  // the scores into sc; candidates past the block's own score -inf, below every real score
+  // the scores into sc; candidates past the block's own score -inf, below every score
   auto store_scores = [&](int cb, float (*sc)[SCS]) {
     const bool tail = cb + 64 > qb;
 #pragma unroll
@@ -602,13 +594,15 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       *reinterpret_cast<f32x4*>(&sc[64 * rh + 16 * nt + nn][16 * cw + 4 * g]) = a4;
     }
   };
+  auto buffer = [&](int chunk) { return scb[NB == 2 ? (chunk & 1) : 0]; };
   // One pass over the chunks: select(cb, sc) sees each chunk's scores in turn.  On
   // entry kf holds chunk 0, and on return again (the last prefetch wraps to chunk 0).
   auto pass = [&](auto&& select) {
     mfma_chunk();
     load_frags(nchunks > 1 ? 1 : 0);
     for (int chunk = 0; chunk < nchunks; ++chunk) {
-      float (*sc)[SCS] = scb[chunk & 1];
+      float (*sc)[SCS] = buffer(chunk);
+      if (NB == 1 && chunk > 0) __syncthreads();  // the previous chunk's scores are read
       store_scores(chunk * 64, sc);
       if (chunk + 1 < nchunks) {
         mfma_chunk();
@@ -627,8 +621,9 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       for (int e = 0; e < 4; ++e) v[4 * k + e] = v4[e];
     }
   };
+
   // ---- pass 1: approximate scores from the hi term alone (a third of the loads and
-  // MFMAs).  The largest of each of the row's 64 candidate classes (block index mod
+  // MFMAs).  The T largest of each of the row's 64 candidate classes (block index mod
   // 64, 16 per lane) and the m-th largest t of those mean that m distinct keys have
   // approximate scores >= t.  An approximate score is within eps of the float32 score
   // used for the keys, so (t - eps, any block) is at most the row's m-th key.
@@ -651,15 +646,16 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(kh[cc], qf[nt][cc], acc[nt]);
   };
-  float cmax[16];
+  float c1[16], c2[16];  // the largest (and for T = 2 the second largest) per class
 #pragma unroll
-  for (int s = 0; s < 16; ++s) cmax[s] = -inf;
+  for (int s = 0; s < 16; ++s) c1[s] = c2[s] = -inf;
   load_hi(0);
   mfma_hi();
   if (nchunks > 1) load_hi(1);
   else load_frags(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
-    float (*sc)[SCS] = scb[chunk & 1];
+    float (*sc)[SCS] = buffer(chunk);
+    if (NB == 1 && chunk > 0) __syncthreads();
     store_scores(chunk * 64, sc);
     if (chunk + 1 < nchunks) {
       mfma_hi();
@@ -670,7 +666,10 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
     float v[16];
     read_scores(sc, v);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) cmax[s] = max_f32(cmax[s], v[s]);
+    for (int s = 0; s < 16; ++s) {
+      if constexpr (T == 2) c2[s] = med3_f32(c1[s], c2[s], v[s]);
+      c1[s] = max_f32(c1[s], v[s]);
+    }
   }
   __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
   // The bound as a float tf and a block limit jmax: key (x, j) is at or above it iff
@@ -696,15 +695,26 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
     const float* kn2h = kn2 + kvh * nck;
     for (int c = 0; c < nchunks; ++c) kk = fmaxf(kk, kn2h[c]);
     const float eps = 1.02f * 0x1p-8f * __builtin_sqrtf(qq * kk);
-    uint32_t u[16];
+    uint32_t u1[16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) u[s] = orderable_f32(cmax[s]);
-    tf = unorderable_f32(mth_largest_quad(u, m)) - eps;
+    for (int s = 0; s < 16; ++s) u1[s] = orderable_f32(c1[s]);
+    uint32_t t;
+    if constexpr (T == 2) {
+      uint32_t u2[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) u2[s] = orderable_f32(c2[s]);
+      t = mth_largest_quad128(u1, u2, m);
+    } else {
+      t = mth_largest_quad(u1, m);
+    }
+    tf = unorderable_f32(t) - eps;
   }
   bool act = true;  // rows done keep tf = +inf, so that nothing reaches their bound
 
   // ---- pass 2: collect the keys at or above the bound, in index order
   int cnt = 0;
+  float* erow = &esc[row][0];
+  uint16_t* irow = &eix[row][0];
   auto collect = [&](auto first_c) {
     constexpr bool kFirst = decltype(first_c)::value;  // every block index at tf qualifies
     pass([&](int cb, const float (*sc)[SCS]) {
@@ -726,25 +736,21 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       for (int s = 0; s < 16; ++s) c += f[s];
       int tot;
       int pos = cnt + quad_excl_sum(c, &tot);
-      // entries hold 0xFFFFFFFF - j and the raw score bits; the order-preserving key is
-      // formed when they are read (raw_key)
-      uint32_t* b32 = reinterpret_cast<uint32_t*>(&buf[row][0]);
-      const uint32_t lo0 = 0xFFFFFFFFu - (uint32_t)j0;
-      if (__builtin_amdgcn_ballot_w64(cnt + tot > 64) == 0) {
+      if (__builtin_amdgcn_ballot_w64(cnt + tot > CAP) == 0) {
 #pragma unroll
         for (int s = 0; s < 16; ++s)
           if (f[s]) {
-            b32[2 * pos] = lo0 - s;
-            b32[2 * pos + 1] = __float_as_uint(v[s]);
+            erow[pos] = v[s];
+            irow[pos] = (uint16_t)(j0 + s);
             ++pos;
           }
-      } else {  // some row of the wave overflows: keep its first 64 entries
+      } else {  // some row of the wave overflows: keep its first CAP entries
 #pragma unroll
         for (int s = 0; s < 16; ++s)
           if (f[s]) {
-            if (pos < 64) {
-              b32[2 * pos] = lo0 - s;
-              b32[2 * pos + 1] = __float_as_uint(v[s]);
+            if (pos < CAP) {
+              erow[pos] = v[s];
+              irow[pos] = (uint16_t)(j0 + s);
             }
             ++pos;
           }
@@ -752,30 +758,76 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       cnt += tot;
     });
   };
+  // The cut of each of the wave's rows among its first min(count, CAP) entries (in
+  // index order): t = the m-th largest score bits; the entries above t, and the first
+  // `need` at t, are the row's m best.  per_row(i, c, y[], take[], m-th key) is called
+  // for row 16 w + i with the entries' keys in lane order (entry 64 h + lane in y[h]).
+  auto cut_rows = [&](auto&& per_row) {
+    const int cl = min(cnt, CAP);
+    uint32_t tq;
+    {
+      uint32_t ha[16], hb[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = 16 * p + k;
+        ha[k] = e < cl ? orderable_f32(erow[e]) : 0u;
+        if constexpr (NH == 2) hb[k] = 64 + e < cl ? orderable_f32(erow[64 + e]) : 0u;
+      }
+      if constexpr (NH == 2) tq = mth_largest_quad128(ha, hb, m);
+      else tq = mth_largest_quad(ha, m);
+    }
+    for (int i = 0; i < 16; ++i) {
+      const int r = 16 * w + i;
+      const int c = __builtin_amdgcn_readlane(cl, 4 * i);
+      const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tq, 4 * i);
+      uint64_t y[NH];
+      int gt = 0;
+      uint64_t eq[NH];
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int e = 64 * h + lane;
+        y[h] = e < c ? make_key(esc[r][e], eix[r][e]) : 0ull;
+        const uint32_t hi = (uint32_t)(y[h] >> 32);
+        gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));
+        eq[h] = __builtin_amdgcn_ballot_w64(hi == t);
+      }
+      const int need = m - gt;  // >= 1
+      bool take[NH];
+      uint64_t kth = 0;
+      int before = 0;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const uint32_t hi = (uint32_t)(y[h] >> 32);
+        const int rank = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq[h] >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)eq[h], 0));
+        take[h] = 64 * h + lane < c && (hi > t || (hi == t && rank < need));
+        const uint64_t at = __builtin_amdgcn_ballot_w64(hi == t && rank == need - 1 && 64 * h + lane < c);
+        if (at) kth = shfl_u64(y[h], (int)__builtin_ctzll(at));
+        before += __builtin_popcountll(eq[h]);
+      }
+      per_row(i, r, y, take, kth);
+    }
+  };
   collect(std::true_type{});
   for (;;) {
-    __syncthreads();  // buf complete; a repeated pass scores chunk 0 into buffer 0 again
-    // rows that collected more than 64 keys: raise the bound to the m-th largest of
-    // the first 64 collected (a strictly higher bound) and collect again
-    bool again = false;
-    for (int i = 0; i < 16; ++i) {
+    __syncthreads();  // the entries are complete; a repeated pass scores chunk 0 again
+    // rows that collected more than CAP keys: raise the bound to the m-th largest of
+    // the first CAP collected (a strictly higher bound) and collect again
+    const bool any_over = __syncthreads_or(act && cnt > CAP);
+    if (!any_over) break;
+    cut_rows([&](int i, int, const uint64_t (&)[NH], const bool (&)[NH], uint64_t kth) {
       const int ci = __builtin_amdgcn_readlane(act ? cnt : 0, 4 * i);
-      if (ci > 64) {
-        uint32_t t;
-        int need;
-        uint64_t eq;
-        const uint64_t thr = kth_key_index_ordered(raw_key(buf[16 * w + i][lane]), m, &t, &need, &eq);
-        if (rq == i) {
-          tf = key_score(thr);
-          jmax = key_index(thr);
+      if (rq == i) {
+        if (ci > CAP) {
+          tf = key_score(kth);
+          jmax = key_index(kth);
+        } else {
+          act = false;
+          tf = inf;
         }
-        again = true;
-      } else if (rq == i) {
-        act = false;
-        tf = inf;
       }
-    }
-    if (!__syncthreads_or(again)) break;
+    });
+    __syncthreads();  // the cut read every row's entries before they are collected again
     if (act) cnt = 0;
     collect(std::false_type{});
   }
@@ -783,50 +835,32 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
   // ---- output: the m keys at or above the row's exact m-th key, in index order.  The
   // m-th largest score bits t of each row's collected keys come from the quad network;
   // equal scores at t are settled by index (the keys sit in index order).
-  uint32_t tt[16];
-  {  // t for the lane's row, from its entries 16 p .. +15 (absent ones 0)
-    uint32_t hq[16];
-    const uint64_t* bq = &buf[row][16 * p];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) hq[k] = 16 * p + k < cnt ? (uint32_t)(raw_key(bq[k]) >> 32) : 0u;
-    const uint32_t t = mth_largest_quad(hq, m);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tt[i] = (uint32_t)__builtin_amdgcn_readlane((int)t, 4 * i);
-  }
-  uint64_t yy[16];
-  int cr[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    cr[i] = __builtin_amdgcn_readlane(cnt, 4 * i);
-    yy[i] = lane < cr[i] ? raw_key(buf[16 * w + i][lane]) : 0ull;
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = 16 * w + i;
-    const uint64_t y = yy[i];
-    const uint32_t t = tt[i];
-    const uint32_t hi = (uint32_t)(y >> 32);
-    const int need = m - __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));  // >= 1
-    const uint64_t eq = __builtin_amdgcn_ballot_w64(hi == t);
-    // all keys with score bits above t, and the first `need` (lowest blocks) at t
-    const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0));
-    const bool take = lane < cr[i] && (hi > t || (hi == t && rank < need));
-    const uint64_t mask = __builtin_amdgcn_ballot_w64(take);
-    const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+  cut_rows([&](int, int r, const uint64_t (&y)[NH], const bool (&take)[NH], uint64_t) {
     int32_t* orow = ih + (int64_t)r * topk;
     float* srow = sh ? sh + (int64_t)r * topk : nullptr;
-    if (take) {
-      orow[pos] = key_index(y);
-      if (srow) srow[pos] = key_score(y);
+    int before = 0;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(take[h]);
+      const int pos = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      if (take[h]) {
+        orow[pos] = key_index(y[h]);
+        if (srow) srow[pos] = key_score(y[h]);
+      }
+      before += __builtin_popcountll(mask);
     }
     for (int pp = m + lane; pp < topk; pp += 64) {
       orow[pp] = pp == m ? qb : -1;
       if (srow) srow[pp] = pp == m ? inf : -inf;
     }
-  }
+  });
 }
 
-constexpr int kSelectMaxM = 40;  // largest m = topk - 1 given to the two-pass selection
+// Largest m = topk - 1 given to the two-pass selection with one approximate score per
+// candidate class, and with two (above that the class maxima alone bound the m-th key
+// loosely: rows would collect several times m keys).
+constexpr int kSelectMaxM1 = 40, kSelectMaxM2 = 64;
 
 static int e_for(int topk) {
   const int need = topk - 1;
@@ -837,11 +871,12 @@ static int e_for(int topk) {
 
 bool topk_mfma_supported(const Dims& d, int topk) {
   if (d.dtype != 1 || (d.D != 64 && d.D != 128)) return false;
-  const int e = e_for(topk);
-  return d.S * 64 * e <= 8192;  // running lists: S rows x KP keys x 8 bytes <= 64 KB
+  if (d.n() > 65536) return false;  // block indices are collected as 16 bits
+  if (topk - 1 <= kSelectMaxM2) return true;
+  return d.S * 64 * e_for(topk) <= 8192;  // running lists: S rows x KP keys x 8 bytes <= 64 KB
 }
 
-template <int D, int S>
+template <int D, int S, int T, int CAP, int NB>
 static hipError_t run_select(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                              hipStream_t st) {
   const int n = d.n(), nck = (n + 63) / 64;
@@ -856,7 +891,7 @@ static hipError_t run_select(const Dims& d, const void* q, const float* km, int 
   e = hipGetLastError();
   if (e == hipSuccess) {
     const int64_t grid = (int64_t)n * d.bh();
-    hipLaunchKernelGGL((topk_select_kernel<D, S>), dim3((unsigned)grid), dim3(S * 4), 0, st,
+    hipLaunchKernelGGL((topk_select_kernel<D, S, T, CAP, NB>), dim3((unsigned)grid), dim3(S * 4), 0, st,
                        static_cast<const uint16_t*>(q), ks, kn2, km, idx, sel, d.L, n, nck, topk, d.G());
     e = hipGetLastError();
   }
@@ -876,16 +911,13 @@ static hipError_t run_topk(const Dims& d, const void* q, const float* km, int to
 template <int D>
 static hipError_t dispatch_topk(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
                                 hipStream_t st) {
-  // Two-pass selection while its first bound is tight (m well below 64); above that the
-  // bound from 64 lane maxima is weak, rows collect far more than 64 keys and refine
-  // many times, so the sort-and-merge kernel is faster (measured: m = 39 select 1.68 ms
-  // vs merge 1.93 ms; m = 47 select 2.25 ms vs merge 1.91 ms at L = 32768, 32 heads).
-  if (topk - 1 <= kSelectMaxM) return d.S == 64 ? run_select<D, 64>(d, q, km, topk, idx, sel, st)
-                                                 : run_select<D, 128>(d, q, km, topk, idx, sel, st);
-  const int e = e_for(topk);
-  if (e == 1) return d.S == 64 ? run_topk<D, 64, 1>(d, q, km, topk, idx, sel, st)
-                                : run_topk<D, 128, 1>(d, q, km, topk, idx, sel, st);
-  return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);  // S = 128 with E = 2 is not supported
+  if (topk - 1 <= kSelectMaxM1)
+    return d.S == 64 ? run_select<D, 64, 1, 64, 2>(d, q, km, topk, idx, sel, st)
+                     : run_select<D, 128, 1, 64, 2>(d, q, km, topk, idx, sel, st);
+  if (topk - 1 <= kSelectMaxM2)
+    return d.S == 64 ? run_select<D, 64, 2, 128, 1>(d, q, km, topk, idx, sel, st)
+                     : run_select<D, 128, 2, 128, 1>(d, q, km, topk, idx, sel, st);
+  return run_topk<D, 64, 2>(d, q, km, topk, idx, sel, st);  // m > 64: S = 64 only (see supported)
 }
 
 LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* km, int topk, int32_t* idx, float* sel,
