@@ -758,103 +758,112 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       cnt += tot;
     });
   };
-  // The cut of each of the wave's rows among its first min(count, CAP) entries (in
-  // index order): t = the m-th largest score bits; the entries above t, and the first
-  // `need` at t, are the row's m best.  per_row(i, c, y[], take[], m-th key) is called
-  // for row 16 w + i with the entries' keys in lane order (entry 64 h + lane in y[h]).
-  auto cut_rows = [&](auto&& per_row) {
+  // The cut of the lane's row among its first min(count, CAP) entries (in index order;
+  // lane (r, p) holds entries 64 h + 16 p + k in hv[h][k], as order-preserving score
+  // bits, absent ones 0): t = the m-th largest score bits; the entries above t, and
+  // the first `need` at t, are the row's m best.  Returns the row's m-th key (in every
+  // lane of the quad); with kOut the m best are written to the outputs in index order.
+  auto cut = [&](auto out_c) -> uint64_t {
+    constexpr bool kOut = decltype(out_c)::value;
     const int cl = min(cnt, CAP);
-    uint32_t tq;
+    uint32_t hv[NH][16];
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int e = 64 * h + 16 * p + k;
+        hv[h][k] = e < cl ? orderable_f32(erow[e]) : 0u;
+      }
+    uint32_t t;
     {
       uint32_t ha[16], hb[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
-        const int e = 16 * p + k;
-        ha[k] = e < cl ? orderable_f32(erow[e]) : 0u;
-        if constexpr (NH == 2) hb[k] = 64 + e < cl ? orderable_f32(erow[64 + e]) : 0u;
+        ha[k] = hv[0][k];
+        hb[k] = hv[NH - 1][k];
       }
-      if constexpr (NH == 2) tq = mth_largest_quad128(ha, hb, m);
-      else tq = mth_largest_quad(ha, m);
+      if constexpr (NH == 2) t = mth_largest_quad128(ha, hb, m);
+      else t = mth_largest_quad(ha, m);
     }
-    for (int i = 0; i < 16; ++i) {
-      const int r = 16 * w + i;
-      const int c = __builtin_amdgcn_readlane(cl, 4 * i);
-      const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)tq, 4 * i);
-      uint64_t y[NH];
-      int gt = 0;
-      uint64_t eq[NH];
+    int gt = 0, eqn[NH];
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const int e = 64 * h + lane;
-        y[h] = e < c ? make_key(esc[r][e], eix[r][e]) : 0ull;
-        const uint32_t hi = (uint32_t)(y[h] >> 32);
-        gt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(hi > t));
-        eq[h] = __builtin_amdgcn_ballot_w64(hi == t);
-      }
-      const int need = m - gt;  // >= 1
-      bool take[NH];
-      uint64_t kth = 0;
-      int before = 0;
+    for (int h = 0; h < NH; ++h) {
+      eqn[h] = 0;
 #pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        const uint32_t hi = (uint32_t)(y[h] >> 32);
-        const int rank = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq[h] >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)eq[h], 0));
-        take[h] = 64 * h + lane < c && (hi > t || (hi == t && rank < need));
-        const uint64_t at = __builtin_amdgcn_ballot_w64(hi == t && rank == need - 1 && 64 * h + lane < c);
-        if (at) kth = shfl_u64(y[h], (int)__builtin_ctzll(at));
-        before += __builtin_popcountll(eq[h]);
+      for (int k = 0; k < 16; ++k) {
+        gt += hv[h][k] > t;
+        eqn[h] += hv[h][k] == t;
       }
-      per_row(i, r, y, take, kth);
     }
+    int tot;
+    quad_excl_sum(gt, &tot);
+    const int need = m - tot;  // >= 1
+    int rank_base = 0, pos_base = 0, kj = -1;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      int eq_tot;
+      const int rank0 = rank_base + quad_excl_sum(eqn[h], &eq_tot);
+      int rank = rank0, tk = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const bool at = hv[h][k] == t;
+        tk += hv[h][k] > t || (at && rank < need);
+        if (at && rank == need - 1) kj = 64 * h + 16 * p + k;
+        rank += at;
+      }
+      if constexpr (kOut) {
+        int tk_tot;
+        int pos = pos_base + quad_excl_sum(tk, &tk_tot);
+        int32_t* orow = ih + (int64_t)row * topk;
+        float* srow = sh ? sh + (int64_t)row * topk : nullptr;
+        rank = rank0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const bool at = hv[h][k] == t;
+          if (hv[h][k] > t || (at && rank < need)) {
+            const int e = 64 * h + 16 * p + k;
+            orow[pos] = irow[e];
+            if (srow) srow[pos] = erow[e];
+            ++pos;
+          }
+          rank += at;
+        }
+        pos_base += tk_tot;
+      }
+      rank_base += eq_tot;
+    }
+    // the m-th key's entry: held by one lane of the quad
+    kj = max(kj, (int)quad_lane<0xB1>((uint32_t)kj));
+    kj = max(kj, (int)quad_lane<0x4E>((uint32_t)kj));
+    return ((uint64_t)t << 32) | (0xFFFFFFFFu - (uint32_t)irow[max(kj, 0)]);
   };
   collect(std::true_type{});
   for (;;) {
     __syncthreads();  // the entries are complete; a repeated pass scores chunk 0 again
     // rows that collected more than CAP keys: raise the bound to the m-th largest of
     // the first CAP collected (a strictly higher bound) and collect again
-    const bool any_over = __syncthreads_or(act && cnt > CAP);
-    if (!any_over) break;
-    cut_rows([&](int i, int, const uint64_t (&)[NH], const bool (&)[NH], uint64_t kth) {
-      const int ci = __builtin_amdgcn_readlane(act ? cnt : 0, 4 * i);
-      if (rq == i) {
-        if (ci > CAP) {
-          tf = key_score(kth);
-          jmax = key_index(kth);
-        } else {
-          act = false;
-          tf = inf;
-        }
-      }
-    });
-    __syncthreads();  // the cut read every row's entries before they are collected again
+    if (!__syncthreads_or(act && cnt > CAP)) break;
+    const uint64_t kth = cut(std::false_type{});
+    if (act && cnt > CAP) {
+      tf = key_score(kth);
+      jmax = key_index(kth);
+    } else {
+      act = false;
+      tf = inf;
+    }
+    __syncthreads();  // every row's entries are read before they are collected again
     if (act) cnt = 0;
     collect(std::false_type{});
   }
 
-  // ---- output: the m keys at or above the row's exact m-th key, in index order.  The
-  // m-th largest score bits t of each row's collected keys come from the quad network;
-  // equal scores at t are settled by index (the keys sit in index order).
-  cut_rows([&](int, int r, const uint64_t (&y)[NH], const bool (&take)[NH], uint64_t) {
-    int32_t* orow = ih + (int64_t)r * topk;
-    float* srow = sh ? sh + (int64_t)r * topk : nullptr;
-    int before = 0;
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const uint64_t mask = __builtin_amdgcn_ballot_w64(take[h]);
-      const int pos = before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-      if (take[h]) {
-        orow[pos] = key_index(y[h]);
-        if (srow) srow[pos] = key_score(y[h]);
-      }
-      before += __builtin_popcountll(mask);
-    }
-    for (int pp = m + lane; pp < topk; pp += 64) {
-      orow[pp] = pp == m ? qb : -1;
-      if (srow) srow[pp] = pp == m ? inf : -inf;
-    }
-  });
+  // ---- output: the m keys at or above the row's exact m-th key, in index order
+  (void)cut(std::true_type{});
+  int32_t* orow = ih + (int64_t)row * topk;
+  float* srow = sh ? sh + (int64_t)row * topk : nullptr;
+  for (int pp = m + p; pp < topk; pp += 4) {
+    orow[pp] = pp == m ? qb : -1;
+    if (srow) srow[pp] = pp == m ? inf : -inf;
+  }
 }
 
 // Largest m = topk - 1 given to the two-pass selection with one approximate score per
