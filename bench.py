@@ -83,12 +83,23 @@ def work_model(w: W.Workload, k: int) -> dict:
     }
 
 
-KERNEL_SOURCES = {"pool": "pool.hip", "topk": "topk_mfma.hip", "sparse": "sparse_mfma.hip",
-                  "full": "full_mfma.hip", "align": "align.hip"}
+# The sources each call's kernels come from (the sparse call also runs the fragment-order
+# passes and hands full 64-row chunks to the dense kernel).
+KERNEL_SOURCES = {"pool": ("pool.hip",), "topk": ("topk_mfma.hip",),
+                  "sparse": ("sparse_mfma.hip", "vfrag.hip", "full_mfma.hip"),
+                  "full": ("full_mfma.hip", "vfrag.hip"), "align": ("align.hip",)}
 SHARED_HEADERS = ("common.hpp", "mfma.hpp", "rowattn.hpp")
 
 
-DECODE_SOURCES = {"append": "decode.hip", "sparse": "decode.hip", "full": "decode.hip", "align": "align.hip"}
+DECODE_SOURCES = {"append": ("decode.hip",), "sparse": ("decode.hip",), "full": ("decode.hip",),
+                  "align": ("align.hip",)}
+
+
+def sources_sha256(files) -> str:
+    """sha256 of the named csrc files, concatenated in order."""
+    import hashlib
+    csrc = os.path.join(ROOT, "block_sparse_top_ssa_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in files)).hexdigest()
 
 
 def measured_traffic(workload: str, sources: dict = KERNEL_SOURCES) -> dict:
@@ -96,7 +107,6 @@ def measured_traffic(workload: str, sources: dict = KERNEL_SOURCES) -> dict:
     (profiles/hbm_traffic.json, or profiles/hbm_traffic_<workload>.json), per kernel,
     only where the kernel's source and the shared headers are unchanged since the
     counters were taken; otherwise None."""
-    import hashlib
     out = {k: None for k in sources}
     rec = None
     for fn in ("hbm_traffic.json", f"hbm_traffic_{workload}.json"):
@@ -109,14 +119,12 @@ def measured_traffic(workload: str, sources: dict = KERNEL_SOURCES) -> dict:
             break
     if rec is None:
         return out
-    csrc = os.path.join(ROOT, "block_sparse_top_ssa_amd", "csrc")
-    hdr = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in SHARED_HEADERS)).hexdigest()
-    for k, fn in sources.items():
+    hdr = sources_sha256(SHARED_HEADERS)
+    for k, files in sources.items():
         t = rec.get("kernels", {}).get(k)
         if not t:
             continue
-        src = hashlib.sha256(open(os.path.join(csrc, fn), "rb").read()).hexdigest()
-        if t.get("source_sha256") == src and t.get("headers_sha256") == hdr:
+        if t.get("source_sha256") == sources_sha256(files) and t.get("headers_sha256") == hdr:
             out[k] = int(round(t["fetch_bytes"] + t["write_bytes"]))
     return out
 
