@@ -23,6 +23,7 @@
  *               returns and writes nothing outside the outputs named by a call.  These
  *               calls take a transient workspace from a per-device stream-ordered pool
  *               (sizes and error behaviour under ssa_sparse_attn_fwd and each call):
+ *                 - ssa_block_topk (bf16)
  *                 - ssa_sparse_attn_fwd (bf16)
  *                 - ssa_full_attn_fwd (bf16, with o given)
  *                 - ssa_decode_sparse_fwd, ssa_decode_full_fwd
@@ -108,6 +109,10 @@ ssa_status ssa_block_pool(const ssa_dims* dims, const void* k, float* k_mean, vo
  *              ascending order; slots m+1..topk-1 hold -1.
  *   sel_score  [B,H,L,topk] float32 or NULL out (optional): the score of each listed block;
  *              +inf for b_t, -inf for the -1 slots.
+ *   Workspace (bf16 with topk <= 65 and n <= 65536): B*Hkv*ceil(n/64)*(64*D*6 + 4)
+ *   bytes holding k_mean split into three bf16 terms in the layout the matrix-core products
+ *   read, from the stream-ordered pool described under ssa_sparse_attn_fwd, with the same
+ *   error behaviour.
  */
 ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_mean, int32_t topk,
                           int32_t* idx, float* sel_score, void* stream);
@@ -127,8 +132,8 @@ ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_me
  *   o        [B,H,L,D] (dtype)               out: o(t) = sum_{i in A(t)} softmax_i(scale q_t.k_i) v_i,
  *            A(t) = {i <= t : i/s attended}
  *   lse      [B,H,L] float32 or NULL         out (optional): log sum_{i in A(t)} exp(scale q_t.k_i)
- *   Workspace (bf16 only): B*Hkv*L*D*2 bytes holding v in the layout the matrix-core
- *   products read, taken from a stream-ordered memory pool that the library keeps per
+ *   Workspace (bf16 only): 2*B*Hkv*L*D*2 bytes holding v and k in the layouts the
+ *   matrix-core products read, taken from a stream-ordered memory pool that the library keeps per
  *   device and returned to it on `stream` before the call returns.  The pool keeps the
  *   memory for reuse, so after the first call of a given size the allocation neither
  *   blocks the host nor synchronises the device.  If it cannot be had, the call
