@@ -184,9 +184,34 @@ def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want
     return (out if want_o else None), (lse if want_lse else None)
 
 
+def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
+                        want_entropy: bool = True, want_hist: bool = True, block: int = 64,
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """full_attn_fwd with the full stream's row entropy [B, H, L] and attention mass by
+    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist)."""
+    d = _dims(q, block, _kv_heads(q, k, v))
+    scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
+    if want_o and out is None:
+        out = torch.empty_like(q)
+    if want_o:
+        _expect(out, q.shape, q.dtype, q.device, "full_attn_fwd_stats out")
+    if want_lse and lse is None:
+        lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "full_attn_fwd_stats lse")
+    ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
+    hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
+    check(load().ssa_full_attn_fwd_stats(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale),
+                                         _ptr(out if want_o else None), _ptr(lse if want_lse else None),
+                                         _ptr(ent), _ptr(hist), _stream(q)))
+    return (out if want_o else None), (lse if want_lse else None), ent, hist
+
+
 def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, block: int = 64,
-                dims_like: torch.Tensor | None = None):
-    """Per-token L2 distance (needs the o pair) and dropped mass (needs the lse pair)."""
+                dims_like: torch.Tensor | None = None, want_retained_hist: bool = False):
+    """Per-token L2 distance (needs the o pair) and dropped mass (needs the lse pair); with
+    want_retained_hist also the per-head histogram [B, H, 16] of the retained mass
+    1 - dropped (counts of rows per sixteenth), returned third."""
     ref = o_full if o_full is not None else dims_like
     if ref is None:
         raise SSAError(1, "align_stats needs o_full or dims_like to know [B, H, L, D]")
@@ -203,9 +228,16 @@ def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, bloc
     _expect(lse_sparse, (d.B, d.H, d.L), torch.float32, ref.device, "lse_sparse")
     dist = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if o_full is not None else None
     drop = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=ref.device) if lse_full is not None else None
-    check(load().ssa_align_stats(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
-                                 _ptr(lse_sparse), _ptr(dist), _ptr(drop), _stream(ref)))
-    return dist, drop
+    if not want_retained_hist:
+        check(load().ssa_align_stats(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
+                                     _ptr(lse_sparse), _ptr(dist), _ptr(drop), _stream(ref)))
+        return dist, drop
+    if lse_full is None:
+        raise SSAError(1, "the retained-mass histogram needs lse_full and lse_sparse")
+    rh = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=ref.device)
+    check(load().ssa_align_stats_hist(ctypes.byref(d), _ptr(o_full), _ptr(o_sparse), _ptr(lse_full),
+                                      _ptr(lse_sparse), _ptr(dist), _ptr(drop), _ptr(rh), _stream(ref)))
+    return dist, drop, rh
 
 
 # ---------------------------------------------------------------- decoding

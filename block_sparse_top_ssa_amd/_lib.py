@@ -32,7 +32,9 @@ PROTOTYPES = {
     "ssa_block_topk": (_I32, [_DP, _VP, _VP, _I32, _VP, _VP, _VP]),
     "ssa_sparse_attn_fwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP]),
     "ssa_full_attn_fwd": (_I32, [_DP, _VP, _VP, _VP, _F, _VP, _VP, _VP]),
+    "ssa_full_attn_fwd_stats": (_I32, [_DP, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP, _VP]),
     "ssa_align_stats": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "ssa_align_stats_hist": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_decode_append": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_decode_sparse_fwd": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),
     "ssa_decode_sparse_fwd_noalloc": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP]),

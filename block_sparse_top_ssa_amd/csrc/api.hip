@@ -167,11 +167,46 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
   return finish(ssa::launch_full_generic(d, q, k, v, scale, o, lse, st), "ssa_full_attn_fwd");
 }
 
+ssa_status ssa_full_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v, float scale,
+                                   void* o, float* lse, float* entropy, float* dist_hist, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(v, "v", 16));
+  if (!entropy && !dist_hist) return fail(SSA_ERR_NULL, "ssa_full_attn_fwd_stats needs entropy or dist_hist");
+  SSA_TRY(check_opt_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  SSA_TRY(check_opt_ptr(entropy, "entropy", 4));
+  SSA_TRY(check_opt_ptr(dist_hist, "dist_hist", 4));
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::full_mfma_supported(d))
+    return finish(ssa::launch_full_mfma_stats(d, q, k, v, scale, o, lse, entropy, dist_hist, st),
+                  "ssa_full_attn_fwd_stats");
+  return finish(ssa::launch_full_stats_unfused(d, q, k, v, scale, o, lse, entropy, dist_hist, st),
+                "ssa_full_attn_fwd_stats");
+}
+
 ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void* o_sparse, const float* lse_full,
                            const float* lse_sparse, float* l2_dist, float* dropped, void* stream) {
+  return ssa_align_stats_hist(dims, o_full, o_sparse, lse_full, lse_sparse, l2_dist, dropped, nullptr, stream);
+}
+
+ssa_status ssa_align_stats_hist(const ssa_dims* dims, const void* o_full, const void* o_sparse,
+                                const float* lse_full, const float* lse_sparse, float* l2_dist, float* dropped,
+                                float* retained_hist, void* stream) {
   ssa::Dims d;
   SSA_TRY(check_dims(dims, &d, false));
-  if (!l2_dist && !dropped) return fail(SSA_ERR_NULL, "ssa_align_stats needs l2_dist or dropped");
+  if (!l2_dist && !dropped && !retained_hist)
+    return fail(SSA_ERR_NULL, "ssa_align_stats needs l2_dist, dropped or retained_hist");
+  if (retained_hist) {
+    SSA_TRY(check_ptr(lse_full, "lse_full", 4));
+    SSA_TRY(check_ptr(lse_sparse, "lse_sparse", 4));
+    SSA_TRY(check_ptr(retained_hist, "retained_hist", 4));
+    if (d.L % 64) return fail(SSA_ERR_SHAPE, "retained_hist needs L %% 64 == 0 (got L=%d)", d.L);
+  }
   if (l2_dist) {
     SSA_TRY(check_ptr(o_full, "o_full", 16));
     SSA_TRY(check_ptr(o_sparse, "o_sparse", 16));
@@ -183,7 +218,8 @@ ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void*
     SSA_TRY(check_ptr(dropped, "dropped", 4));
   }
   SSA_TRY(check_device());
-  return finish(ssa::launch_align(d, o_full, o_sparse, lse_full, lse_sparse, l2_dist, dropped, (hipStream_t)stream),
+  return finish(ssa::launch_align(d, o_full, o_sparse, lse_full, lse_sparse, l2_dist, dropped, (hipStream_t)stream,
+                                  retained_hist),
                 "ssa_align_stats");
 }
 

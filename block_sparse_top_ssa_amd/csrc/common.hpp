@@ -112,6 +112,15 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// ---------------------------------------------------------------- attention distance buckets
+// Bucket of a block distance d = b_t - b_i: 0 for the own block, 1 + floor(log2 d) for
+// d >= 1, the last of the kDistBuckets buckets also collecting everything beyond.
+constexpr int kDistBuckets = 16;
+__device__ __forceinline__ int dist_bucket(int d) {
+  if (d <= 0) return 0;
+  return min(32 - __clz(d), kDistBuckets - 1);  // 1 + floor(log2 d)
+}
+
 // ---------------------------------------------------------------- selection keys
 // 64-bit key ordering candidates by (score descending, block index ascending):
 // high word = order-preserving image of the float score (-0 folded onto +0),

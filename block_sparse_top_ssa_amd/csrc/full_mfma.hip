@@ -20,6 +20,15 @@
 // Given a sparse stream's idx (full rows of the sparse stream), a workgroup writes only
 // the 64-row query chunks whose rows all keep every earlier block -- those rows of the
 // sparse stream are exactly causal attention -- and leaves the rest to the sparse kernel.
+// With STATS the sweep also gives the attention-pattern measurements of the full stream
+// (paper App. H, Table A9: entropy; App. K.2, p. 31: mass by distance) from its own
+// probabilities: per row B = sum_i p_i e_i (e_i = log2 p_i against the reference, kept
+// through reference moves like l), so entropy = ln l - ln 2 B / l; and per row the mass
+// of each distance bucket -- a wave's rows share one block, so a chunk's bucket is the
+// same for the whole wave and, chunks coming in order, changes at most 16 times: the
+// running bucket mass is kept beside l and flushed to LDS when the bucket changes.  At
+// the end each row's bucket masses are divided by its l and summed over the workgroup's
+// rows into one partial per (b, h, tile), summed in a fixed order by a second kernel.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -36,11 +45,11 @@ constexpr float kLag = 8.f;  // max path: log2 units the row max may pass the re
 // X(c-1), A(c-1), S(c): one wave's matrix products run while its partner's softmax
 // does, instead of both waves queueing on the same unit at the same time.  The stage
 // of chunk c-1 (its V) is still read while chunk c+1 is written, hence three stages.
-template <int D, bool WANT_O>
+template <int D, bool WANT_O, bool STATS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void full_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const u32x4* __restrict__ vt,
     uint16_t* __restrict__ o, float* __restrict__ lse, int L, int BH, int ntile, float sl2, int G,
-    const int32_t* __restrict__ didx, int dtopk, int dS) {
+    const int32_t* __restrict__ didx, int dtopk, int dS, float* __restrict__ ent, float* __restrict__ hpart) {
   constexpr int NT = 2;        // 16-row column tiles per wave
   constexpr int NW = 8;        // waves per workgroup (256 rows)
   constexpr int NC = D / 32;   // contraction chunks of d for S^T
@@ -50,6 +59,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KF_W = KF / NW, VF_W = VF / NW;  // fragments each wave loads
   __shared__ u32x4 sk[3][KF][64];
   __shared__ u32x4 sv[WANT_O ? 3 : 1][WANT_O ? VF : 1][64];
+  // STATS: per wave, per distance bucket, per row of the wave: flushed bucket masses
+  __shared__ float hst[STATS ? NW : 1][STATS ? kDistBuckets : 1][STATS ? 32 : 1];
+  __shared__ float hred[STATS ? NW : 1][STATS ? kDistBuckets : 1];
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -88,13 +100,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   f32x4 oacc[WANT_O ? NDT : 1][NT];
   float m[NT], lsum[NT];
+  float eb[NT], hb[NT];  // STATS: sum p e and the running bucket's mass (lane partials)
+  int cur_b = -1;        // STATS: the running bucket (wave-uniform)
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     m[nt] = -__builtin_huge_valf();
     lsum[nt] = 0.f;
+    eb[nt] = hb[nt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < (WANT_O ? NDT : 1); ++dt) oacc[dt][nt] = f32x4{0, 0, 0, 0};
   }
+  if constexpr (STATS) {
+#pragma unroll
+    for (int i = 0; i < kDistBuckets * 32 / 64; ++i) (&hst[w][0][0])[i * 64 + lane] = 0.f;
+  }
+  const int bt = r0 / dS;  // the block of this wave's rows
+  // STATS: the running bucket's mass of each row goes to LDS (summed over its 4 lanes)
+  auto flush = [&](int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x = hb[nt];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (g == 0) hst[w][b][16 * nt + n] += x;
+      hb[nt] = 0.f;
+    }
+  };
 
   // Each wave copies its share of every chunk's K and V^T fragments from global memory
   // into the LDS stages, through one of two register sets: the loads for chunk c + 2
@@ -164,19 +195,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // row maximum passes it by more than kLag (the row maximum across the four lanes of a
   // row is formed only when some lane's own maximum passes), rescaling O and l.  p up to
   // 2^64 keeps O and l far from the float32 range even over the longest rows.
-  auto softmax = [&](bool diag) __attribute__((always_inline)) {
+  auto softmax = [&](bool diag, int c) __attribute__((always_inline)) {
+    if constexpr (STATS) {
+      const int bk = dist_bucket(bt - c * 64 / dS);
+      if (bk != cur_b) {
+        if (cur_b >= 0) flush(cur_b);
+        cur_b = bk;
+      }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float sr[16];
-      float ps = 0.f;
+      float ps = 0.f, pe = 0.f;
       if (!diag) {
         const float mneg = -m[nt];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            sr[kt * 4 + i] = fast_exp2(fmaf(sacc[kt][nt][i], sl2, mneg));
+            const float e = fmaf(sacc[kt][nt][i], sl2, mneg);
+            sr[kt * 4 + i] = fast_exp2(e);
             ps += sr[kt * 4 + i];
+            if constexpr (STATS) pe = fmaf(sr[kt * 4 + i], e, pe);
           }
       }
       if (diag || __builtin_amdgcn_ballot_w64(!(ps <= 0x1p64f))) {
@@ -195,6 +235,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const bool need = mxs > m[nt] + kLag;
           const float mnew = need ? mxs : m[nt];
           const float alpha = fast_exp2(m[nt] - mnew);
+          if constexpr (STATS) {  // e moves by m - mnew: B' = alpha (B + (m - mnew) l)
+            eb[nt] = lsum[nt] > 0.f ? alpha * fmaf(m[nt] - mnew, lsum[nt], eb[nt]) : 0.f;  // first chunk: m = -inf
+            hb[nt] *= alpha;
+            if (g == 0)
+#pragma unroll
+              for (int b = 0; b < kDistBuckets; ++b) hst[w][b][16 * nt + n] *= alpha;
+          }
           lsum[nt] *= alpha;
           if (WANT_O) {
 #pragma unroll
@@ -204,13 +251,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         const float mneg = -m[nt];
         ps = 0.f;
+        pe = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sr[i] = fast_exp2(fmaf(sr[i], sl2, mneg));
+          const float e = fmaf(sr[i], sl2, mneg);
+          sr[i] = fast_exp2(e);
           ps += sr[i];
+          if constexpr (STATS) pe = fmaf(sr[i], fmaxf(e, -0x1p100f), pe);  // masked keys: p = 0
         }
       }
       lsum[nt] += ps;
+      if constexpr (STATS) {
+        eb[nt] += pe;
+        hb[nt] += ps;
+      }
       if (WANT_O) {
         pf[nt][0] = pack_p(&sr[0], &sr[4]);
         pf[nt][1] = pack_p(&sr[8], &sr[12]);
@@ -312,8 +366,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool cur = active && c <= cw;                 // chunk c to start
     // (the causal mask is compiled only into the diagonal chunk's softmax)
     if (late && prev) {
-      if (c - 1 == cw) softmax(true);
-      else softmax(false);
+      if (c - 1 == cw) softmax(true, c - 1);
+      else softmax(false, c - 1);
     }
     // Steady state: the value products of chunk c - 1 and the score products of chunk c
     // as one pipelined stream (acc_scores); the loads for chunk c + 2 go out between
@@ -327,8 +381,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if (cur) scores(s0);
     }
     if (!late && cur) {
-      if (c == cw) softmax(true);
-      else softmax(false);
+      if (c == cw) softmax(true, c);
+      else softmax(false, c);
     }
     // Unconditional, like the loads, so the compiler's load counting stays exact: past
     // the last chunk the stage written holds a chunk that no wave reads again.
@@ -341,6 +395,41 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (c + 1 <= cmax + 1) interval(c + 1, kB, vB, kA, vA);
   }
 
+  if constexpr (STATS) {
+    // entropy of each row; the workgroup's bucket masses, each row's divided by its l
+    float hw[4] = {0.f, 0.f, 0.f, 0.f};  // buckets 4 g .. 4 g + 3, this lane's rows
+    if (active) {
+      if (cur_b >= 0) flush(cur_b);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float l = lsum[nt], e = eb[nt];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        e += __shfl_xor(e, 16);
+        e += __shfl_xor(e, 32);
+        const float inv = 1.f / l;
+        if (ent && g == 0) ent[bh * (int64_t)L + r0 + 16 * nt + n] = logf(l) - kLn2 * e * inv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hw[j] = fmaf(hst[w][4 * g + j][16 * nt + n], inv, hw[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // sum over the wave's rows (lanes n)
+      float x = hw[j];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (n == 0) hred[w][4 * g + j] = x;
+    }
+    __syncthreads();
+    if (hpart && threadIdx.x < kDistBuckets) {
+      float x = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) x += hred[ww][threadIdx.x];
+      hpart[((int64_t)bh * ntile + tile) * kDistBuckets + threadIdx.x] = x;
+    }
+  }
   if (!active || (didx && !chunk_full[w & 3])) return;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -365,17 +454,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 bool full_mfma_supported(const Dims& d) { return d.dtype == 1 && (d.D == 64 || d.D == 128) && d.L % 64 == 0; }
 
-template <int D, bool WANT_O>
+template <int D, bool WANT_O, bool STATS = false>
 static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
-                           float* lse, hipStream_t st, const int32_t* didx = nullptr, int dtopk = 0) {
+                           float* lse, hipStream_t st, const int32_t* didx = nullptr, int dtopk = 0,
+                           float* ent = nullptr, float* hpart = nullptr) {
   // with didx only the leading rows t < topk * s can keep every earlier block
   const int rows = didx ? (int)std::min<int64_t>(d.L, (int64_t)dtopk * d.S) : d.L;
   const int ntile = (rows + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
-  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O>), dim3((unsigned)grid), dim3(512), 0, st,
+  hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O, STATS>), dim3((unsigned)grid), dim3(512), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      vt, static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile,
-                     scale * kLog2e, d.G(), didx, dtopk, d.S);
+                     scale * kLog2e, d.G(), didx, dtopk, d.S, ent, hpart);
   return hipGetLastError();
 }
 
@@ -384,6 +474,39 @@ hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* 
                                       hipStream_t st) {
   return d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st, idx, topk)
                     : run_full<64, true>(d, q, k, vt, scale, o, lse, st, idx, topk);
+}
+
+LaunchResult launch_full_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                                    void* o, float* lse, float* entropy, float* hist, hipStream_t st) {
+  LaunchResult r;
+  const int ntile = (d.L + 255) / 256;
+  void* hws = nullptr;
+  float* hpart = nullptr;
+  if (hist) {
+    r.err = workspace_alloc((size_t)d.bh() * ntile * kDistBuckets * sizeof(float), &hws, st);
+    if (r.err != hipSuccess) return r;
+    hpart = static_cast<float*>(hws);
+  }
+  if (o) {
+    void* ws = nullptr;
+    r.err = vfrag_acquire(d.kv(), v, &ws, st);
+    if (r.err == hipSuccess) {
+      const u32x4* vt = static_cast<const u32x4*>(ws);
+      r.err = d.D == 128 ? run_full<128, true, true>(d, q, k, vt, scale, o, lse, st, nullptr, 0, entropy, hpart)
+                         : run_full<64, true, true>(d, q, k, vt, scale, o, lse, st, nullptr, 0, entropy, hpart);
+      const hipError_t ef = vfrag_release(ws, st);
+      if (r.err == hipSuccess) r.err = ef;
+    }
+  } else {
+    r.err = d.D == 128 ? run_full<128, false, true>(d, q, k, nullptr, scale, o, lse, st, nullptr, 0, entropy, hpart)
+                       : run_full<64, false, true>(d, q, k, nullptr, scale, o, lse, st, nullptr, 0, entropy, hpart);
+  }
+  if (r.err == hipSuccess && hist) r.err = launch_hist_sum(hpart, hist, d.bh(), ntile, st);
+  if (hws) {
+    const hipError_t ef = vfrag_release(hws, st);
+    if (r.err == hipSuccess) r.err = ef;
+  }
+  return r;
 }
 
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,

@@ -28,7 +28,8 @@ struct LaunchResult {
 
 LaunchResult launch_pool(const Dims& d, const void* k, float* k_mean, hipStream_t st);
 LaunchResult launch_align(const Dims& d, const void* o_full, const void* o_sparse, const float* lse_full,
-                          const float* lse_sparse, float* dist, float* dropped, hipStream_t st);
+                          const float* lse_sparse, float* dist, float* dropped, hipStream_t st,
+                          float* retained_hist = nullptr);
 
 // Portable vector-ALU kernels (any dtype, D in {64,128}).
 LaunchResult launch_topk_generic(const Dims& d, const void* q, const float* k_mean, int topk, int32_t* idx,
@@ -118,6 +119,15 @@ LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean,
 bool full_mfma_supported(const Dims& d);
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale,
                               void* o, float* lse, hipStream_t st);
+// The same with the full stream's measurements from the sweep's own probabilities:
+// entropy [B,H,L] and the distance histogram [B,H,kDistBuckets] (either may be null).
+LaunchResult launch_full_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                                    void* o, float* lse, float* entropy, float* hist, hipStream_t st);
+// The unfused form: the full forward, then the measurement pass over its lse.
+LaunchResult launch_full_stats_unfused(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                                       void* o, float* lse, float* entropy, float* hist, hipStream_t st);
+// hist[bh][m] = sum over the P partials part[bh][p][m], in order (one kernel).
+hipError_t launch_hist_sum(const float* part, float* hist, int64_t bh, int P, hipStream_t st);
 // The dense kernel over the sparse stream's full rows: writes o and lse of the 64-row
 // query chunks whose rows all keep every earlier block (row_keeps_all), nothing else.
 hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* k, const u32x4* vt,

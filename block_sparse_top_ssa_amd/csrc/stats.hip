@@ -22,12 +22,7 @@ namespace ssa {
 
 namespace {
 
-constexpr int kBuckets = 16;
-
-__device__ __forceinline__ int dist_bucket(int d) {
-  if (d <= 0) return 0;
-  return min(32 - __clz(d), kBuckets - 1);  // 1 + floor(log2 d)
-}
+constexpr int kBuckets = kDistBuckets;
 
 // hist[m] += x for a wave-uniform bucket m (registers cannot be indexed at run time)
 __device__ __forceinline__ void add_bucket(float (&h)[kBuckets], int m, float x) {
@@ -257,6 +252,33 @@ __global__ __launch_bounds__(64) void attn_stats_sum_kernel(const float* __restr
   double x = 0.0;
   for (int p = 0; p < P; ++p) x += part[(bh * P + p) * kBuckets + m];
   hist[bh * kBuckets + m] = (float)x;
+}
+
+hipError_t launch_hist_sum(const float* part, float* hist, int64_t bh, int P, hipStream_t st) {
+  hipLaunchKernelGGL(attn_stats_sum_kernel, dim3((unsigned)bh), dim3(64), 0, st, part, hist, P);
+  return hipGetLastError();
+}
+
+// The full forward then the measurement pass, for the shapes and dtypes the fused
+// matrix-core sweep does not take (a transient lse when the caller wants none).
+LaunchResult launch_full_stats_unfused(const Dims& d, const void* q, const void* k, const void* v, float scale,
+                                       void* o, float* lse, float* entropy, float* hist, hipStream_t st) {
+  LaunchResult r;
+  void* ws = nullptr;
+  float* l = lse;
+  if (!l) {
+    r.err = workspace_alloc((size_t)d.tokens() * sizeof(float), &ws, st);
+    if (r.err != hipSuccess) return r;
+    l = static_cast<float*>(ws);
+  }
+  r = launch_full_generic(d, q, k, v, scale, o, l, st);
+  if (r.err == hipSuccess && !r.unsupported)
+    r = launch_attn_stats(d, false, q, k, l, nullptr, 1, scale, entropy, hist, st);
+  if (ws) {
+    const hipError_t ef = vfrag_release(ws, st);
+    if (r.err == hipSuccess) r.err = ef;
+  }
+  return r;
 }
 
 // ---------------------------------------------------------------- launcher

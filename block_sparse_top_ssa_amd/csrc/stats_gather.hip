@@ -21,7 +21,7 @@ namespace ssa {
 
 namespace {
 
-constexpr int kGBuckets = 16;
+constexpr int kGBuckets = kDistBuckets;
 constexpr int kGWaves = 8, kGThreads = 512;
 
 struct GatherLds {
@@ -44,10 +44,6 @@ __host__ __device__ inline GatherLds gather_lds_layout(int T, int nb, int topk) 
 
 constexpr int kGatherMaxLds = 160 * 1024 - 256;  // room for the static LDS of the scan
 
-__device__ __forceinline__ int gbucket(int d) {
-  if (d <= 0) return 0;
-  return min(32 - __clz(d), kGBuckets - 1);  // 1 + floor(log2 d)
-}
 
 }  // namespace
 
@@ -209,7 +205,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     ms += __shfl_xor(ms, 32);
     if (rr >= 0) {
       if (g == 0) atomicAdd(&ent[rr], es);
-      const int m = gbucket(tq / S - jj);
+      const int m = dist_bucket(tq / S - jj);
 #pragma unroll
       for (int b2 = 0; b2 < kGBuckets; ++b2)
         if (b2 == m && g == 0) hacc[b2] += ms;

@@ -28,6 +28,7 @@
  *                 - ssa_full_attn_fwd (bf16, with o given)
  *                 - ssa_decode_sparse_fwd, ssa_decode_full_fwd
  *                 - ssa_full_attn_bwd, ssa_sparse_attn_bwd
+ *                 - ssa_full_attn_fwd_stats
  *                 - ssa_attn_stats, ssa_align_loss
  *               ssa_decode_sparse_fwd_noalloc allocates nothing (a fixed device array).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
@@ -61,8 +62,9 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 6 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
-                             6: allocation-free sparse decoding */
+#define SSA_ABI_VERSION 7 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
+                             6: allocation-free sparse decoding; 7: measurements fused into the full
+                             forward and the stream comparison */
 
 typedef int32_t ssa_status;
 enum {
@@ -159,6 +161,29 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
                              float scale, void* o, float* lse, void* stream);
 
 /*
+ * ssa_full_attn_fwd_stats -- ssa_full_attn_fwd with the full stream's attention-pattern
+ *   measurements taken from the same sweep's probabilities.
+ *   The pages compare methods by attention entropy (App. H, Table A9) and by the
+ *   attention mass at each distance (App. K.2, p. 31); these are the quantities
+ *   ssa_attn_stats gives for idx NULL, without its second pass over q and k.
+ *   q, k, v, scale, o, lse   as for ssa_full_attn_fwd, except that o and lse may both be NULL
+ *   entropy    [B,H,L] float32 or NULL   out: -sum_{i<=t} p_ti ln p_ti (nats)
+ *   dist_hist  [B,H,16] float32 or NULL  out: sum_t sum_{i<=t} p_ti over keys whose block
+ *              distance b_t - b_i falls in bucket m (0 for the own block, 1 + floor(log2 d)
+ *              for d >= 1, bucket 15 also collecting everything beyond); each head's
+ *              buckets sum to L.  Summed in a fixed order (deterministic).
+ *   At least one of entropy, dist_hist must be given.  On bf16 the measurements come from
+ *   the forward's own sweep; on float32 (and shapes the matrix-core kernel does not take)
+ *   the call runs ssa_full_attn_fwd and then the measurement pass.
+ *   Workspace, from the pool: B*H*ceil(L/256)*64 bytes of histogram partials (bf16), the
+ *   V copy of ssa_full_attn_fwd when o is given, and on the unfused path B*H*L*4 bytes
+ *   of log-sum-exp when lse is NULL plus ssa_attn_stats' partials.
+ */
+ssa_status ssa_full_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                   float scale, void* o, float* lse, float* entropy, float* dist_hist,
+                                   void* stream);
+
+/*
  * ssa_align_stats -- per-token comparison of the full and sparse streams.
  *   Paper sec. 5 (pp. 6-7): the two streams' outputs are compared at every layer;
  *   App. B (p. 19) and sec. 4.2 (p. 6): the dropped attention mass delta(t), the
@@ -175,6 +200,20 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
 ssa_status ssa_align_stats(const ssa_dims* dims, const void* o_full, const void* o_sparse,
                            const float* lse_full, const float* lse_sparse, float* l2_dist,
                            float* dropped, void* stream);
+
+/*
+ * ssa_align_stats_hist -- ssa_align_stats with the distribution of the retained mass
+ *   counted in the same pass.  The pages measure attention sparsity as the attention
+ *   mass the kept blocks hold (App. H, Table A9); per head this is its histogram.
+ *   retained_hist  [B,H,16] float32 or NULL  out: the number of rows t whose retained mass
+ *                  1 - dropped(t) lies in [m/16, (m+1)/16) (m = 15 also holding 1); each
+ *                  head's counts sum to L.  Needs the lse pair and L % 64 == 0.  Whole
+ *                  numbers, so the result does not depend on the order of the additions.
+ *   Other arguments as for ssa_align_stats; at least one output must be given.
+ */
+ssa_status ssa_align_stats_hist(const ssa_dims* dims, const void* o_full, const void* o_sparse,
+                                const float* lse_full, const float* lse_sparse, float* l2_dist,
+                                float* dropped, float* retained_hist, void* stream);
 
 /*
  * Decoding with a key/value cache -- one new query per sequence per step.

@@ -41,6 +41,9 @@ Space" (arXiv 2511.20102; the v4 summary page's section tags are cited):
                         A9: sparsity; App. K.2, p. 31: entropy and distance histograms):
                         each row's attention entropy and, per head, the attention mass
                         by block distance in powers of two.
+  retained_mass_hist    App. H (Table A9) measures attention sparsity as the attention
+                        mass the kept blocks hold: per head, the number of rows whose
+                        retained mass 1 - dropped(t) falls in each sixteenth of [0, 1].
   align_loss            the bidirectional alignment objective of sec. 5 (pp. 6-7): a
                         sparsity term pulling the full output toward the (held) sparse
                         one and a commitment term pulling the sparse output toward the
@@ -70,6 +73,7 @@ __all__ = [
     "attend_sparse_gather", "dropped_mass", "align_stats", "attended_blocks",
     "attended_count", "open_block_mean", "decode_step", "attend_full_bwd",
     "attend_sparse_bwd", "smooth_l1", "align_loss", "attention_stats", "distance_bucket",
+    "retained_mass_hist",
 ]
 
 
@@ -428,6 +432,22 @@ def align_loss(o_full, o_sparse, alpha: float, beta: float = 1.0):
 # App. H / App. K.2: attention-pattern measurements
 # ----------------------------------------------------------------------------------
 N_DIST_BUCKETS = 16
+N_RETAINED_BINS = 16
+
+
+def retained_mass_hist(dropped) -> np.ndarray:
+    """Per (b, h), the number of rows t whose retained mass r = 1 - dropped(t) lies in
+    [m/16, (m+1)/16), for m = 0..15 (r = 1 counts in the last bin).  dropped: [B,H,L].
+    Returns [B,H,16] (float64 counts)."""
+    r = 1.0 - np.asarray(dropped, dtype=np.float64)
+    B, H, L = r.shape
+    out = np.zeros((B, H, N_RETAINED_BINS))
+    for b in range(B):
+        for h in range(H):
+            for t in range(L):
+                m = min(int(np.floor(r[b, h, t] * N_RETAINED_BINS)), N_RETAINED_BINS - 1)
+                out[b, h, m] += 1.0
+    return out
 
 
 def distance_bucket(d: int) -> int:

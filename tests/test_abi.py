@@ -157,6 +157,21 @@ def test_stats_argument_checks(libssa):
     assert libssa.ssa_attn_stats(ctypes.byref(d), F, F, F, None, 0, -0.1, F, None, None) == 4
 
 
+def test_fused_measurement_argument_checks(libssa):
+    d = _dims()
+    F = FAKE
+    # the fused full forward needs at least one measurement output; q, k, v required, scale > 0
+    assert libssa.ssa_full_attn_fwd_stats(ctypes.byref(d), F, F, F, 0.1, F, F, None, None, None) == 1
+    assert libssa.ssa_full_attn_fwd_stats(ctypes.byref(d), F, None, F, 0.1, None, None, F, None, None) == 1
+    assert libssa.ssa_full_attn_fwd_stats(ctypes.byref(d), F, F, MISALIGNED, 0.1, None, None, F, None, None) == 4
+    assert libssa.ssa_full_attn_fwd_stats(ctypes.byref(d), F, F, F, -0.1, None, None, None, F, None) == 4
+    # the retained-mass histogram needs the lse pair and whole 64-row groups
+    assert libssa.ssa_align_stats_hist(ctypes.byref(d), None, None, None, None, None, None, None, None) == 1
+    assert libssa.ssa_align_stats_hist(ctypes.byref(d), None, None, F, None, None, None, F, None) == 1
+    d1 = _dims(L=1, block=0)
+    assert libssa.ssa_align_stats_hist(ctypes.byref(d1), None, None, F, F, None, None, F, None) == 2
+
+
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path; a GPU is present")
 def test_align_ignores_block(libssa):
     """ssa_align_stats does not use the block partition, so L = 1 (one decoding step) and

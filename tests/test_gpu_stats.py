@@ -92,3 +92,74 @@ def test_sparse_stats_gathered_rows(B, H, Hkv, L, D, s, topk, padded):
     assert err_e <= 1e-3, err_e
     assert err_h <= 1e-4 * L, err_h
     np.testing.assert_allclose(gh.sum(axis=-1), L, rtol=1e-4)
+
+
+@pytest.mark.parametrize("dtype,D,s,Hkv,L", [(W.BF16, 128, 64, 2, 1024), (W.BF16, 64, 128, 1, 1152),
+                                             (W.BF16, 128, 128, 1, 640), (W.F32, 128, 64, 2, 1024)])
+@pytest.mark.parametrize("want_o", [True, False])
+def test_full_fwd_stats_fused(dtype, D, s, Hkv, L, want_o):
+    """ssa_full_attn_fwd_stats: the full stream's entropy and distance histogram from the
+    forward's own sweep (bf16; float32 runs the forward and the measurement pass) against
+    the oracle, its o and lse those of ssa_full_attn_fwd; ragged last tile at L = 1152."""
+    B, H = 1, 2
+    inp = W.make_qkv(B, H, L, D, s, dtype, "sink", seed=4500 + D + s + L, hkv=Hkv)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] fused stats {dtype} D={D} s={s} Hkv={Hkv} L={L} want_o={want_o}", flush=True)
+    o, lse, ent, hist = ssa.full_attn_fwd_stats(q, k, v, scale, want_o=want_o, block=s)
+    o2, lse2 = ssa.full_attn_fwd(q, k, v, scale, want_o=want_o, block=s)
+    torch.cuda.synchronize()
+    # the same arithmetic for o and lse as the plain forward (checked against the oracle there)
+    assert torch.equal(lse, lse2)
+    if want_o:
+        assert torch.equal(o, o2)
+    q64 = inp.as_f64("q")
+    k64 = inp.kv_per_query_head(inp.as_f64("k"))
+    ref_e, ref_h = O.attention_stats(q64, k64, s, scale)
+    ge, gh = to_f64(ent), to_f64(hist)
+    err_e = float(np.abs(ge - ref_e).max())
+    err_h = float(np.abs(gh - ref_h).max())
+    print(f"[oracle] fused full stats: entropy {err_e:.2e} hist {err_h:.2e} (sum {gh.sum(-1).tolist()})", flush=True)
+    assert err_e <= 1e-3, err_e
+    assert err_h <= 1e-4 * L, err_h
+    np.testing.assert_allclose(gh.sum(axis=-1), L, rtol=1e-4)
+    # only one of the measurements
+    _, _, e_only, h_none = ssa.full_attn_fwd_stats(q, k, v, scale, want_o=False, want_lse=False, want_hist=False,
+                                                   block=s)
+    assert h_none is None and float(np.abs(to_f64(e_only) - ref_e).max()) <= 1e-3
+
+
+@pytest.mark.parametrize("dtype,D,s,topk,L,B,H", [(W.BF16, 128, 64, 4, 1024, 2, 2), (W.F32, 64, 64, 2, 512, 1, 3),
+                                                   (W.BF16, 64, 128, 3, 1280, 1, 2)])
+def test_align_retained_hist(dtype, D, s, topk, L, B, H):
+    """ssa_align_stats_hist: per head, rows counted by retained mass 1 - dropped in
+    sixteenths, against the oracle's dropped mass on the GPU's selection.  A row may land
+    in the neighbouring bin only where the oracle's retained mass lies within the dropped
+    mass tolerance (2 TOL_LSE) of the edge: the cumulative counts are checked edge by edge."""
+    from parity import TOL_LSE
+    inp = W.make_qkv(B, H, L, D, s, dtype, "sink", seed=4700 + L + D, hkv=H)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] retained hist {dtype} D={D} s={s} topk={topk} L={L} B={B} H={H}", flush=True)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, topk)
+    _, lse_s = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+    _, lse_f = ssa.full_attn_fwd(q, k, v, scale, want_o=False, block=s)
+    _, drop, rh = ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q, want_retained_hist=True)
+    _, drop2 = ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)
+    torch.cuda.synchronize()
+    assert torch.equal(drop, drop2)
+    q64 = inp.as_f64("q")
+    k64 = inp.kv_per_query_head(inp.as_f64("k"))
+    ref_drop = O.dropped_mass(q64, k64, idx.cpu().numpy(), s, scale)
+    got = to_f64(rh)
+    assert np.array_equal(got, np.round(got)), "counts are whole numbers"
+    np.testing.assert_array_equal(got.sum(axis=-1), L)
+    tol = 2 * TOL_LSE[dtype]
+    r = 1.0 - ref_drop
+    for m in range(1, 16):
+        edge = m / 16.0
+        below = got[..., :m].sum(axis=-1)
+        lo = (r < edge - tol).sum(axis=-1)
+        hi = (r < edge + tol).sum(axis=-1)
+        assert np.all((lo <= below) & (below <= hi)), (m, below, lo, hi)
+    print(f"[oracle] retained hist ok: {got.reshape(-1, 16)[0].tolist()}", flush=True)

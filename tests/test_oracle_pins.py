@@ -782,3 +782,23 @@ def test_topk_sigma_bounds_hand_worked():
         else:
             assert ex["sigma_m1"][0, 0, 0] == sm1
         assert np.isnan(ex["sigma_m"][0, 0, 1]) and np.isnan(ex["sigma_m1"][0, 0, 1])
+
+
+def test_retained_mass_hist_hand_worked():
+    """Bins of r = 1 - dropped, worked by hand: r = 1 (dropped 0) and r = 15/16 go to the
+    last bin, r = 1/2 to bin 8, r just below 1/2 to bin 7, r = 0.01 and r = 0 to bin 0;
+    a second head with every row at r = 1/4 puts all of them in bin 4."""
+    d0 = np.array([0.0, 1.0 / 16.0, 0.5, 0.5 + 1e-9, 0.99, 1.0])
+    d1 = np.full(6, 0.75)
+    got = O.retained_mass_hist(np.stack([d0, d1])[None])
+    want = np.zeros((1, 2, 16))
+    want[0, 0, 15] = 2
+    want[0, 0, 8] = 1
+    want[0, 0, 7] = 1
+    want[0, 0, 0] = 2
+    want[0, 1, 4] = 6
+    np.testing.assert_array_equal(got, want)
+    # each head's counts sum to L
+    rng = np.random.default_rng(7)
+    dd = rng.random((2, 3, 50))
+    np.testing.assert_array_equal(O.retained_mass_hist(dd).sum(axis=-1), 50)
