@@ -646,32 +646,48 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(kh[cc], qf[nt][cc], acc[nt]);
   };
-  float c1[16], c2[16];  // the largest (and for T = 2 the second largest) per class
+  // The class maxima are kept where the products leave them: lane (nn, g) of wave w
+  // holds, for row 64 rh + 16 nt + nn, the candidates 16 cw + 4 g + i of every chunk,
+  // i.e. the classes 16 cw + 4 g + i.  So this pass needs no LDS and no barrier per
+  // chunk (the other wave on the SIMD covers the products' latency).  At the end the
+  // maxima go through LDS once to the selection layout.
+  float m1[NT][4], m2[NT][4];  // the largest (and for T = 2 the second largest) per class
 #pragma unroll
-  for (int s = 0; s < 16; ++s) c1[s] = c2[s] = -inf;
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m1[nt][i] = m2[nt][i] = -inf;
+  auto take_maxima = [&](int cb) {
+    const bool tail = cb + 64 > qb;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = !tail || cb + 16 * cw + 4 * g + i < qb ? acc[nt][i] : -inf;
+        if constexpr (T == 2) m2[nt][i] = med3_f32(m1[nt][i], m2[nt][i], v);
+        m1[nt][i] = max_f32(m1[nt][i], v);
+      }
+  };
   load_hi(0);
-  mfma_hi();
-  if (nchunks > 1) load_hi(1);
-  else load_frags(0);
   for (int chunk = 0; chunk < nchunks; ++chunk) {
-    float (*sc)[SCS] = buffer(chunk);
-    if (NB == 1 && chunk > 0) __syncthreads();
-    store_scores(chunk * 64, sc);
-    if (chunk + 1 < nchunks) {
-      mfma_hi();
-      if (chunk + 2 < nchunks) load_hi(chunk + 2);
-      else load_frags(0);  // pass 2 starts with chunk 0
-    }
-    __syncthreads();
-    float v[16];
-    read_scores(sc, v);
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if constexpr (T == 2) c2[s] = med3_f32(c1[s], c2[s], v[s]);
-      c1[s] = max_f32(c1[s], v[s]);
-    }
+    mfma_hi();
+    if (chunk + 1 < nchunks) load_hi(chunk + 1);
+    else load_frags(0);  // pass 2 starts with chunk 0
+    take_maxima(chunk * 64);
   }
-  __syncthreads();  // pass 2 scores chunk 0 into buffer 0 again
+  // to the selection layout: row r's classes 16 p .. +15 in lane (r, p)
+  float c1[16], c2[16];
+  auto to_rows = [&](const float (&mx)[NT][4], float (&out)[16]) {
+    float (*sc)[SCS] = scb[0];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      *reinterpret_cast<f32x4*>(&sc[64 * rh + 16 * nt + nn][16 * cw + 4 * g]) =
+          f32x4{mx[nt][0], mx[nt][1], mx[nt][2], mx[nt][3]};
+    __syncthreads();
+    read_scores(sc, out);
+    __syncthreads();
+  };
+  to_rows(m1, c1);
+  if constexpr (T == 2) to_rows(m2, c2);
   // The bound as a float tf and a block limit jmax: key (x, j) is at or above it iff
   // x > tf, or x == tf and j <= jmax (float comparison folds -0 onto +0 as the keys do).
   float tf;
