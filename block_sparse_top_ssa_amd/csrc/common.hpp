@@ -99,6 +99,16 @@ __device__ __forceinline__ float max_over_rows(float x) {
   const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
+// Sum over the same four lanes, in the order (x0 + x1) + (x2 + x3) of their rows, which
+// every lane of the group gets bit for bit.
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
   uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
   lo = __shfl_xor(lo, m);

@@ -312,8 +312,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           p[kt * 4 + i] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_rows(mx);
       float px = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -321,11 +320,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         px += p[i];
       }
       const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-      float ps = sum_bf16x8(pf0) + sum_bf16x8(pf1);  // sum of the rounded p the products use
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      px += __shfl_xor(px, 16);
-      px += __shfl_xor(px, 32);
+      const float ps = sum_over_rows(sum_bf16x8(pf0) + sum_bf16x8(pf1));  // sum of the rounded p the products use
+      px = sum_over_rows(px);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         f32x4 acc = f32x4{0, 0, 0, 0};
@@ -377,11 +373,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
         if (mx > kGuard) flag[r] = 1;
         const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
-        float ps = sum_bf16x8(pf0) + sum_bf16x8(pf1);
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        px += __shfl_xor(px, 16);
-        px += __shfl_xor(px, 32);
+        const float ps = sum_over_rows(sum_bf16x8(pf0) + sum_bf16x8(pf1));
+        px = sum_over_rows(px);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
           f32x4 acc = f32x4{0, 0, 0, 0};
@@ -467,11 +460,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (mx > kGuard) flag[r] = 1;  // mx is -inf for r < 0
     pub0 = pack_p(&p[0], &p[4]);
     pub1 = pack_p(&p[8], &p[12]);
-    pub_ps = sum_bf16x8(pub0) + sum_bf16x8(pub1);  // sum of the rounded p the products use
-    pub_ps += __shfl_xor(pub_ps, 16);
-    pub_ps += __shfl_xor(pub_ps, 32);
-    pub_px = px + __shfl_xor(px, 16);
-    pub_px += __shfl_xor(pub_px, 32);
+    pub_ps = sum_over_rows(sum_bf16x8(pub0) + sum_bf16x8(pub1));  // sum of the rounded p the products use
+    pub_px = sum_over_rows(px);
     pub_r = r;
     pub_c = j * CPB + ch;
     // advance to the next tile and issue its loads (scored next round)
@@ -545,12 +535,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // are free once the products are issued); (5) read-add-write into the owned
       // columns, slot by slot (slots may share rows).
       int sc[4], sn[4], sr[4];
+      float sps[4];  // value wave 0: rounded-p row sums, wave 1: exact ones
       u32x4 sp[4][2];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         sc[s] = __builtin_amdgcn_readfirstlane(cs[s].chunk);  // uniform: scalar branches
         sn[s] = __builtin_amdgcn_readfirstlane(cs[s].next_chunk);
         sr[s] = cs[s].rows[n];
+        sps[s] = pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
         sp[s][0] = cs[s].p[0][lane];
         sp[s][1] = cs[s].p[1][lane];
       }
@@ -579,7 +571,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
       // any lane), and the in-order LDS queue of the wave makes each slot's writes land
       // before the next slot's reads.  Value wave 0 also adds the rounded-p row sums,
-      // wave 1 the exact ones.
+      // wave 1 the exact ones: the sum is read with the O granules and written after
+      // them, so the O writes wait for one LDS round trip only.
+      float* const ls = pw == 0 ? lst : lsx;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = sr[s];
@@ -591,12 +585,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             gp[dl] = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
             cv[dl] = *gp[dl];
           }
-          if (pw < 2 && g == 0) {
-            float* ls = pw == 0 ? lst : lsx;
-            ls[r] += pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
-          }
+          const float lv = pw < 2 ? ls[r] : 0.f;
 #pragma unroll
           for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
+          if (pw < 2 && g == 0) ls[r] = lv + sps[s];
         }
       }
       __syncthreads();
