@@ -14,7 +14,10 @@
 //     instead of 16 half lines: the CU's address unit, the busiest resource here, pays
 //     per line);
 //  1. inverted index: from idx, count per block the rows that kept it, prefix-sum,
-//     and list the row ids per block (LDS, one byte per entry);
+//     and list the row ids per block (LDS, one byte per entry).  The tile is as tall as
+//     the O state allows (256 rows at D = 128); when its lists exceed the LDS left
+//     over (long idx rows, e.g. 64 blocks per row), they are built and consumed in
+//     batches of consecutive blocks, phase 3 running once per batch;
 //  2. own-block phase: each 64-row query chunk against its own 64-key chunk (causal)
 //     on MFMA; the row max of these logits becomes the row's fixed reference m_ref,
 //     and O, l start from this chunk;
@@ -57,7 +60,7 @@ struct SparseLds {
 };
 
 template <int D>
-__host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) {
+__host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int list_cap) {
   SparseLds s;
   int o = 0;
   s.ost = o;   o += T * D * 4;   // O state, rows of D floats, 16-byte granules XOR-swizzled by row
@@ -70,7 +73,7 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int topk) 
   s.slots = o;  // 2 sets x 4 slots; the per-block counters of the index build live here first
   o += 8 * kSlotBytes > nb * 4 ? 8 * kSlotBytes : nb * 4;
   s.flag = o;  o += T;
-  s.list = o;  o += T * topk;  // malformed rows may list up to topk blocks below b_t
+  s.list = o;  o += list_cap;  // row lists of one batch of blocks (at least T entries)
   s.total = (o + 15) & ~15;
   return s;
 }
@@ -97,12 +100,12 @@ __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
   return s;
 }
 
-template <int D, int S, int T>
+template <int D, int S, int T, bool BATCHED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const u32x4* __restrict__ vt, const u32x4* __restrict__ ktf, const int32_t* __restrict__ idx, int topk,
     uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G) {
+    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G, int list_cap) {
   constexpr int NW = 8, NTH = 512;
   constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
   constexpr int DTW = NDT / 4;  // d tiles per value wave
@@ -118,7 +121,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t0 = tile * T;
   const int rows = min(T, L - t0);
   const int nb = (t0 + rows - 1) / S;  // candidate blocks: those below the last row's block
-  const SparseLds lay = sparse_lds_layout<D>(T, nb, topk);
+  const SparseLds lay = sparse_lds_layout<D>(T, nb, list_cap);
   float* ost = reinterpret_cast<float*>(smem + lay.ost);
   float* lst = reinterpret_cast<float*>(smem + lay.lst);
   float* lsx = reinterpret_cast<float*>(smem + lay.lse2);
@@ -270,10 +273,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     if (tid == NTH - 1) off[nb] = base + incl;
   }
+  // off[] now holds every block's offset in one virtual row list.  When the whole list
+  // fits the list area it is built here, where its LDS atomics overlap the own-block
+  // phase; otherwise phase 3 builds it batch by batch, as many blocks as fit at a time.
   __syncthreads();
-  for (int j = tid; j < nb; j += NTH) cnt[j] = off[j];  // cnt becomes the fill cursor
-  __syncthreads();
-  if (tid < rows && row_here(tid)) for_each_entry(t0 + tid, [&](int j) { list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid; });
+  const bool one_batch = !BATCHED || off[nb] <= list_cap;  // uniform
+  if (one_batch) {
+    for (int j = tid; j < nb; j += NTH) cnt[j] = off[j];  // cnt becomes the fill cursor
+    __syncthreads();
+    if (tid < rows && row_here(tid)) for_each_entry(t0 + tid, [&](int j) { list[atomicAdd(&cnt[j], 1)] = (uint8_t)tid; });
+  }
 
   // ---------------------------------------------------------------- 2. own-block phase
   // Unit = 32 rows (two 16-row column tiles) of one 64-row query chunk against the
@@ -393,26 +402,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // ---------------------------------------------------------------- 3. kept-block phase
   // score wave s (w < 4) owns blocks j = s (mod 4); its items are (block, chunk, tile)
-  auto next_block = [&](int from) -> int {  // next non-empty block >= from, same residue
+  // The blocks are taken in batches [jb, je) whose row lists fit the list area (lbase:
+  // the batch's first entry in the virtual list).
+  int jb = 0, je = 0, lbase = 0, my_items = 0, rounds = 0;
+  auto next_block = [&](int from) -> int {  // next non-empty block >= from in the batch, same residue
     int j = from;
-    while (j < nb && off[j + 1] == off[j]) j += 4;
-    return j < nb ? j : nb;
+    while (j < je && off[j + 1] == off[j]) j += 4;
+    return j < je ? j : je;
   };
-  __syncthreads();  // off[] and the own-block state are complete
-  if (w < 4) {  // items of score wave w: tiles of the blocks j = w (mod 4), all lanes counting
-    int items = 0;
-    for (int j = w + 4 * lane; j < nb; j += 256) items += CPB * ((off[j + 1] - off[j] + 15) / 16);
-#pragma unroll
-    for (int o2 = 32; o2 > 0; o2 >>= 1) items += __shfl_xor(items, o2);
-    if (lane == 0) misc[w] = items;
-  }
-  __syncthreads();
-  const int my_items = w < 4 ? misc[w] : 0;
-  const int rounds = max(max(misc[0], misc[1]), max(misc[2], misc[3]));
 
   // score-wave state (waves 0-3): the loaded operands of the next tile to score, and
   // the scored tile waiting to be published
-  int j = w < 4 ? next_block(w) : nb, ch = 0, it = 0, r_cur = -1;
+  int j = je, ch = 0, it = 0, r_cur = -1;
   // Operand registers live across rounds: a score wave keeps the K fragments of its
   // current chunk in `ra`, a value wave its V^T fragments; one array serves both roles
   // so the two never hold registers at the same time.
@@ -423,7 +424,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float pub_ps = 0.f, pub_px = 0.f;
   int scored = 0;
   auto load_item = [&](bool new_chunk) {
-    const int beg = off[j], count = off[j + 1] - beg;
+    const int beg = off[j] - lbase, count = off[j + 1] - off[j];
     const int e = it * 16 + n;
     r_cur = e < count ? (int)list[beg + e] : -1;
     if (new_chunk) {
@@ -480,10 +481,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     pub_nc = more ? j * CPB + ch : -1;
     if (more) load_item(new_chunk);
   };
-  if (w < 4 && my_items > 0) {
-    load_item(true);
-    score_item();
-  }
   // value-wave state (waves 4-7): V^T fragments of its column slice, per score-wave stream
   const int pw = w - 4;
   int vchunk[4] = {-1, -1, -1, -1};
@@ -511,89 +508,133 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       sl.next_chunk = have ? pub_nc : -1;
     }
   };
-  if (w < 4) publish(0, my_items > 0);
-  __syncthreads();
-  // Round rd: the value waves fold slot set rd % 2 while the score waves score their
-  // next tile and publish it in the other set; one barrier per round.  Each role runs
-  // its own loop (same number of rounds, so the barriers pair up), which keeps the
-  // compiler's load counting of one role free of the other's pending loads.
-  if (w < 4) {
-    for (int rd = 0; rd < rounds; ++rd) {
-      // ------------------------------------------------------------ score wave: next tile
-      const bool more = rd + 1 < my_items;
-      if (more) score_item();
-      publish((rd + 1) & 1, more);
+  __syncthreads();  // off[] and the own-block state are complete
+  do {
+    // ------------------------------------------------------------ one batch of blocks
+    lbase = off[jb];
+    if (one_batch) {
+      je = nb;
+    } else {
+      {  // the largest je with off[je] - off[jb] <= list_cap (one block lists at most T rows)
+        int lo = jb + 1, hi = nb;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] - lbase <= list_cap) lo = mid;
+          else hi = mid - 1;
+        }
+        je = lo;
+      }
+      for (int jj = jb + tid; jj < je; jj += NTH) cnt[jj - jb] = off[jj] - lbase;  // fill cursors
       __syncthreads();
+      if (tid < rows && row_here(tid))
+        for_each_entry(t0 + tid, [&](int jj) {
+          if (jj >= jb && jj < je) list[atomicAdd(&cnt[jj - jb], 1)] = (uint8_t)tid;
+        });
     }
-  } else {
-    for (int rd = 0; rd < rounds; ++rd) {
-      // ------------------------------------------------------------ value wave
-      const Slot* const cs = slots + (rd & 1) * 4;
-      // ------------------------------------------------------------ value wave
-      // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
-      // loaded a round ahead); (3) all products; (4) next round's V^T loads (registers
-      // are free once the products are issued); (5) read-add-write into the owned
-      // columns, slot by slot (slots may share rows).
-      int sc[4], sn[4], sr[4];
-      float sps[4];  // value wave 0: rounded-p row sums, wave 1: exact ones
-      u32x4 sp[4][2];
+    if (w < 4) {  // items of score wave w: tiles of the batch's blocks j = w (mod 4), all lanes counting
+      int items = 0;
+      for (int jj = jb + ((w - jb) & 3) + 4 * lane; jj < je; jj += 256) items += CPB * ((off[jj + 1] - off[jj] + 15) / 16);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        sc[s] = __builtin_amdgcn_readfirstlane(cs[s].chunk);  // uniform: scalar branches
-        sn[s] = __builtin_amdgcn_readfirstlane(cs[s].next_chunk);
-        sr[s] = cs[s].rows[n];
-        sps[s] = pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
-        sp[s][0] = cs[s].p[0][lane];
-        sp[s][1] = cs[s].p[1][lane];
+      for (int o2 = 32; o2 > 0; o2 >>= 1) items += __shfl_xor(items, o2);
+      if (lane == 0) misc[w] = items;
+    }
+    __syncthreads();  // row lists, item counts
+    my_items = w < 4 ? misc[w] : 0;
+    rounds = max(max(misc[0], misc[1]), max(misc[2], misc[3]));
+    j = w < 4 ? next_block(jb + ((w - jb) & 3)) : je;
+    ch = 0;
+    it = 0;
+    scored = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) vchunk[s2] = -1;
+    if (w < 4 && my_items > 0) {
+      load_item(true);
+      score_item();
+    }
+    if (w < 4) publish(0, my_items > 0);
+    __syncthreads();
+    // Round rd: the value waves fold slot set rd % 2 while the score waves score their
+    // next tile and publish it in the other set; one barrier per round.  Each role runs
+    // its own loop (same number of rounds, so the barriers pair up), which keeps the
+    // compiler's load counting of one role free of the other's pending loads.
+    if (w < 4) {
+      for (int rd = 0; rd < rounds; ++rd) {
+        // ------------------------------------------------------------ score wave: next tile
+        const bool more = rd + 1 < my_items;
+        if (more) score_item();
+        publish((rd + 1) & 1, more);
+        __syncthreads();
       }
+    } else {
+      for (int rd = 0; rd < rounds; ++rd) {
+        // ------------------------------------------------------------ value wave
+        const Slot* const cs = slots + (rd & 1) * 4;
+        // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
+        // loaded a round ahead); (3) all products; (4) next round's V^T loads (registers
+        // are free once the products are issued); (5) read-add-write into the owned
+        // columns, slot by slot (slots may share rows).
+        int sc[4], sn[4], sr[4];
+        float sps[4];  // value wave 0: rounded-p row sums, wave 1: exact ones
+        u32x4 sp[4][2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (sc[s] >= 0 && sc[s] != vchunk[s]) {  // first tile of a stream: not prefetched
-          load_v(s, sc[s]);
-          vchunk[s] = sc[s];
+        for (int s = 0; s < 4; ++s) {
+          sc[s] = __builtin_amdgcn_readfirstlane(cs[s].chunk);  // uniform: scalar branches
+          sn[s] = __builtin_amdgcn_readfirstlane(cs[s].next_chunk);
+          sr[s] = cs[s].rows[n];
+          sps[s] = pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
+          sp[s][0] = cs[s].p[0][lane];
+          sp[s][1] = cs[s].p[1][lane];
         }
-      }
-      f32x4 acc[4][DTW];
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int dl = 0; dl < DTW; ++dl) {
-          acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2], sp[s][0], f32x4{0, 0, 0, 0});
-          acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2 + 1], sp[s][1], acc[s][dl]);
+        for (int s = 0; s < 4; ++s) {
+          if (sc[s] >= 0 && sc[s] != vchunk[s]) {  // first tile of a stream: not prefetched
+            load_v(s, sc[s]);
+            vchunk[s] = sc[s];
+          }
         }
+        f32x4 acc[4][DTW];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (sc[s] >= 0 && sn[s] >= 0 && sn[s] != sc[s]) {
-          load_v(s, sn[s]);  // used next round
-          vchunk[s] = sn[s];
-        }
-      }
-      // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
-      // any lane), and the in-order LDS queue of the wave makes each slot's writes land
-      // before the next slot's reads.  Value wave 0 also adds the rounded-p row sums,
-      // wave 1 the exact ones: the sum is read with the O granules and written after
-      // them, so the O writes wait for one LDS round trip only.
-      float* const ls = pw == 0 ? lst : lsx;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int r = sr[s];
-        if (sc[s] >= 0 && r >= 0) {
-          f32x4 cv[DTW];
-          f32x4* gp[DTW];
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
           for (int dl = 0; dl < DTW; ++dl) {
-            gp[dl] = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
-            cv[dl] = *gp[dl];
+            acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2], sp[s][0], f32x4{0, 0, 0, 0});
+            acc[s][dl] = mfma_bf16(ra[(s * DTW + dl) * 2 + 1], sp[s][1], acc[s][dl]);
           }
-          const float lv = pw < 2 ? ls[r] : 0.f;
 #pragma unroll
-          for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
-          if (pw < 2 && g == 0) ls[r] = lv + sps[s];
+        for (int s = 0; s < 4; ++s) {
+          if (sc[s] >= 0 && sn[s] >= 0 && sn[s] != sc[s]) {
+            load_v(s, sn[s]);  // used next round
+            vchunk[s] = sn[s];
+          }
         }
+        // (5) read-add-write, slot by slot: a row can sit in several slots of a round (at
+        // any lane), and the in-order LDS queue of the wave makes each slot's writes land
+        // before the next slot's reads.  Value wave 0 also adds the rounded-p row sums,
+        // wave 1 the exact ones: the sum is read with the O granules and written after
+        // them, so the O writes wait for one LDS round trip only.
+        float* const ls = pw == 0 ? lst : lsx;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = sr[s];
+          if (sc[s] >= 0 && r >= 0) {
+            f32x4 cv[DTW];
+            f32x4* gp[DTW];
+#pragma unroll
+            for (int dl = 0; dl < DTW; ++dl) {
+              gp[dl] = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
+              cv[dl] = *gp[dl];
+            }
+            const float lv = pw < 2 ? ls[r] : 0.f;
+#pragma unroll
+            for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
+            if (pw < 2 && g == 0) ls[r] = lv + sps[s];
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
+    jb = je;
+  } while (BATCHED && jb < nb);  // batches
 
   // ---------------------------------------------------------------- 4. finalize
   for (int it = tid; it < rows * (D / 8); it += NTH) {
@@ -633,46 +674,58 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-static constexpr int kMaxLds = 160 * 1024 - 256;  // leave room for the static LDS (scan partials)
+static constexpr int kMaxLds = 160 * 1024 - 512;  // leave room for the static LDS (scan partials, 288 bytes)
 
-// Rows per tile: the most (so each visited block serves the most rows) whose LDS fits.
+struct SparseTile {
+  int T, list_cap;
+};
+// Rows per tile: the most (so each visited block serves the most rows) whose LDS fits
+// with a list area of at least T entries; the list area takes what is left, up to a
+// tile's whole row lists (T * topk entries), so long idx rows only add batches.
 template <int D>
-static int pick_tile(const Dims& d, int topk) {
+static SparseTile pick_tile(const Dims& d, int topk) {
   for (int T : {256, 192, 128}) {
-    const int nb = d.n();  // upper bound on candidate blocks of any tile
-    if (sparse_lds_layout<D>(T, nb, topk).total <= kMaxLds) return T;
+    const int fixed = sparse_lds_layout<D>(T, d.n(), 0).total;  // d.n(): bound on any tile's blocks
+    const int room = (kMaxLds - fixed) & ~15;
+    if (room >= T) return {T, min((T * topk + 15) & ~15, room)};
   }
-  return 0;
+  return {0, 0};
 }
 
 bool sparse_mfma_supported(const Dims& d, int topk) {
   if (d.dtype != 1 || (d.D != 64 && d.D != 128) || d.L % 64) return false;
-  return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)) > 0;
+  return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)).T > 0;
 }
 
-template <int D, int S, int T>
+template <int D, int S, int T, bool BATCHED>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
-                             const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse,
-                             hipStream_t st) {
+                             const u32x4* kt, const int32_t* idx, int topk, int list_cap, float scale, void* o,
+                             float* lse, hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
-  const int lds = sparse_lds_layout<D>(T, d.n(), topk).total;
-  auto kern = sparse_fwd_kernel<D, S, T>;
+  const int lds = sparse_lds_layout<D>(T, d.n(), list_cap).total;
+  auto kern = sparse_fwd_kernel<D, S, T, BATCHED>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, kt, idx, topk,
-                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G());
+                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G(), list_cap);
   return hipGetLastError();
 }
 
 template <int D, int S>
 static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
                              const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
-  const int T = pick_tile<D>(d, topk);
-  if (T == 256) return run_sparse<D, S, 256>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
-  if (T == 192) return run_sparse<D, S, 192>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
-  return run_sparse<D, S, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  const SparseTile t = pick_tile<D>(d, topk);
+  // the batched kernel only where a tile's row lists (T * topk entries at most) may not fit
+  if (t.list_cap >= t.T * topk) {
+    if (t.T == 256) return run_sparse<D, S, 256, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+    if (t.T == 192) return run_sparse<D, S, 192, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+    return run_sparse<D, S, 128, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+  }
+  if (t.T == 256) return run_sparse<D, S, 256, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+  if (t.T == 192) return run_sparse<D, S, 192, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+  return run_sparse<D, S, 128, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
 }
 
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
