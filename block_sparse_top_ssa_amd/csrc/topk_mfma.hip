@@ -513,7 +513,7 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
   constexpr int NC = D / 32, NF = 3 * NC, NT = 4, NTH = S * 4, SCS = 68, NH = CAP / 64;
   // Scores of a chunk; rows 68 words apart: 16-byte aligned, and the quads' 16-byte
   // reads fall in distinct banks.
-  __shared__ float scb[NB][S][SCS];
+  __shared__ __align__(16) float scb[NB][S][SCS];
   // Collected entries, in index order: raw score and block index (rows start in
   // different banks).
   __shared__ float esc[S][CAP + 1];
@@ -779,6 +779,20 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
   // bits, absent ones 0): t = the m-th largest score bits; the entries above t, and
   // the first `need` at t, are the row's m best.  Returns the row's m-th key (in every
   // lane of the quad); with kOut the m best are written to the outputs in index order.
+  // Output staging: the block's rows of idx (and of sel) in the score buffer when they fit.
+  constexpr int kScbBytes = NB * S * SCS * 4;
+  const bool stage_i = S * topk * 4 <= kScbBytes;          // uniform
+  const bool stage_f = sh && S * topk * 8 <= kScbBytes;
+  int32_t* const ob_i = reinterpret_cast<int32_t*>(&scb[0][0][0]);
+  float* const ob_f = reinterpret_cast<float*>(ob_i + S * topk);
+  auto put = [&](int pos, int32_t bi, float sv) {
+    if (stage_i) ob_i[row * topk + pos] = bi;
+    else ih[(int64_t)row * topk + pos] = bi;
+    if (sh) {
+      if (stage_f) ob_f[row * topk + pos] = sv;
+      else sh[(int64_t)row * topk + pos] = sv;
+    }
+  };
   auto cut = [&](auto out_c) -> uint64_t {
     constexpr bool kOut = decltype(out_c)::value;
     const int cl = min(cnt, CAP);
@@ -830,16 +844,13 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
       if constexpr (kOut) {
         int tk_tot;
         int pos = pos_base + quad_excl_sum(tk, &tk_tot);
-        int32_t* orow = ih + (int64_t)row * topk;
-        float* srow = sh ? sh + (int64_t)row * topk : nullptr;
         rank = rank0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const bool at = hv[h][k] == t;
           if (hv[h][k] > t || (at && rank < need)) {
             const int e = 64 * h + 16 * p + k;
-            orow[pos] = irow[e];
-            if (srow) srow[pos] = erow[e];
+            put(pos, (int32_t)irow[e], erow[e]);
             ++pos;
           }
           rank += at;
@@ -872,13 +883,28 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
     collect(std::false_type{});
   }
 
-  // ---- output: the m keys at or above the row's exact m-th key, in index order
+  // ---- output: the m keys at or above the row's exact m-th key, in index order, then
+  // the own block, then -1.  The S rows are assembled in the score buffer (free now)
+  // and stored with 16-byte writes of the block's contiguous rows; written one entry
+  // per lane instead, each store would touch 16 rows' lines.
   (void)cut(std::true_type{});
-  int32_t* orow = ih + (int64_t)row * topk;
-  float* srow = sh ? sh + (int64_t)row * topk : nullptr;
-  for (int pp = m + p; pp < topk; pp += 4) {
-    orow[pp] = pp == m ? qb : -1;
-    if (srow) srow[pp] = pp == m ? inf : -inf;
+  for (int pp = m + p; pp < topk; pp += 4) put(pp, pp == m ? qb : -1, pp == m ? inf : -inf);
+  if (stage_i) {
+    __syncthreads();  // uniform: the block's rows are assembled
+    const int total = S * topk;
+    const bool vec = (total % 4 == 0) & ((reinterpret_cast<uintptr_t>(ih) & 15) == 0) &
+                     (!stage_f || (reinterpret_cast<uintptr_t>(sh) & 15) == 0);
+    if (vec) {
+      for (int i = 4 * tid; i < total; i += 4 * NTH) {
+        *reinterpret_cast<int4*>(ih + i) = *reinterpret_cast<const int4*>(ob_i + i);
+        if (stage_f) *reinterpret_cast<f32x4*>(sh + i) = *reinterpret_cast<const f32x4*>(ob_f + i);
+      }
+    } else {
+      for (int i = tid; i < total; i += NTH) {
+        ih[i] = ob_i[i];
+        if (stage_f) sh[i] = ob_f[i];
+      }
+    }
   }
 }
 
