@@ -415,6 +415,7 @@ def _guards_intact(big, shape):
     (1, 2, 384, 128, 128, 2),    # block 128, ragged tile
     (2, 1, 640, 64, 64, 3),      # D = 64
     (1, 2, 1344, 128, 64, 6),    # leading chunks left to the dense kernel, ragged last tile
+    (1, 1, 4096, 128, 64, 48),   # long idx rows: the sparse kernel's row lists built in batches
 ])
 def test_outputs_guarded(variant, B, H, L, D, s, topk):
     """Every output of the whole path written into a buffer with sentinel guard bands:
