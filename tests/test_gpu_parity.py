@@ -233,17 +233,18 @@ def test_bf16_L8192_ksweep(topk):
         assert np.all(g["drop"] <= 1e-4)
 
 
-@pytest.mark.parametrize("L,s,topk", [
-    (16384, 64, 96),    # row lists of a 256-row tile up to 24 KB: about three batches
-    (16384, 128, 48),   # block 128 (two 64-key chunks per block): two batches
+@pytest.mark.parametrize("H,Hkv,L,s,topk", [
+    (2, 2, 16384, 64, 96),    # row lists of a 256-row tile up to 24 KB: about three batches
+    (2, 2, 16384, 128, 48),   # block 128 (two 64-key chunks per block): two batches
+    (4, 2, 8192, 64, 80),     # grouped K/V heads; m = 79 takes the merge selection
 ])
-def test_sparse_row_lists_in_batches(L, s, topk):
+def test_sparse_row_lists_in_batches(H, Hkv, L, s, topk):
     """Long idx rows: a 256-row tile's row lists (one byte per kept block per row) do not
     fit beside its 128 KB O state, so the sparse kernel builds and consumes them in
     batches of consecutive blocks; every output must match the oracle as for short rows."""
-    B, H, D = 1, 2, 128
-    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=21)
-    inp.workload = W.Workload("batches", B, H, L, D, s, (topk,), W.BF16, "none", 21, sample_rows=384)
+    B, D = 1, 128
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=21, hkv=Hkv)
+    inp.workload = W.Workload("batches", B, H, L, D, s, (topk,), W.BF16, "none", 21, sample_rows=384, Hkv=Hkv)
     g = gpu_pipeline(inp, topk, tag=f"row-list batches L={L} s={s} k={topk}")
     rows = W.sample_rows(L, s, topk, 384, seed=21)
     rep = _oracle_checks(inp, g, topk, rows=rows)
