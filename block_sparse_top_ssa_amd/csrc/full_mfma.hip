@@ -458,8 +458,9 @@ template <int D, bool WANT_O, bool STATS = false>
 static hipError_t run_full(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale, void* o,
                            float* lse, hipStream_t st, const int32_t* didx = nullptr, int dtopk = 0,
                            float* ent = nullptr, float* hpart = nullptr) {
-  // with didx only the leading rows t < topk * s can keep every earlier block
-  const int rows = didx ? (int)std::min<int64_t>(d.L, (int64_t)dtopk * d.S) : d.L;
+  // with didx only rows whose block b_t <= topk can keep every earlier block (b_t
+  // distinct valid entries below b_t), i.e. t < (topk + 1) * s
+  const int rows = didx ? (int)std::min<int64_t>(d.L, ((int64_t)dtopk + 1) * d.S) : d.L;
   const int ntile = (rows + 255) / 256;
   const int64_t grid = (int64_t)ntile * d.bh();
   hipLaunchKernelGGL((full_fwd_kernel<D, WANT_O, STATS>), dim3((unsigned)grid), dim3(512), 0, st,

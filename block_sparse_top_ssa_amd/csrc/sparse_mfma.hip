@@ -37,9 +37,10 @@
 //     blocks simply add, in any order, with no rescaling.
 //  4. finalize: o = O / l (bf16), lse = m_ref + log l.
 // A 64-row query chunk whose rows all keep every block below their own (the leading
-// rows t < topk * s, or every row when topk covers all blocks) is plain causal
-// attention; this kernel skips it and the dense kernel, launched next on the same
-// stream, writes it (it keeps each row's O in registers, which gathered rows cannot).
+// rows t < topk * s, every row when topk covers all blocks; a row can only do so if
+// b_t <= topk) is plain causal attention; this kernel skips it and the dense kernel,
+// launched next on the same stream over the rows t < (topk + 1) * s, writes it (it
+// keeps each row's O in registers, which gathered rows cannot).
 //
 // m_ref is an attained logit of the row, so l >= 1 and nothing underflows.  If any
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass

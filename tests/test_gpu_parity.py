@@ -251,6 +251,27 @@ def test_sparse_row_lists_in_batches(H, Hkv, L, s, topk):
     say(f"[oracle] row-list batches L={L} s={s} k={topk}: {rep}")
 
 
+@pytest.mark.parametrize("s,topk", [(64, 4), (128, 3)])
+def test_full_chunk_of_the_kth_block(variant, s, topk):
+    """Rows of block k that list all k earlier blocks (the own block left out, which is
+    always attended anyway) keep every earlier block, so their 64-row chunks are plain
+    causal attention, which the sparse call hands to the dense kernel; those rows lie just
+    past the k * s leading rows.  Every row must be written and match the oracle."""
+    B, H, L, D = 1, 2, 1024, 128
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=22)
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, topk).cpu().numpy().copy()
+    idx[:, :, topk * s:(topk + 1) * s, :] = np.arange(topk, dtype=np.int32)
+    big, o = _guarded(q.shape, torch.bfloat16)  # sentinel bits everywhere: unwritten rows show
+    o_s, lse_s = ssa.sparse_attn_fwd(q, k, v, torch.from_numpy(idx.astype(np.int32)).cuda(), s, scale, out=o)
+    torch.cuda.synchronize()
+    assert _guards_intact(big, q.shape)
+    o_ref, lse_ref = O.attend_sparse(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), idx, s, scale)
+    assert_close(to_f64(o_s), o_ref, TOL[W.BF16], "o_sparse, full chunk of block k")
+    assert_close(to_f64(lse_s), lse_ref, TOL_LSE[W.BF16], "lse_sparse, full chunk of block k")
+
+
 # ----------------------------------------------------------------------------------
 # closed forms on the GPU
 # ----------------------------------------------------------------------------------
