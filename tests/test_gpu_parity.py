@@ -251,6 +251,32 @@ def test_sparse_row_lists_in_batches(H, Hkv, L, s, topk):
     say(f"[oracle] row-list batches L={L} s={s} k={topk}: {rep}")
 
 
+def test_sparse_row_lists_in_batches_d64():
+    """D = 64 leaves most of the LDS to the row lists; idx rows of 400 blocks still need
+    two batches per late tile.  The idx is a valid selection drawn at random (no top-k
+    call): 399 earlier blocks, ascending, then the own block."""
+    B, H, L, D, s, topk = 1, 1, 32768, 64, 64, 400
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=31)
+    rng = np.random.default_rng(5)
+    idx = np.full((B, H, L, topk), -1, np.int32)
+    for t in range(L):
+        bt = t // s
+        m = min(topk - 1, bt)
+        idx[0, 0, t, :m] = np.sort(rng.choice(bt, size=m, replace=False)) if m < bt else np.arange(bt)
+        idx[0, 0, t, m] = bt
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    o, lse = ssa.sparse_attn_fwd(q, k, v, torch.from_numpy(idx).cuda(), s, scale)
+    torch.cuda.synchronize()
+    late = rng.choice(np.arange((topk - 1) * s, L), 96, replace=False)
+    rows = np.unique(np.concatenate([late, [0, s - 1, s, (topk - 1) * s - 1, (topk - 1) * s, L - 1]]))
+    o_ref, lse_ref = O.attend_sparse(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), idx[:, :, rows], s, scale,
+                                     rows=rows)
+    eo = assert_close(to_f64(o)[:, :, rows], o_ref, TOL[W.BF16], "o_sparse, D = 64, batched row lists")
+    el = assert_close(to_f64(lse)[:, :, rows], lse_ref, TOL_LSE[W.BF16], "lse_sparse, D = 64, batched row lists")
+    say(f"[oracle] D = 64 batched row lists: o {eo:.2e} lse {el:.2e}")
+
+
 @pytest.mark.parametrize("s,topk", [(64, 4), (128, 3)])
 def test_full_chunk_of_the_kth_block(variant, s, topk):
     """Rows of block k that list all k earlier blocks (the own block left out, which is
