@@ -15,8 +15,13 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def libssa():
-    """The built C-ABI library (built in-tree first if it is missing)."""
+    """The built C-ABI library (built in-tree first if it is missing).  SSA_HOST_CHECK_LIB
+    names another build of the same ABI to test instead: the host-sanitizer build of the
+    argument checks (tests/test_host_sanitizers.py)."""
     from block_sparse_top_ssa_amd import _lib
+    other = os.environ.get("SSA_HOST_CHECK_LIB")
+    if other:
+        return _lib.load(other)
     if not os.path.exists(_lib.LIB_PATH):
         from block_sparse_top_ssa_amd import build
         build.build()
