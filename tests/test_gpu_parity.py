@@ -251,6 +251,27 @@ def test_sparse_row_lists_in_batches(H, Hkv, L, s, topk):
     say(f"[oracle] row-list batches L={L} s={s} k={topk}: {rep}")
 
 
+@pytest.mark.parametrize("B,H,Hkv,L,D,s,topk", [
+    (1, 4, 2, 8192, 128, 64, 80),     # batched row lists with grouped K/V heads
+    (1, 2, 2, 12288, 128, 128, 40),   # block 128, batched
+    (2, 2, 1, 6144, 128, 64, 33),     # odd k, all query heads on one K/V head, two sequences
+    (1, 3, 3, 5120, 64, 64, 50),      # D = 64: long rows in one batch
+    (1, 2, 2, 16448, 128, 64, 120),   # ragged last 256-row tile, many batches, merge selection
+    (3, 1, 1, 2304, 128, 128, 7),     # three sequences, block 128, ragged last tile
+])
+def test_mixed_shapes(B, H, Hkv, L, D, s, topk):
+    """Shapes that combine the features the other cases take one at a time: batch size,
+    grouped heads, long idx rows, ragged tiles and both block sizes, through the whole path
+    against the oracle on sampled rows (the selection on every row)."""
+    seed = 1000 + topk
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=seed, hkv=Hkv)
+    inp.workload = W.Workload("mixed", B, H, L, D, s, (topk,), W.BF16, "none", seed, Hkv=Hkv, sample_rows=256)
+    g = gpu_pipeline(inp, topk, tag=f"mixed {B}x{H}/{Hkv}x{L}x{D} s={s} k={topk}")
+    rows = W.sample_rows(L, s, topk, 256, seed=seed)
+    rep = _oracle_checks(inp, g, topk, rows=rows)
+    say(f"[oracle] mixed {B}x{H}/{Hkv}x{L}x{D} s={s} k={topk}: {rep}")
+
+
 def test_sparse_row_lists_in_batches_d64():
     """D = 64 leaves most of the LDS to the row lists; idx rows of 400 blocks still need
     two batches per late tile.  The idx is a valid selection drawn at random (no top-k

@@ -211,11 +211,11 @@ def integer_tensor(shape, lo, hi, seed, dtype=np.float32) -> np.ndarray:
 
 def sample_rows(L: int, s: int, k: int, count: int, seed: int) -> np.ndarray:
     """Seeded, sorted sample of query rows that always includes the edge rows
-    0, s-1, s, k*s-1, k*s, L-1 and the last row of every 16th block."""
+    0, s-1, s, k*s-1, k*s, (k+1)*s-1, (k+1)*s, L-1 and the last row of every 16th block."""
     if count <= 0 or count >= L:
         return np.arange(L)
     rng = np.random.default_rng(seed)
-    must = {0, s - 1, s, k * s - 1, k * s, L - 1}
+    must = {0, s - 1, s, k * s - 1, k * s, (k + 1) * s - 1, (k + 1) * s, L - 1}
     must |= {j * s + s - 1 for j in range(0, L // s, 16)}
     must = {r for r in must if 0 <= r < L}
     rest = rng.choice(L, size=max(0, count - len(must)), replace=False)
