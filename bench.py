@@ -2,17 +2,19 @@
 """Throughput of the SSA per-layer attention forward (both streams) on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input already
-resident in HBM: block pool -> causal top-k selection -> sparse attention -> full
-attention -> alignment statistics (L2 distance and dropped mass).  Default workload:
-bf16, B=1, H=32, L=32768, D=128, s=64, k=32 (token 0 an 8x-norm sink key).
+resident in HBM: block pool -> causal top-k selection -> k and v in the operand layouts
+(ssa_kv_frag, once, into buffers owned here) -> sparse attention -> full attention (both
+reading those layouts) -> alignment statistics (L2 distance and dropped mass).  Default
+workload: bf16, B=1, H=32, L=32768, D=128, s=64, k=32 (token 0 an 8x-norm sink key).
 
 Prints ONE JSON line.  `value` is the metric's quantity, the sparse-attention forward's
-tokens/s (B*L / the ssa_sparse_attn_fwd time inside the timed steps); the whole step's
-rate (B*L / step time) is `step_tokens_per_s`, its time `ms_per_step`.  The
-per-kernel times come from HIP events recorded on the stream the kernels run on
-(torch's current stream) around each call inside the timed steps.  `roofline` is
-given for the sparse-attention kernel, the one the metric names, on its useful
-FLOPs 4*D*sum_t |A(t)|.  `cpu_baseline` times the CPU oracle's sparse stream on a
+tokens/s: B*L / (the ssa_kv_frag time + the ssa_sparse_attn_fwd_frag time) inside the
+timed steps, so the layout pass the dense forward shares is counted against the sparse
+one; the whole step's rate (B*L / step time) is `step_tokens_per_s`, its time
+`ms_per_step`.  The per-kernel times come from HIP events recorded on the stream the
+kernels run on (torch's current stream) around each call inside the timed steps.
+`roofline` is given for the sparse-attention call, the kernel the metric names, on its
+useful FLOPs 4*D*sum_t |A(t)|.  `cpu_baseline` times the CPU oracle's sparse stream on a
 bounded sample of the same workload (rank 0, this process).
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
@@ -77,17 +79,19 @@ def work_model(w: W.Workload, k: int) -> dict:
     return {
         "pool": {"bytes": BHkv * (L * D * e + n * D * 4)},
         "topk": {"flops": 2 * D * BH * cand, "bytes": BH * (L * D * e + L * k * 4) + BHkv * n * D * 4},
+        # k and v read and written once in the operand layouts (bf16 only)
+        "kvfrag": {"bytes": 4 * BHkv * L * D * e if w.dtype == W.BF16 else 0},
         "sparse": {"flops": 4 * D * BH * attended_total(L, s, k)},
         "full": {"flops": 4 * D * BH * (L * (L + 1) // 2)},
         "align": {"bytes": BH * L * (2 * D * e + 4 * 4)},
     }
 
 
-# The sources each call's kernels come from (the sparse call also runs the fragment-order
-# passes and hands full 64-row chunks to the dense kernel).
-KERNEL_SOURCES = {"pool": ("pool.hip",), "topk": ("topk_mfma.hip",),
-                  "sparse": ("sparse_mfma.hip", "vfrag.hip", "full_mfma.hip"),
-                  "full": ("full_mfma.hip", "vfrag.hip"), "align": ("align.hip",)}
+# The sources each call's kernels come from (the sparse call hands full 64-row chunks to
+# the dense kernel; the fragment-order copies both forwards read are the kvfrag call).
+KERNEL_SOURCES = {"pool": ("pool.hip",), "topk": ("topk_mfma.hip",), "kvfrag": ("vfrag.hip",),
+                  "sparse": ("sparse_mfma.hip", "full_mfma.hip"),
+                  "full": ("full_mfma.hip",), "align": ("align.hip",)}
 SHARED_HEADERS = ("common.hpp", "mfma.hpp", "rowattn.hpp")
 
 
@@ -293,7 +297,17 @@ def main():
     lse_s = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
     lse_f = torch.empty_like(lse_s)
 
-    names = ["pool", "topk", "sparse", "full", "align"]
+    # k and v in the matrix-core operand layouts, written once per step into buffers owned
+    # here and read by both forwards (bf16; float32 takes no copies)
+    frag = w.dtype == W.BF16
+    nfrag = ssa.kv_frag_bytes(kk, s)
+    kf = torch.empty(nfrag, dtype=torch.uint8, device="cuda") if frag else None
+    vf = torch.empty(nfrag, dtype=torch.uint8, device="cuda") if frag else None
+    names = ["pool", "topk", "kvfrag", "sparse", "full", "align"]
+
+    def kv_layout():
+        if frag:
+            ssa.kv_frag(kk, v, s, k_frag=kf, v_frag=vf)
 
     def step(ev=None):
         def mark(i):
@@ -304,20 +318,22 @@ def main():
         mark(1)
         ssa.block_topk(q, km, s, k, out=idx)
         mark(2)
-        ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s)
+        kv_layout()
         mark(3)
-        ssa.full_attn_fwd(q, kk, v, scale, want_o=o_f is not None, block=s, out=o_f, lse=lse_f)
+        ssa.sparse_attn_fwd_frag(q, kk, v, kf, vf, idx, s, scale, out=o_s, lse=lse_s)
         mark(4)
+        ssa.full_attn_fwd_frag(q, kk, v, vf, scale, want_o=o_f is not None, block=s, out=o_f, lse=lse_f)
+        mark(5)
         if o_f is not None:
             ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)
         else:
             ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)
-        mark(5)
+        mark(6)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -340,8 +356,14 @@ def main():
         calls = {
             "pool": lambda: ssa.block_pool(kk, s, out=km),
             "topk": lambda: ssa.block_topk(q, km, s, k, out=idx),
-            "sparse": lambda: ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s),
-            "full": lambda: ssa.full_attn_fwd(q, kk, v, scale, want_o=o_f is not None, block=s, out=o_f, lse=lse_f),
+            "kvfrag": kv_layout,
+            "sparse": lambda: ssa.sparse_attn_fwd_frag(q, kk, v, kf, vf, idx, s, scale, out=o_s, lse=lse_s),
+            "full": lambda: ssa.full_attn_fwd_frag(q, kk, v, vf, scale, want_o=o_f is not None, block=s, out=o_f,
+                                                   lse=lse_f),
+            # the default calls, which write their own transient copies
+            "sparse_own_copies": lambda: ssa.sparse_attn_fwd(q, kk, v, idx, s, scale, out=o_s, lse=lse_s),
+            "full_own_copy": lambda: ssa.full_attn_fwd(q, kk, v, scale, want_o=o_f is not None, block=s, out=o_f,
+                                                       lse=lse_f),
             "align": (lambda: ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)) if o_f is not None
             else (lambda: ssa.align_stats(None, None, lse_f, lse_s, block=s, dims_like=q)),
         }
@@ -369,13 +391,18 @@ def main():
         kernels["full"]["note"] = "log-sum-exp only (value products skipped)"
         kernels["full"]["tflops"] = round(model["full"]["flops"] / 2 / (per["full"] * 1e-3) / 1e12, 2)
 
-    sp_tflops = model["sparse"]["flops"] / (per["sparse"] * 1e-3) / 1e12
+    # the sparse stream's forward: its attention call plus the operand layouts it reads
+    # (both copies counted here, although the dense forward reads the v copy too)
+    sp_ms = per["kvfrag"] + per["sparse"]
+    sp_tflops = model["sparse"]["flops"] / (sp_ms * 1e-3) / 1e12
+    attn_tflops = model["sparse"]["flops"] / (per["sparse"] * 1e-3) / 1e12
     tokens = B * L
     out = {
         "metric": METRIC,
-        # the metric's quantity: sparse-attention forward tokens/s, from the sparse call's
-        # HIP-event time inside the timed steps; the whole step's rate is step_tokens_per_s
-        "value": round(tokens / (per["sparse"] * 1e-3), 1),
+        # the metric's quantity: sparse-attention forward tokens/s, from the HIP-event times
+        # of the sparse call and the layout pass inside the timed steps; the whole step's
+        # rate is step_tokens_per_s
+        "value": round(tokens / (sp_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -388,12 +415,16 @@ def main():
         "dtype": "bf16" if w.dtype == W.BF16 else "f32",
         "data": "synthetic (seeded N(0,1) q, k, v with the workload's key structure; no dataset, no weights)",
         "config": {"workload": w.name, "B": B, "H": H, "Hkv": w.hkv, "L": L, "D": D, "block": s, "topk": k,
-                   "step": "pool+topk+sparse_attn+full_attn" + ("(lse only)" if o_f is None else "") + "+align"},
-        "sparse_attn": {"tokens_per_s": round(tokens / (per["sparse"] * 1e-3), 1),
+                   "step": "pool+topk+kv_frag+sparse_attn+full_attn" + ("(lse only)" if o_f is None else "")
+                   + "+align"},
+        "sparse_attn": {"tokens_per_s": round(tokens / (sp_ms * 1e-3), 1),
                         "tflops": round(sp_tflops, 2), "pct_mfma_bf16_peak": round(100 * sp_tflops / PEAK_BF16_TFLOPS, 2),
-                        "ms": round(per["sparse"], 4), "useful_flops": model["sparse"]["flops"]},
-        "roofline": {"kernel": "ssa_sparse_attn_fwd", "bound": "mfma", "achieved": round(sp_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(sp_tflops / PEAK_BF16_TFLOPS, 4),
+                        "ms": round(sp_ms, 4), "ms_layout": round(per["kvfrag"], 4),
+                        "ms_attention": round(per["sparse"], 4), "useful_flops": model["sparse"]["flops"]},
+        # the dominant kernel: the sparse attention call (sparse_fwd_kernel and the dense
+        # kernel on the 64-row chunks whose rows keep every earlier block)
+        "roofline": {"kernel": "ssa_sparse_attn_fwd_frag", "bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic["sparse"], "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + "
                      "WRITE_SIZE, scaled by a 1 GiB copy; null when the kernel changed since)"},
         "kernels": kernels,

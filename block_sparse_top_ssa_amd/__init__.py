@@ -10,6 +10,13 @@ and the stream: each call enqueues on torch's current stream and does not synchr
     o_f, lse_f = full_attn_fwd(q, k, v)
     dist, dropped = align_stats(o_f, o_s, lse_f, lse_s)
 
+With both streams over one k, v (bf16), their operand layouts can be written once into
+buffers the caller owns, and the forwards then take no workspace:
+
+    k_frag, v_frag = kv_frag(k, v, block)
+    o_s, lse_s = sparse_attn_fwd_frag(q, k, v, k_frag, v_frag, idx, block)
+    o_f, lse_f = full_attn_fwd_frag(q, k, v, v_frag)
+
 Decoding with a key/value cache (one new query per sequence, positions in a device
 int32 tensor `pos`, caches [B, Hkv, L, D] with L the capacity):
 
@@ -39,6 +46,7 @@ import torch
 from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
+           "kv_frag_bytes", "kv_frag", "sparse_attn_fwd_frag", "full_attn_fwd_frag",
            "decode_append", "decode_sparse_fwd", "decode_sparse_fwd_noalloc", "decode_full_fwd",
            "full_attn_bwd", "sparse_attn_bwd", "align_loss", "attn_stats",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
@@ -145,12 +153,10 @@ def block_topk(q: torch.Tensor, k_mean: torch.Tensor, block: int, topk: int, wan
     return (out, sel) if want_scores else out
 
 
-def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
-                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+def _sparse_args(q, k, v, idx, block, scale, want_lse, out, lse):
     d = _dims(q, block, _kv_heads(q, k, v))
     if idx.dim() != 4 or tuple(idx.shape[:3]) != (d.B, d.H, d.L) or idx.dtype != torch.int32:
         raise SSAError(2, "idx must be int32 [B, H, L, topk]")
-    topk = idx.shape[3]
     _expect(idx, idx.shape, torch.int32, q.device, "idx")
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if out is None:
@@ -160,28 +166,92 @@ def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_l
         lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
     if want_lse:
         _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "sparse_attn_fwd lse")
-    check(load().ssa_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(topk),
-                                     ctypes.c_float(scale), _ptr(out), _ptr(lse if want_lse else None),
-                                     _stream(q)))
-    return out, (lse if want_lse else None)
+    return d, scale, out, (lse if want_lse else None)
 
 
-def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
-                  block: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+def sparse_attn_fwd(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
+                    out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    d, scale, out, lse = _sparse_args(q, k, v, idx, block, scale, want_lse, out, lse)
+    check(load().ssa_sparse_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(idx.shape[3]),
+                                     ctypes.c_float(scale), _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse
+
+
+def _full_args(q, k, v, block, scale, want_o, want_lse, out, lse, what="full_attn_fwd"):
     d = _dims(q, block, _kv_heads(q, k, v))
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if want_o and out is None:
         out = torch.empty_like(q)
     if want_o:
-        _expect(out, q.shape, q.dtype, q.device, "full_attn_fwd out")
+        _expect(out, q.shape, q.dtype, q.device, f"{what} out")
     if want_lse and lse is None:
         lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
     if want_lse:
-        _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "full_attn_fwd lse")
+        _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, f"{what} lse")
+    return d, scale, (out if want_o else None), (lse if want_lse else None)
+
+
+def full_attn_fwd(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
+                  block: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    d, scale, out, lse = _full_args(q, k, v, block, scale, want_o, want_lse, out, lse)
     check(load().ssa_full_attn_fwd(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale),
-                                   _ptr(out if want_o else None), _ptr(lse if want_lse else None),
-                                   _stream(q)))
-    return (out if want_o else None), (lse if want_lse else None)
+                                   _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse
+
+
+def kv_frag_bytes(k: torch.Tensor, block: int = 64) -> int:
+    """Bytes of one fragment-order copy of k or v ([B, Hkv, L, D]); 0 for float32."""
+    d = _dims(k, block)
+    n = ctypes.c_int64(0)
+    check(load().ssa_kv_frag_bytes(ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
+def _frag_buf(t, nbytes, device, what):
+    if t is None:
+        return None
+    return _expect(t, (nbytes,), torch.uint8, device, what)
+
+
+def kv_frag(k: torch.Tensor, v: torch.Tensor, block: int = 64, want_k: bool = True, want_v: bool = True,
+            k_frag: torch.Tensor | None = None, v_frag: torch.Tensor | None = None):
+    """k and v (bf16 [B, Hkv, L, D]) written once in the layouts the matrix-core forwards
+    read, into uint8 buffers of kv_frag_bytes(k) each: (k_frag, v_frag), None where not
+    asked for.  Pass them to sparse_attn_fwd_frag / full_attn_fwd_frag with the same k, v."""
+    _same(k, v, "k/v")
+    d = _dims(k, block)
+    nbytes = kv_frag_bytes(k, block)
+    if want_k and k_frag is None:
+        k_frag = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    if want_v and v_frag is None:
+        v_frag = torch.empty(nbytes, dtype=torch.uint8, device=k.device)
+    kf = _frag_buf(k_frag if want_k else None, nbytes, k.device, "k_frag")
+    vf = _frag_buf(v_frag if want_v else None, nbytes, k.device, "v_frag")
+    check(load().ssa_kv_frag(ctypes.byref(d), _ptr(k), _ptr(v), _ptr(kf), _ptr(vf), _stream(k)))
+    return kf, vf
+
+
+def sparse_attn_fwd_frag(q, k, v, k_frag, v_frag, idx, block: int, scale: float | None = None,
+                         want_lse: bool = True, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """sparse_attn_fwd with the copies kv_frag wrote from the same k, v (no workspace)."""
+    d, scale, out, lse = _sparse_args(q, k, v, idx, block, scale, want_lse, out, lse)
+    nbytes = kv_frag_bytes(k, block)
+    kf = _frag_buf(k_frag, nbytes, q.device, "k_frag")
+    vf = _frag_buf(v_frag, nbytes, q.device, "v_frag")
+    check(load().ssa_sparse_attn_fwd_frag(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(kf), _ptr(vf), _ptr(idx),
+                                          int(idx.shape[3]), ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                          _stream(q)))
+    return out, lse
+
+
+def full_attn_fwd_frag(q, k, v, v_frag, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
+                       block: int = 64, out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """full_attn_fwd with the copy of v kv_frag wrote (no workspace)."""
+    d, scale, out, lse = _full_args(q, k, v, block, scale, want_o, want_lse, out, lse, "full_attn_fwd_frag")
+    vf = _frag_buf(v_frag, kv_frag_bytes(k, block), q.device, "v_frag")
+    check(load().ssa_full_attn_fwd_frag(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(vf), ctypes.c_float(scale),
+                                        _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse
 
 
 def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,

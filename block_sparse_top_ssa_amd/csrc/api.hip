@@ -130,13 +130,23 @@ ssa_status ssa_block_topk(const ssa_dims* dims, const void* q, const float* k_me
   return finish(ssa::launch_topk_generic(d, q, k_mean, topk, idx, sel_score, st), "ssa_block_topk");
 }
 
-ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,
-                               int32_t topk, float scale, void* o, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ssa_sparse_attn_fwd with (frag) or without the caller's fragment-order copies of k, v.
+ssa_status sparse_fwd(const char* what, bool frag, const ssa_dims* dims, const void* q, const void* k, const void* v,
+                      const void* k_frag, const void* v_frag, const int32_t* idx, int32_t topk, float scale, void* o,
+                      float* lse, void* stream) {
   ssa::Dims d;
   SSA_TRY(check_dims(dims, &d));
   SSA_TRY(check_ptr(q, "q", 16));
   SSA_TRY(check_ptr(k, "k", 16));
   SSA_TRY(check_ptr(v, "v", 16));
+  if (frag && d.dtype == SSA_BF16) {
+    SSA_TRY(check_ptr(k_frag, "k_frag", 16));
+    SSA_TRY(check_ptr(v_frag, "v_frag", 16));
+  }
   SSA_TRY(check_ptr(idx, "idx", 4));
   SSA_TRY(check_ptr(o, "o", 16));
   SSA_TRY(check_opt_ptr(lse, "lse", 4));
@@ -144,27 +154,92 @@ ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* 
   SSA_TRY(check_scale(scale));
   SSA_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
-  if (d.dtype == SSA_BF16 && use_mfma() && ssa::sparse_mfma_supported(d, topk))
-    return finish(ssa::launch_sparse_mfma(d, q, k, v, idx, topk, scale, o, lse, st), "ssa_sparse_attn_fwd");
-  return finish(ssa::launch_sparse_generic(d, q, k, v, idx, topk, scale, o, lse, st), "ssa_sparse_attn_fwd");
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::sparse_mfma_supported(d, topk)) {
+    if (frag)
+      return finish(ssa::launch_sparse_mfma_frag(d, q, k, v, static_cast<const ssa::u32x4*>(k_frag),
+                                                 static_cast<const ssa::u32x4*>(v_frag), idx, topk, scale, o, lse, st),
+                    what);
+    return finish(ssa::launch_sparse_mfma(d, q, k, v, idx, topk, scale, o, lse, st), what);
+  }
+  return finish(ssa::launch_sparse_generic(d, q, k, v, idx, topk, scale, o, lse, st), what);
 }
 
-ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, float scale, void* o,
-                             float* lse, void* stream) {
+// ssa_full_attn_fwd with (frag) or without the caller's fragment-order copy of v.
+ssa_status full_fwd(const char* what, bool frag, const ssa_dims* dims, const void* q, const void* k, const void* v,
+                    const void* v_frag, float scale, void* o, float* lse, void* stream) {
   ssa::Dims d;
   SSA_TRY(check_dims(dims, &d));
   SSA_TRY(check_ptr(q, "q", 16));
   SSA_TRY(check_ptr(k, "k", 16));
   SSA_TRY(check_ptr(v, "v", 16));
-  if (!o && !lse) return fail(SSA_ERR_NULL, "ssa_full_attn_fwd needs o or lse");
+  if (!o && !lse) return fail(SSA_ERR_NULL, "%s needs o or lse", what);
+  if (frag && d.dtype == SSA_BF16 && o) SSA_TRY(check_ptr(v_frag, "v_frag", 16));
   SSA_TRY(check_opt_ptr(o, "o", 16));
   SSA_TRY(check_opt_ptr(lse, "lse", 4));
   SSA_TRY(check_scale(scale));
   SSA_TRY(check_device());
   hipStream_t st = (hipStream_t)stream;
-  if (d.dtype == SSA_BF16 && use_mfma() && ssa::full_mfma_supported(d))
-    return finish(ssa::launch_full_mfma(d, q, k, v, scale, o, lse, st), "ssa_full_attn_fwd");
-  return finish(ssa::launch_full_generic(d, q, k, v, scale, o, lse, st), "ssa_full_attn_fwd");
+  if (d.dtype == SSA_BF16 && use_mfma() && ssa::full_mfma_supported(d)) {
+    if (frag)
+      return finish(ssa::launch_full_mfma_frag(d, q, k, o ? static_cast<const ssa::u32x4*>(v_frag) : nullptr, scale, o,
+                                               lse, st),
+                    what);
+    return finish(ssa::launch_full_mfma(d, q, k, v, scale, o, lse, st), what);
+  }
+  return finish(ssa::launch_full_generic(d, q, k, v, scale, o, lse, st), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, const int32_t* idx,
+                               int32_t topk, float scale, void* o, float* lse, void* stream) {
+  return sparse_fwd("ssa_sparse_attn_fwd", false, dims, q, k, v, nullptr, nullptr, idx, topk, scale, o, lse, stream);
+}
+
+ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v, float scale, void* o,
+                             float* lse, void* stream) {
+  return full_fwd("ssa_full_attn_fwd", false, dims, q, k, v, nullptr, scale, o, lse, stream);
+}
+
+ssa_status ssa_kv_frag_bytes(const ssa_dims* dims, int64_t* bytes) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  if (!bytes) return fail(SSA_ERR_NULL, "bytes is NULL");
+  *bytes = d.dtype == SSA_BF16 ? (int64_t)d.B * d.Hkv * d.L * d.D * 2 : 0;
+  g_last_error[0] = '\0';
+  return SSA_OK;
+}
+
+ssa_status ssa_kv_frag(const ssa_dims* dims, const void* k, const void* v, void* k_frag, void* v_frag, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  if (d.dtype != SSA_BF16) return fail(SSA_ERR_DTYPE, "ssa_kv_frag: the fragment-order copies exist for bf16 only");
+  if (!k_frag && !v_frag) return fail(SSA_ERR_NULL, "ssa_kv_frag needs k_frag or v_frag");
+  if (k_frag) {
+    SSA_TRY(check_ptr(k, "k", 16));
+    SSA_TRY(check_ptr(k_frag, "k_frag", 16));
+  }
+  if (v_frag) {
+    SSA_TRY(check_ptr(v, "v", 16));
+    SSA_TRY(check_ptr(v_frag, "v_frag", 16));
+  }
+  SSA_TRY(check_device());
+  ssa::LaunchResult r;
+  r.err = ssa::kv_frag_into(d.kv(), k, v, k_frag, v_frag, (hipStream_t)stream);
+  return finish(r, "ssa_kv_frag");
+}
+
+ssa_status ssa_sparse_attn_fwd_frag(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                    const void* k_frag, const void* v_frag, const int32_t* idx, int32_t topk,
+                                    float scale, void* o, float* lse, void* stream) {
+  return sparse_fwd("ssa_sparse_attn_fwd_frag", true, dims, q, k, v, k_frag, v_frag, idx, topk, scale, o, lse, stream);
+}
+
+ssa_status ssa_full_attn_fwd_frag(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                  const void* v_frag, float scale, void* o, float* lse, void* stream) {
+  return full_fwd("ssa_full_attn_fwd_frag", true, dims, q, k, v, v_frag, scale, o, lse, stream);
 }
 
 ssa_status ssa_full_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v, float scale,

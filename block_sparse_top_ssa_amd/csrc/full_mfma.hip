@@ -510,22 +510,28 @@ LaunchResult launch_full_mfma_stats(const Dims& d, const void* q, const void* k,
   return r;
 }
 
-LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
-                              float* lse, hipStream_t st) {
+LaunchResult launch_full_mfma_frag(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale,
+                                   void* o, float* lse, hipStream_t st) {
   LaunchResult r;
-  if (o) {
-    void* ws = nullptr;
-    r.err = vfrag_acquire(d.kv(), v, &ws, st);
-    if (r.err != hipSuccess) return r;
-    const u32x4* vt = static_cast<const u32x4*>(ws);
+  if (o)
     r.err = d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st)
                        : run_full<64, true>(d, q, k, vt, scale, o, lse, st);
-    const hipError_t ef = vfrag_release(ws, st);
-    if (r.err == hipSuccess) r.err = ef;
-  } else {  // log-sum-exp only: V is not read
+  else  // log-sum-exp only: V is not read
     r.err = d.D == 128 ? run_full<128, false>(d, q, k, nullptr, scale, o, lse, st)
                        : run_full<64, false>(d, q, k, nullptr, scale, o, lse, st);
-  }
+  return r;
+}
+
+LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale, void* o,
+                              float* lse, hipStream_t st) {
+  if (!o) return launch_full_mfma_frag(d, q, k, nullptr, scale, o, lse, st);
+  LaunchResult r;
+  void* ws = nullptr;
+  r.err = vfrag_acquire(d.kv(), v, &ws, st);
+  if (r.err != hipSuccess) return r;
+  r = launch_full_mfma_frag(d, q, k, static_cast<const u32x4*>(ws), scale, o, lse, st);
+  const hipError_t ef = vfrag_release(ws, st);
+  if (r.err == hipSuccess) r.err = ef;
   return r;
 }
 

@@ -52,6 +52,10 @@ hipError_t vfrag_release(void* ws, hipStream_t st);
 // lane 16 g + i holding K[64 c + 16 kt + i][32 cc + 8 g .. +7]; B*H*L*D*2 bytes from the
 // same pool (d holds the key/value head count in H), given back with vfrag_release.
 hipError_t kfrag_acquire(const Dims& d, const void* k, void** ws, hipStream_t st);
+// Both rewrites into caller-given buffers of B*H*L*D*2 bytes each (d holds the key/value
+// head count in H): kf as kfrag_acquire's copy of k, vf as vfrag_acquire's copy of v;
+// a null kf or vf skips that copy.
+hipError_t kv_frag_into(const Dims& d, const void* k, const void* v, void* kf, void* vf, hipStream_t st);
 // The same rewrite of any bf16 [B,H,L,D] tensor (d.H heads) into a caller-given buffer.
 hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st);
 
@@ -119,6 +123,10 @@ LaunchResult launch_topk_mfma(const Dims& d, const void* q, const float* k_mean,
 bool full_mfma_supported(const Dims& d);
 LaunchResult launch_full_mfma(const Dims& d, const void* q, const void* k, const void* v, float scale,
                               void* o, float* lse, hipStream_t st);
+// The same with v already in fragment order (vt as written by vfrag_acquire; unused, and
+// may be null, when o is null): no workspace.
+LaunchResult launch_full_mfma_frag(const Dims& d, const void* q, const void* k, const u32x4* vt, float scale,
+                                   void* o, float* lse, hipStream_t st);
 // The same with the full stream's measurements from the sweep's own probabilities:
 // entropy [B,H,L] and the distance histogram [B,H,kDistBuckets] (either may be null).
 LaunchResult launch_full_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, float scale,
@@ -137,5 +145,10 @@ bool sparse_mfma_supported(const Dims& d, int topk);
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v,
                                 const int32_t* idx, int topk, float scale, void* o, float* lse,
                                 hipStream_t st);
+// The same with k and v already in fragment order (kt, vt as kfrag_acquire and
+// vfrag_acquire write them): no workspace.
+LaunchResult launch_sparse_mfma_frag(const Dims& d, const void* q, const void* k, const void* v, const u32x4* kt,
+                                     const u32x4* vt, const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                     hipStream_t st);
 
 }  // namespace ssa

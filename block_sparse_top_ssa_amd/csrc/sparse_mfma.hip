@@ -729,6 +729,20 @@ static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const 
   return run_sparse<D, S, 128, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
 }
 
+LaunchResult launch_sparse_mfma_frag(const Dims& d, const void* q, const void* k, const void* v, const u32x4* kt,
+                                     const u32x4* vt, const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                     hipStream_t st) {
+  LaunchResult r;
+  if (d.D == 128)
+    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<128, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  else
+    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
+                      : dispatch_t<64, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st);
+  return r;
+}
+
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
                                 int topk, float scale, void* o, float* lse, hipStream_t st) {
   LaunchResult r;
@@ -741,15 +755,8 @@ LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, con
     (void)vfrag_release(ws, st);
     return r;
   }
-  const u32x4* vt = static_cast<const u32x4*>(ws);
-  const u32x4* kt = static_cast<const u32x4*>(kws);
-  if (d.D == 128)
-    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<128, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
-  else
-    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<64, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
-  if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st);
+  r = launch_sparse_mfma_frag(d, q, k, v, static_cast<const u32x4*>(kws), static_cast<const u32x4*>(ws), idx, topk,
+                              scale, o, lse, st);
   const hipError_t ef = vfrag_release(ws, st);
   const hipError_t ek = vfrag_release(kws, st);
   if (r.err == hipSuccess) r.err = ef != hipSuccess ? ef : ek;

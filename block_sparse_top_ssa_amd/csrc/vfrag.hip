@@ -122,6 +122,15 @@ hipError_t kfrag_acquire(const Dims& d, const void* k, void** ws, hipStream_t st
   return e;
 }
 
+hipError_t kv_frag_into(const Dims& d, const void* k, const void* v, void* kf, void* vf, hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (kf)
+    e = d.D == 128 ? run_kfrag<128>(d, k, static_cast<u32x4*>(kf), st) : run_kfrag<64>(d, k, static_cast<u32x4*>(kf), st);
+  if (e == hipSuccess && vf)
+    e = d.D == 128 ? run_vfrag<128>(d, v, static_cast<u32x4*>(vf), st) : run_vfrag<64>(d, v, static_cast<u32x4*>(vf), st);
+  return e;
+}
+
 hipError_t frag_order_into(const Dims& d, const void* x, void* out, hipStream_t st) {
   return d.D == 128 ? run_vfrag<128>(d, x, static_cast<u32x4*>(out), st)
                     : run_vfrag<64>(d, x, static_cast<u32x4*>(out), st);

@@ -30,7 +30,9 @@
  *                 - ssa_full_attn_bwd, ssa_sparse_attn_bwd
  *                 - ssa_full_attn_fwd_stats
  *                 - ssa_attn_stats, ssa_align_loss
- *               ssa_decode_sparse_fwd_noalloc allocates nothing (a fixed device array).
+ *               ssa_decode_sparse_fwd_noalloc allocates nothing (a fixed device array);
+               ssa_kv_frag, ssa_sparse_attn_fwd_frag and ssa_full_attn_fwd_frag allocate
+               nothing (the copies are buffers the caller owns).
  *  Stream       `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *               Calls only enqueue work on that stream and return; there is no hidden
  *               synchronisation.  Outputs are valid once the stream reaches that point.
@@ -62,9 +64,10 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 7 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
+#define SSA_ABI_VERSION 8 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
                              6: allocation-free sparse decoding; 7: measurements fused into the full
-                             forward and the stream comparison */
+                             forward and the stream comparison; 8: caller-owned fragment-order
+                             copies of k and v shared by both forwards */
 
 typedef int32_t ssa_status;
 enum {
@@ -159,6 +162,57 @@ ssa_status ssa_sparse_attn_fwd(const ssa_dims* dims, const void* q, const void* 
  */
 ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k, const void* v,
                              float scale, void* o, float* lse, void* stream);
+
+/*
+ * Key and value layouts shared by the two forwards (bf16).
+ *   Both streams of a layer read the same keys and values (sec. 5, pp. 6-7: the full and
+ *   the sparse stream run side by side on one layer's q, k, v).  On bf16 the matrix-core
+ *   kernels read v, and the sparse kernel also k, in the order of their operands, so
+ *   ssa_sparse_attn_fwd and ssa_full_attn_fwd each rewrite them into a transient copy.  A
+ *   caller running both can write the copies once into buffers it owns with ssa_kv_frag
+ *   and pass them to the _frag forms below, which take no workspace at all.  The layouts
+ *   are internal to this library version: use a copy only with the k, v it was written
+ *   from, and write it again after k or v change.
+ *
+ * ssa_kv_frag_bytes -- size of one copy.
+ *   bytes    out: B*Hkv*L*D*2 for bf16, 0 for float32 (no copy exists; the _frag forms
+ *            then ignore k_frag and v_frag).  dims is checked as for the forwards.
+ */
+ssa_status ssa_kv_frag_bytes(const ssa_dims* dims, int64_t* bytes);
+
+/*
+ * ssa_kv_frag -- write k and/or v in the operand layouts.
+ *   k, v       [B,Hkv,L,D] bf16                      in (each needed only with its copy)
+ *   k_frag     ssa_kv_frag_bytes bytes or NULL       out: k as the sparse kernel's score
+ *              operand reads it (per 64-key chunk, 16-key tile and 32-column slice, one
+ *              contiguous 1 KB fragment)
+ *   v_frag     ssa_kv_frag_bytes bytes or NULL       out: v as both forwards' value-product
+ *              operand reads it (per 64-key chunk, 16-column tile and key half, one 1 KB
+ *              fragment)
+ *   At least one copy must be asked for; buffers 16-byte aligned, not overlapping k or v.
+ *   float32 dims return SSA_ERR_DTYPE.  Allocates nothing.
+ */
+ssa_status ssa_kv_frag(const ssa_dims* dims, const void* k, const void* v, void* k_frag, void* v_frag,
+                       void* stream);
+
+/*
+ * ssa_sparse_attn_fwd_frag -- ssa_sparse_attn_fwd reading the copies ssa_kv_frag wrote
+ *   from the same k and v.  Arguments and results as ssa_sparse_attn_fwd (k and v are
+ *   still read: rows whose logits need the exact recompute, and the leading query chunks
+ *   the dense kernel writes); k_frag and v_frag are required on bf16 and ignored (may be
+ *   NULL) on float32.  Allocates nothing.
+ */
+ssa_status ssa_sparse_attn_fwd_frag(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                    const void* k_frag, const void* v_frag, const int32_t* idx, int32_t topk,
+                                    float scale, void* o, float* lse, void* stream);
+
+/*
+ * ssa_full_attn_fwd_frag -- ssa_full_attn_fwd reading the copy of v that ssa_kv_frag
+ *   wrote.  Arguments and results as ssa_full_attn_fwd (bit for bit); v_frag is required
+ *   on bf16 when o is given, and ignored (may be NULL) otherwise.  Allocates nothing.
+ */
+ssa_status ssa_full_attn_fwd_frag(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                  const void* v_frag, float scale, void* o, float* lse, void* stream);
 
 /*
  * ssa_full_attn_fwd_stats -- ssa_full_attn_fwd with the full stream's attention-pattern

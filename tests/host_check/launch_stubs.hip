@@ -83,5 +83,16 @@ LaunchResult launch_sparse_mfma(const Dims&, const void*, const void*, const voi
                                 void*, float*, hipStream_t) {
   return refused();
 }
+LaunchResult launch_sparse_mfma_frag(const Dims&, const void*, const void*, const void*, const u32x4*,
+                                     const u32x4*, const int32_t*, int, float, void*, float*, hipStream_t) {
+  return refused();
+}
+LaunchResult launch_full_mfma_frag(const Dims&, const void*, const void*, const u32x4*, float, void*, float*,
+                                   hipStream_t) {
+  return refused();
+}
+hipError_t kv_frag_into(const Dims&, const void*, const void*, void*, void*, hipStream_t) {
+  return hipErrorInvalidValue;
+}
 
 }  // namespace ssa

@@ -216,3 +216,33 @@ def test_decode_noalloc_argument_checks(libssa):
     assert libssa.ssa_decode_sparse_fwd_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 16, 0.1,
                                                 FAKE, None, FAKE, None) == 2
     assert "scratch" in libssa.ssa_last_error().decode()
+
+
+def test_kv_frag_argument_checks(libssa):
+    """The shared fragment-order copies: size query, the copy call (bf16 only, at least one
+    copy, aligned buffers) and the forwards that read them (copies required on bf16)."""
+    d = _dims(B=2, H=4, L=256, D=128, Hkv=2)
+    n = ctypes.c_int64(-1)
+    assert libssa.ssa_kv_frag_bytes(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 2 * 2 * 256 * 128 * 2
+    f32 = _dims(dtype=_lib.SSA_F32)
+    assert libssa.ssa_kv_frag_bytes(ctypes.byref(f32), ctypes.byref(n)) == 0 and n.value == 0
+    assert libssa.ssa_kv_frag_bytes(ctypes.byref(d), None) == 1
+    assert libssa.ssa_kv_frag_bytes(ctypes.byref(_dims(D=96)), ctypes.byref(n)) == 2
+    F = FAKE
+    assert libssa.ssa_kv_frag(ctypes.byref(d), F, F, None, None, None) == 1
+    assert libssa.ssa_kv_frag(ctypes.byref(f32), F, F, F, F, None) == 3
+    assert libssa.ssa_kv_frag(ctypes.byref(d), None, F, F, None, None) == 1
+    assert libssa.ssa_kv_frag(ctypes.byref(d), F, F, F, MISALIGNED, None) == 4
+    assert libssa.ssa_sparse_attn_fwd_frag(ctypes.byref(d), F, F, F, None, F, F, 2, 0.1, F, None, None) == 1
+    assert libssa.ssa_sparse_attn_fwd_frag(ctypes.byref(d), F, F, F, F, MISALIGNED, F, 2, 0.1, F, None, None) == 4
+    assert libssa.ssa_sparse_attn_fwd_frag(ctypes.byref(d), F, F, F, F, F, F, 5, 0.1, F, None, None) == 2
+    assert libssa.ssa_full_attn_fwd_frag(ctypes.byref(d), F, F, F, None, 0.1, F, None, None) == 1
+    assert libssa.ssa_full_attn_fwd_frag(ctypes.byref(d), F, F, F, F, 0.1, None, None, None) == 1
+    assert libssa.ssa_full_attn_fwd_frag(ctypes.byref(d), F, F, F, F, -0.1, F, None, None) == 4
+    if not gpu_available():
+        # without o the copy of v is not needed; on float32 no copy is needed at all
+        assert libssa.ssa_full_attn_fwd_frag(ctypes.byref(d), F, F, F, None, 0.1, None, F, None) == 5
+        assert libssa.ssa_sparse_attn_fwd_frag(ctypes.byref(f32), F, F, F, None, None, F, 2, 0.1, F, None,
+                                               None) == 5
+        assert libssa.ssa_kv_frag(ctypes.byref(d), F, None, F, None, None) == 5
