@@ -290,7 +290,7 @@ def main():
     q, kk, v = dev(inp.q), dev(inp.k), dev(inp.v)
     s, scale = w.s, 1.0 / math.sqrt(w.D)
     B, H, L, D = w.B, w.H, w.L, w.D
-    km = torch.empty((B, H, w.n, D), dtype=torch.float32, device="cuda")
+    km = torch.empty((B, w.hkv, w.n, D), dtype=torch.float32, device="cuda")  # pooled keys of the K/V heads
     idx = torch.empty((B, H, L, k), dtype=torch.int32, device="cuda")
     o_s = torch.empty_like(q)
     o_f = None if w.sparse_only else torch.empty_like(q)
