@@ -47,6 +47,7 @@ from ._lib import SSA_BF16, SSA_F32, Dims, SSAError, check, load
 
 __all__ = ["block_pool", "block_topk", "sparse_attn_fwd", "full_attn_fwd", "align_stats",
            "kv_frag_bytes", "kv_frag", "sparse_attn_fwd_frag", "full_attn_fwd_frag",
+           "full_attn_fwd_stats", "sparse_attn_fwd_stats",
            "decode_append", "decode_sparse_fwd", "decode_sparse_fwd_noalloc", "decode_full_fwd",
            "full_attn_bwd", "sparse_attn_bwd", "align_loss", "attn_stats",
            "set_kernel_variant", "SSAError", "lib", "abi_version"]
@@ -275,6 +276,20 @@ def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True
                                          _ptr(out if want_o else None), _ptr(lse if want_lse else None),
                                          _ptr(ent), _ptr(hist), _stream(q)))
     return (out if want_o else None), (lse if want_lse else None), ent, hist
+
+
+def sparse_attn_fwd_stats(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
+                          want_entropy: bool = True, want_hist: bool = True, out: torch.Tensor | None = None,
+                          lse: torch.Tensor | None = None):
+    """sparse_attn_fwd with the sparse stream's row entropy [B, H, L] and attention mass by
+    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist)."""
+    d, scale, out, lse = _sparse_args(q, k, v, idx, block, scale, want_lse, out, lse)
+    ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
+    hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
+    check(load().ssa_sparse_attn_fwd_stats(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(idx.shape[3]),
+                                           ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ent), _ptr(hist),
+                                           _stream(q)))
+    return out, lse, ent, hist
 
 
 def align_stats(o_full=None, o_sparse=None, lse_full=None, lse_sparse=None, block: int = 64,

@@ -36,6 +36,7 @@ PROTOTYPES = {
     "ssa_kv_frag": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_sparse_attn_fwd_frag": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP]),
     "ssa_full_attn_fwd_frag": (_I32, [_DP, _VP, _VP, _VP, _VP, _F, _VP, _VP, _VP]),
+    "ssa_sparse_attn_fwd_stats": (_I32, [_DP, _VP, _VP, _VP, _VP, _I32, _F, _VP, _VP, _VP, _VP, _VP]),
     "ssa_full_attn_fwd_stats": (_I32, [_DP, _VP, _VP, _VP, _F, _VP, _VP, _VP, _VP, _VP]),
     "ssa_align_stats": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ssa_align_stats_hist": (_I32, [_DP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),

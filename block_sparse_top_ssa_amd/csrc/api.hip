@@ -203,6 +203,32 @@ ssa_status ssa_full_attn_fwd(const ssa_dims* dims, const void* q, const void* k,
   return full_fwd("ssa_full_attn_fwd", false, dims, q, k, v, nullptr, scale, o, lse, stream);
 }
 
+ssa_status ssa_sparse_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                    const int32_t* idx, int32_t topk, float scale, void* o, float* lse,
+                                    float* entropy, float* dist_hist, void* stream) {
+  ssa::Dims d;
+  SSA_TRY(check_dims(dims, &d));
+  SSA_TRY(check_ptr(q, "q", 16));
+  SSA_TRY(check_ptr(k, "k", 16));
+  SSA_TRY(check_ptr(v, "v", 16));
+  SSA_TRY(check_ptr(idx, "idx", 4));
+  SSA_TRY(check_ptr(o, "o", 16));
+  SSA_TRY(check_opt_ptr(lse, "lse", 4));
+  if (!entropy && !dist_hist) return fail(SSA_ERR_NULL, "ssa_sparse_attn_fwd_stats needs entropy or dist_hist");
+  SSA_TRY(check_opt_ptr(entropy, "entropy", 4));
+  SSA_TRY(check_opt_ptr(dist_hist, "dist_hist", 4));
+  if (topk < 1 || topk > d.n()) return fail(SSA_ERR_SHAPE, "topk=%d outside [1, n=%d]", topk, d.n());
+  SSA_TRY(check_scale(scale));
+  SSA_TRY(check_device());
+  hipStream_t st = (hipStream_t)stream;
+  const bool mfma = d.dtype == SSA_BF16 && use_mfma();
+  if (mfma && ssa::sparse_mfma_stats_supported(d, topk))
+    return finish(ssa::launch_sparse_mfma_stats(d, q, k, v, idx, topk, scale, o, lse, entropy, dist_hist, st),
+                  "ssa_sparse_attn_fwd_stats");
+  return finish(ssa::launch_sparse_stats_unfused(d, mfma, q, k, v, idx, topk, scale, o, lse, entropy, dist_hist, st),
+                "ssa_sparse_attn_fwd_stats");
+}
+
 ssa_status ssa_kv_frag_bytes(const ssa_dims* dims, int64_t* bytes) {
   ssa::Dims d;
   SSA_TRY(check_dims(dims, &d));

@@ -83,7 +83,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (threadIdx.x < 256 && t < L && !row_keeps_all(didx + (bh * (int64_t)L + t) * dtopk, dtopk, t / dS))
       chunk_full[threadIdx.x / 64] = 0;
     __syncthreads();
-    if (!(chunk_full[0] | chunk_full[1] | chunk_full[2] | chunk_full[3])) return;  // uniform
+    if (!(chunk_full[0] | chunk_full[1] | chunk_full[2] | chunk_full[3])) {  // uniform
+      if constexpr (STATS)
+        if (hpart && threadIdx.x < kDistBuckets) hpart[((int64_t)bh * ntile + tile) * kDistBuckets + threadIdx.x] = 0.f;
+      return;
+    }
   }
   const int rq = late ? 32 : 0;              // row offset inside the diagonal chunk
   const int r0 = tile * 256 + 64 * (w & 3) + rq;  // first row of this wave
@@ -397,8 +401,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   if constexpr (STATS) {
     // entropy of each row; the workgroup's bucket masses, each row's divided by its l
+    // (with didx only the rows of the chunks this workgroup writes)
     float hw[4] = {0.f, 0.f, 0.f, 0.f};  // buckets 4 g .. 4 g + 3, this lane's rows
-    if (active) {
+    if (active && (!didx || chunk_full[w & 3])) {
       if (cur_b >= 0) flush(cur_b);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -472,7 +477,10 @@ static hipError_t run_full(const Dims& d, const void* q, const void* k, const u3
 
 hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* k, const u32x4* vt,
                                       const int32_t* idx, int topk, float scale, void* o, float* lse,
-                                      hipStream_t st) {
+                                      hipStream_t st, float* ent, float* hpart) {
+  if (ent || hpart)
+    return d.D == 128 ? run_full<128, true, true>(d, q, k, vt, scale, o, lse, st, idx, topk, ent, hpart)
+                      : run_full<64, true, true>(d, q, k, vt, scale, o, lse, st, idx, topk, ent, hpart);
   return d.D == 128 ? run_full<128, true>(d, q, k, vt, scale, o, lse, st, idx, topk)
                     : run_full<64, true>(d, q, k, vt, scale, o, lse, st, idx, topk);
 }

@@ -131,6 +131,11 @@ LaunchResult launch_full_mfma_frag(const Dims& d, const void* q, const void* k, 
 // entropy [B,H,L] and the distance histogram [B,H,kDistBuckets] (either may be null).
 LaunchResult launch_full_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, float scale,
                                     void* o, float* lse, float* entropy, float* hist, hipStream_t st);
+// The unfused sparse form: the sparse forward (matrix-core kernel if mfma and the shape
+// fits, else the portable one), then the measurement pass over its lse.
+LaunchResult launch_sparse_stats_unfused(const Dims& d, bool mfma, const void* q, const void* k, const void* v,
+                                         const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                         float* entropy, float* hist, hipStream_t st);
 // The unfused form: the full forward, then the measurement pass over its lse.
 LaunchResult launch_full_stats_unfused(const Dims& d, const void* q, const void* k, const void* v, float scale,
                                        void* o, float* lse, float* entropy, float* hist, hipStream_t st);
@@ -138,10 +143,19 @@ LaunchResult launch_full_stats_unfused(const Dims& d, const void* q, const void*
 hipError_t launch_hist_sum(const float* part, float* hist, int64_t bh, int P, hipStream_t st);
 // The dense kernel over the sparse stream's full rows: writes o and lse of the 64-row
 // query chunks whose rows all keep every earlier block (row_keeps_all), nothing else.
+// With ent or hpart it also writes those rows' entropy and one distance-histogram partial
+// per (b, h, 256-row tile) of the rows t < (topk + 1) * block (0 where it writes no row).
 hipError_t launch_full_rows_of_sparse(const Dims& d, const void* q, const void* k, const u32x4* vt,
                                       const int32_t* idx, int topk, float scale, void* o, float* lse,
-                                      hipStream_t st);
+                                      hipStream_t st, float* ent = nullptr, float* hpart = nullptr);
 bool sparse_mfma_supported(const Dims& d, int topk);
+// The sparse forward with the sparse stream's measurements from its own sweep (entropy
+// [B,H,L], distance histogram [B,H,kDistBuckets]; either may be null): the tile that fits
+// the measurement state in LDS, and the launcher (transient copies and partials from the pool).
+bool sparse_mfma_stats_supported(const Dims& d, int topk);
+LaunchResult launch_sparse_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                                      int topk, float scale, void* o, float* lse, float* ent, float* hist,
+                                      hipStream_t st);
 LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, const void* v,
                                 const int32_t* idx, int topk, float scale, void* o, float* lse,
                                 hipStream_t st);

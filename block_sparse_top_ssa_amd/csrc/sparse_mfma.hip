@@ -46,6 +46,9 @@
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass
 // 2^kGuard), the row is flagged and recomputed exactly by one wave with a running-max
 // softmax at the end; with unit-scale inputs this does not happen.
+#include <algorithm>
+#include <type_traits>
+
 #include "launch.hpp"
 #include "mfma.hpp"
 #include "rowattn.hpp"
@@ -57,10 +60,13 @@ constexpr int kSlotBytes = 2256;  // P^T fragments (2 KB), 16 row ids, 2 x 16 ro
 
 struct SparseLds {
   // byte offsets inside the dynamic LDS block
-  int ost, lst, lse2, mref, off, misc, slots, flag, list, total;
+  int ost, lst, lse2, mref, lent, hbk, off, misc, slots, flag, list, total;
 };
 
-template <int D>
+// STATS: the layout also holds each row's sum of p x (x = log2 p against m_ref, for the
+// entropy) and its mass in each block-distance bucket, and the slots carry four row sums.
+constexpr int kSlotBytesStats = 2384;  // P^T fragments (2 KB), 16 row ids, 4 x 16 row sums, chunk ids
+template <int D, bool STATS = false>
 __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int list_cap) {
   SparseLds s;
   int o = 0;
@@ -68,11 +74,14 @@ __host__ __device__ inline SparseLds sparse_lds_layout(int T, int nb, int list_c
   s.lst = o;   o += T * 4;   // row sums of the bf16-rounded p (normalise o)
   s.lse2 = o;  o += T * 4;   // row sums of the float32 p (log-sum-exp)
   s.mref = o;  o += T * 4;
+  s.lent = o;  o += STATS ? T * 4 : 0;
+  s.hbk = o;   o += STATS ? T * kDistBuckets * 4 : 0;
   s.off = o;   o += (nb + 1) * 4;
   s.misc = o;  o += 48;  // 4 item counts, 4 chunk flags
   o = (o + 15) & ~15;
   s.slots = o;  // 2 sets x 4 slots; the per-block counters of the index build live here first
-  o += 8 * kSlotBytes > nb * 4 ? 8 * kSlotBytes : nb * 4;
+  const int slot_bytes = STATS ? kSlotBytesStats : kSlotBytes;
+  o += 8 * slot_bytes > nb * 4 ? 8 * slot_bytes : nb * 4;
   s.flag = o;  o += T;
   s.list = o;  o += list_cap;  // row lists of one batch of blocks (at least T entries)
   s.total = (o + 15) & ~15;
@@ -92,6 +101,15 @@ struct Slot {
   int chunk, next_chunk, pad0, pad1;
 };
 static_assert(sizeof(Slot) == kSlotBytes, "slot layout");
+// The slot of the measuring instance: the rounded and exact p sums, the p x sums and the
+// exact sums again, so value wave i adds sums[i] (its own row array) with no selection.
+struct SlotStats {
+  u32x4 p[2][64];
+  int rows[16];
+  float sums[4][16];
+  int chunk, next_chunk, pad0, pad1;
+};
+static_assert(sizeof(SlotStats) == kSlotBytesStats, "slot layout");
 
 // sum of the 8 bf16 values packed in a P^T fragment
 __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
@@ -101,12 +119,55 @@ __device__ __forceinline__ float sum_bf16x8(const u32x4& w) {
   return s;
 }
 
-template <int D, int S, int T, bool BATCHED>
+// The sparse stream's measurements of one query row t from its exact log-sum-exp (nats),
+// one wave: returns the entropy -sum p ln p over A(t) and adds the mass of each
+// block-distance bucket to hb (lane 0), walking the keys as attend_sparse_row does (the
+// row's own block causally, then each valid listed block below it).  qs holds q in float.
+template <int D>
+__device__ float sparse_row_stats(const uint16_t* __restrict__ kh, const float* qs, const int32_t* __restrict__ ir,
+                                  int topk, int t, int S, float scale, float lse, float* hb) {
+  const int lane = threadIdx.x & 63;
+  const int bt = t / S, cpb = S / 64;
+  float ent = 0.f;
+  auto chunk = [&](int c, int bucket) {
+    const int key = c * 64 + lane;
+    float p = 0.f, pl = 0.f;
+    if (key <= t) {
+      const uint16_t* kr = kh + (int64_t)key * D;
+      float acc = 0.f;
+      for (int d = 0; d < D; d += 8) {
+        float x[8];
+        Elem<uint16_t>::unpack(load16(kr + d), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(qs[d + e], x[e], acc);
+      }
+      const float lg = acc * scale - lse;  // ln p
+      p = expf(lg);
+      pl = p * lg;
+    }
+    const float mass = wave_sum(p);
+    ent -= wave_sum(pl);
+    if (lane == 0) hb[bucket] += mass;
+  };
+  for (int c = bt * cpb; c <= t / 64; ++c) chunk(c, 0);
+  int prev = -1;
+  for (int e = 0; e < topk; ++e) {
+    const int j = ir[e];
+    if (j > prev && j < bt) {
+      prev = j;
+      for (int ch = 0; ch < cpb; ++ch) chunk(j * cpb + ch, dist_bucket(bt - j));
+    }
+  }
+  return ent;
+}
+
+template <int D, int S, int T, bool BATCHED, bool STATS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void sparse_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const u32x4* __restrict__ vt, const u32x4* __restrict__ ktf, const int32_t* __restrict__ idx, int topk,
     uint16_t* __restrict__ o,
-    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G, int list_cap) {
+    float* __restrict__ lse, int L, int BH, int ntile, float sl2, float scale, int G, int list_cap,
+    float* __restrict__ ent_out, float* __restrict__ hpart) {
   constexpr int NW = 8, NTH = 512;
   constexpr int NC = D / 32, NDT = D / 16, CPB = S / 64;
   constexpr int DTW = NDT / 4;  // d tiles per value wave
@@ -122,7 +183,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int t0 = tile * T;
   const int rows = min(T, L - t0);
   const int nb = (t0 + rows - 1) / S;  // candidate blocks: those below the last row's block
-  const SparseLds lay = sparse_lds_layout<D>(T, nb, list_cap);
+  const SparseLds lay = sparse_lds_layout<D, STATS>(T, nb, list_cap);
   float* ost = reinterpret_cast<float*>(smem + lay.ost);
   float* lst = reinterpret_cast<float*>(smem + lay.lst);
   float* lsx = reinterpret_cast<float*>(smem + lay.lse2);
@@ -131,9 +192,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   int* off = reinterpret_cast<int*>(smem + lay.off);
   int* misc = reinterpret_cast<int*>(smem + lay.misc);
   int* chunk_full = misc + 4;  // per 64-row query chunk: its rows all keep every earlier block
-  Slot* slots = reinterpret_cast<Slot*>(smem + lay.slots);  // [2][4]: set, score wave
+  using SlotT = std::conditional_t<STATS, SlotStats, Slot>;
+  SlotT* slots = reinterpret_cast<SlotT*>(smem + lay.slots);  // [2][4]: set, score wave
   uint8_t* flag = smem + lay.flag;
   uint8_t* list = smem + lay.list;
+  float* lent = reinterpret_cast<float*>(smem + lay.lent);  // STATS: per row sum of p x
+  float* hbk = reinterpret_cast<float*>(smem + lay.hbk);    // STATS: [row][bucket] mass
 
   const uint16_t* qh = q + bh * (int64_t)L * D;
   const int64_t kvh = bh / G;  // K/V head of this query head
@@ -237,6 +301,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (launched after this one, it applies the same test) and takes no part here.
   for (int j = tid; j < nb; j += NTH) cnt[j] = 0;
   for (int r = tid; r < T; r += NTH) flag[r] = 0;
+  if constexpr (STATS)
+    for (int i = tid; i < T * kDistBuckets; i += NTH) hbk[i] = 0.f;
   if (tid < 4) chunk_full[tid] = 1;
   __syncthreads();
   if (tid < rows) {
@@ -247,7 +313,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __syncthreads();
   bool tile_full = true;
   for (int c = 0; c < rows / 64; ++c) tile_full = tile_full && chunk_full[c];
-  if (tile_full) return;  // uniform: the dense kernel writes every row of this tile
+  if (tile_full) {  // uniform: the dense kernel writes (and measures) every row of this tile
+    if constexpr (STATS)
+      if (hpart && tid < kDistBuckets) hpart[((int64_t)bh * ntile + tile) * kDistBuckets + tid] = 0.f;
+    return;
+  }
   auto row_here = [&](int r) { return !chunk_full[r / 64]; };
   if (tid < rows && row_here(tid)) for_each_entry(t0 + tid, [&](int j) { atomicAdd(&cnt[j], 1); });
   __syncthreads();
@@ -323,15 +393,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           mx = fmaxf(mx, x);
         }
       mx = max_over_rows(mx);
-      float px = 0.f;
+      float px = 0.f, pe = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(p[i] - mx);
+        const float e = p[i] - mx;
+        p[i] = fast_exp2(e);
         px += p[i];
+        if constexpr (STATS) pe = fmaf(p[i], fmaxf(e, -0x1p100f), pe);  // masked keys: p = 0
       }
       const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
       const float ps = sum_over_rows(sum_bf16x8(pf0) + sum_bf16x8(pf1));  // sum of the rounded p the products use
       px = sum_over_rows(px);
+      if constexpr (STATS) pe = sum_over_rows(pe);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         f32x4 acc = f32x4{0, 0, 0, 0};
@@ -343,6 +416,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         lst[r] = ps;
         lsx[r] = px;
         mrf[r] = mx;
+        if constexpr (STATS) {
+          lent[r] = pe;
+          hbk[r * kDistBuckets] = px;  // distance bucket 0: the own block
+        }
       }
     }
     if (CPB == 2 && (c_diag & 1)) {
@@ -371,7 +448,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(kf[kt][cc], qf[cc], sacc[kt]);
         }
         const float mr = mrf[r];
-        float p[16], mx = -__builtin_huge_valf(), px = 0.f;
+        float p[16], mx = -__builtin_huge_valf(), px = 0.f, pe = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -380,6 +457,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             mx = fmaxf(mx, x);
             p[kt * 4 + i] = fast_exp2(x);
             px += p[kt * 4 + i];
+            if constexpr (STATS) pe = fmaf(p[kt * 4 + i], x, pe);
           }
         if (mx > kGuard) flag[r] = 1;
         const u32x4 pf0 = pack_p(&p[0], &p[4]), pf1 = pack_p(&p[8], &p[12]);
@@ -393,9 +471,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           f32x4* gp = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * dt + 4 * g));
           *gp = *gp + acc;
         }
+        if constexpr (STATS) pe = sum_over_rows(pe);
         if (g == 0) {
           lst[r] += ps;
           lsx[r] += px;
+          if constexpr (STATS) {
+            lent[r] += pe;
+            hbk[r * kDistBuckets] += px;
+          }
         }
       }
     }
@@ -422,7 +505,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   u32x4 ra[RA], qf[NC];
   u32x4 pub0 = u32x4{0, 0, 0, 0}, pub1 = u32x4{0, 0, 0, 0};
   int pub_r = -1, pub_c = -1, pub_nc = -1;
-  float pub_ps = 0.f, pub_px = 0.f;
+  float pub_ps = 0.f, pub_px = 0.f, pub_pe = 0.f;
   int scored = 0;
   auto load_item = [&](bool new_chunk) {
     const int beg = off[j] - lbase, count = off[j + 1] - off[j];
@@ -449,7 +532,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int cc = 0; cc < NC; ++cc) sacc[kt] = mfma_bf16(ra[kt * NC + cc], qf[cc], sacc[kt]);
     }
-    float p[16], mx = -__builtin_huge_valf(), px = 0.f;
+    float p[16], mx = -__builtin_huge_valf(), px = 0.f, pe = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -458,12 +541,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         mx = fmaxf(mx, x);
         p[kt * 4 + i] = fast_exp2(x);
         px += p[kt * 4 + i];
+        if constexpr (STATS) pe = fmaf(p[kt * 4 + i], fmaxf(x, -0x1p100f), pe);  // r < 0: x = -inf, p = 0
       }
     if (mx > kGuard) flag[r] = 1;  // mx is -inf for r < 0
     pub0 = pack_p(&p[0], &p[4]);
     pub1 = pack_p(&p[8], &p[12]);
     pub_ps = sum_over_rows(sum_bf16x8(pub0) + sum_bf16x8(pub1));  // sum of the rounded p the products use
     pub_px = sum_over_rows(px);
+    if constexpr (STATS) pub_pe = sum_over_rows(pe);
     pub_r = r;
     pub_c = j * CPB + ch;
     // advance to the next tile and issue its loads (scored next round)
@@ -484,6 +569,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   // value-wave state (waves 4-7): V^T fragments of its column slice, per score-wave stream
   const int pw = w - 4;
+  // the same as a scalar (the compiler cannot see that w is uniform across the wave);
+  // STATS: value wave i keeps the row sums sums[i] of the slots in lsum: the rounded and
+  // the exact p sums, the p x sums, and per row and distance bucket the exact p sums
+  const int pu = __builtin_amdgcn_readfirstlane(pw);
+  float* const lsum = pu == 0 ? lst : pu == 1 ? lsx : pu == 2 ? lent : hbk;
   int vchunk[4] = {-1, -1, -1, -1};
   auto load_v = [&](int s, int c) {
 #pragma unroll
@@ -494,14 +584,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // The tile scored last goes to the wave's slot in set `set` (chunk -1: nothing).
   auto publish = [&](int set, bool have) {
-    Slot& sl = slots[set * 4 + w];
+    SlotT& sl = slots[set * 4 + w];
     if (have) {
       sl.p[0][lane] = pub0;
       sl.p[1][lane] = pub1;
       if (g == 0) {
         sl.rows[n] = pub_r;
-        sl.ps_round[n] = pub_ps;
-        sl.ps_exact[n] = pub_px;
+        if constexpr (STATS) {
+          sl.sums[0][n] = pub_ps;
+          sl.sums[1][n] = pub_px;
+          sl.sums[2][n] = pub_pe;
+          sl.sums[3][n] = pub_px;
+        } else {
+          sl.ps_round[n] = pub_ps;
+          sl.ps_exact[n] = pub_px;
+        }
       }
     }
     if (lane == 0) {
@@ -569,7 +666,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     } else {
       for (int rd = 0; rd < rounds; ++rd) {
         // ------------------------------------------------------------ value wave
-        const Slot* const cs = slots + (rd & 1) * 4;
+        const SlotT* const cs = slots + (rd & 1) * 4;
         // (1) slot headers and P^T; (2) V^T of a stream's first chunk (later chunks were
         // loaded a round ahead); (3) all products; (4) next round's V^T loads (registers
         // are free once the products are issued); (5) read-add-write into the owned
@@ -582,7 +679,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           sc[s] = __builtin_amdgcn_readfirstlane(cs[s].chunk);  // uniform: scalar branches
           sn[s] = __builtin_amdgcn_readfirstlane(cs[s].next_chunk);
           sr[s] = cs[s].rows[n];
-          sps[s] = pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
+          if constexpr (STATS)
+            sps[s] = cs[s].sums[pu][n];
+          else
+            sps[s] = pw == 0 ? cs[s].ps_round[n] : cs[s].ps_exact[n];
           sp[s][0] = cs[s].p[0][lane];
           sp[s][1] = cs[s].p[1][lane];
         }
@@ -625,10 +725,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
               gp[dl] = reinterpret_cast<f32x4*>(ost + ost_granule<D>(r, 16 * (pw * DTW + dl) + 4 * g));
               cv[dl] = *gp[dl];
             }
-            const float lv = pw < 2 ? ls[r] : 0.f;
+            if constexpr (STATS) {
+              // value waves 2 and 3 also keep a row sum each: the p x sums (entropy) and
+              // the mass in the distance bucket of this slot's block
+              const int li = pu == 3 ? r * kDistBuckets + dist_bucket((t0 + r) / S - sc[s] / CPB) : r;
+              const float lv = lsum[li];
 #pragma unroll
-            for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
-            if (pw < 2 && g == 0) ls[r] = lv + sps[s];
+              for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
+              if (g == 0) lsum[li] = lv + sps[s];
+            } else {
+              const float lv = pw < 2 ? ls[r] : 0.f;
+#pragma unroll
+              for (int dl = 0; dl < DTW; ++dl) *gp[dl] = cv[dl] + acc[s][dl];
+              if (pw < 2 && g == 0) ls[r] = lv + sps[s];
+            }
           }
         }
         __syncthreads();
@@ -650,28 +760,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (lse)
     for (int r = tid; r < rows; r += NTH)
       if (!flag[r] && row_here(r)) lse[bh * (int64_t)L + t0 + r] = (mrf[r] + log2f(lsx[r])) * kLn2;
+  if constexpr (STATS)  // entropy = ln l - ln 2 sum(p x) / l, with p = 2^x against m_ref
+    if (ent_out)
+      for (int r = tid; r < rows; r += NTH)
+        if (!flag[r] && row_here(r)) ent_out[bh * (int64_t)L + t0 + r] = logf(lsx[r]) - kLn2 * lent[r] / lsx[r];
 
   // ---------------------------------------------------------------- 5. exact recompute of flagged rows
   int any = 0;
   for (int r = tid; r < rows; r += NTH) any |= flag[r];
-  if (!__syncthreads_or(any)) return;
-  float* qs = reinterpret_cast<float*>(smem + lay.ost) + w * D;  // O state no longer needed
-  for (int r = w; r < rows; r += NW) {
-    if (!flag[r]) continue;
-    const int t = t0 + r;
-    for (int d = lane; d < D; d += 64) qs[d] = bf16_bits_to_f32(qh[(int64_t)t * D + d]);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    float m = -__builtin_huge_valf(), l = 0.f, acc[D / 64];
+  const bool any_flag = __syncthreads_or(any);
+  if constexpr (!STATS) {
+    if (!any_flag) return;
+  }
+  if (any_flag) {
+    float* qs = reinterpret_cast<float*>(smem + lay.ost) + w * D;  // O state no longer needed
+    for (int r = w; r < rows; r += NW) {
+      if (!flag[r]) continue;
+      const int t = t0 + r;
+      for (int d = lane; d < D; d += 64) qs[d] = bf16_bits_to_f32(qh[(int64_t)t * D + d]);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      float m = -__builtin_huge_valf(), l = 0.f, acc[D / 64];
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-    attend_sparse_row<uint16_t, D>(kh, vh, qs, ih + (int64_t)t * topk, topk, t, S, scale, m, l, acc);
-    const float inv = 1.f / l;
+      for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+      attend_sparse_row<uint16_t, D>(kh, vh, qs, ih + (int64_t)t * topk, topk, t, S, scale, m, l, acc);
+      const float inv = 1.f / l;
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e)
-      o[(bh * (int64_t)L + t) * D + lane + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
-    if (lse && lane == 0) lse[bh * (int64_t)L + t] = m + logf(l);
-    __builtin_amdgcn_wave_barrier();
+      for (int e = 0; e < D / 64; ++e)
+        o[(bh * (int64_t)L + t) * D + lane + 64 * e] = (uint16_t)f32_to_bf16_bits(acc[e] * inv);
+      if (lse && lane == 0) lse[bh * (int64_t)L + t] = m + logf(l);
+      if constexpr (STATS) {
+        // the row's measurements from its exact log-sum-exp; its bucket masses are then
+        // normalised already, so its divisor becomes 1
+        float* hr = hbk + r * kDistBuckets;
+        if (lane < kDistBuckets) hr[lane] = 0.f;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const float e = sparse_row_stats<D>(kh, qs, ih + (int64_t)t * topk, topk, t, S, scale, m + logf(l), hr);
+        if (lane == 0) {
+          if (ent_out) ent_out[bh * (int64_t)L + t] = e;
+          lsx[r] = 1.f;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if constexpr (STATS) {
+    // this tile's distance histogram: each row's bucket masses divided by its l, summed
+    // over the rows in a fixed order (row groups, then the groups) into one partial
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem + lay.ost);  // [row group][bucket]; the O state is done
+    constexpr int RG = NTH / kDistBuckets;
+    {
+      const int b = tid % kDistBuckets, rg = tid / kDistBuckets;
+      float x = 0.f;
+      for (int r = rg; r < rows; r += RG)
+        if (row_here(r)) x += hbk[r * kDistBuckets + b] / lsx[r];
+      red[rg * kDistBuckets + b] = x;
+    }
+    __syncthreads();
+    if (hpart && tid < kDistBuckets) {
+      float y = 0.f;
+      for (int i = 0; i < RG; ++i) y += red[i * kDistBuckets + tid];
+      hpart[((int64_t)bh * ntile + tile) * kDistBuckets + tid] = y;
+    }
   }
 }
 
@@ -683,10 +834,10 @@ struct SparseTile {
 // Rows per tile: the most (so each visited block serves the most rows) whose LDS fits
 // with a list area of at least T entries; the list area takes what is left, up to a
 // tile's whole row lists (T * topk entries), so long idx rows only add batches.
-template <int D>
+template <int D, bool STATS = false>
 static SparseTile pick_tile(const Dims& d, int topk) {
   for (int T : {256, 192, 128}) {
-    const int fixed = sparse_lds_layout<D>(T, d.n(), 0).total;  // d.n(): bound on any tile's blocks
+    const int fixed = sparse_lds_layout<D, STATS>(T, d.n(), 0).total;  // d.n(): bound on any tile's blocks
     const int room = (kMaxLds - fixed) & ~15;
     if (room >= T) return {T, min((T * topk + 15) & ~15, room)};
   }
@@ -698,47 +849,64 @@ bool sparse_mfma_supported(const Dims& d, int topk) {
   return (d.D == 128 ? pick_tile<128>(d, topk) : pick_tile<64>(d, topk)).T > 0;
 }
 
-template <int D, int S, int T, bool BATCHED>
+bool sparse_mfma_stats_supported(const Dims& d, int topk) {
+  if (!sparse_mfma_supported(d, topk)) return false;
+  return (d.D == 128 ? pick_tile<128, true>(d, topk) : pick_tile<64, true>(d, topk)).T > 0;
+}
+
+template <int D, int S, int T, bool BATCHED, bool STATS>
 static hipError_t run_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
                              const u32x4* kt, const int32_t* idx, int topk, int list_cap, float scale, void* o,
-                             float* lse, hipStream_t st) {
+                             float* lse, float* ent, float* hpart, hipStream_t st) {
   const int ntile = (d.L + T - 1) / T;
   const int64_t grid = (int64_t)ntile * d.bh();
-  const int lds = sparse_lds_layout<D>(T, d.n(), list_cap).total;
-  auto kern = sparse_fwd_kernel<D, S, T, BATCHED>;
+  const int lds = sparse_lds_layout<D, STATS>(T, d.n(), list_cap).total;
+  auto kern = sparse_fwd_kernel<D, S, T, BATCHED, STATS>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), vt, kt, idx, topk,
-                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G(), list_cap);
+                     static_cast<uint16_t*>(o), lse, d.L, (int)d.bh(), ntile, scale * kLog2e, scale, d.G(), list_cap,
+                     ent, hpart);
   return hipGetLastError();
 }
 
-template <int D, int S>
+template <int D, int S, bool STATS>
 static hipError_t dispatch_t(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
-                             const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse, hipStream_t st) {
-  const SparseTile t = pick_tile<D>(d, topk);
+                             const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse,
+                             float* ent, float* hpart, hipStream_t st) {
+  const SparseTile t = pick_tile<D, STATS>(d, topk);
   // the batched kernel only where a tile's row lists (T * topk entries at most) may not fit
   if (t.list_cap >= t.T * topk) {
-    if (t.T == 256) return run_sparse<D, S, 256, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
-    if (t.T == 192) return run_sparse<D, S, 192, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
-    return run_sparse<D, S, 128, false>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+    if (t.T == 256)
+      return run_sparse<D, S, 256, false, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
+    if (t.T == 192)
+      return run_sparse<D, S, 192, false, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
+    return run_sparse<D, S, 128, false, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
   }
-  if (t.T == 256) return run_sparse<D, S, 256, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
-  if (t.T == 192) return run_sparse<D, S, 192, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
-  return run_sparse<D, S, 128, true>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, st);
+  if (t.T == 256)
+    return run_sparse<D, S, 256, true, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
+  if (t.T == 192)
+    return run_sparse<D, S, 192, true, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
+  return run_sparse<D, S, 128, true, STATS>(d, q, k, v, vt, kt, idx, topk, t.list_cap, scale, o, lse, ent, hpart, st);
+}
+
+template <bool STATS>
+static hipError_t dispatch_sparse(const Dims& d, const void* q, const void* k, const void* v, const u32x4* vt,
+                                  const u32x4* kt, const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                  float* ent, float* hpart, hipStream_t st) {
+  if (d.D == 128)
+    return d.S == 64 ? dispatch_t<128, 64, STATS>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, ent, hpart, st)
+                     : dispatch_t<128, 128, STATS>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, ent, hpart, st);
+  return d.S == 64 ? dispatch_t<64, 64, STATS>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, ent, hpart, st)
+                   : dispatch_t<64, 128, STATS>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, ent, hpart, st);
 }
 
 LaunchResult launch_sparse_mfma_frag(const Dims& d, const void* q, const void* k, const void* v, const u32x4* kt,
                                      const u32x4* vt, const int32_t* idx, int topk, float scale, void* o, float* lse,
                                      hipStream_t st) {
   LaunchResult r;
-  if (d.D == 128)
-    r.err = d.S == 64 ? dispatch_t<128, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<128, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
-  else
-    r.err = d.S == 64 ? dispatch_t<64, 64>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st)
-                      : dispatch_t<64, 128>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, st);
+  r.err = dispatch_sparse<false>(d, q, k, v, vt, kt, idx, topk, scale, o, lse, nullptr, nullptr, st);
   if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st);
   return r;
 }
@@ -760,6 +928,56 @@ LaunchResult launch_sparse_mfma(const Dims& d, const void* q, const void* k, con
   const hipError_t ef = vfrag_release(ws, st);
   const hipError_t ek = vfrag_release(kws, st);
   if (r.err == hipSuccess) r.err = ef != hipSuccess ? ef : ek;
+  return r;
+}
+
+// hist[bh][m] = the sum of the sparse kernel's Ps partials of (b, h), then of the dense
+// kernel's Pd partials, in order.
+__global__ __launch_bounds__(64) void sparse_hist_sum_kernel(const float* __restrict__ ps, int Ps,
+                                                             const float* __restrict__ pd, int Pd,
+                                                             float* __restrict__ hist) {
+  const int64_t bh = blockIdx.x;
+  const int m = threadIdx.x;
+  if (m >= kDistBuckets) return;
+  double x = 0.0;
+  for (int p = 0; p < Ps; ++p) x += ps[(bh * Ps + p) * kDistBuckets + m];
+  for (int p = 0; p < Pd; ++p) x += pd[(bh * Pd + p) * kDistBuckets + m];
+  hist[bh * kDistBuckets + m] = (float)x;
+}
+
+LaunchResult launch_sparse_mfma_stats(const Dims& d, const void* q, const void* k, const void* v, const int32_t* idx,
+                                      int topk, float scale, void* o, float* lse, float* ent, float* hist,
+                                      hipStream_t st) {
+  LaunchResult r;
+  const int T = (d.D == 128 ? pick_tile<128, true>(d, topk) : pick_tile<64, true>(d, topk)).T;
+  const int Ps = (d.L + T - 1) / T;                                                 // sparse kernel tiles
+  const int Pd = (int)((std::min<int64_t>(d.L, ((int64_t)topk + 1) * d.S) + 255) / 256);  // dense-chunk tiles
+  void* hws = nullptr;
+  float *ps = nullptr, *pd = nullptr;
+  if (hist) {
+    r.err = workspace_alloc((size_t)d.bh() * (Ps + Pd) * kDistBuckets * sizeof(float), &hws, st);
+    if (r.err != hipSuccess) return r;
+    ps = static_cast<float*>(hws);
+    pd = ps + (size_t)d.bh() * Ps * kDistBuckets;
+  }
+  void* ws = nullptr;
+  void* kws = nullptr;
+  r.err = vfrag_acquire(d.kv(), v, &ws, st);
+  if (r.err == hipSuccess) r.err = kfrag_acquire(d.kv(), k, &kws, st);
+  if (r.err == hipSuccess) {
+    const u32x4* vt = static_cast<const u32x4*>(ws);
+    r.err = dispatch_sparse<true>(d, q, k, v, vt, static_cast<const u32x4*>(kws), idx, topk, scale, o, lse, ent, ps,
+                                  st);
+    if (r.err == hipSuccess) r.err = launch_full_rows_of_sparse(d, q, k, vt, idx, topk, scale, o, lse, st, ent, pd);
+    if (r.err == hipSuccess && hist) {
+      hipLaunchKernelGGL(sparse_hist_sum_kernel, dim3((unsigned)d.bh()), dim3(64), 0, st, ps, Ps, pd, Pd, hist);
+      r.err = hipGetLastError();
+    }
+  }
+  for (void* p : {ws, kws, hws}) {
+    const hipError_t e = vfrag_release(p, st);
+    if (r.err == hipSuccess) r.err = e;
+  }
   return r;
 }
 

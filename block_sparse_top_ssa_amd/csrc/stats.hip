@@ -281,6 +281,29 @@ LaunchResult launch_full_stats_unfused(const Dims& d, const void* q, const void*
   return r;
 }
 
+// The sparse forward then the measurement pass over its lse, for the dtypes and shapes
+// the fused matrix-core kernel does not take (a transient lse when the caller wants none).
+LaunchResult launch_sparse_stats_unfused(const Dims& d, bool mfma, const void* q, const void* k, const void* v,
+                                         const int32_t* idx, int topk, float scale, void* o, float* lse,
+                                         float* entropy, float* hist, hipStream_t st) {
+  LaunchResult r;
+  void* ws = nullptr;
+  float* l = lse;
+  if (!l) {
+    r.err = workspace_alloc((size_t)d.tokens() * sizeof(float), &ws, st);
+    if (r.err != hipSuccess) return r;
+    l = static_cast<float*>(ws);
+  }
+  r = mfma && sparse_mfma_supported(d, topk) ? launch_sparse_mfma(d, q, k, v, idx, topk, scale, o, l, st)
+                                             : launch_sparse_generic(d, q, k, v, idx, topk, scale, o, l, st);
+  if (r.err == hipSuccess && !r.unsupported) r = launch_attn_stats(d, mfma, q, k, l, idx, topk, scale, entropy, hist, st);
+  if (ws) {
+    const hipError_t ef = vfrag_release(ws, st);
+    if (r.err == hipSuccess) r.err = ef;
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------- launcher
 LaunchResult launch_attn_stats(const Dims& d, bool mfma, const void* q, const void* k, const float* lse,
                                const int32_t* idx, int topk, float scale, float* entropy, float* hist,

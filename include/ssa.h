@@ -28,7 +28,7 @@
  *                 - ssa_full_attn_fwd (bf16, with o given)
  *                 - ssa_decode_sparse_fwd, ssa_decode_full_fwd
  *                 - ssa_full_attn_bwd, ssa_sparse_attn_bwd
- *                 - ssa_full_attn_fwd_stats
+ *                 - ssa_full_attn_fwd_stats, ssa_sparse_attn_fwd_stats
  *                 - ssa_attn_stats, ssa_align_loss
  *               ssa_decode_sparse_fwd_noalloc allocates nothing (a fixed device array);
                ssa_kv_frag, ssa_sparse_attn_fwd_frag and ssa_full_attn_fwd_frag allocate
@@ -64,10 +64,11 @@
 extern "C" {
 #endif
 
-#define SSA_ABI_VERSION 8 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
+#define SSA_ABI_VERSION 9 /* 2: Hkv; 3: decoding; 4: backward and alignment loss; 5: attention stats;
                              6: allocation-free sparse decoding; 7: measurements fused into the full
                              forward and the stream comparison; 8: caller-owned fragment-order
-                             copies of k and v shared by both forwards */
+                             copies of k and v shared by both forwards; 9: measurements fused
+                             into the sparse forward */
 
 typedef int32_t ssa_status;
 enum {
@@ -236,6 +237,30 @@ ssa_status ssa_full_attn_fwd_frag(const ssa_dims* dims, const void* q, const voi
 ssa_status ssa_full_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v,
                                    float scale, void* o, float* lse, float* entropy, float* dist_hist,
                                    void* stream);
+
+/*
+ * ssa_sparse_attn_fwd_stats -- ssa_sparse_attn_fwd with the sparse stream's
+ *   attention-pattern measurements taken from the same sweep's probabilities.
+ *   The pages compare methods by attention entropy (App. H, Table A9) and by the
+ *   attention mass at each distance (App. K.2, p. 31); these are the quantities
+ *   ssa_attn_stats gives for the same idx, without its second pass over q and k.
+ *   q, k, v, idx, topk, scale, o, lse   as for ssa_sparse_attn_fwd
+ *   entropy    [B,H,L] float32 or NULL   out: -sum_{i in A(t)} p_ti ln p_ti (nats)
+ *   dist_hist  [B,H,16] float32 or NULL  out: sum_t sum_{i in A(t)} p_ti over keys whose
+ *              block distance b_t - b_i falls in bucket m (buckets as for
+ *              ssa_full_attn_fwd_stats); each head's buckets sum to L.  Summed in a fixed order.
+ *   At least one of entropy, dist_hist must be given.  On bf16 the measurements come from
+ *   the sparse kernel's own rounds (on 192-row tiles where the measurement state does not
+ *   fit beside 256 rows); on float32 (and shapes the matrix-core kernel does not take) the
+ *   call runs ssa_sparse_attn_fwd and then the measurement pass.  The entropies can differ
+ *   in the last bits from run to run, like o.
+ *   Workspace, from the pool: the transient k, v copies of ssa_sparse_attn_fwd and
+ *   64 bytes of histogram partials per (b, h) and tile; on the unfused path B*H*L*4 bytes
+ *   of log-sum-exp when lse is NULL plus ssa_attn_stats' workspace.
+ */
+ssa_status ssa_sparse_attn_fwd_stats(const ssa_dims* dims, const void* q, const void* k, const void* v,
+                                     const int32_t* idx, int32_t topk, float scale, void* o, float* lse,
+                                     float* entropy, float* dist_hist, void* stream);
 
 /*
  * ssa_align_stats -- per-token comparison of the full and sparse streams.

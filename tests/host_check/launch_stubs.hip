@@ -91,6 +91,15 @@ LaunchResult launch_full_mfma_frag(const Dims&, const void*, const void*, const 
                                    hipStream_t) {
   return refused();
 }
+bool sparse_mfma_stats_supported(const Dims&, int) { return false; }
+LaunchResult launch_sparse_mfma_stats(const Dims&, const void*, const void*, const void*, const int32_t*, int, float,
+                                      void*, float*, float*, float*, hipStream_t) {
+  return refused();
+}
+LaunchResult launch_sparse_stats_unfused(const Dims&, bool, const void*, const void*, const void*, const int32_t*, int,
+                                         float, void*, float*, float*, float*, hipStream_t) {
+  return refused();
+}
 hipError_t kv_frag_into(const Dims&, const void*, const void*, void*, void*, hipStream_t) {
   return hipErrorInvalidValue;
 }

@@ -246,3 +246,17 @@ def test_kv_frag_argument_checks(libssa):
         assert libssa.ssa_sparse_attn_fwd_frag(ctypes.byref(f32), F, F, F, None, None, F, 2, 0.1, F, None,
                                                None) == 5
         assert libssa.ssa_kv_frag(ctypes.byref(d), F, None, F, None, None) == 5
+
+
+def test_sparse_fwd_stats_argument_checks(libssa):
+    """The fused sparse measurements check like ssa_sparse_attn_fwd and need at least one
+    measurement output."""
+    d = _dims()
+    F = FAKE
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, F, 2, 0.1, F, None, None, None, None) == 1
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, None, 2, 0.1, F, None, F, None, None) == 1
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, F, 2, 0.1, None, None, F, None, None) == 1
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, F, 9, 0.1, F, None, F, None, None) == 2
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, F, 2, -0.1, F, None, None, F, None) == 4
+    assert libssa.ssa_sparse_attn_fwd_stats(ctypes.byref(d), F, F, F, F, 2, 0.1, F, None, MISALIGNED, None,
+                                            None) == 4

@@ -163,3 +163,73 @@ def test_align_retained_hist(dtype, D, s, topk, L, B, H):
         hi = (r < edge + tol).sum(axis=-1)
         assert np.all((lo <= below) & (below <= hi)), (m, below, lo, hi)
     print(f"[oracle] retained hist ok: {got.reshape(-1, 16)[0].tolist()}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,B,H,Hkv,L,D,s,topk,padded", [
+    (W.BF16, 1, 2, 2, 1024, 128, 64, 4, False),
+    (W.BF16, 2, 2, 1, 1152, 64, 128, 3, False),   # ragged last tile, 128-token blocks, grouped heads
+    (W.BF16, 1, 1, 1, 4096, 128, 64, 32, False),  # 32 entries per row, as in the long-context workload
+    (W.BF16, 1, 2, 2, 4096, 64, 64, 48, True),    # more than 32 entries per row, malformed entries
+    (W.BF16, 1, 2, 1, 1024, 128, 64, 16, False),  # k = n: every query chunk goes to the dense kernel
+    (W.F32, 1, 2, 2, 1024, 128, 64, 4, False),    # float32: the forward, then the measurement pass
+])
+def test_sparse_fwd_stats_fused(variant, dtype, B, H, Hkv, L, D, s, topk, padded):
+    """ssa_sparse_attn_fwd_stats: the sparse stream's entropy and distance histogram from
+    its own forward (bf16 matrix-core kernel, or the forward then the measurement pass)
+    against the oracle on the same idx; its o and lse those of ssa_sparse_attn_fwd."""
+    inp = W.make_qkv(B, H, L, D, s, dtype, "sink", seed=4800 + L + topk + D, hkv=Hkv)
+    q, k, v = (to_device(a, dtype) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    print(f"[case] fused sparse stats {dtype} B={B} H={H}/{Hkv} L={L} D={D} s={s} k={topk} padded={padded} "
+          f"variant={variant}", flush=True)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, topk)
+    if padded:
+        rng = np.random.default_rng(4900 + L)
+        g = idx.cpu().numpy()
+        hit = rng.random(g.shape) < 0.25
+        g = np.where(hit, np.where(rng.random(g.shape) < 0.5, -1, L // s + 7), g).astype(np.int32)
+        idx = torch.from_numpy(g).to(idx.device)
+    o, lse, ent, hist = ssa.sparse_attn_fwd_stats(q, k, v, idx, s, scale)
+    o2, lse2 = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+    torch.cuda.synchronize()
+    a, b = to_f64(o), to_f64(o2)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
+    np.testing.assert_allclose(to_f64(lse), to_f64(lse2), rtol=1e-6, atol=1e-6)
+    q64 = inp.as_f64("q")
+    k64 = inp.kv_per_query_head(inp.as_f64("k"))
+    ref_e, ref_h = O.attention_stats(q64, k64, s, scale, idx.cpu().numpy())
+    ge, gh = to_f64(ent), to_f64(hist)
+    err_e = float(np.abs(ge - ref_e).max())
+    err_h = float(np.abs(gh - ref_h).max())
+    print(f"[oracle] fused sparse stats: entropy {err_e:.2e} hist {err_h:.2e} (sum {gh.sum(-1).tolist()})", flush=True)
+    assert err_e <= 1e-3, err_e
+    assert err_h <= 1e-4 * L, err_h
+    np.testing.assert_allclose(gh.sum(axis=-1), L, rtol=1e-4)
+    # only one of the measurements
+    _, _, e_only, h_none = ssa.sparse_attn_fwd_stats(q, k, v, idx, s, scale, want_lse=False, want_hist=False)
+    assert h_none is None and float(np.abs(to_f64(e_only) - ref_e).max()) <= 1e-3
+
+
+def test_sparse_fwd_stats_recomputed_row():
+    """A kept key far above everything in the query's own block (logit gap ~75) sends the
+    row to the exact recompute; its measurements must come out exact too."""
+    B, H, L, D, s = 1, 1, 1024, 128, 64
+    inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=17)
+    qf, kf = W.bf16_bits_to_f32(inp.q), W.bf16_bits_to_f32(inp.k)
+    qf[0, 0, 900] = 0.0
+    qf[0, 0, 900, 0] = 30.0
+    kf[0, 0, 130] = 0.0
+    kf[0, 0, 130, 0] = 30.0
+    inp.q, inp.k = W.f32_to_bf16_bits(qf), W.f32_to_bf16_bits(kf)
+    q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
+    scale = 1.0 / math.sqrt(D)
+    print("[case] fused sparse stats, recomputed row", flush=True)
+    idx = ssa.block_topk(q, ssa.block_pool(k, s), s, 4)
+    assert 2 in idx[0, 0, 900].tolist()
+    _, _, ent, hist = ssa.sparse_attn_fwd_stats(q, k, v, idx, s, scale)
+    torch.cuda.synchronize()
+    ref_e, ref_h = O.attention_stats(inp.as_f64("q"), inp.as_f64("k"), s, scale, idx.cpu().numpy())
+    ge, gh = to_f64(ent), to_f64(hist)
+    assert abs(ge[0, 0, 900] - ref_e[0, 0, 900]) <= 1e-3
+    assert float(np.abs(ge - ref_e).max()) <= 1e-3
+    assert float(np.abs(gh - ref_h).max()) <= 1e-4 * L
