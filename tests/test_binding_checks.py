@@ -30,7 +30,12 @@ def code_of(fn):
     return e.value.code
 
 
+def u8(n):
+    return torch.zeros(n, dtype=torch.uint8)
+
+
 QKV = dict(q=bf(B, H, L, D), k=bf(B, H, L, D), v=bf(B, H, L, D))
+NFRAG = B * H * L * D * 2  # bytes of one fragment-order copy of k or v (bf16)
 
 
 @pytest.mark.parametrize("fn,code", [
@@ -66,6 +71,15 @@ QKV = dict(q=bf(B, H, L, D), k=bf(B, H, L, D), v=bf(B, H, L, D))
     (lambda: ssa.attn_stats(QKV["q"], QKV["k"], f32(B, H, L - 1), S), 2),
     (lambda: ssa.attn_stats(QKV["q"], f32(B, H, L, D), f32(B, H, L), S), 3),
     (lambda: ssa.attn_stats(QKV["q"], QKV["k"], f32(B, H, L), S, idx=i32(B, H, L)), 2),
+    # the fragment-order copies: sized by kv_frag_bytes, bytes (uint8), k and v alike
+    (lambda: ssa.kv_frag(QKV["k"], bf(B, H, L, D + 64), S), 2),
+    (lambda: ssa.kv_frag(QKV["k"], QKV["v"], S, k_frag=u8(NFRAG - 16)), 2),
+    (lambda: ssa.sparse_attn_fwd_frag(**QKV, k_frag=u8(NFRAG), v_frag=u8(NFRAG // 2), idx=i32(B, H, L, 2), block=S), 2),
+    (lambda: ssa.full_attn_fwd_frag(**QKV, v_frag=u8(NFRAG + 16)), 2),
+    (lambda: ssa.full_attn_fwd_frag(**QKV, v_frag=torch.zeros(NFRAG, dtype=torch.int8)), 3),
+    # the fused sparse measurements: the forward's own checks
+    (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L, 2), block=S, lse=f32(B, H, L + 1)), 2),
+    (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L), block=S), 2),
 ])
 def test_mismatched_tensor_raises_before_launch(fn, code):
     assert code_of(fn) == code
