@@ -29,6 +29,9 @@
 // running bucket mass is kept beside l and flushed to LDS when the bucket changes.  At
 // the end each row's bucket masses are divided by its l and summed over the workgroup's
 // rows into one partial per (b, h, tile), summed in a fixed order by a second kernel.
+// With a sparse stream's idx as well, only the rows of the chunks the workgroup writes are
+// measured (the sparse stream's measurements of those rows; a tile with none writes a zero
+// partial).
 #include <algorithm>
 
 #include "launch.hpp"

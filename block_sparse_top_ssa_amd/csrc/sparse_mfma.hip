@@ -42,6 +42,13 @@
 // launched next on the same stream over the rows t < (topk + 1) * s, writes it (it
 // keeps each row's O in registers, which gathered rows cannot).
 //
+// A second instance (STATS) also measures the sparse stream (App. H, Table A9: entropy;
+// App. K.2, p. 31: attention mass by distance) from the same probabilities: beside l each
+// row keeps sum p x (x = log2 p against m_ref; entropy = ln l - ln 2 sum p x / l) and its
+// mass in each block-distance bucket, and each tile sums its rows' bucket masses over l
+// into one partial.  That state takes 16 floats per row, so this instance runs on 192-row
+// tiles.
+//
 // m_ref is an attained logit of the row, so l >= 1 and nothing underflows.  If any
 // kept logit exceeds m_ref by more than kGuard (log2 units, i.e. exp would pass
 // 2^kGuard), the row is flagged and recomputed exactly by one wave with a running-max
