@@ -633,12 +633,14 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
   // 2^-8 (2^-9 + 2^-7.4) of it for D <= 128; so with Cauchy-Schwarz
   // |approx - score| <= 1.008 2^-8 |q| |kbar|, and eps = 1.02 2^-8 |q| max|kbar|
   // (the norms' own float32 rounding is far inside the difference).
-  u32x4 kh[NC];
-  auto load_hi = [&](int c) {
+  // two register sets of hi-term fragments, so the loads run two chunks ahead (the
+  // pass-2 fragment registers are free during this pass)
+  u32x4 khA[NC], khB[NC];
+  auto load_hi = [&](u32x4 (&kh)[NC], int c) {
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) kh[cc] = kst[((int64_t)c * 4 * NF + 3 * cc) * 64];
   };
-  auto mfma_hi = [&]() {
+  auto mfma_hi = [&](const u32x4 (&kh)[NC]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0, 0, 0, 0};
 #pragma unroll
@@ -667,13 +669,19 @@ __global__ __launch_bounds__(S * 4, 2) void topk_select_kernel(const uint16_t* _
         m1[nt][i] = max_f32(m1[nt][i], v);
       }
   };
-  load_hi(0);
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
-    mfma_hi();
-    if (chunk + 1 < nchunks) load_hi(chunk + 1);
-    else load_frags(0);  // pass 2 starts with chunk 0
+  load_hi(khA, 0);
+  if (nchunks > 1) load_hi(khB, 1);
+  for (int chunk = 0; chunk < nchunks; chunk += 2) {
+    mfma_hi(khA);
+    if (chunk + 2 < nchunks) load_hi(khA, chunk + 2);
     take_maxima(chunk * 64);
+    if (chunk + 1 < nchunks) {
+      mfma_hi(khB);
+      if (chunk + 3 < nchunks) load_hi(khB, chunk + 3);
+      take_maxima((chunk + 1) * 64);
+    }
   }
+  load_frags(0);  // pass 2 starts with chunk 0
   // to the selection layout: row r's classes 16 p .. +15 in lane (r, p)
   float c1[16], c2[16];
   auto to_rows = [&](const float (&mx)[NT][4], float (&out)[16]) {
