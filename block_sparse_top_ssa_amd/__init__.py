@@ -255,11 +255,31 @@ def full_attn_fwd_frag(q, k, v, v_frag, scale: float | None = None, want_o: bool
     return out, lse
 
 
+def _stats_outs(d: Dims, device, want_entropy, want_hist, entropy, hist, what):
+    """The measurement outputs: entropy [B, H, L] and hist [B, H, 16] in float32, the given
+    ones checked, the others allocated; None where not wanted."""
+    if not want_entropy:
+        entropy = None
+    elif entropy is None:
+        entropy = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=device)
+    else:
+        _expect(entropy, (d.B, d.H, d.L), torch.float32, device, what + " entropy")
+    if not want_hist:
+        hist = None
+    elif hist is None:
+        hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=device)
+    else:
+        _expect(hist, (d.B, d.H, 16), torch.float32, device, what + " hist")
+    return entropy, hist
+
+
 def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True, want_lse: bool = True,
                         want_entropy: bool = True, want_hist: bool = True, block: int = 64,
-                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+                        out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                        entropy: torch.Tensor | None = None, hist: torch.Tensor | None = None):
     """full_attn_fwd with the full stream's row entropy [B, H, L] and attention mass by
-    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist)."""
+    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist).  Every output
+    may be given (float32 for lse, entropy and hist), else it is allocated."""
     d = _dims(q, block, _kv_heads(q, k, v))
     scale = 1.0 / math.sqrt(d.D) if scale is None else float(scale)
     if want_o and out is None:
@@ -270,8 +290,7 @@ def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True
         lse = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device)
     if want_lse:
         _expect(lse, (d.B, d.H, d.L), torch.float32, q.device, "full_attn_fwd_stats lse")
-    ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
-    hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
+    ent, hist = _stats_outs(d, q.device, want_entropy, want_hist, entropy, hist, "full_attn_fwd_stats")
     check(load().ssa_full_attn_fwd_stats(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), ctypes.c_float(scale),
                                          _ptr(out if want_o else None), _ptr(lse if want_lse else None),
                                          _ptr(ent), _ptr(hist), _stream(q)))
@@ -280,12 +299,13 @@ def full_attn_fwd_stats(q, k, v, scale: float | None = None, want_o: bool = True
 
 def sparse_attn_fwd_stats(q, k, v, idx, block: int, scale: float | None = None, want_lse: bool = True,
                           want_entropy: bool = True, want_hist: bool = True, out: torch.Tensor | None = None,
-                          lse: torch.Tensor | None = None):
+                          lse: torch.Tensor | None = None, entropy: torch.Tensor | None = None,
+                          hist: torch.Tensor | None = None):
     """sparse_attn_fwd with the sparse stream's row entropy [B, H, L] and attention mass by
-    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist)."""
+    block distance [B, H, 16] from the same sweep: (o, lse, entropy, hist).  Every output
+    may be given (float32 for lse, entropy and hist), else it is allocated."""
     d, scale, out, lse = _sparse_args(q, k, v, idx, block, scale, want_lse, out, lse)
-    ent = torch.empty((d.B, d.H, d.L), dtype=torch.float32, device=q.device) if want_entropy else None
-    hist = torch.empty((d.B, d.H, 16), dtype=torch.float32, device=q.device) if want_hist else None
+    ent, hist = _stats_outs(d, q.device, want_entropy, want_hist, entropy, hist, "sparse_attn_fwd_stats")
     check(load().ssa_sparse_attn_fwd_stats(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(idx), int(idx.shape[3]),
                                            ctypes.c_float(scale), _ptr(out), _ptr(lse), _ptr(ent), _ptr(hist),
                                            _stream(q)))

@@ -80,6 +80,11 @@ NFRAG = B * H * L * D * 2  # bytes of one fragment-order copy of k or v (bf16)
     # the fused sparse measurements: the forward's own checks
     (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L, 2), block=S, lse=f32(B, H, L + 1)), 2),
     (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L), block=S), 2),
+    # caller-given measurement outputs: entropy [B, H, L] and hist [B, H, 16], float32
+    (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L, 2), block=S, entropy=f32(B, H, L - 1)), 2),
+    (lambda: ssa.sparse_attn_fwd_stats(**QKV, idx=i32(B, H, L, 2), block=S, hist=bf(B, H, 16)), 3),
+    (lambda: ssa.full_attn_fwd_stats(**QKV, block=S, hist=f32(B, H, 15)), 2),
+    (lambda: ssa.full_attn_fwd_stats(**QKV, block=S, entropy=f32(B, H, L, 1)), 2),
 ])
 def test_mismatched_tensor_raises_before_launch(fn, code):
     assert code_of(fn) == code

@@ -459,7 +459,7 @@ def test_bf16_L32768_gqa2():
 # ----------------------------------------------------------------------------------
 _PAD = 1024
 _SENTINEL = {torch.bfloat16: (torch.int16, 0x5A5A), torch.float32: (torch.int32, 0x5A5A5A5A),
-             torch.int32: (torch.int32, 0x5A5A5A5A)}
+             torch.int32: (torch.int32, 0x5A5A5A5A), torch.uint8: (torch.uint8, 0x5A)}
 
 
 def _guarded(shape, dtype):
@@ -487,10 +487,12 @@ def _guards_intact(big, shape):
     (1, 1, 4096, 128, 64, 48),   # long idx rows: the sparse kernel's row lists built in batches
 ])
 def test_outputs_guarded(variant, B, H, L, D, s, topk):
-    """Every output of the whole path written into a buffer with sentinel guard bands:
-    the bands stay intact, on the selection the path makes and on idx rows with a
-    quarter of the entries replaced by -1 or by blocks past the query's own block or past
-    the end; the outputs on the malformed rows match the oracle on the same rows."""
+    """Every output of the whole path written into a buffer with sentinel guard bands
+    (the fragment-order copies, the forwards that read them and the forwards with
+    measurements included): the bands stay intact, on the selection the path makes and on
+    idx rows with a quarter of the entries replaced by -1 or by blocks past the query's own
+    block or past the end; the outputs on the malformed rows match the oracle on the same
+    rows."""
     inp = W.make_qkv(B, H, L, D, s, W.BF16, "none", seed=19)
     say(f"[gpu] guarded {B}x{H}x{L}x{D} s={s} topk={topk}")
     q, k, v = (to_device(a, W.BF16) for a in (inp.q, inp.k, inp.v))
@@ -507,6 +509,22 @@ def test_outputs_guarded(variant, B, H, L, D, s, topk):
                         lse=out("lse_s", (B, H, L), torch.float32))
     ssa.full_attn_fwd(q, k, v, scale, block=s, out=out("o_f", q.shape, torch.bfloat16),
                       lse=out("lse_f", (B, H, L), torch.float32))
+    # the fragment-order copies, the forwards that read them, the forwards with measurements
+    nbytes = ssa.kv_frag_bytes(k, s)
+    kf, vf = ssa.kv_frag(k, v, s, k_frag=out("k_frag", (nbytes,), torch.uint8),
+                         v_frag=out("v_frag", (nbytes,), torch.uint8))
+    ssa.sparse_attn_fwd_frag(q, k, v, kf, vf, idx, s, scale, out=out("o_sf", q.shape, torch.bfloat16),
+                             lse=out("lse_sf", (B, H, L), torch.float32))
+    ssa.full_attn_fwd_frag(q, k, v, vf, scale, block=s, out=out("o_ff", q.shape, torch.bfloat16),
+                           lse=out("lse_ff", (B, H, L), torch.float32))
+    ssa.sparse_attn_fwd_stats(q, k, v, idx, s, scale, out=out("o_ss", q.shape, torch.bfloat16),
+                              lse=out("lse_ss", (B, H, L), torch.float32),
+                              entropy=out("ent_s", (B, H, L), torch.float32),
+                              hist=out("hist_s", (B, H, 16), torch.float32))
+    ssa.full_attn_fwd_stats(q, k, v, scale, block=s, out=out("o_fs", q.shape, torch.bfloat16),
+                            lse=out("lse_fs", (B, H, L), torch.float32),
+                            entropy=out("ent_f", (B, H, L), torch.float32),
+                            hist=out("hist_f", (B, H, 16), torch.float32))
     # malformed rows: a quarter of the entries become -1, a block past b_t, or past the end
     bad = idx.cpu().numpy().copy()
     rng = np.random.default_rng(20)
@@ -519,9 +537,18 @@ def test_outputs_guarded(variant, B, H, L, D, s, topk):
     bad_d = torch.from_numpy(bad.astype(np.int32)).cuda()
     o_bad, lse_bad = ssa.sparse_attn_fwd(q, k, v, bad_d, s, scale, out=out("o_bad", q.shape, torch.bfloat16),
                                          lse=out("lse_bad", (B, H, L), torch.float32))
+    o_bad_f, lse_bad_f = ssa.sparse_attn_fwd_frag(q, k, v, kf, vf, bad_d, s, scale,
+                                                  out=out("o_bad_f", q.shape, torch.bfloat16),
+                                                  lse=out("lse_bad_f", (B, H, L), torch.float32))
+    ssa.sparse_attn_fwd_stats(q, k, v, bad_d, s, scale, out=out("o_bad_s", q.shape, torch.bfloat16),
+                              lse=out("lse_bad_s", (B, H, L), torch.float32),
+                              entropy=out("ent_bad", (B, H, L), torch.float32),
+                              hist=out("hist_bad", (B, H, 16), torch.float32))
     torch.cuda.synchronize()
     for name, (big, _, shape) in bufs.items():
         assert _guards_intact(big, shape), f"{name}: write outside the output"
     o_ref, lse_ref = O.attend_sparse(inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v"), bad, s, scale)
     assert_close(to_f64(o_bad), o_ref, TOL[W.BF16], "o_sparse on malformed idx")
     assert_close(to_f64(lse_bad), lse_ref, TOL_LSE[W.BF16], "lse_sparse on malformed idx")
+    assert_close(to_f64(o_bad_f), o_ref, TOL[W.BF16], "o_sparse (frag) on malformed idx")
+    assert_close(to_f64(lse_bad_f), lse_ref, TOL_LSE[W.BF16], "lse_sparse (frag) on malformed idx")
