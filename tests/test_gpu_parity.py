@@ -41,15 +41,35 @@ def variant(request):
     ssa.set_kernel_variant(prev)
 
 
-def gpu_pipeline(inp: W.Inputs, topk: int, lse_only_full=False, tag=""):
+def gpu_pipeline(inp: W.Inputs, topk: int, lse_only_full=False, tag="", frag=False):
+    """The whole path on the GPU.  With frag (bf16), the forwards run as bench.py times
+    them: k and v written once by kv_frag, then the _frag forms; their outputs are also
+    held to the default calls' on the same idx (the dense forward's bits, the sparse
+    forward's within one bf16 step: its partial sums may be added in another order)."""
     w = inp.workload
     s, scale = w.s, 1.0 / math.sqrt(w.D)
-    say(f"[gpu] {tag} B={w.B} H={w.H} L={w.L} D={w.D} s={s} topk={topk} dtype={w.dtype}")
+    say(f"[gpu] {tag} B={w.B} H={w.H} L={w.L} D={w.D} s={s} topk={topk} dtype={w.dtype} frag={frag}")
     q, k, v = (to_device(a, w.dtype) for a in (inp.q, inp.k, inp.v))
     km = ssa.block_pool(k, s)
     idx, sel = ssa.block_topk(q, km, s, topk, want_scores=True)
-    o_s, lse_s = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
-    o_f, lse_f = ssa.full_attn_fwd(q, k, v, scale, want_o=not lse_only_full, block=s)
+    if frag:
+        kf, vf = ssa.kv_frag(k, v, s)
+        o_s, lse_s = ssa.sparse_attn_fwd_frag(q, k, v, kf, vf, idx, s, scale)
+        o_f, lse_f = ssa.full_attn_fwd_frag(q, k, v, vf, scale, want_o=not lse_only_full, block=s)
+        del kf, vf
+        o_s2, lse_s2 = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+        o_f2, lse_f2 = ssa.full_attn_fwd(q, k, v, scale, want_o=not lse_only_full, block=s)
+        torch.cuda.synchronize()
+        assert torch.equal(lse_f, lse_f2) and (o_f is None or torch.equal(o_f.view(torch.int16),
+                                                                          o_f2.view(torch.int16)))
+        step = (o_s.float() - o_s2.float()).abs() <= 2.0 ** -7 * torch.maximum(o_s.float().abs(),
+                                                                               o_s2.float().abs()) + 1e-6
+        assert bool(step.all()), "sparse _frag form and default call differ by more than one bf16 step"
+        torch.testing.assert_close(lse_s, lse_s2, rtol=1e-6, atol=1e-6)
+        del o_s2, lse_s2, o_f2, lse_f2
+    else:
+        o_s, lse_s = ssa.sparse_attn_fwd(q, k, v, idx, s, scale)
+        o_f, lse_f = ssa.full_attn_fwd(q, k, v, scale, want_o=not lse_only_full, block=s)
     if o_f is not None:
         dist, drop = ssa.align_stats(o_f, o_s, lse_f, lse_s, block=s)
     else:
@@ -217,7 +237,7 @@ def test_bf16_L4096_lowrank_all_rows(variant):
 def test_bf16_L8192_ksweep(topk):
     inp = _inputs("bf16_L8192_ksweep")
     w = inp.workload
-    g = gpu_pipeline(inp, topk, tag=f"bf16_L8192_ksweep k={topk}")
+    g = gpu_pipeline(inp, topk, tag=f"bf16_L8192_ksweep k={topk}", frag=True)
     rows = W.sample_rows(w.L, w.s, topk, w.sample_rows, seed=w.seed + topk)
     rep = _oracle_checks(inp, g, topk, rows=rows, check_idx=False)
     # selection on every row
@@ -418,13 +438,14 @@ def test_full_stream_growing_logits(variant):
 
 
 # ----------------------------------------------------------------------------------
-# long-context workloads: sampled rows for outputs, selection on every row
+# long-context workloads, in bench.py's launch configuration: sampled rows for outputs,
+# selection on every row
 # ----------------------------------------------------------------------------------
 def _big(name, head_groups):
     inp = _inputs(name)
     w = inp.workload
     topk = w.ks[0]
-    g = gpu_pipeline(inp, topk, lse_only_full=w.sparse_only, tag=name)
+    g = gpu_pipeline(inp, topk, lse_only_full=w.sparse_only, tag=name, frag=True)
     rows = W.sample_rows(w.L, w.s, topk, w.sample_rows, seed=w.seed)
     _oracle_checks(inp, g, topk, rows=rows, lse_only_full=w.sparse_only, check_idx=False)
     q64 = inp.as_f64("q")
