@@ -9,21 +9,45 @@
 
 namespace ssa {
 
+// ---------------------------------------------------------------- one chunk through LDS
+// The 64 rows of a 64-key chunk (contiguous in a [B,H,L,D] tensor) read with 16-byte
+// loads of consecutive words, so each wave instruction moves 1 KB of whole cache lines,
+// into LDS rows of D/8 + 1 words (the extra word staggers the rows over the banks).
+// Both copies below then take each lane's 16 bytes, one word of one row, from LDS.
+template <int D>
+struct ChunkTile {
+  static constexpr int RW = D / 8, RS = RW + 1;  // 16-byte words per row; LDS row stride
+  u32x4 w[64 * RS];
+};
+template <int D>
+__device__ __forceinline__ void stage_chunk(ChunkTile<D>& t, const uint16_t* __restrict__ x, int64_t bh, int L,
+                                            int c) {
+  constexpr int RW = ChunkTile<D>::RW, RS = ChunkTile<D>::RS;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + (bh * (int64_t)L + 64 * c) * D);
+#pragma unroll
+  for (int i = threadIdx.x; i < 64 * RW; i += 256) t.w[(i / RW) * RS + i % RW] = src[i];
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------- V in fragment order
 // Fragment (chunk c, d tile dt, key half kc) of a head: 64 lanes x 16 bytes; lane
 // l = 16 g + i holds V[64 c + kappa(kc, g, 0..7)][16 dt + i], the A operand of
-// O^T = V^T P^T.  One workgroup per 64-key chunk.
+// O^T = V^T P^T.  One workgroup per 64-key chunk: lane 16 g + 8 h + p takes row
+// kappa(kc, g, p), columns 16 dt + 8 h .. +7, and an 8x8 transpose inside each group of
+// 8 lanes turns rows into columns.
 template <int D>
 __global__ __launch_bounds__(256) void vfrag_kernel(const uint16_t* __restrict__ v, u32x4* __restrict__ vt, int L) {
-  constexpr int F = 2 * (D / 16);  // fragments per chunk
+  constexpr int F = 2 * (D / 16), RS = ChunkTile<D>::RS;  // fragments per chunk
+  __shared__ ChunkTile<D> tile;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, h = (lane >> 3) & 1, p = lane & 7;
   const int64_t chunk = blockIdx.x;  // over B*H*(L/64), head-major
   const int nck = L / 64;
-  const int64_t bh = chunk / nck;
-  const int c = (int)(chunk % nck);
-  const uint16_t* vh = v + bh * (int64_t)L * D;
-  for (int f = w; f < F; f += 4)
-    vt[(chunk * F + f) * 64 + lane] = transpose8x8_b16_dpp(load_v_raw<D>(vh, c * 64, f >> 1, f & 1));
+  stage_chunk<D>(tile, v, chunk / nck, L, (int)(chunk % nck));
+  for (int f = w; f < F; f += 4) {
+    const int dt = f >> 1, kc = f & 1;
+    vt[(chunk * F + f) * 64 + lane] = transpose8x8_b16_dpp(tile.w[kappa(kc, g, p) * RS + 2 * dt + h]);
+  }
 }
 
 // ---------------------------------------------------------------- K in fragment order
@@ -33,14 +57,14 @@ __global__ __launch_bounds__(256) void vfrag_kernel(const uint16_t* __restrict__
 // lines) instead of 16 half lines of K's rows.  One workgroup per 64-key chunk.
 template <int D>
 __global__ __launch_bounds__(256) void kfrag_kernel(const uint16_t* __restrict__ k, u32x4* __restrict__ kt, int L) {
-  constexpr int F = 4 * (D / 32);  // fragments per chunk
+  constexpr int NC = D / 32, F = 4 * NC, RS = ChunkTile<D>::RS;  // fragments per chunk
+  __shared__ ChunkTile<D> tile;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t chunk = blockIdx.x;  // over B*H*(L/64), head-major
   const int nck = L / 64;
-  const int64_t bh = chunk / nck;
-  const int c = (int)(chunk % nck);
-  const uint16_t* kh = k + bh * (int64_t)L * D;
-  for (int f = w; f < F; f += 4) kt[(chunk * F + f) * 64 + lane] = load_k_frag<D>(kh, c * 64 + 16 * (f / (D / 32)), f % (D / 32));
+  stage_chunk<D>(tile, k, chunk / nck, L, (int)(chunk % nck));
+  for (int f = w; f < F; f += 4)
+    kt[(chunk * F + f) * 64 + lane] = tile.w[(16 * (f / NC) + (lane & 15)) * RS + 4 * (f % NC) + (lane >> 4)];
 }
 
 // ---------------------------------------------------------------- workspace
