@@ -12,8 +12,10 @@ namespace ssa {
 // ---------------------------------------------------------------- one chunk through LDS
 // The 64 rows of a 64-key chunk (contiguous in a [B,H,L,D] tensor) read with 16-byte
 // loads of consecutive words, so each wave instruction moves 1 KB of whole cache lines,
-// into LDS rows of D/8 + 1 words (the extra word staggers the rows over the banks).
-// Both copies below then take each lane's 16 bytes, one word of one row, from LDS.
+// into LDS rows of D/8 + 1 words (the extra word staggers neighbouring rows over the
+// banks; rows 16 apart still meet, a 2-way conflict on the fragment reads that costs
+// nothing next to the HBM traffic).  Both copies below then take each lane's 16 bytes,
+// one word of one row, from LDS.
 template <int D>
 struct ChunkTile {
   static constexpr int RW = D / 8, RS = RW + 1;  // 16-byte words per row; LDS row stride
